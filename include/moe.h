@@ -1,0 +1,185 @@
+/*
+ * moe.h -- C ABI of libmoe: the routed int4 Mixture-of-Experts FFN layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one the pages walk through per transformer layer and
+ * token (es.news.hada.io, "Proceso de generacion de tokens"; yodev.dev,
+ * "Por que funciona: el A4B del nombre"; imasters.com.br, "O truque"):
+ * an 8-bit router scores the experts from resident weights, the top 8 of 128
+ * are selected, the selected 4-bit experts (MLX affine, group 64) run as GLU
+ * blocks, and their gate-weighted outputs are combined with a resident shared
+ * expert.  Prefill works on chunks of up to 128 tokens so that an expert
+ * fetched once serves several rows (es.news.hada.io, same section).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers marked "device" are HBM addresses (hipMalloc / torch tensors);
+ * "host" pointers are ordinary process memory.  The caller owns every buffer
+ * passed in; the library keeps no pointer past the call except inside a pool
+ * (moe_pool_create).  Calls are asynchronous on `stream` (a hipStream_t; NULL
+ * is the default stream) unless stated otherwise.  Arguments are validated
+ * before anything is launched: a negative status means nothing was enqueued.
+ * MOE_E_HIP reports a HIP runtime error from a launch or copy; device faults
+ * surface at the caller's next synchronisation.  No call aborts and no C++
+ * exception crosses this boundary.  Results are bitwise reproducible: every
+ * reduction has a fixed order and no floating-point atomics are used.
+ *
+ * Quantised matrix storage (W[rows, cols], w = scale * q + bias per 64
+ * consecutive columns of a row; codes unsigned, bits in {4, 8}):
+ *   codes: 16-byte chunks of 128/bits consecutive columns of one row; chunk
+ *          (r, cc) at byte (cc * rows + r) * 16; the code of the j-th column
+ *          of a chunk at bits [bits*j, bits*j+bits) of the little-endian chunk.
+ *   meta:  u32 [cols/64][rows]; bits 0-15 fp16 scale, bits 16-31 fp16 bias.
+ * Expert blob (4-bit GLU expert, model width D, hidden width F): sections
+ *   gate.codes [F,D] | up.codes [F,D] | down.codes [D,F] | gate.meta |
+ *   up.meta | down.meta, each 256-byte aligned; moe_blob_bytes gives the size
+ *   (3,345,408 bytes at D = 2816, F = 704: the pages' "3.36 MB" per expert,
+ *   hndistilled.com, "Enfoque tecnico").
+ * Expert FFN: y = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T, fp32 accumulation.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_E_INVALID (-1)     /* bad argument: null pointer, shape, dtype, k   */
+#define MOE_E_UNSUPPORTED (-2) /* valid but not implemented (e.g. bits = 2)     */
+#define MOE_E_HIP (-3)         /* a HIP runtime call failed                     */
+#define MOE_E_WORKSPACE (-4)   /* ws_bytes smaller than moe_workspace_bytes()   */
+#define MOE_E_POOL (-5)        /* expert pool misuse or copy failure            */
+
+#define MOE_F16 1
+#define MOE_BF16 2
+#define MOE_F32 3
+
+/* One affine-quantised matrix (layout above).  Router: rows = E, cols = D,
+ * bits = 8 (es.news.hada.io, "Estructura de ejecucion...": 8-bit router). */
+typedef struct moe_qmat {
+  const void *codes; /* device, rows*cols*bits/8 bytes, 16-byte aligned */
+  const void *meta;  /* device, (cols/64)*rows u32 words */
+  int32_t rows, cols, bits;
+} moe_qmat;
+
+/* A bank of E GLU experts of shape (D, F), one blob per expert. */
+typedef struct moe_bank {
+  const void *const *blobs; /* DEVICE array [E] of device blob pointers (256-B aligned) */
+  int32_t E, D, F;
+} moe_bank;
+
+typedef struct moe_pool moe_pool;
+
+typedef struct moe_pool_stats {
+  uint64_t lookups;     /* expert uses served (tokens * k)          */
+  uint64_t hits;        /* uses already resident in an HBM slot     */
+  uint64_t misses;      /* uses copied host -> HBM                  */
+  uint64_t evictions;   /* resident experts replaced                */
+  uint64_t bytes_h2d;   /* bytes copied host -> HBM                 */
+} moe_pool_stats;
+
+/* Size of one expert blob in bytes. */
+size_t moe_blob_bytes(int32_t D, int32_t F);
+
+/* Scratch bytes `ws` must hold for calls with these sizes (F_shared = 0: no
+ * shared expert).  The same workspace serves moe_route, moe_expert_ffn and
+ * moe_layer_forward at or below these sizes.  It must be zero-filled before
+ * its first use; every call leaves its synchronisation counters at zero.
+ * Two calls that overlap in time must not share a workspace. */
+size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t D, int32_t F,
+                           int32_t F_shared);
+
+/* Router and selection (es.news.hada.io, "Proceso de generacion de tokens":
+ * top-8 expert IDs per layer; stork.ai blog, "Por que la mayor parte...":
+ * 8 of 128 experts).  logits[t,e] = x[t] . Wr[e] + logit_bias[e] (fp32);
+ * ids[t, 0..k) are the k largest logits, largest first, equal logits to the
+ * lower index; gates[t, :] = softmax of the selected logits.
+ *   x         device [T, D] fp16 or bf16 (x_dtype MOE_F16 / MOE_BF16), 16-byte
+ *             aligned (every call that takes x requires this)
+ *   router    8-bit matrix [E, D], D % 64 == 0, 1 <= E <= 1024
+ *   logit_bias device [E] fp32 or NULL;  1 <= k <= min(E, 64)
+ *   ids       device [T, k] int32;  gates device [T, k] fp32
+ *   logits    device [T, E] fp32 or NULL
+ *   ws        device scratch of moe_workspace_bytes(T, k, E, D, 64, 0) bytes */
+moe_status moe_route(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *router,
+                     const float *logit_bias, int32_t k, int32_t *ids, float *gates,
+                     float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFN of every (token, slot) pair: y[t, j, :] = FFN_{ids[t,j]}(x[t]).
+ *   bank      experts of shape (D, F); D, F multiples of 64
+ *   ids       device [T, k] int32 in [0, E), or NULL: every row uses expert 0
+ *             and k must be 1 (the shared expert)
+ *   y         device [T, k, D] fp32
+ *   ws        device scratch of moe_workspace_bytes(T, k, E, D, F, 0) bytes */
+moe_status moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_bank *bank,
+                          const int32_t *ids, int32_t k, float *y, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Combine (es.news.hada.io, "Proceso de generacion de tokens": the shared and
+ * routed outputs are combined): out[t] = y_shared[t] + sum_j gates[t,j] y[t,j],
+ * summed in j order.  y device [T,k,D] fp32; gates device [T,k] fp32;
+ * y_shared device [T,D] fp32 or NULL; out device [T,D] of out_dtype
+ * (MOE_F32, MOE_BF16 or MOE_F16, round to nearest even). */
+moe_status moe_combine(const float *y, const float *gates, const float *y_shared, int32_t T,
+                       int32_t k, int32_t D, void *out, int32_t out_dtype, void *stream);
+
+/* Token -> expert permutation of a prefill chunk (chunks of up to 128 tokens
+ * let one fetched expert serve several rows: es.news.hada.io, "Proceso de
+ * generacion de tokens").  counts[e] = pairs routed to e; offsets = exclusive
+ * prefix sum (E + 1 entries); perm[p] = flat index t*k + j of the p-th pair in
+ * (expert, flat index) order; inv[t*k + j] = its position.  All device int32;
+ * T * k <= 65536. */
+moe_status moe_permute(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv, void *stream);
+
+/* The whole layer: route, run the selected experts and the shared expert,
+ * combine.  out device [T, D] (out_dtype); ids_out / gates_out device [T, k]
+ * or NULL.  shared may be NULL (no shared expert) or a bank with E = 1.
+ * pool == NULL: `routed` holds all E experts resident in HBM.  pool != NULL:
+ * `routed` may be NULL; the experts of layer `layer` are served from the
+ * pool's HBM slots, missing ones copied from pinned host memory on the
+ * pool's side stream while the shared expert runs; this call then blocks the
+ * host once to read the selected ids back (the pages' CPU fetch plan:
+ * es.news.hada.io, "Proceso de generacion de tokens"). */
+moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *router,
+                             const float *logit_bias, int32_t k, const moe_bank *routed,
+                             const moe_bank *shared, moe_pool *pool, int32_t layer, void *out,
+                             int32_t out_dtype, int32_t *ids_out, float *gates_out, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* HBM expert slot pool (per layer `slots` blobs in HBM; least-frequently-used
+ * replacement: stork.ai blog, "Mas inteligente que tu RAM"; 16 slots per
+ * layer: hndistilled.com, "Enfoque tecnico").  host_blobs is a HOST array of
+ * n_layers * E pointers to page-locked host memory (hipHostMalloc), blob of
+ * layer l, expert e at [l * E + e]; the blobs must outlive the pool.  The
+ * pool owns its slots, pointer tables, side stream and events.  Requires
+ * slots >= k of every forward call.  Single host thread. */
+moe_status moe_pool_create(moe_pool **pool, int32_t n_layers, int32_t slots, int32_t E,
+                           int32_t D, int32_t F, const void *const *host_blobs);
+moe_status moe_pool_destroy(moe_pool *pool);
+moe_status moe_pool_get_stats(const moe_pool *pool, moe_pool_stats *stats);
+moe_status moe_pool_reset_stats(moe_pool *pool);
+
+/* Host-only replay of the pool's replacement policy, for tests without a GPU:
+ * ids host [n_tokens, k]; events host [n_tokens, k, 4] receives (expert,
+ * slot, hit 0/1, evicted expert or -1) in ids order. */
+moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
+                          const int32_t *ids, int32_t *events);
+
+/* Tuning knobs of the launch shapes ("glu_ks", "down_ks", ...); returns
+ * MOE_E_INVALID for an unknown key or value.  Process-wide. */
+moe_status moe_set_tuning(const char *key, int32_t value);
+
+/* Static text for a status code. */
+const char *moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,227 @@
+// Device helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+  return __uint_as_float((bits & 0xFFFFu) << 16);
+}
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Two-element dot product with fp32 accumulation: v_dot2c_f32_{bf16,f16}.
+template <bool F16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
+template <>
+__device__ __forceinline__ float dot2<false>(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+template <>
+__device__ __forceinline__ float dot2<true>(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                c, false);
+}
+
+// Global-address-space views: loads through them are global_load (not flat).
+template <class T>
+using gptr = const __attribute__((address_space(1))) T *;
+template <class T>
+__device__ __forceinline__ gptr<T> as_global(const T *p) {
+  return (gptr<T>)(p);
+}
+
+// A register holding v with its value hidden from the optimiser, so that the
+// mask-and-insert of the code unpacking stays one v_and_or_b32 (gfx9 VOP3
+// takes no literal operand).
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// 4-bit codes to a pair of 16-bit floats without a conversion instruction:
+// OR-ing a nibble into the mantissa of 128.0 (bf16 0x4300) gives 128 + q
+// exactly; for fp16 the base is 1024.0 (0x6400).  Word w holds the codes of 8
+// consecutive columns, nibble i = column i; (w >> 4m) & 0x000F000F selects
+// columns m and m + 4, so the activation pairs are (x[m], x[m + 4]).
+template <bool F16>
+struct Magic;
+template <>
+struct Magic<false> {
+  static constexpr uint32_t bits = 0x43004300u;
+  static constexpr float offset = 128.0f;
+};
+template <>
+struct Magic<true> {
+  static constexpr uint32_t bits = 0x64006400u;
+  static constexpr float offset = 1024.0f;
+};
+
+// sum over the 32 columns of one 16-byte chunk of (offset + q) * x, with the
+// activation pairs xw[i * 4 + m] = (x[8i + m], x[8i + m + 4]).
+template <bool F16>
+__device__ __forceinline__ float dot_chunk(const u32x4 q, const uint32_t *xw, float acc,
+                                           uint32_t magic) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t qp = ((w[i] >> (4 * m)) & 0x000F000Fu) | magic;
+      acc = dot2<F16>(xw[i * 4 + m], qp, acc);
+    }
+  }
+  return acc;
+}
+
+// Same with the activation split as hi + lo bf16 halves: xw[i*8 + m] are the
+// hi pairs, xw[i*8 + 4 + m] the lo pairs of word i.
+__device__ __forceinline__ float dot_chunk_hilo(const u32x4 q, const uint32_t *xw, float acc,
+                                                uint32_t magic) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t qp = ((w[i] >> (4 * m)) & 0x000F000Fu) | magic;
+      acc = dot2<false>(xw[i * 8 + m], qp, acc);
+      acc = dot2<false>(xw[i * 8 + 4 + m], qp, acc);
+    }
+  }
+  return acc;
+}
+
+// View of global memory through the constant address space: wave-uniform
+// loads through it become scalar loads into SGPRs.  Only for data written by
+// an earlier kernel (the scalar cache does not see stores of the same kernel).
+template <class T>
+using const_ptr = const __attribute__((address_space(4))) T *;
+template <class T>
+__device__ __forceinline__ const_ptr<T> as_const(const T *p) {
+  return (const_ptr<T>)(p);
+}
+
+// Copy N wave-uniform words into registers (scalar loads).
+template <int N>
+__device__ __forceinline__ void load_uniform(const uint32_t *src, uint32_t (&dst)[N]) {
+  const_ptr<uint32_t> p = as_const(src);
+#pragma unroll
+  for (int i = 0; i < N; ++i) dst[i] = p[i];
+}
+
+// Device-coherent handoff between blocks without a full-cache fence: the
+// producer writes with device-scope stores (they bypass the XCD-private L2),
+// waits for them to complete, then bumps a counter with a device-scope atomic;
+// a consumer that sees the count reads with device-scope loads.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t *p) {
+  return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all outstanding memory operations of this wave have completed
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Sum over 64 codes (two chunks) of q * h with fp32 products: the codes are
+// spread to bytes and converted exactly (v_cvt_f32_ubyte*), h is fp32 and
+// wave-uniform.  Word i of chunk c holds columns 8i..8i+7 of the chunk.
+__device__ __forceinline__ float dot_group_f32(const u32x4 q0, const u32x4 q1, const float *h) {
+  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t ev = w[i] & 0x0F0F0F0Fu;         // columns 8i, 8i+2, 8i+4, 8i+6
+    const uint32_t od = (w[i] >> 4) & 0x0F0F0F0Fu;  // columns 8i+1, 8i+3, 8i+5, 8i+7
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc = fmaf((float)((ev >> (8 * b)) & 0xFFu), h[8 * i + 2 * b], acc);
+      acc = fmaf((float)((od >> (8 * b)) & 0xFFu), h[8 * i + 2 * b + 1], acc);
+    }
+  }
+  return acc;
+}
+
+template <int N>
+__device__ __forceinline__ void load_uniform_f(const float *src, float (&dst)[N]) {
+  const_ptr<float> p = as_const(src);
+#pragma unroll
+  for (int i = 0; i < N; ++i) dst[i] = p[i];
+}
+
+// Wave-wide reductions through DPP row operations (no LDS round trips).  The
+// combination order is fixed, so results are bitwise reproducible; every lane
+// receives lane 63's total.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v, float identity) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int v, int identity) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xF, false);
+}
+// quad_perm xor 1, xor 2; row_half_mirror; row_mirror; row_bcast15; row_bcast31
+#define MOE_DPP_REDUCE(T, v, op, id, dpp)                 \
+  v = op(v, dpp<0xB1>(v, id));                            \
+  v = op(v, dpp<0x4E>(v, id));                            \
+  v = op(v, dpp<0x141>(v, id));                           \
+  v = op(v, dpp<0x140>(v, id));                           \
+  v = op(v, dpp<0x142, 0xA>(v, id));                      \
+  v = op(v, dpp<0x143, 0xC>(v, id));
+
+__device__ __forceinline__ float f_add(float a, float b) { return a + b; }
+__device__ __forceinline__ int i_min(int a, int b) { return a < b ? a : b; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+  MOE_DPP_REDUCE(float, v, f_add, 0.0f, dpp_f32)
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  MOE_DPP_REDUCE(float, v, fmaxf, -INFINITY, dpp_f32)
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ int wave_min(int v) {
+  MOE_DPP_REDUCE(int, v, i_min, 0x7FFFFFFF, dpp_i32)
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2 / pi)
+  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+
+}  // namespace moe

@@ -1,0 +1,114 @@
+// Internal declarations of libmoe (HIP, gfx950).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 64;      // columns per scale/bias pair (MLX affine group 64)
+constexpr size_t kAlign = 256;  // section alignment inside a blob and the workspace
+constexpr int kMaxE = 1024;     // router width handled by the top-k wave
+constexpr int kMaxK = 64;       // experts per token
+constexpr int kMaxKS = 16;      // split of a reduction over blocks
+constexpr int kMaxSplitBlocks = 4096;  // blocks of a split launch (partial tiles)
+
+__host__ __device__ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets of the sections of one 4-bit GLU expert blob (D model width,
+// F hidden width): gate.codes, up.codes, down.codes, gate.meta, up.meta,
+// down.meta, each 256-byte aligned.
+struct BlobLayout {
+  size_t gate_codes, up_codes, down_codes, gate_meta, up_meta, down_meta, total;
+};
+
+__host__ __device__ inline BlobLayout blob_layout(int D, int F) {
+  BlobLayout L;
+  const size_t cb = (size_t)F * D / 2;        // 4-bit codes of [F, D] or [D, F]
+  const size_t mb = (size_t)(D / kGroup) * F * 4;
+  const size_t mbd = (size_t)(F / kGroup) * D * 4;
+  size_t off = 0;
+  L.gate_codes = off; off = align_up(off + cb);
+  L.up_codes = off;   off = align_up(off + cb);
+  L.down_codes = off; off = align_up(off + cb);
+  L.gate_meta = off;  off = align_up(off + mb);
+  L.up_meta = off;    off = align_up(off + mb);
+  L.down_meta = off;  off = align_up(off + mbd);
+  L.total = off;
+  return L;
+}
+
+// Launch-shape knobs (moe_set_tuning).
+struct Tuning {
+  int glu_ks = 0;      // 0: chosen from the problem size
+  int down_ks = 0;
+  int route_rows = 8;  // experts per router block
+};
+Tuning &tuning();
+
+// Workspace carve-up for one call.  Every region is 256-byte aligned.
+struct Workspace {
+  uint32_t *xp;        // x as dot2 pairs [T][D/2]
+  float *xs;           // x group sums [T][D/64]
+  float *logits;       // [T][E]
+  int32_t *ids;        // [T][k]
+  const void **slot_blob;  // [T][k]
+  float *gates;        // [T][k]
+  float *h;            // GLU output, one float per hidden unit
+  float *hs;           // h group sums, one float per 64 hidden units
+  float *part;         // split-reduction partials
+  uint32_t *counters;  // last-block-done counters (zero between calls)
+  int32_t *perm_counts, *perm_offsets, *perm, *perm_inv;
+  size_t total;
+};
+
+struct Dims {
+  int T, k, E, D, F, Fs;
+};
+
+Workspace carve_workspace(void *base, const Dims &d);
+size_t workspace_bytes(const Dims &d);
+
+// Host-side launchers (return hipError_t of the launch).
+struct RouteLaunch {
+  const void *x; int f16x; int T, D, E, k;
+  const uint8_t *codes; const uint32_t *meta;
+  const float *logit_bias;
+  float *logits; int32_t *ids; float *gates;
+  uint32_t *xp; float *xs; uint32_t *counters;
+  const void *const *table;           // routed bank (for slot_blob) or null
+  const void **slot_blob;             // [T][k] blob of each selected expert, or null
+};
+hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
+// x pairs and 64-column sums for the expert kernels without routing
+hipError_t launch_prep_x(const void *x, int f16x, int T, int D, uint32_t *xp, float *xs,
+                         hipStream_t s);
+
+struct ExpertLaunch {
+  int f16x; int T, k, D, E;           // E: experts in the routed bank (ids range)
+  const uint32_t *xp; const float *xs;
+  const int32_t *ids;                 // [T][k] or null (expert 0)
+  const void *const *slot_blob;       // [T][k] blob per slot (from the router) or null
+  const float *gates;                 // [T][k] (combine mode)
+  const void *const *rblobs; int F;   // routed bank
+  const void *const *sblobs; int Fs;  // shared bank or null (Fs = 0)
+  float *h; float *hs; float *part; uint32_t *counters;
+  // outputs: y [T*k][D] (per-slot mode) or out [T][D] (combine mode)
+  float *y; void *out; int out_dtype;
+  int glu_first, glu_count;           // GLU block range: routed tiles first, then shared
+  int glu_ks;                         // reduction split of the GLU (0: from glu_count)
+};
+int pick_ks(int blocks, int reduce_len, int min_ks, int override_ks);
+int glu_min_ks(int D);
+int glu_blocks(const ExpertLaunch &a);
+hipError_t launch_glu(const ExpertLaunch &a, hipStream_t s);
+hipError_t launch_down(const ExpertLaunch &a, bool combine, hipStream_t s);
+hipError_t launch_combine(const float *y, const float *gates, const float *ys, int T, int k,
+                          int D, void *out, int out_dtype, hipStream_t s);
+hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
+                          int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);
+
+}  // namespace moe

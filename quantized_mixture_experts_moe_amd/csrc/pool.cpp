@@ -1,0 +1,248 @@
+// HBM expert slot pool: per-layer slots refilled from pinned host memory.
+//
+// The pages keep 16 expert slots per layer, plan the fetches of each token's
+// top-8 experts on the CPU against a least-frequently-used cache, and read the
+// misses while the GPU computes the resident shared expert (es.news.hada.io,
+// "Proceso de generacion de tokens"; stork.ai blog, "Mas inteligente que tu
+// RAM"; yodev.dev, "El loop por token").  On MI355X the slots live in HBM and
+// the misses come from page-locked host memory by hipMemcpyAsync on a side
+// stream; the main stream waits on an event before the routed experts run.
+#include "pool.h"
+
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+namespace moe {
+
+LfuPlanner::LfuPlanner(int slots, int E)
+    : slots_(slots), count_(E, 0), last_(E, -1), slot_of_(E, -1), expert_in_(slots, -1) {}
+
+bool LfuPlanner::access(const int *experts, int n, std::vector<Event> *events) {
+  if (n > slots_) return false;
+  for (int i = 0; i < n; ++i) {
+    count_[experts[i]] += 1;
+    last_[experts[i]] = now_;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int e = experts[i];
+    if (slot_of_[e] >= 0) {
+      if (events) events->push_back({e, slot_of_[e], 1, -1});
+      continue;
+    }
+    int slot = -1, victim = -1;
+    for (int s = 0; s < slots_; ++s) {
+      if (expert_in_[s] < 0) {
+        slot = s;
+        break;
+      }
+    }
+    if (slot < 0) {
+      for (int s = 0; s < slots_; ++s) {
+        const int v = expert_in_[s];
+        bool needed = false;
+        for (int j = 0; j < n; ++j) needed |= experts[j] == v;
+        if (needed) continue;
+        if (victim < 0 || count_[v] < count_[victim] ||
+            (count_[v] == count_[victim] && last_[v] < last_[victim])) {
+          victim = v;
+          slot = s;
+        }
+      }
+      if (slot < 0) return false;
+      slot_of_[victim] = -1;
+    }
+    expert_in_[slot] = e;
+    slot_of_[e] = slot;
+    if (events) events->push_back({e, slot, 0, victim});
+  }
+  ++now_;
+  return true;
+}
+
+}  // namespace moe
+
+struct moe_pool {
+  int n_layers = 0, slots = 0, E = 0, D = 0, F = 0;
+  size_t blob_bytes = 0;
+  std::vector<const void *> host_blobs;       // [n_layers * E], pinned host
+  std::vector<moe::LfuPlanner> planners;      // per layer
+  uint8_t *slot_mem = nullptr;                // device [n_layers][slots][blob]
+  const void **d_tables = nullptr;            // device [n_layers][E] blob pointers
+  const void **h_tables = nullptr;            // pinned host mirror of d_tables
+  int32_t *h_ids = nullptr;                   // pinned host ids of the last call
+  int ids_cap = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_ids = nullptr, ev_copies = nullptr;
+  moe_pool_stats stats{};
+};
+
+namespace moe {
+
+moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k) {
+  if (!p || layer < 0 || layer >= p->n_layers) return MOE_E_INVALID;
+  if (p->E != E || p->D != D) return MOE_E_INVALID;
+  if (k > p->slots) return MOE_E_POOL;
+  return MOE_OK;
+}
+
+int pool_F(const moe_pool *p) { return p->F; }
+
+moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s) {
+  if (n > p->ids_cap) {
+    if (p->h_ids) (void)hipHostFree(p->h_ids);
+    p->h_ids = nullptr;
+    if (hipHostMalloc((void **)&p->h_ids, sizeof(int32_t) * n, hipHostMallocDefault) !=
+        hipSuccess)
+      return MOE_E_HIP;
+    p->ids_cap = n;
+  }
+  if (hipMemcpyAsync(p->h_ids, d_ids, sizeof(int32_t) * n, hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return MOE_E_HIP;
+  if (hipEventRecord(p->ev_ids, s) != hipSuccess) return MOE_E_HIP;
+  return MOE_OK;
+}
+
+moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
+                              const void *const **table) {
+  if (hipEventSynchronize(p->ev_ids) != hipSuccess) return MOE_E_HIP;
+  // distinct experts of the call in first-use order
+  std::vector<int> need;
+  need.reserve(T * k);
+  for (int i = 0; i < T * k; ++i) {
+    const int e = p->h_ids[i];
+    if (e < 0 || e >= p->E) return MOE_E_POOL;
+    if (std::find(need.begin(), need.end(), e) == need.end()) need.push_back(e);
+  }
+  std::vector<LfuPlanner::Event> ev;
+  if (!p->planners[layer].access(need.data(), (int)need.size(), &ev)) return MOE_E_POOL;
+  // counts: one lookup per (token, slot) use; the call's first use of a
+  // missing expert is its miss, repeated uses inside the call are hits
+  p->stats.lookups += (uint64_t)T * k;
+  const void **tab = p->h_tables + (size_t)layer * p->E;
+  uint8_t *base = p->slot_mem + (size_t)layer * p->slots * p->blob_bytes;
+  int copies = 0;
+  for (const auto &e : ev) {
+    if (e.hit) continue;
+    uint8_t *dst = base + (size_t)e.slot * p->blob_bytes;
+    const void *src = p->host_blobs[(size_t)layer * p->E + e.expert];
+    if (hipMemcpyAsync(dst, src, p->blob_bytes, hipMemcpyHostToDevice, p->side) != hipSuccess)
+      return MOE_E_HIP;
+    if (e.evicted >= 0) {
+      tab[e.evicted] = base;  // not resident; never read for a call that does not select it
+      p->stats.evictions += 1;
+    }
+    tab[e.expert] = dst;
+    p->stats.misses += 1;
+    p->stats.bytes_h2d += p->blob_bytes;
+    ++copies;
+  }
+  p->stats.hits += (uint64_t)T * k - copies;
+  if (copies) {
+    if (hipMemcpyAsync(p->d_tables + (size_t)layer * p->E, tab, sizeof(void *) * p->E,
+                       hipMemcpyHostToDevice, p->side) != hipSuccess)
+      return MOE_E_HIP;
+    if (hipEventRecord(p->ev_copies, p->side) != hipSuccess) return MOE_E_HIP;
+    if (hipStreamWaitEvent(s, p->ev_copies, 0) != hipSuccess) return MOE_E_HIP;
+  }
+  *table = p->d_tables + (size_t)layer * p->E;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
+                          const int32_t *ids, int32_t *events) {
+  if (slots < 1 || E < 1 || k < 1 || k > slots || n_tokens < 0 || !ids || !events)
+    return MOE_E_INVALID;
+  LfuPlanner pl(slots, E);
+  std::vector<LfuPlanner::Event> ev;
+  for (int t = 0; t < n_tokens; ++t) {
+    const int32_t *row = ids + (size_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      if (row[j] < 0 || row[j] >= E) return MOE_E_INVALID;
+      for (int i = 0; i < j; ++i)
+        if (row[i] == row[j]) return MOE_E_INVALID;
+    }
+    ev.clear();
+    if (!pl.access(row, k, &ev)) return MOE_E_POOL;
+    for (int j = 0; j < k; ++j) {
+      int32_t *o = events + ((size_t)t * k + j) * 4;
+      o[0] = ev[j].expert;
+      o[1] = ev[j].slot;
+      o[2] = ev[j].hit;
+      o[3] = ev[j].evicted;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int32_t E, int32_t D,
+                           int32_t F, const void *const *host_blobs) {
+  if (!out || n_layers < 1 || slots < 1 || E < 1 || slots > E || !host_blobs) return MOE_E_INVALID;
+  if (D < 64 || F < 64 || D % 64 || F % 64) return MOE_E_INVALID;
+  for (size_t i = 0; i < (size_t)n_layers * E; ++i)
+    if (!host_blobs[i]) return MOE_E_INVALID;
+  moe_pool *p = new (std::nothrow) moe_pool;
+  if (!p) return MOE_E_POOL;
+  p->n_layers = n_layers; p->slots = slots; p->E = E; p->D = D; p->F = F;
+  p->blob_bytes = blob_layout(D, F).total;
+  p->host_blobs.assign(host_blobs, host_blobs + (size_t)n_layers * E);
+  for (int l = 0; l < n_layers; ++l) p->planners.emplace_back(slots, E);
+  bool ok = hipMalloc((void **)&p->slot_mem, (size_t)n_layers * slots * p->blob_bytes) ==
+            hipSuccess;
+  ok = ok && hipMalloc((void **)&p->d_tables, sizeof(void *) * n_layers * E) == hipSuccess;
+  ok = ok && hipHostMalloc((void **)&p->h_tables, sizeof(void *) * n_layers * E,
+                           hipHostMallocDefault) == hipSuccess;
+  ok = ok && hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->ev_ids, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->ev_copies, hipEventDisableTiming) == hipSuccess;
+  if (ok) {
+    // every table entry starts at the layer's first slot (nothing resident yet)
+    for (int l = 0; l < n_layers; ++l)
+      for (int e = 0; e < E; ++e)
+        p->h_tables[(size_t)l * E + e] = p->slot_mem + (size_t)l * slots * p->blob_bytes;
+    ok = hipMemcpy(p->d_tables, p->h_tables, sizeof(void *) * n_layers * E,
+                   hipMemcpyHostToDevice) == hipSuccess;
+  }
+  if (!ok) {
+    moe_pool_destroy(p);
+    return MOE_E_HIP;
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+moe_status moe_pool_destroy(moe_pool *p) {
+  if (!p) return MOE_E_INVALID;
+  if (p->side) (void)hipStreamSynchronize(p->side);
+  if (p->slot_mem) (void)hipFree(p->slot_mem);
+  if (p->d_tables) (void)hipFree(p->d_tables);
+  if (p->h_tables) (void)hipHostFree(p->h_tables);
+  if (p->h_ids) (void)hipHostFree(p->h_ids);
+  if (p->ev_ids) (void)hipEventDestroy(p->ev_ids);
+  if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  delete p;
+  return MOE_OK;
+}
+
+moe_status moe_pool_get_stats(const moe_pool *p, moe_pool_stats *st) {
+  if (!p || !st) return MOE_E_INVALID;
+  *st = p->stats;
+  return MOE_OK;
+}
+
+moe_status moe_pool_reset_stats(moe_pool *p) {
+  if (!p) return MOE_E_INVALID;
+  p->stats = moe_pool_stats{};
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// HBM expert slot pool (internal interface used by moe_layer_forward).
+#pragma once
+
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Least-frequently-used slot planner of one layer.  Use counts are per
+// expert, cumulative, and kept after eviction; the victim is a resident
+// expert the current call does not need with the smallest count, ties to the
+// least recently used, then the lowest slot; empty slots fill in slot order.
+class LfuPlanner {
+ public:
+  struct Event {
+    int expert, slot, hit, evicted;
+  };
+  LfuPlanner(int slots, int E);
+  // Serve the experts of one call (distinct, in first-use order).  Returns
+  // false if they do not fit the slots.
+  bool access(const int *experts, int n, std::vector<Event> *events);
+  int slot_of(int e) const { return slot_of_[e]; }
+
+ private:
+  int slots_;
+  long now_ = 0;
+  std::vector<long> count_, last_;
+  std::vector<int> slot_of_, expert_in_;
+};
+
+moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k);
+int pool_F(const moe_pool *p);
+moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s);
+moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
+                              const void *const **table);
+
+}  // namespace moe

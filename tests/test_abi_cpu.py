@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports what include/moe.h declares,
+and its host-only logic (sizes, argument checks, the LFU slot planner) holds.
+No call here launches GPU work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synthetic import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("quantized_mixture_experts_moe_amd.moe",
+                          reason="libmoe.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = _declared_functions()
+    assert set(names) == set(moe.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+
+
+def test_blob_and_workspace_sizes():
+    assert moe.moe_blob_bytes(2816, 704) == 3_345_408 == gen.blob_bytes(2816, 704)
+    assert moe.moe_blob_bytes(2816, 2112) == 10_036_224
+    assert moe.moe_blob_bytes(256, 128) == 55_296
+    assert moe.moe_blob_bytes(100, 64) == 0
+    assert moe.moe_workspace_bytes(1, 8, 128, 2816, 704, 2112) > 0
+    assert moe.moe_workspace_bytes(0, 8, 128, 2816, 704, 2112) == 0
+    big = moe.moe_workspace_bytes(128, 8, 128, 2816, 704, 2112)
+    assert big > moe.moe_workspace_bytes(1, 8, 128, 2816, 704, 2112)
+
+
+def test_status_strings():
+    assert moe.status_string(0) == "ok"
+    assert moe.status_string(moe.MOE_E_WORKSPACE) == "workspace too small"
+    assert moe.status_string(-99) == "unknown status"
+
+
+def test_argument_checks_launch_nothing():
+    lib = moe.lib
+    q = moe.moe_qmat(1, 1, 128, 256, 8)
+    ids = ctypes.c_void_p(256)  # never dereferenced: every call fails its checks first
+    # null x
+    assert lib.moe_route(None, moe.MOE_BF16, 1, ctypes.byref(q), None, 8, ids, ids, None,
+                         ids, 1 << 30, None) == moe.MOE_E_INVALID
+    # k > E
+    assert lib.moe_route(ids, moe.MOE_BF16, 1, ctypes.byref(q), None, 129, ids, ids, None,
+                         ids, 1 << 30, None) == moe.MOE_E_INVALID
+    # D not a multiple of 64
+    q2 = moe.moe_qmat(1, 1, 128, 100, 8)
+    assert lib.moe_route(ids, moe.MOE_BF16, 1, ctypes.byref(q2), None, 8, ids, ids, None,
+                         ids, 1 << 30, None) == moe.MOE_E_INVALID
+    # 4-bit router is valid but not implemented
+    q3 = moe.moe_qmat(1, 1, 128, 256, 4)
+    assert lib.moe_route(ids, moe.MOE_BF16, 1, ctypes.byref(q3), None, 8, ids, ids, None,
+                         ids, 1 << 30, None) == moe.MOE_E_UNSUPPORTED
+    # workspace too small
+    assert lib.moe_route(ids, moe.MOE_BF16, 1, ctypes.byref(q), None, 8, ids, ids, None,
+                         ids, 16, None) == moe.MOE_E_WORKSPACE
+    # fp32 activations are not accepted
+    assert lib.moe_route(ids, moe.MOE_F32, 1, ctypes.byref(q), None, 8, ids, ids, None,
+                         ids, 1 << 30, None) == moe.MOE_E_INVALID
+    bank = moe.moe_bank(1, 128, 256, 96)  # F not a multiple of 64
+    assert lib.moe_layer_forward(ids, moe.MOE_BF16, 1, ctypes.byref(q), None, 8,
+                                 ctypes.byref(bank), None, None, 0, ids, moe.MOE_F32, None, None,
+                                 ids, 1 << 30, None) == moe.MOE_E_INVALID
+    bank_e = moe.moe_bank(1, 64, 256, 128)  # bank E differs from the router's
+    assert lib.moe_layer_forward(ids, moe.MOE_BF16, 1, ctypes.byref(q), None, 8,
+                                 ctypes.byref(bank_e), None, None, 0, ids, moe.MOE_F32, None,
+                                 None, ids, 1 << 30, None) == moe.MOE_E_INVALID
+    # expert FFN without ids needs k == 1
+    bank_ok = moe.moe_bank(1, 1, 256, 128)
+    assert lib.moe_expert_ffn(ids, moe.MOE_BF16, 1, ctypes.byref(bank_ok), None, 2, ids, ids,
+                              1 << 30, None) == moe.MOE_E_INVALID
+    assert lib.moe_combine(None, ids, None, 1, 1, 64, ids, moe.MOE_F32, None) == moe.MOE_E_INVALID
+    assert lib.moe_combine(ids, ids, None, 1, 1, 64, ids, 7, None) == moe.MOE_E_INVALID
+    assert lib.moe_permute(ids, 65537, 1, 16, ids, ids, ids, ids, None) == moe.MOE_E_INVALID
+    assert lib.moe_set_tuning(b"no_such_knob", 1) == moe.MOE_E_INVALID
+    # activations must be 16-byte aligned
+    assert lib.moe_route(ctypes.c_void_p(258), moe.MOE_BF16, 1, ctypes.byref(q), None, 8, ids, ids,
+                         None, ids, 1 << 30, None) == moe.MOE_E_INVALID
+
+
+def _golden_lfu():
+    with open(os.path.join(ROOT, "tests", "golden", "lfu_trace.txt")) as f:
+        lines = [l.strip() for l in f if l.strip() and not l.startswith("#")]
+    slots, E = map(int, lines[0].split())
+    ids, evs = [], []
+    for l in lines[1:]:
+        _, rest = l.split(":", 1)
+        a, b = rest.split(";")
+        ids.append([int(v) for v in a.split()])
+        row = []
+        for item in b.split():
+            e, s, h, v = item.split(":")
+            row.append([int(e), int(s), 1 if h == "hit" else 0, int(v)])
+        evs.append(row)
+    return slots, E, np.array(ids), np.array(evs)
+
+
+def test_lfu_planner_handworked_trace():
+    slots, E, ids, evs = _golden_lfu()
+    assert np.array_equal(moe.moe_lfu_replay(slots, E, ids), evs)
+
+
+@pytest.mark.parametrize("beta", [0.0, 4.0, 6.5])
+def test_lfu_planner_matches_oracle_model(beta):
+    rng = np.random.default_rng(int(beta * 10))
+    E, k, slots, n = 128, 8, 16, 400
+    w = np.exp(-beta * 1.1 * np.log(1 + rng.permutation(E)) / 4)
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=w / w.sum()) for _ in range(n)])
+    got = moe.moe_lfu_replay(slots, E, ids)
+    model = O.LFUCache(slots, E)
+    for t in range(n):
+        ref = [(e, s, 1 if h else 0, v) for (e, s, h, v) in model.access(ids[t])]
+        assert [tuple(r) for r in got[t]] == ref, t
+
+
+def test_lfu_planner_rejects_bad_traces():
+    with pytest.raises(moe.MoEError):
+        moe.moe_lfu_replay(4, 16, np.array([[1, 1]]))   # repeated expert
+    with pytest.raises(moe.MoEError):
+        moe.moe_lfu_replay(4, 16, np.array([[1, 16]]))  # out of range
+    with pytest.raises(moe.MoEError):
+        moe.moe_lfu_replay(2, 16, np.array([[1, 2, 3]]))  # k > slots

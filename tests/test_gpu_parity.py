@@ -1,0 +1,305 @@
+"""GPU parity: every C-ABI call against the CPU oracle on seeded inputs.
+
+Bars: expert ids bit-exact where the oracle's k-th/(k+1)-th logit gap
+exceeds 1e-3 (elsewhere any valid top-k, and the outputs are then compared
+with the oracle re-run on the GPU's ids); fp32 outputs within relative L2
+1e-3 and max-abs 2e-2; integer work (permutation, pool trace) bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synthetic import gen
+from tests._helpers import GAP, MAX_ABS, REL_L2, check_ids, max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("quantized_mixture_experts_moe_amd.moe")
+
+TORCH_X = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+class DevLayer:
+    """A seeded layer in host memory (for the oracle) and in HBM."""
+
+    def __init__(self, cfg, seed=0, layer=0):
+        self.cfg = cfg
+        self.lw = gen.layer_weights(seed, layer, cfg)
+        self.router = moe.DeviceQMat(self.lw.router.codes, self.lw.router.meta, cfg.E, cfg.D, 8)
+        self.routed = moe.DeviceBank.from_numpy(self.lw.experts, cfg.D, cfg.F)
+        self.shared = (moe.DeviceBank.from_numpy(self.lw.shared[None, :], cfg.D, cfg.F_shared)
+                       if cfg.F_shared else None)
+
+
+_LAYERS = {}
+
+
+def dev_layer(name, seed=0, layer=0):
+    key = (name, seed, layer)
+    if key not in _LAYERS:
+        _LAYERS[key] = DevLayer(gen.CONFIGS[name], seed, layer)
+    return _LAYERS[key]
+
+
+def x_dev(bits, dtype):
+    return torch.from_numpy(bits.astype(np.int16)).cuda().view(TORCH_X[dtype])
+
+
+def x_float(bits, dtype):
+    return O.activations_to_float(bits, dtype)
+
+
+def oracle_layer(L, xf, k, bias=None, ids=None):
+    return O.layer_forward(xf, L.lw, k, bias, ids=ids)
+
+
+# ---------------------------------------------------------------- router
+@pytest.mark.parametrize("name,T,beta", [("tiny", 4, 0.0), ("tiny", 37, 1.0), ("decode", 1, 0.0),
+                                         ("decode", 5, 6.5), ("decode", 128, 1.5)])
+def test_route_parity(name, T, beta):
+    _case(f"route {name} T={T} beta={beta}")
+    L = dev_layer(name)
+    cfg = L.cfg
+    xb = gen.activations(1, 0, T, T, cfg.D, cfg.x_dtype)
+    bias = gen.zipf_bias(0, 0, cfg.E, beta) if beta else None
+    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, 64, 0)
+    ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+    logits = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+    bias_d = torch.from_numpy(bias).cuda() if bias is not None else None
+    moe.moe_route(x_dev(xb, cfg.x_dtype), L.router, cfg.k, ids, gates, ws, bias_d, logits)
+    torch.cuda.synchronize()
+    ref = O.router_logits(x_float(xb, cfg.x_dtype), L.lw.router, bias)
+    got_l = logits.cpu().numpy()
+    assert rel_l2(got_l, ref) < 1e-5
+    got_ids = ids.cpu().numpy()
+    check_ids(ref, got_ids, cfg.k)
+    # gates: softmax of the oracle logits at the GPU's ids
+    sel = np.take_along_axis(ref, got_ids.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(gates.cpu().numpy(), z / z.sum(axis=1, keepdims=True), atol=2e-6)
+    assert np.allclose(gates.cpu().numpy().sum(axis=1), 1.0, atol=1e-6)
+    assert np.all(np.diff(gates.cpu().numpy(), axis=1) <= 0)
+
+
+def test_route_x_zero_closed_form():
+    _case("route x=0")
+    L = dev_layer("tiny")
+    cfg = L.cfg
+    ws = moe.Workspace(3, cfg.k, cfg.E, cfg.D, 64, 0)
+    x = torch.zeros(3, cfg.D, dtype=torch.float16, device="cuda")
+    ids = torch.empty(3, cfg.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(3, cfg.k, dtype=torch.float32, device="cuda")
+    moe.moe_route(x, L.router, cfg.k, ids, gates, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), np.tile(np.arange(cfg.k), (3, 1)))
+    assert np.all(gates.cpu().numpy() == 1.0 / cfg.k)
+
+
+# ---------------------------------------------------------------- expert FFN
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 2)])
+def test_expert_ffn_parity(name, T):
+    _case(f"expert_ffn {name} T={T}")
+    L = dev_layer(name)
+    cfg = L.cfg
+    rng = np.random.default_rng(5)
+    ids_np = np.stack([rng.choice(cfg.E, size=cfg.k, replace=False) for _ in range(T)]).astype(np.int32)
+    xb = gen.activations(2, 0, 0, T, cfg.D, cfg.x_dtype)
+    xf = x_float(xb, cfg.x_dtype)
+    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    y = torch.empty(T, cfg.k, cfg.D, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(x_dev(xb, cfg.x_dtype), L.routed, torch.from_numpy(ids_np).cuda(), cfg.k, y, ws)
+    ys = torch.empty(T, 1, cfg.D, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(x_dev(xb, cfg.x_dtype), L.shared, None, 1, ys, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    for t in range(T):
+        for j in range(cfg.k):
+            ref = O.expert_forward(xf[t:t + 1], L.lw.experts[ids_np[t, j]], cfg.D, cfg.F)[0]
+            assert rel_l2(got[t, j], ref) < REL_L2 and max_abs(got[t, j], ref) < MAX_ABS, (t, j)
+            # fp16 activations meet codes as 1024 + q: the cancellation costs ~1e-5
+            assert rel_l2(got[t, j], ref) < (1e-4 if cfg.x_dtype == "fp16" else 2e-5)
+    ref_s = O.expert_forward(xf, L.lw.shared, cfg.D, cfg.F_shared)
+    assert rel_l2(ys.cpu().numpy()[:, 0], ref_s) < (1e-4 if cfg.x_dtype == "fp16" else 2e-5)
+
+
+def test_expert_ffn_invalid_id_gives_zero_rows():
+    _case("expert_ffn invalid id")
+    L = dev_layer("tiny")
+    cfg = L.cfg
+    xb = gen.activations(3, 0, 0, 2, cfg.D, cfg.x_dtype)
+    ids = torch.tensor([[0, 1, cfg.E, -1], [2, 3, 4, 5]], dtype=torch.int32, device="cuda")
+    ws = moe.Workspace(2, 4, cfg.E, cfg.D, cfg.F, 0)
+    y = torch.full((2, 4, cfg.D), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(x_dev(xb, cfg.x_dtype), L.routed, ids, 4, y, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.all(got[0, 2] == 0) and np.all(got[0, 3] == 0)
+    assert np.any(got[0, 0] != 0)
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_combine_parity(out_dtype):
+    _case(f"combine {out_dtype}")
+    rng = np.random.default_rng(9)
+    T, k, D = 5, 8, 2816
+    y = rng.standard_normal((T, k, D)).astype(np.float32) * 30
+    g = rng.random((T, k)).astype(np.float32)
+    ys = rng.standard_normal((T, D)).astype(np.float32) * 60
+    out = torch.empty(T, D, dtype=out_dtype, device="cuda")
+    moe.moe_combine(torch.from_numpy(y).cuda(), torch.from_numpy(g).cuda(),
+                    torch.from_numpy(ys).cuda(), out)
+    torch.cuda.synchronize()
+    ref = O.combine(y, g, ys)
+    got = out.float().cpu().numpy()
+    if out_dtype == torch.float32:
+        assert max_abs(got, ref) < 1e-4
+    else:
+        assert rel_l2(got, ref) < 4e-3
+
+
+# ---------------------------------------------------------------- permutation
+@pytest.mark.parametrize("T,k,E,beta", [(128, 8, 128, 1.5), (77, 8, 128, 0.0), (4, 4, 16, 0.0),
+                                        (1, 8, 128, 0.0), (128, 8, 128, 8.0)])
+def test_permute_bit_exact(T, k, E, beta):
+    _case(f"permute T={T} k={k} E={E}")
+    rng = np.random.default_rng(T + E)
+    w = np.exp(-beta * 1.1 * np.log(1 + rng.permutation(E)))
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=w / w.sum()) for _ in range(T)]).astype(np.int32)
+    d = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+    counts, offsets, perm, inv = d(E), d(E + 1), d(T * k), d(T * k)
+    moe.moe_permute(torch.from_numpy(ids).cuda(), E, counts, offsets, perm, inv)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = O.permutation(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+# ---------------------------------------------------------------- whole layer
+def _layer_gpu(L, xb, k, bias=None, T=None, out_dtype=torch.float32):
+    cfg = L.cfg
+    T = xb.shape[0]
+    ws = moe.Workspace(T, k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    out = torch.empty(T, cfg.D, dtype=out_dtype, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    bias_d = torch.from_numpy(bias).cuda() if bias is not None else None
+    moe.moe_layer_forward(x_dev(xb, cfg.x_dtype), L.router, k, L.routed, L.shared, out, ws,
+                          logit_bias=bias_d, ids_out=ids, gates_out=gates)
+    torch.cuda.synchronize()
+    return out, ids.cpu().numpy(), gates.cpu().numpy()
+
+
+def _check_layer(L, xb, got_out, got_ids, k, bias=None, tokens=None):
+    cfg = L.cfg
+    xf = x_float(xb, cfg.x_dtype)
+    tokens = list(range(xb.shape[0])) if tokens is None else tokens
+    logits = O.router_logits(xf[tokens], L.lw.router, bias)
+    check_ids(logits, got_ids[tokens], k)
+    ref = oracle_layer(L, xf[tokens], k, bias, ids=got_ids[tokens])
+    got = got_out[tokens]
+    r, m = rel_l2(got, ref["out"]), max_abs(got, ref["out"])
+    print(f"    rel_l2={r:.2e} max_abs={m:.2e}", flush=True)
+    assert r < REL_L2 and m < MAX_ABS
+    return ref
+
+
+@pytest.mark.parametrize("name,T,beta", [("tiny", 4, 0.0), ("tiny", 9, 2.0), ("decode", 1, 0.0),
+                                         ("decode", 3, 6.5)])
+def test_layer_forward_parity(name, T, beta):
+    _case(f"layer_forward {name} T={T} beta={beta}")
+    L = dev_layer(name)
+    cfg = L.cfg
+    xb = gen.activations(4, 0, T, T, cfg.D, cfg.x_dtype)
+    bias = gen.zipf_bias(0, 0, cfg.E, beta) if beta else None
+    out, ids, gates = _layer_gpu(L, xb, cfg.k, bias)
+    _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias)
+
+
+def test_layer_forward_prefill_chunk_sampled():
+    _case("layer_forward prefill T=128 (sampled tokens)")
+    L = dev_layer("decode")
+    cfg = gen.CONFIGS["prefill"]
+    xb = gen.activations(0, 0, 0, cfg.T, cfg.D, cfg.x_dtype)
+    bias = gen.zipf_bias(0, 0, cfg.E, cfg.beta)
+    out, ids, _ = _layer_gpu(L, xb, cfg.k, bias)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    print(f"    max rows per expert {counts.max()}, distinct {np.count_nonzero(counts)}")
+    _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=[0, 1, 63, 64, 127])
+    # prefill rows equal single-token decode of the same tokens
+    for t in (0, 77, 127):
+        o1, i1, _ = _layer_gpu(L, xb[t:t + 1], cfg.k, bias)
+        assert np.array_equal(i1[0], ids[t])
+        assert rel_l2(o1.cpu().numpy()[0], out.cpu().numpy()[t]) < 1e-5
+
+
+def test_layer_forward_bf16_output_is_rounded_fp32():
+    _case("layer_forward bf16 out")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    xb = gen.activations(6, 0, 0, 2, cfg.D, cfg.x_dtype)
+    o32, _, _ = _layer_gpu(L, xb, cfg.k)
+    o16, _, _ = _layer_gpu(L, xb, cfg.k, out_dtype=torch.bfloat16)
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+
+
+def test_layer_forward_bitwise_repeatable():
+    _case("layer_forward repeatability")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    xb = gen.activations(7, 0, 0, 1, cfg.D, cfg.x_dtype)
+    a, ia, _ = _layer_gpu(L, xb, cfg.k)
+    b, ib, _ = _layer_gpu(L, xb, cfg.k)
+    assert np.array_equal(ia, ib) and torch.equal(a, b)
+
+
+def test_layer_forward_x_zero():
+    _case("layer_forward x=0")
+    L = dev_layer("tiny")
+    cfg = L.cfg
+    xb = np.zeros((2, cfg.D), dtype=np.uint16)
+    out, ids, gates = _layer_gpu(L, xb, cfg.k)
+    assert np.all(out.cpu().numpy() == 0.0)
+    assert np.array_equal(ids, np.tile(np.arange(cfg.k), (2, 1)))
+    assert np.all(gates == 1.0 / cfg.k)
+
+
+# ---------------------------------------------------------------- streamed experts (pool)
+def test_pool_streamed_equals_resident_and_trace():
+    _case("pool streamed vs resident (tiny, 2 layers, 4 slots)")
+    cfg = gen.CONFIGS["tiny"]
+    layers = [dev_layer("tiny", seed=3, layer=l) for l in range(2)]
+    host = [torch.from_numpy(L.lw.experts.copy()).pin_memory() for L in layers]
+    pool = moe.Pool(host, 2, 4, cfg.E, cfg.D, cfg.F)
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    models = [O.LFUCache(4, cfg.E) for _ in range(2)]
+    misses = 0
+    for tok in range(24):
+        for l, L in enumerate(layers):
+            xb = gen.activations(3, l, tok, 1, cfg.D, cfg.x_dtype)
+            bias = torch.from_numpy(gen.zipf_bias(3, l, cfg.E, 4.0)).cuda()
+            x = x_dev(xb, cfg.x_dtype)
+            o_s = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+            o_r = torch.empty_like(o_s)
+            ids = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
+            g = torch.empty(1, cfg.k, dtype=torch.float32, device="cuda")
+            moe.moe_layer_forward(x, L.router, cfg.k, None, L.shared, o_s, ws, logit_bias=bias,
+                                  pool=pool, layer=l, ids_out=ids, gates_out=g)
+            moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, o_r, ws, logit_bias=bias)
+            torch.cuda.synchronize()
+            assert torch.equal(o_s, o_r), (tok, l)
+            ev = models[l].access(ids.cpu().numpy()[0])
+            misses += sum(1 for e in ev if not e[2])
+    st = pool.stats()
+    assert st["lookups"] == 24 * 2 * cfg.k
+    assert st["misses"] == misses and st["hits"] == st["lookups"] - misses
+    assert st["bytes_h2d"] == misses * moe.moe_blob_bytes(cfg.D, cfg.F)
+    pool.close()
