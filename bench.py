@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune", action="append", default=[],
+                    help="launch-shape knob key=value (moe_set_tuning), repeatable")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -94,6 +96,9 @@ def main():
     from quantized_mixture_experts_moe_amd import moe
 
     torch.cuda.set_device(0)
+    for kv in a.tune:
+        key, val = kv.split("=")
+        moe.moe_set_tuning(key, int(val))
     cfg = gen.CONFIGS[a.config]
     n_layers = cfg.layers
     T = cfg.T

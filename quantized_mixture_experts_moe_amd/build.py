@@ -22,8 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "libmoe")
 
-SOURCES = ["moe_api.cpp", "pool.cpp", "route.hip", "expert_gemv.hip", "permute.hip",
-           "prefill_mfma.hip"]
+SOURCES = ["moe_api.cpp", "pool.cpp", "route.hip", "expert_gemv.hip", "expert_fused.hip",
+           "permute.hip", "prefill_mfma.hip"]
 
 
 def hipcc() -> str:

@@ -28,6 +28,13 @@ struct Carver {
   }
 };
 
+// counters of the one-launch expert phase: tiles, output tiles, slots, and the
+// replicated slot-ready flags (one 32-word line per copy)
+size_t fused_counter_words(const Dims &d) {
+  const size_t slots = (size_t)d.T * (d.k + 1);
+  return 2 * (size_t)kMaxSplitBlocks + slots + slots * kFlagCopies * 32 + 64;
+}
+
 Workspace carve(void *base, const Dims &d) {
   Carver c{(uint8_t *)base};
   Workspace w;
@@ -43,10 +50,17 @@ Workspace carve(void *base, const Dims &d) {
   w.hs = c.take<float>(units / 64 + 1, 4);
   w.part = c.take<float>((size_t)kMaxSplitBlocks * 128, 4);
   w.counters = c.take<uint32_t>((size_t)kMaxSplitBlocks + T, 4);
+  w.dpart = c.take<float>((size_t)kMaxSplitBlocks * 64, 4);
+  w.fcounters = c.take<uint32_t>(fused_counter_words(d), 4);
+  w.err = c.take<uint32_t>(1, 4);
   w.perm_counts = c.take<int32_t>(d.E, 4);
   w.perm_offsets = c.take<int32_t>(d.E + 1, 4);
   w.perm = c.take<int32_t>(T * k, 4);
   w.perm_inv = c.take<int32_t>(T * k, 4);
+  w.hplanes = c.take<uint16_t>(3 * units, 2);
+  w.hsum = c.take<float>(units / 64 + 1, 4);
+  w.y = c.take<float>(T * k * (size_t)d.D, 4);
+  w.ys = c.take<float>(T * (size_t)d.D, 4);
   w.total = c.off;
   return w;
 }
@@ -70,6 +84,44 @@ moe_status check_bank(const moe_bank *b, int D) {
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Choose the splits of the one-launch expert phase; false if its grid would
+// not be resident all at once (then the three-kernel path runs).
+bool plan_fused(const ExpertLaunch &a, const Workspace &w, FusedLaunch *f) {
+  const int G = a.D / 64, NB = a.D / 64;
+  const int n_gtiles = a.T * a.k * (a.F / 64) + (a.sblobs ? a.T * (a.Fs / 64) : 0);
+  const int U = a.k * (a.F / 64) + (a.sblobs ? a.Fs / 64 : 0);
+  // about two blocks per compute unit, each wave with at most 4 groups / units
+  const int target = 512;
+  int ksg = tuning().fused_ksg > 0 ? tuning().fused_ksg : (target + n_gtiles - 1) / n_gtiles;
+  ksg = clampi(ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
+  int ksd = tuning().fused_ksd > 0 ? tuning().fused_ksd
+                                   : (ksg * n_gtiles + a.T * NB - 1) / (a.T * NB);
+  ksd = clampi(ksd, (U + 15) / 16, U < kMaxFusedKSd ? U : kMaxFusedKSd);
+  if ((G + ksg - 1) / ksg > 16 || (U + ksd - 1) / ksd > 16) return false;
+  f->a = a;
+  f->KSg = ksg;
+  f->KSd = ksd;
+  f->n_gtiles = n_gtiles;
+  int cap = 0;
+  if (fused_capacity(*f, &cap) != hipSuccess || cap <= 0) return false;
+  const int grid = fused_grid(*f);
+  if (grid > cap || (long)n_gtiles * ksg > kMaxSplitBlocks || (long)a.T * NB * ksd > kMaxSplitBlocks)
+    return false;
+  // counters packed at the start of the region (cleared by the router kernel),
+  // then the flag lines
+  f->tile_cnt = w.fcounters;
+  f->out_cnt = f->tile_cnt + n_gtiles;
+  f->slot_cnt = f->out_cnt + a.T * NB;
+  f->slot_flag = w.fcounters + 2 * kMaxSplitBlocks + (size_t)a.T * (a.k + 1);
+  f->slot_flag += (32 - ((uintptr_t)f->slot_flag / 4) % 32) % 32;  // 128-byte lines
+  f->err = w.err;
+  f->gpart = w.part;
+  f->dpart = w.dpart;
+  return true;
+}
 
 }  // namespace
 
@@ -111,6 +163,14 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().glu_ks = value;
   } else if (!strcmp(key, "down_ks")) {
     tuning().down_ks = value;
+  } else if (!strcmp(key, "fused")) {
+    tuning().fused = value;
+  } else if (!strcmp(key, "fused_ksg")) {
+    tuning().fused_ksg = value;
+  } else if (!strcmp(key, "fused_ksd")) {
+    tuning().fused_ksd = value;
+  } else if (!strcmp(key, "prefill_min_t")) {
+    tuning().prefill_min_t = value;
   } else {
     return MOE_E_INVALID;
   }
@@ -136,6 +196,7 @@ moe_status moe_route(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *
   a.logits = logits ? logits : w.logits; a.ids = ids; a.gates = gates;
   a.xp = w.xp; a.xs = w.xs; a.counters = w.counters;
   a.table = nullptr; a.slot_blob = nullptr;
+  a.zero = nullptr; a.zero_words = 0; a.zero2 = nullptr; a.zero2_count = 0; a.zero2_stride = 0;
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -215,6 +276,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   hipStream_t s = (hipStream_t)stream;
 
   RouteLaunch r;
+  r.zero = nullptr; r.zero_words = 0; r.zero2 = nullptr; r.zero2_count = 0; r.zero2_stride = 0;
   r.x = x; r.f16x = x_dtype == MOE_F16; r.T = T; r.D = D; r.E = E; r.k = k;
   r.codes = (const uint8_t *)router->codes; r.meta = (const uint32_t *)router->meta;
   r.logit_bias = logit_bias;
@@ -223,7 +285,6 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   // resident experts: the router also resolves each selected expert's blob
   r.table = pool ? nullptr : routed->blobs;
   r.slot_blob = pool ? nullptr : w.slot_blob;
-  if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
 
   ExpertLaunch a{};
   a.f16x = r.f16x; a.T = T; a.k = k; a.D = D; a.E = E;
@@ -232,6 +293,34 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   a.sblobs = shared ? shared->blobs : nullptr; a.Fs = Fs;
   a.h = w.h; a.hs = w.hs; a.part = w.part; a.counters = w.counters;
   a.y = nullptr; a.out = out; a.out_dtype = out_dtype;
+  FusedLaunch f;
+  const bool fused = !pool && tuning().fused && plan_fused(a, w, &f);
+  if (fused) {
+    r.zero = w.fcounters;
+    r.zero_words = (int)(f.slot_cnt + T * (k + 1) - w.fcounters);
+    r.zero2 = f.slot_flag;
+    r.zero2_count = T * (k + 1) * kFlagCopies;
+    r.zero2_stride = 32;
+  }
+  if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
+  if (fused) return hip_status(launch_fused(f, s));
+
+  // prefill chunk: group the (token, slot) pairs by expert, then matrix cores
+  if (!pool && T >= tuning().prefill_min_t && T * k <= 65536 && D / 64 <= kMaxDGroups &&
+      F / 64 <= kMaxHGroups && Fs / 64 <= kMaxHGroups) {
+    if (launch_permute(r.ids, T, k, E, w.perm_counts, w.perm_offsets, w.perm, w.perm_inv, s) !=
+        hipSuccess)
+      return MOE_E_HIP;
+    PrefillLaunch pl;
+    pl.f16x = r.f16x; pl.T = T; pl.k = k; pl.E = E; pl.D = D; pl.F = F; pl.Fs = Fs;
+    pl.counts = w.perm_counts; pl.offsets = w.perm_offsets; pl.perm = w.perm; pl.inv = w.perm_inv;
+    pl.gates = r.gates; pl.rblobs = routed->blobs; pl.sblobs = shared ? shared->blobs : nullptr;
+    pl.xp = w.xp; pl.xs = w.xs;
+    pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;
+    pl.hsum = w.hsum; pl.y = w.y; pl.ys = w.ys; pl.out = out; pl.out_dtype = out_dtype;
+    return hip_status(launch_prefill_experts(pl, s));
+  }
+
   const int routed_blocks = T * k * (F / 64);
   const int all_blocks = glu_blocks(a);
   // one reduction split for the whole layer, so the streamed path (shared and

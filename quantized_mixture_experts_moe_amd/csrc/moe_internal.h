@@ -15,6 +15,9 @@ constexpr int kMaxE = 1024;     // router width handled by the top-k wave
 constexpr int kMaxK = 64;       // experts per token
 constexpr int kMaxKS = 16;      // split of a reduction over blocks
 constexpr int kMaxSplitBlocks = 4096;  // blocks of a split launch (partial tiles)
+constexpr int kMaxFusedKSd = 16;       // output splits of the one-launch expert phase
+constexpr int kMaxDGroups = 128;       // model width / 64 handled by the prefill kernels
+constexpr int kMaxHGroups = 64;        // hidden width / 64 handled by the prefill kernels
 
 __host__ __device__ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -45,6 +48,10 @@ __host__ __device__ inline BlobLayout blob_layout(int D, int F) {
 struct Tuning {
   int glu_ks = 0;      // 0: chosen from the problem size
   int down_ks = 0;
+  int fused = 1;       // one-launch expert phase for decode when it fits
+  int fused_ksg = 0;   // its gate/up and down splits (0: chosen)
+  int fused_ksd = 0;
+  int prefill_min_t = 16;  // tokens per call from which the grouped matrix-core path runs
   int route_rows = 8;  // experts per router block
 };
 Tuning &tuning();
@@ -61,7 +68,13 @@ struct Workspace {
   float *hs;           // h group sums, one float per 64 hidden units
   float *part;         // split-reduction partials
   uint32_t *counters;  // last-block-done counters (zero between calls)
+  float *dpart;        // output-split partials of the one-launch expert phase
+  uint32_t *fcounters; // its counters (zero between calls)
+  uint32_t *err;       // sticky count of timed-out waits
   int32_t *perm_counts, *perm_offsets, *perm, *perm_inv;
+  uint16_t *hplanes;   // prefill: hidden activations as three bf16 planes
+  float *hsum;         // prefill: 64-unit sums of the hidden activations
+  float *y, *ys;       // prefill: routed outputs per pair, shared outputs per token
   size_t total;
 };
 
@@ -81,6 +94,10 @@ struct RouteLaunch {
   uint32_t *xp; float *xs; uint32_t *counters;
   const void *const *table;           // routed bank (for slot_blob) or null
   const void **slot_blob;             // [T][k] blob of each selected expert, or null
+  // words cleared for the next kernel: zero[0, zero_words) and every
+  // zero2_stride-th word of zero2, zero2_count of them
+  uint32_t *zero; int zero_words;
+  uint32_t *zero2; int zero2_count, zero2_stride;
 };
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 // x pairs and 64-column sums for the expert kernels without routing
@@ -101,6 +118,21 @@ struct ExpertLaunch {
   int glu_first, glu_count;           // GLU block range: routed tiles first, then shared
   int glu_ks;                         // reduction split of the GLU (0: from glu_count)
 };
+// One-launch expert phase (gate/up + down + combine) for a few tokens.
+constexpr int kFlagCopies = 16;  // replicas of each slot-ready flag (one 128-byte line each)
+struct FusedLaunch {
+  ExpertLaunch a;           // needs slot_blob (resident experts)
+  int KSg, KSd, n_gtiles;
+  // counters and flags: zeroed by the router kernel launched just before
+  uint32_t *tile_cnt, *slot_cnt, *out_cnt, *slot_flag, *err;
+  float *gpart, *dpart;
+};
+int fused_grid(const FusedLaunch &f);
+int fused_max_g(const FusedLaunch &f);
+int fused_max_u(const FusedLaunch &f);
+hipError_t fused_capacity(const FusedLaunch &f, int *cap);
+hipError_t launch_fused(const FusedLaunch &f, hipStream_t s);
+
 int pick_ks(int blocks, int reduce_len, int min_ks, int override_ks);
 int glu_min_ks(int D);
 int glu_blocks(const ExpertLaunch &a);
@@ -108,6 +140,19 @@ hipError_t launch_glu(const ExpertLaunch &a, hipStream_t s);
 hipError_t launch_down(const ExpertLaunch &a, bool combine, hipStream_t s);
 hipError_t launch_combine(const float *y, const float *gates, const float *ys, int T, int k,
                           int D, void *out, int out_dtype, hipStream_t s);
+// Grouped (permuted) expert phase of a prefill chunk on the matrix cores.
+struct PrefillLaunch {
+  int f16x, T, k, E, D, F, Fs;
+  const int32_t *counts, *offsets, *perm, *inv;
+  const float *gates;
+  const void *const *rblobs, *const *sblobs;
+  const uint32_t *xp; const float *xs;
+  uint16_t *hp; size_t plane;         // three planes of `plane` elements
+  float *hsum, *y, *ys;
+  void *out; int out_dtype;
+};
+hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s);
+
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);
 

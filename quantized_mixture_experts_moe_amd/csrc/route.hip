@@ -110,6 +110,14 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.y * TT;
+  // clear the counters of the kernel that follows (visible to it at the launch
+  // boundary)
+  if (a.zero && blockIdx.y == 0) {
+    for (int i = blockIdx.x * kThreads + tid; i < a.zero_words; i += gridDim.x * kThreads)
+      a.zero[i] = 0u;
+    for (int i = blockIdx.x * kThreads + tid; i < a.zero2_count; i += gridDim.x * kThreads)
+      a.zero2[(size_t)i * a.zero2_stride] = 0u;
+  }
   const int nt = min(TT, a.T - t0);
   const uint16_t *x = (const uint16_t *)a.x + (size_t)t0 * D;
 

@@ -213,7 +213,7 @@ def _check_layer(L, xb, got_out, got_ids, k, bias=None, tokens=None):
 
 
 @pytest.mark.parametrize("name,T,beta", [("tiny", 4, 0.0), ("tiny", 9, 2.0), ("decode", 1, 0.0),
-                                         ("decode", 3, 6.5)])
+                                         ("decode", 3, 6.5), ("tiny", 40, 1.0), ("tiny", 130, 0.0)])
 def test_layer_forward_parity(name, T, beta):
     _case(f"layer_forward {name} T={T} beta={beta}")
     L = dev_layer(name)
@@ -234,6 +234,10 @@ def test_layer_forward_prefill_chunk_sampled():
     counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
     print(f"    max rows per expert {counts.max()}, distinct {np.count_nonzero(counts)}")
     _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=[0, 1, 63, 64, 127])
+    # the expert holding the most rows of the chunk: every one of its tokens
+    busiest = int(np.argmax(counts))
+    toks = sorted(set(np.nonzero(ids == busiest)[0].tolist()))[:24]
+    _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=toks)
     # prefill rows equal single-token decode of the same tokens
     for t in (0, 77, 127):
         o1, i1, _ = _layer_gpu(L, xb[t:t + 1], cfg.k, bias)
@@ -303,3 +307,36 @@ def test_pool_streamed_equals_resident_and_trace():
     assert st["misses"] == misses and st["hits"] == st["lookups"] - misses
     assert st["bytes_h2d"] == misses * moe.moe_blob_bytes(cfg.D, cfg.F)
     pool.close()
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_layer_forward_decode_both_expert_paths(fused):
+    """The one-launch expert phase and the three-kernel path both meet the bar."""
+    _case(f"layer_forward decode fused={fused}")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    moe.moe_set_tuning("fused", fused)
+    try:
+        for tok in range(3):
+            xb = gen.activations(8, 0, tok, 1, cfg.D, cfg.x_dtype)
+            out, ids, _ = _layer_gpu(L, xb, cfg.k)
+            _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k)
+            again, _, _ = _layer_gpu(L, xb, cfg.k)
+            assert torch.equal(out, again)
+    finally:
+        moe.moe_set_tuning("fused", 1)
+
+
+def test_layer_forward_prefill_ragged_chunk():
+    """A chunk of 77 tokens (not a multiple of the 64-row tiles), skewed routing."""
+    _case("layer_forward prefill T=77 beta=4")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    xb = gen.activations(0, 1, 0, 77, cfg.D, cfg.x_dtype)
+    bias = gen.zipf_bias(0, 1, cfg.E, 4.0)
+    out, ids, _ = _layer_gpu(L, xb, cfg.k, bias)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    assert counts.max() > 64  # exercises the second row chunk of a group
+    busiest = int(np.argmax(counts))
+    toks = sorted(set(np.nonzero(ids == busiest)[0].tolist()))
+    _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=toks[:6] + toks[-6:] + [76])
