@@ -74,16 +74,154 @@ def cpu_baseline(cfg, seed, budget_s):
                       f"host cpu_count {os.cpu_count()})"}
 
 
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_mixture_experts_moe_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(k_bytes):
+    """HBM bytes per expert-phase launch from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), only if they were taken
+    on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "decode_expert_phase_traffic.json")
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_stack(cfg, a, moe, torch):
+    """30-layer decode: every token goes through all layers in order."""
+    n_layers, n_tok = cfg.layers, cfg.tokens
+    log(f"stack: generating {n_layers} layers ({n_layers * cfg.E * gen.blob_bytes(cfg.D, cfg.F) / 1e9:.1f} GB of experts)")
+    t0 = time.perf_counter()
+    layers = build_layers(cfg, n_layers, a.seed, moe, torch)
+    log(f"layers resident in HBM ({time.perf_counter() - t0:.1f} s)")
+    xb = np.stack([gen.activations(a.seed, 2000 + l, 0, n_tok, cfg.D, cfg.x_dtype)
+                   for l in range(n_layers)])  # [layer, token, D]
+    x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty(n_layers, 1, cfg.D, dtype=torch.float32, device="cuda")
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+
+    def token(t):
+        for l in range(n_layers):
+            router, routed, shared, bias = layers[l]
+            moe.moe_layer_forward(x_all[l, t:t + 1], router, cfg.k, routed, shared, out[l], ws,
+                                  logit_bias=bias)
+
+    G = 8
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for t in range(G):
+            token(t)
+    torch.cuda.synchronize()
+    for g0 in range(0, n_tok, G):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for t in range(g0, g0 + G):
+                token(t)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graphs[0].replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    per_token = gen.algorithmic_decode_bytes(cfg) * n_layers
+    res = {"tokens": n_tok, "layers": n_layers, "ms": ms, "tokens_per_s": n_tok / (ms / 1e3),
+           "us_per_token": ms * 1e3 / n_tok, "us_per_layer_token": ms * 1e3 / n_tok / n_layers,
+           "GBps": per_token * n_tok / (ms / 1e3) / 1e9, "beta": cfg.beta}
+    log(f"stack: {res}")
+    return res
+
+
+def run_streamed(cfg, a, moe, torch):
+    """30 layers, 16 HBM slots per layer, experts streamed from pinned host memory."""
+    n_layers, n_tok = cfg.layers, a.stream_tokens
+    nb = gen.blob_bytes(cfg.D, cfg.F)
+    log(f"streamed: pinning {n_layers * cfg.E * nb / 1e9:.1f} GB of host experts")
+    t0 = time.perf_counter()
+    host, devs = [], []
+    for l in range(n_layers):
+        h = torch.empty((cfg.E, nb), dtype=torch.uint8, pin_memory=True)
+        lw = gen.layer_weights(a.seed, l, cfg, experts_out=h.numpy())
+        host.append(h)
+        devs.append((moe.DeviceQMat(lw.router.codes, lw.router.meta, cfg.E, cfg.D, 8),
+                     moe.DeviceBank.from_numpy(lw.shared[None, :], cfg.D, cfg.F_shared),
+                     torch.from_numpy(gen.zipf_bias(a.seed, l, cfg.E, cfg.beta)).cuda()))
+    log(f"host experts ready ({time.perf_counter() - t0:.1f} s)")
+    pool = moe.Pool(host, n_layers, cfg.slots, cfg.E, cfg.D, cfg.F)
+    xb = np.stack([gen.activations(a.seed, 2000 + l, 0, n_tok + 16, cfg.D, cfg.x_dtype)
+                   for l in range(n_layers)])
+    x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+
+    def token(t):
+        for l in range(n_layers):
+            router, shared, bias = devs[l]
+            moe.moe_layer_forward(x_all[l, t:t + 1], router, cfg.k, None, shared, out, ws,
+                                  logit_bias=bias, pool=pool, layer=l)
+
+    for t in range(16):  # warm the slots
+        token(n_tok + t)
+    torch.cuda.synchronize()
+    pool.reset_stats()
+    t0 = time.perf_counter()
+    for t in range(n_tok):
+        token(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    st = pool.stats()
+    # pinned host -> HBM copy peak for comparison
+    src = host[0].reshape(-1)[: 256 << 20]
+    dst = torch.empty(src.numel(), dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(4):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    peak = 4 * src.numel() / (time.perf_counter() - t1) / 1e9
+    res = {"tokens": n_tok, "layers": n_layers, "slots": cfg.slots, "s": el,
+           "tokens_per_s": n_tok / el, "hit_rate": st["hits"] / max(1, st["lookups"]),
+           "miss_MB_per_token": st["bytes_h2d"] / n_tok / 1e6,
+           "h2d_GBps": st["bytes_h2d"] / el / 1e9, "pinned_copy_peak_GBps": peak, "beta": cfg.beta}
+    log(f"streamed: {res}")
+    pool.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=256)
-    ap.add_argument("--config", default="decode", choices=["decode", "prefill", "stack30"])
+    ap.add_argument("--config", default="decode",
+                    choices=["decode", "prefill", "stack30", "streamed"])
+    ap.add_argument("--stream-tokens", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device copy (counter calibration)")
     ap.add_argument("--tune", action="append", default=[],
                     help="launch-shape knob key=value (moe_set_tuning), repeatable")
     a = ap.parse_args()
@@ -100,6 +238,10 @@ def main():
         key, val = kv.split("=")
         moe.moe_set_tuning(key, int(val))
     cfg = gen.CONFIGS[a.config]
+    if a.config in ("stack30", "streamed"):
+        res = (run_stack if a.config == "stack30" else run_streamed)(cfg, a, moe, torch)
+        print(json.dumps({"config": a.config, **res}), flush=True)
+        return
     n_layers = cfg.layers
     T = cfg.T
     log(f"config {cfg.name}: generating {n_layers} layer(s)")
@@ -152,6 +294,34 @@ def main():
     log(f"{steps} steps in {ms:.2f} ms: {ms_step * 1e3:.2f} us/step, {tokens_per_s:,.0f} tokens/s"
         + (f", {gbps:,.0f} GB/s" if gbps else ""))
 
+    # expert-phase kernel duration, measured with events the library records
+    # around that launch on its own stream (eager steps)
+    n_prof = min(512, steps)
+    with moe.ProfileEvents(n_prof) as pe, torch.cuda.stream(stream):
+        for i in range(n_prof):
+            step(i)
+        torch.cuda.synchronize()
+        kms = pe.elapsed_ms(n_prof)
+    k_us = 1e3 * float(np.mean(kms))
+    if T == 1:
+        k_bytes = gen.algorithmic_decode_bytes(cfg) - gen.codes_bytes(cfg.E, cfg.D, 8) \
+            - gen.meta_bytes(cfg.E, cfg.D)
+        k_name = "experts_fused_kernel (gate/up + down + combine of the 8 routed and the shared expert)"
+    else:
+        k_bytes = None
+        k_name = "grouped prefill expert kernels"
+    k_gbps = k_bytes / (k_us * 1e-6) / 1e9 if k_bytes else None
+    log(f"expert phase: {k_us:.2f} us per launch" + (f", {k_gbps:,.0f} GB/s" if k_gbps else ""))
+    traffic = stored_traffic(k_bytes)
+
+    if a.calibrate_copy:
+        # a plain copy of known size, for scaling the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     cpu = None
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -177,9 +347,10 @@ def main():
                                f"rotated", "tokens_per_step": T, "layers_rotated": n_layers,
                    "parallelism": "single GPU"},
         "hbm_GBps": gbps,
-        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS if gbps else None, "traffic": None,
-                     "kernel": "whole layer step (route, glu, down_combine)"},
+        "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": k_gbps / HBM_PEAK_GBPS if k_gbps else None, "traffic": traffic,
+                     "kernel": k_name, "us_per_launch": k_us,
+                     "algorithmic_bytes_per_launch": k_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

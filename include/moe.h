@@ -171,6 +171,15 @@ moe_status moe_pool_reset_stats(moe_pool *pool);
 moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
                           const int32_t *ids, int32_t *events);
 
+/* Timing probe for measurement tools: while set, every moe_layer_forward
+ * records events[2i] (a hipEvent_t) on its stream just before its expert
+ * phase -- all work after routing: the one-launch expert kernel for decode,
+ * the grouped matrix-core kernels for prefill -- and events[2i + 1] just
+ * after it, i cycling through 0..n_pairs-1.  events: HOST array of 2*n_pairs
+ * event handles owned by the caller; NULL / 0 turns the probe off.
+ * Process-wide, single host thread. */
+moe_status moe_set_profile_events(void *const *events, int32_t n_pairs);
+
 /* Tuning knobs of the launch shapes ("glu_ks", "down_ks", ...); returns
  * MOE_E_INVALID for an unknown key or value.  Process-wide. */
 moe_status moe_set_tuning(const char *key, int32_t value);

@@ -66,8 +66,8 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;
   const int D = a.D, G = D / 64, NB = D / 64;
-  const bool has_g = b < f.n_gtiles * f.KSg;
-  const bool has_d = b < a.T * NB * f.KSd;
+  const bool has_g = b < (f.tile_end - f.tile_begin) * f.KSg;
+  const bool has_d = f.do_down && b < a.T * NB * f.KSd;
 
   // ---------------- issue the gate/up loads of this block's tile split
   GluTile gt{};
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
   u32x4 qg0[kMaxG], qg1[kMaxG], qu0[kMaxG], qu1[kMaxG];
   uint32_t mg[kMaxG], mu[kMaxG];
   if (has_g) {
-    const int tile = b / f.KSg, ks = b - tile * f.KSg;
+    const int tile = f.tile_begin + b / f.KSg, ks = b % f.KSg;
     gt = fused_tile(f, tile);
     g0 = ks * G / f.KSg;
     g1 = (ks + 1) * G / f.KSg;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
         v0 += red[w][0][lane];
         v1 += red[w][1][lane];
       }
-      const int tile = b / f.KSg, ks = b - tile * f.KSg;
+      const int tile = f.tile_begin + b / f.KSg, ks = b % f.KSg;
       bool last = true;
       if (f.KSg > 1) {
         float *part = f.gpart + (size_t)tile * f.KSg * 128;
@@ -315,8 +315,8 @@ int g_capacity[4096];  // co-resident blocks per (device, dtype, kernel shape)
 }  // namespace
 
 int fused_grid(const FusedLaunch &f) {
-  const int g = f.n_gtiles * f.KSg;
-  const int d = f.a.T * (f.a.D / 64) * f.KSd;
+  const int g = (f.tile_end - f.tile_begin) * f.KSg;
+  const int d = f.do_down ? f.a.T * (f.a.D / 64) * f.KSd : 0;
   return g > d ? g : d;
 }
 
@@ -373,6 +373,7 @@ hipError_t fused_capacity(const FusedLaunch &f, int *cap) {
 
 hipError_t launch_fused(const FusedLaunch &f, hipStream_t s) {
   const int grid = fused_grid(f);
+  if (grid <= 0) return hipSuccess;
   const int mg = fused_max_g(f), mu = fused_max_u(f);
   KernelFn k = f.a.f16x ? pick_kernel<true>(mg, mu) : pick_kernel<false>(mg, mu);
   if (!k) return hipErrorInvalidValue;

@@ -14,6 +14,27 @@ Tuning &tuning() {
 }
 
 namespace {
+struct ProfileEvents {
+  void *const *events = nullptr;
+  int n = 0, next = 0;
+};
+ProfileEvents g_prof;
+
+// Records the probe's begin event of the next pair (returns the pair index).
+int prof_begin(hipStream_t s) {
+  if (!g_prof.events || g_prof.n <= 0) return -1;
+  const int i = g_prof.next;
+  g_prof.next = (g_prof.next + 1) % g_prof.n;
+  (void)hipEventRecord((hipEvent_t)g_prof.events[2 * i], s);
+  return i;
+}
+hipError_t prof_end(int i, hipStream_t s, hipError_t e) {
+  if (i >= 0) (void)hipEventRecord((hipEvent_t)g_prof.events[2 * i + 1], s);
+  return e;
+}
+}  // namespace
+
+namespace {
 
 // Reserves aligned regions of a workspace in a fixed order.  With base ==
 // nullptr it only measures.
@@ -105,6 +126,9 @@ bool plan_fused(const ExpertLaunch &a, const Workspace &w, FusedLaunch *f) {
   f->KSg = ksg;
   f->KSd = ksd;
   f->n_gtiles = n_gtiles;
+  f->tile_begin = 0;
+  f->tile_end = n_gtiles;
+  f->do_down = 1;
   int cap = 0;
   if (fused_capacity(*f, &cap) != hipSuccess || cap <= 0) return false;
   const int grid = fused_grid(*f);
@@ -155,6 +179,14 @@ const char *moe_status_string(moe_status st) {
     case MOE_E_POOL: return "expert pool error";
     default: return "unknown status";
   }
+}
+
+moe_status moe_set_profile_events(void *const *events, int32_t n_pairs) {
+  if (events && n_pairs <= 0) return MOE_E_INVALID;
+  g_prof.events = n_pairs > 0 ? events : nullptr;
+  g_prof.n = events ? n_pairs : 0;
+  g_prof.next = 0;
+  return MOE_OK;
 }
 
 moe_status moe_set_tuning(const char *key, int32_t value) {
@@ -282,19 +314,20 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   r.logit_bias = logit_bias;
   r.logits = w.logits; r.ids = ids_out ? ids_out : w.ids; r.gates = gates_out ? gates_out : w.gates;
   r.xp = w.xp; r.xs = w.xs; r.counters = w.counters;
-  // resident experts: the router also resolves each selected expert's blob
+  // resident experts: the router also resolves each selected expert's blob;
+  // streamed experts: the pool writes the slot addresses after its copies
   r.table = pool ? nullptr : routed->blobs;
   r.slot_blob = pool ? nullptr : w.slot_blob;
 
   ExpertLaunch a{};
   a.f16x = r.f16x; a.T = T; a.k = k; a.D = D; a.E = E;
-  a.xp = w.xp; a.xs = w.xs; a.ids = r.ids; a.gates = r.gates; a.slot_blob = r.slot_blob;
+  a.xp = w.xp; a.xs = w.xs; a.ids = r.ids; a.gates = r.gates; a.slot_blob = w.slot_blob;
   a.rblobs = pool ? nullptr : routed->blobs; a.F = F;
   a.sblobs = shared ? shared->blobs : nullptr; a.Fs = Fs;
   a.h = w.h; a.hs = w.hs; a.part = w.part; a.counters = w.counters;
   a.y = nullptr; a.out = out; a.out_dtype = out_dtype;
   FusedLaunch f;
-  const bool fused = !pool && tuning().fused && plan_fused(a, w, &f);
+  const bool fused = tuning().fused && plan_fused(a, w, &f);
   if (fused) {
     r.zero = w.fcounters;
     r.zero_words = (int)(f.slot_cnt + T * (k + 1) - w.fcounters);
@@ -303,8 +336,29 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     r.zero2_stride = 32;
   }
   if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
-  if (fused) return hip_status(launch_fused(f, s));
+  if (fused && !pool) {
+    const int pi = prof_begin(s);
+    return hip_status(prof_end(pi, s, launch_fused(f, s)));
+  }
 
+  if (pool && fused) {
+    // Streamed experts: ids back to the host; the shared expert's gate/up
+    // tiles run while the host plans and the side stream copies the missing
+    // experts into HBM slots; then the routed tiles, down and combine.  The
+    // splits are those of the resident launch, so results are bitwise equal.
+    st = pool_fetch_ids(pool, r.ids, T * k, s);
+    if (st) return st;
+    const int n_routed_tiles = T * k * (F / 64);
+    FusedLaunch fs = f;
+    fs.tile_begin = n_routed_tiles;
+    fs.do_down = 0;
+    if (launch_fused(fs, s) != hipSuccess) return MOE_E_HIP;
+    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, w.slot_blob);
+    if (st) return st;
+    FusedLaunch fr = f;
+    fr.tile_end = n_routed_tiles;
+    return hip_status(launch_fused(fr, s));
+  }
   // prefill chunk: group the (token, slot) pairs by expert, then matrix cores
   if (!pool && T >= tuning().prefill_min_t && T * k <= 65536 && D / 64 <= kMaxDGroups &&
       F / 64 <= kMaxHGroups && Fs / 64 <= kMaxHGroups) {
@@ -318,11 +372,13 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     pl.xp = w.xp; pl.xs = w.xs;
     pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;
     pl.hsum = w.hsum; pl.y = w.y; pl.ys = w.ys; pl.out = out; pl.out_dtype = out_dtype;
-    return hip_status(launch_prefill_experts(pl, s));
+    const int pi = prof_begin(s);
+    return hip_status(prof_end(pi, s, launch_prefill_experts(pl, s)));
   }
 
   const int routed_blocks = T * k * (F / 64);
   const int all_blocks = glu_blocks(a);
+  a.slot_blob = pool ? nullptr : w.slot_blob;
   // one reduction split for the whole layer, so the streamed path (shared and
   // routed tiles launched apart) sums in the same order as the resident one
   a.glu_ks = pick_ks(all_blocks, D / 64, glu_min_ks(D), tuning().glu_ks);
@@ -333,8 +389,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     return hip_status(launch_down(a, true, s));
   }
 
-  // Streamed experts: ids back to the host, shared expert on the GPU while the
-  // host plans and the side stream copies the misses into HBM slots.
+  // streamed experts, three-kernel shape (when the one-launch grid does not fit)
   st = pool_fetch_ids(pool, r.ids, T * k, s);
   if (st) return st;
   if (shared) {
@@ -342,7 +397,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     if (launch_glu(a, s) != hipSuccess) return MOE_E_HIP;
   }
   const void *const *table = nullptr;
-  st = pool_plan_and_copy(pool, layer, T, k, s, &table);
+  st = pool_plan_and_copy(pool, layer, T, k, s, &table, nullptr);
   if (st) return st;
   a.rblobs = table;
   a.glu_first = 0; a.glu_count = routed_blocks;

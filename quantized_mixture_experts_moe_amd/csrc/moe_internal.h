@@ -123,6 +123,8 @@ constexpr int kFlagCopies = 16;  // replicas of each slot-ready flag (one 128-by
 struct FusedLaunch {
   ExpertLaunch a;           // needs slot_blob (resident experts)
   int KSg, KSd, n_gtiles;
+  int tile_begin, tile_end; // gate/up tiles of this launch (routed tiles, then shared)
+  int do_down;              // this launch also runs the down projection and combine
   // counters and flags: zeroed by the router kernel launched just before
   uint32_t *tile_cnt, *slot_cnt, *out_cnt, *slot_flag, *err;
   float *gpart, *dpart;

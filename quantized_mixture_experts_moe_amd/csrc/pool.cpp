@@ -72,6 +72,7 @@ struct moe_pool {
   const void **d_tables = nullptr;            // device [n_layers][E] blob pointers
   const void **h_tables = nullptr;            // pinned host mirror of d_tables
   int32_t *h_ids = nullptr;                   // pinned host ids of the last call
+  const void **h_slot = nullptr;              // pinned staging of per-pair slot addresses
   int ids_cap = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_ids = nullptr, ev_copies = nullptr;
@@ -91,10 +92,17 @@ int pool_F(const moe_pool *p) { return p->F; }
 
 moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s) {
   if (n > p->ids_cap) {
+    // earlier copies from the staging buffers have completed: every call
+    // waits on its id readback, which follows the previous call's kernels
     if (p->h_ids) (void)hipHostFree(p->h_ids);
+    if (p->h_slot) (void)hipHostFree(p->h_slot);
     p->h_ids = nullptr;
+    p->h_slot = nullptr;
+    p->ids_cap = 0;
     if (hipHostMalloc((void **)&p->h_ids, sizeof(int32_t) * n, hipHostMallocDefault) !=
-        hipSuccess)
+            hipSuccess ||
+        hipHostMalloc((void **)&p->h_slot, sizeof(void *) * n, hipHostMallocDefault) !=
+            hipSuccess)
       return MOE_E_HIP;
     p->ids_cap = n;
   }
@@ -106,7 +114,7 @@ moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t 
 }
 
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
-                              const void *const **table) {
+                              const void *const **table, const void **slot_blob) {
   if (hipEventSynchronize(p->ev_ids) != hipSuccess) return MOE_E_HIP;
   // distinct experts of the call in first-use order
   std::vector<int> need;
@@ -140,14 +148,24 @@ moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t 
     ++copies;
   }
   p->stats.hits += (uint64_t)T * k - copies;
-  if (copies) {
+  bool queued = copies > 0;
+  if (copies && table) {
     if (hipMemcpyAsync(p->d_tables + (size_t)layer * p->E, tab, sizeof(void *) * p->E,
                        hipMemcpyHostToDevice, p->side) != hipSuccess)
       return MOE_E_HIP;
+  }
+  if (slot_blob) {
+    for (int i = 0; i < T * k; ++i) p->h_slot[i] = tab[p->h_ids[i]];
+    if (hipMemcpyAsync(slot_blob, p->h_slot, sizeof(void *) * T * k, hipMemcpyHostToDevice,
+                       p->side) != hipSuccess)
+      return MOE_E_HIP;
+    queued = true;
+  }
+  if (queued) {
     if (hipEventRecord(p->ev_copies, p->side) != hipSuccess) return MOE_E_HIP;
     if (hipStreamWaitEvent(s, p->ev_copies, 0) != hipSuccess) return MOE_E_HIP;
   }
-  *table = p->d_tables + (size_t)layer * p->E;
+  if (table) *table = p->d_tables + (size_t)layer * p->E;
   return MOE_OK;
 }
 
@@ -226,6 +244,7 @@ moe_status moe_pool_destroy(moe_pool *p) {
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->h_tables) (void)hipHostFree(p->h_tables);
   if (p->h_ids) (void)hipHostFree(p->h_ids);
+  if (p->h_slot) (void)hipHostFree(p->h_slot);
   if (p->ev_ids) (void)hipEventDestroy(p->ev_ids);
   if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
   if (p->side) (void)hipStreamDestroy(p->side);

@@ -32,7 +32,11 @@ class LfuPlanner {
 moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k);
 int pool_F(const moe_pool *p);
 moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s);
+// Plans the call's experts, copies the misses into HBM slots on the side
+// stream and makes stream s wait for them.  Publishes the layer's device
+// pointer table (*table, if non-null) and, if slot_blob is non-null, the slot
+// address of every (token, slot) pair into that device array.
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
-                              const void *const **table);
+                              const void *const **table, const void **slot_blob);
 
 }  // namespace moe

@@ -35,7 +35,7 @@ EXPORTS = (
     "moe_blob_bytes", "moe_workspace_bytes", "moe_route", "moe_expert_ffn", "moe_combine",
     "moe_permute", "moe_layer_forward", "moe_pool_create", "moe_pool_destroy",
     "moe_pool_get_stats", "moe_pool_reset_stats", "moe_lfu_replay", "moe_set_tuning",
-    "moe_status_string",
+    "moe_set_profile_events", "moe_status_string",
 )
 
 
@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "moe_pool_reset_stats": (i32, [vp]),
         "moe_lfu_replay": (i32, [i32, i32, i32, i32, vp, vp]),
         "moe_set_tuning": (i32, [ctypes.c_char_p, i32]),
+        "moe_set_profile_events": (i32, [vp, i32]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -124,6 +125,29 @@ def moe_workspace_bytes(T: int, k: int, E: int, D: int, F: int, F_shared: int) -
 
 def moe_set_tuning(key: str, value: int) -> None:
     _check(lib.moe_set_tuning(key.encode(), value), "moe_set_tuning")
+
+
+class ProfileEvents:
+    """Timing-event pairs the library records around its expert phase."""
+
+    def __init__(self, n_pairs: int):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_pairs)]
+        for e in self.events:  # create the underlying hipEvent
+            e.record()
+        torch.cuda.synchronize()
+        self._arr = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+        self.n = n_pairs
+
+    def __enter__(self):
+        _check(lib.moe_set_profile_events(ctypes.cast(self._arr, ctypes.c_void_p), self.n),
+               "moe_set_profile_events")
+        return self
+
+    def __exit__(self, *exc):
+        lib.moe_set_profile_events(None, 0)
+
+    def elapsed_ms(self, count: int):
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(count)]
 
 
 # --------------------------------------------------------------------------

@@ -340,3 +340,39 @@ def test_layer_forward_prefill_ragged_chunk():
     busiest = int(np.argmax(counts))
     toks = sorted(set(np.nonzero(ids == busiest)[0].tolist()))
     _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=toks[:6] + toks[-6:] + [76])
+
+
+def test_pool_decode_shapes_streamed_equals_resident():
+    """Decode-shaped layers, 16 HBM slots each: streamed output is bitwise the
+    resident output, the pool's hit/miss counts follow the LFU model, and a
+    sampled token matches the oracle."""
+    _case("pool streamed vs resident (decode shapes, 2 layers, 16 slots)")
+    cfg = gen.CONFIGS["decode"]
+    layers = [dev_layer("decode", seed=0, layer=l) for l in range(2)]
+    host = [torch.from_numpy(L.lw.experts).pin_memory() for L in layers]
+    pool = moe.Pool(host, 2, 16, cfg.E, cfg.D, cfg.F)
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    models = [O.LFUCache(16, cfg.E) for _ in range(2)]
+    misses = 0
+    for tok in range(10):
+        for l, L in enumerate(layers):
+            xb = gen.activations(5, l, tok, 1, cfg.D, cfg.x_dtype)
+            bias_np = gen.zipf_bias(0, l, cfg.E, 6.5)
+            bias = torch.from_numpy(bias_np).cuda()
+            x = x_dev(xb, cfg.x_dtype)
+            o_s = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+            o_r = torch.empty_like(o_s)
+            ids = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
+            moe.moe_layer_forward(x, L.router, cfg.k, None, L.shared, o_s, ws, logit_bias=bias,
+                                  pool=pool, layer=l, ids_out=ids)
+            moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, o_r, ws, logit_bias=bias)
+            torch.cuda.synchronize()
+            assert torch.equal(o_s, o_r), (tok, l)
+            got_ids = ids.cpu().numpy()
+            ev = models[l].access(got_ids[0])
+            misses += sum(1 for e in ev if not e[2])
+            if tok == 9 and l == 1:
+                _check_layer(L, xb, o_s.cpu().numpy(), got_ids, cfg.k, bias_np)
+    st = pool.stats()
+    assert st["misses"] == misses and st["lookups"] == 10 * 2 * cfg.k
+    pool.close()
