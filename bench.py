@@ -84,11 +84,11 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(k_bytes):
-    """HBM bytes per expert-phase launch from the committed counter runs
+def stored_traffic(name):
+    """HBM bytes per launch of the timed kernel from the committed counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), only if they were taken
     on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "decode_expert_phase_traffic.json")
+    p = os.path.join(ROOT, "profiles", name)
     try:
         rec = json.load(open(p))
     except (OSError, ValueError):
@@ -294,8 +294,9 @@ def main():
     log(f"{steps} steps in {ms:.2f} ms: {ms_step * 1e3:.2f} us/step, {tokens_per_s:,.0f} tokens/s"
         + (f", {gbps:,.0f} GB/s" if gbps else ""))
 
-    # expert-phase kernel duration, measured with events the library records
-    # around that launch on its own stream (eager steps)
+    # duration of the dominant kernel, measured with events the library records
+    # around that launch on its own stream (eager steps): the one-launch layer
+    # for a decode token, else the expert phase
     n_prof = min(512, steps)
     with moe.ProfileEvents(n_prof) as pe, torch.cuda.stream(stream):
         for i in range(n_prof):
@@ -303,16 +304,23 @@ def main():
         torch.cuda.synchronize()
         kms = pe.elapsed_ms(n_prof)
     k_us = 1e3 * float(np.mean(kms))
-    if T == 1:
+    layer_path = T == 1 and "layer=0" not in a.tune
+    if layer_path:
+        k_bytes = gen.algorithmic_decode_bytes(cfg)
+        k_name = ("decode_layer_kernel (router, top-8, gate/up, down and combine of the 8 "
+                  "routed and the shared expert in one launch)")
+        traffic = stored_traffic("decode_layer_traffic.json")
+    elif T == 1:
         k_bytes = gen.algorithmic_decode_bytes(cfg) - gen.codes_bytes(cfg.E, cfg.D, 8) \
             - gen.meta_bytes(cfg.E, cfg.D)
         k_name = "experts_fused_kernel (gate/up + down + combine of the 8 routed and the shared expert)"
+        traffic = stored_traffic("decode_expert_phase_traffic.json")
     else:
         k_bytes = None
         k_name = "grouped prefill expert kernels"
+        traffic = None
     k_gbps = k_bytes / (k_us * 1e-6) / 1e9 if k_bytes else None
-    log(f"expert phase: {k_us:.2f} us per launch" + (f", {k_gbps:,.0f} GB/s" if k_gbps else ""))
-    traffic = stored_traffic(k_bytes)
+    log(f"timed kernel: {k_us:.2f} us per launch" + (f", {k_gbps:,.0f} GB/s" if k_gbps else ""))
 
     if a.calibrate_copy:
         # a plain copy of known size, for scaling the HBM byte counters

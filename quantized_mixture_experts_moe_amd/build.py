@@ -23,7 +23,7 @@ OUT = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "libmoe")
 
 SOURCES = ["moe_api.cpp", "pool.cpp", "route.hip", "expert_gemv.hip", "expert_fused.hip",
-           "permute.hip", "prefill_mfma.hip"]
+           "permute.hip", "prefill_mfma.hip", "layer_decode.hip"]
 
 
 def hipcc() -> str:

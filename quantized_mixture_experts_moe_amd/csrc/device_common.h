@@ -152,6 +152,12 @@ __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
 __device__ __forceinline__ uint32_t add_dev(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // all outstanding memory operations of this wave have completed
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -172,6 +178,43 @@ __device__ __forceinline__ float dot_group_f32(const u32x4 q0, const u32x4 q1, c
     }
   }
   return acc;
+}
+
+// Deterministic reduction over the splits of a tile (wave-wide, R rows of 64
+// values).  Each split adds its partials, rounded to multiples of 2^-32, into
+// 64-bit integer accumulators with device-scope atomics; integer addition
+// gives the same sum in any arrival order, so results are bitwise
+// reproducible.  After its adds have completed, each split bumps the tile's
+// counter; the split that arrives last reads the sums into out[] (returns
+// true) and puts the accumulators and the counter back to zero, so they are
+// zero between calls.  The rounding is 2^-33 per partial; sums must stay
+// below 2^31 in magnitude.
+__device__ __forceinline__ long long to_fixed32(float v) {
+  return __double2ll_rn((double)v * 4294967296.0);
+}
+__device__ __forceinline__ float from_fixed32(long long a) {
+  return (float)((double)a * (1.0 / 4294967296.0));
+}
+template <int R>
+__device__ __forceinline__ bool split_reduce_fixed(uint64_t *acc, uint32_t *counter, int nsplits,
+                                                   const float (&v)[R], float (&out)[R]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    __hip_atomic_fetch_add(acc + r * 64 + lane, (uint64_t)to_fixed32(v[r]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  wait_all_memory();
+  uint32_t old = 0;
+  if (lane == 0) old = add_dev(counter, 1u);
+  old = __shfl(old, 0, 64);
+  if (old != (uint32_t)(nsplits - 1)) return false;
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r] = from_fixed32((long long)ld_dev(acc + r * 64 + lane));
+  wait_all_memory();
+#pragma unroll
+  for (int r = 0; r < R; ++r) st_dev(acc + r * 64 + lane, (uint64_t)0);
+  if (lane == 0) st_dev(counter, 0u);
+  return true;
 }
 
 template <int N>
@@ -217,6 +260,105 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int wave_min(int v) {
   MOE_DPP_REDUCE(int, v, i_min, 0x7FFFFFFF, dpp_i32)
   return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Sum of 64 values of which each of 8 consecutive lanes (8q .. 8q + 7) holds
+// the in-order sum of 8: the lanes combine through DPP as
+// ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7)); all 8 lanes receive the
+// total.  The 64-column activation sums of the 4-bit kernels use this order
+// everywhere, so every path gets the same bits.
+__device__ __forceinline__ float sum8_lanes(float v) {
+  v = v + dpp_f32<0xB1>(v, 0.0f);   // quad_perm [1, 0, 3, 2]
+  v = v + dpp_f32<0x4E>(v, 0.0f);   // quad_perm [2, 3, 0, 1]
+  v = v + dpp_f32<0x141>(v, 0.0f);  // row_half_mirror
+  return v;
+}
+
+// Order-preserving map of a float to an unsigned key (larger float, larger
+// key); -0 maps like +0, so equal floats get equal keys.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Top-k of one token's logits held by one wave, v[j] = logit of expert
+// lane + 64 j (-inf beyond E): larger first, equal logits to the lower index.
+// Lane r < k receives the r-th id and its softmax gate over the k selected
+// logits.  The k-th largest key is found bit by bit from the top (32 rounds
+// of compare + ballot + popcount), the selected entries are compacted in
+// index order through xch (LDS, 128 entries for this wave) and ranked among
+// themselves.  NV is a compile-time bound so that v[] stays in registers.
+template <int NV>
+__device__ __forceinline__ void topk_regs(float (&v)[NV], int k, uint2 *xch, int32_t *id_out,
+                                          float *gate_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) key[j] = order_key(v[j]);
+  // tau: the largest key with at least k keys >= tau, i.e. the k-th largest
+  uint32_t tau = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= k) tau = cand;
+  }
+  // selected: keys above tau, then keys equal to tau in index order
+  int quota = k;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) quota -= __popcll(__ballot(key[j] > tau));
+  int before = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    uint64_t eq = __ballot(key[j] == tau);
+    uint64_t take = 0;
+    while (quota > 0 && eq) {
+      const uint64_t low = eq & (~eq + 1);
+      take |= low;
+      eq ^= low;
+      --quota;
+    }
+    const uint64_t sel = __ballot(key[j] > tau) | take;
+    if ((sel >> lane) & 1u) xch[before + (int)lanes_below(sel)] = make_uint2(key[j], lane + 64 * j);
+    before += __popcll(sel);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // rank among the selected (entries are in index order): larger keys first,
+  // equal keys by position
+  uint2 mine = make_uint2(0u, 0u);
+  int rank = 0;
+  if (lane < k) {
+    mine = xch[lane];
+    for (int s2 = 0; s2 < k; ++s2) {
+      const uint2 o = xch[s2];
+      rank += (o.x > mine.x || (o.x == mine.x && s2 < lane)) ? 1 : 0;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) xch[64 + rank] = mine;
+  __builtin_amdgcn_wave_barrier();
+  float myv = 0.0f;
+  int myi = 0;
+  if (lane < k) {
+    const uint2 r = xch[64 + lane];
+    myv = key_value(r.x);
+    myi = (int)r.y;
+  }
+  const float m0 =
+      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
+  const float z = lane < k ? expf(myv - m0) : 0.0f;
+  const float sum = wave_sum(z);
+  *id_out = myi;
+  *gate_out = z / sum;
 }
 
 __device__ __forceinline__ float gelu_tanh(float x) {

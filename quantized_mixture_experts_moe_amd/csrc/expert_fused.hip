@@ -179,32 +179,15 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
         v0 += red[w][0][lane];
         v1 += red[w][1][lane];
       }
-      const int tile = f.tile_begin + b / f.KSg, ks = b % f.KSg;
+      const int tile = f.tile_begin + b / f.KSg;
       bool last = true;
       if (f.KSg > 1) {
-        float *part = f.gpart + (size_t)tile * f.KSg * 128;
-        st_dev(part + ks * 128 + lane, v0);
-        st_dev(part + ks * 128 + 64 + lane, v1);
-        wait_all_memory();
-        uint32_t old = 0;
-        if (lane == 0) old = add_dev(f.tile_cnt + tile, 1u);
-        old = __shfl(old, 0, 64);
-        last = old == (uint32_t)(f.KSg - 1);
-        if (last) {
-          float pg[kMaxKS], pu[kMaxKS];
-#pragma unroll
-          for (int p = 0; p < kMaxKS; ++p) {
-            pg[p] = p < f.KSg ? ld_dev(part + p * 128 + lane) : 0.0f;
-            pu[p] = p < f.KSg ? ld_dev(part + p * 128 + 64 + lane) : 0.0f;
-          }
-          v0 = 0.0f;
-          v1 = 0.0f;
-#pragma unroll
-          for (int p = 0; p < kMaxKS; ++p) {
-            v0 += pg[p];
-            v1 += pu[p];
-          }
-        }
+        const float pv[2] = {v0, v1};
+        float sv[2];
+        last = split_reduce_fixed<2>(f.gacc + (size_t)tile * 128, f.gcnt + (size_t)tile * kCntStride,
+                                     f.KSg, pv, sv);
+        v0 = sv[0];
+        v1 = sv[1];
       }
       if (last) {
         const float h = gelu_tanh(v0) * v1;
@@ -277,22 +260,11 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
       const int ot = b / f.KSd;
       bool last = true;
       if (f.KSd > 1) {
-        float *part = f.dpart + (size_t)ot * f.KSd * 64;
-        st_dev(part + ksd * 64 + lane, s);
-        wait_all_memory();
-        uint32_t old = 0;
-        if (lane == 0) old = add_dev(f.out_cnt + ot, 1u);
-        old = __shfl(old, 0, 64);
-        last = old == (uint32_t)(f.KSd - 1);
-        if (last) {
-          float pp[kMaxFusedKSd];
-#pragma unroll
-          for (int p = 0; p < kMaxFusedKSd; ++p)
-            pp[p] = p < f.KSd ? ld_dev(part + p * 64 + lane) : 0.0f;
-          s = 0.0f;
-#pragma unroll
-          for (int p = 0; p < kMaxFusedKSd; ++p) s += pp[p];
-        }
+        const float pv[1] = {s};
+        float sv[1];
+        last = split_reduce_fixed<1>(f.dacc + (size_t)ot * 64, f.dcnt + (size_t)ot * kCntStride,
+                                     f.KSd, pv, sv);
+        s = sv[0];
       }
       if (last) {
         const size_t idx = (size_t)t_out * D + n;

@@ -1,0 +1,700 @@
+// One launch for the whole routed MoE layer of a decode step: router GEMV,
+// top-k and gates, gate/up GLU of the selected and the shared experts, down
+// projection and the weighted combine.
+//
+// Per token the pages score the experts with the resident 8-bit router, take
+// the top 8, run the selected 4-bit experts and the resident shared expert,
+// and add the two outputs (es.news.hada.io, "Proceso de generacion de
+// tokens"; yodev.dev, "Por que funciona: el A4B del nombre").  Routing is a
+// short chain of dependent steps, while the shared expert and the router do
+// not depend on it, so one launch runs them side by side: the router blocks
+// publish their logits first, every block issues the loads that need no
+// routing (shared-expert tiles), and each block that works on routed experts
+// selects them from the logits itself and issues those loads at once.
+//
+// Handoffs between blocks are tagged words: a 64-bit store of (value, tag)
+// with device scope, where the tag is the call's epoch.  A reader loads until
+// every word it needs carries the current tag, so nothing has to be reset
+// between calls and no full-cache fence is needed.  Each block keeps its own
+// copy of the epoch (bep[b]); every block advances all copies in lockstep, so
+// they agree for any grid size.  All blocks of the grid must be resident at
+// once (checked on the host); every wait is bounded and a timeout bumps an
+// error counter.
+//
+// Work split (one token, k = 8, D = 2816, F = 704, F_s = 2112):
+//   router:  E / 8 blocks of 8 experts; every block with routed work then
+//            selects the experts of its token from the published logits;
+//   gate/up: 121 tiles of 64 hidden rows (88 routed + 33 shared) x KSg
+//            reduction splits over the 44 column groups;
+//   down:    44 tiles of 64 output rows x KSd splits of the 121 (slot, group)
+//            units, units ordered slot by slot, the shared expert last.
+// Block b owns router item b, gate/up item b and down item b (those that
+// exist).
+#include <float.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kNW = 4;
+constexpr int kThreads = kNW * 64;
+constexpr int kRows = 8;                   // experts per router block
+constexpr int kKL = kThreads / kRows;      // threads splitting one router row
+constexpr long kSpin = 1L << 20;           // bounded waits, then the error counter
+
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t tagged(uint32_t bits, uint32_t tag) {
+  return (uint64_t)bits | ((uint64_t)tag << 32);
+}
+__device__ __forceinline__ bool has_tag(uint64_t v, uint32_t tag) {
+  return (uint32_t)(v >> 32) == tag;
+}
+
+// Wave-wide: loads the rows p[j * stride + lane] (j < n <= N, lane < lanes)
+// until every word carries `tag`, all rows in one round trip per try;
+// out[j] = value word.
+template <int N>
+__device__ __forceinline__ int wait_rows(const uint64_t *p, size_t stride, int n, uint32_t tag,
+                                         uint32_t *err, uint32_t (&out)[N], int lanes = 64) {
+  const int lane = threadIdx.x & 63;
+  for (long s = 0;; ++s) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      out[j] = 0u;
+      if (j < n && lane < lanes) {
+        const uint64_t v = ld_dev64(p + (size_t)j * stride + lane);
+        ok = ok && has_tag(v, tag);
+        out[j] = (uint32_t)v;
+      }
+    }
+    if (__all(ok)) return (int)s;
+    if (s > kSpin) {
+      if (lane == 0) add_dev(err, 1u);
+      return (int)s;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Wave-wide: polls one word per lane (p, or nothing where p is null) until
+// each carries `tag`.  Waiting on one word per producer store keeps the
+// polling traffic small; the data is read (and checked) afterwards.
+__device__ __forceinline__ int wait_hint(const uint64_t *p, uint32_t tag, uint32_t *err) {
+  const int lane = threadIdx.x & 63;
+  for (long s = 0;; ++s) {
+    const bool ok = !p || has_tag(ld_dev64(p), tag);
+    if (__all(ok)) return (int)s;
+    if (s > kSpin) {
+      if (lane == 0) add_dev(err, 1u);
+      return (int)s;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+template <bool F16X>
+__device__ __forceinline__ float x_to_f32(uint32_t v) {
+  return F16X ? f16_to_f32(v) : bf16_to_f32(v);
+}
+
+struct Tile {
+  int slot, t, j, rb, F;  // j: slot within the token (-1: shared expert)
+  size_t hoff;
+};
+
+__device__ __forceinline__ Tile glu_tile(const LayerLaunch &L, int tile) {
+  Tile g;
+  const int rbr = L.F / 64, n_rt = L.T * L.k * rbr;
+  if (tile < n_rt) {
+    g.slot = tile / rbr;
+    g.rb = tile - g.slot * rbr;
+    g.t = g.slot / L.k;
+    g.j = g.slot - g.t * L.k;
+    g.F = L.F;
+    g.hoff = (size_t)g.slot * L.F;
+  } else {
+    const int rbs = L.Fs / 64, b2 = tile - n_rt;
+    g.t = b2 / rbs;
+    g.rb = b2 - g.t * rbs;
+    g.slot = L.T * L.k + g.t;
+    g.j = -1;
+    g.F = L.Fs;
+    g.hoff = (size_t)L.T * L.k * L.F + (size_t)g.t * L.Fs;
+  }
+  return g;
+}
+
+// Selection for token t by the whole block once every router block has
+// published its logits.  Thread i < E polls logit i; then every thread ranks
+// its candidate against a share of the others with unique 64-bit keys
+// (order-preserving logit bits, then the complemented index, so equal logits
+// rank the lower index first), the partial ranks add up in LDS, and the k
+// winners land in rank order.  Wave 0 computes the softmax gates as the
+// single-wave selection does (same order, same bits) and resolves the blob
+// of each selected expert.  Every block that works on routed experts selects
+// for itself, which saves a round of publishing and polling.
+struct __align__(16) SelectLds {
+  uint64_t key[kThreads + 16];  // padded: rank loops read whole chunks of 16
+  uint32_t rank[kThreads];
+  uint2 sel[kMaxK];
+};
+
+__device__ void block_select(const LayerLaunch &L, int t, uint32_t tag, SelectLds &S,
+                             const void *const *table, const uint8_t **blob_out, float *gate_out,
+                             bool report) {
+  const int tid = threadIdx.x, lane = tid & 63, E = L.E, k = L.k;
+  const uint64_t *lg = L.rlog + (size_t)t * E;
+  float v = -INFINITY;
+  for (long s = 0;; ++s) {
+    bool ok = true;
+    if (tid < E) {
+      const uint64_t w = ld_dev64(lg + tid);
+      ok = has_tag(w, tag);
+      v = __uint_as_float((uint32_t)w);
+    }
+    if (__syncthreads_and(ok)) break;
+    if (s > kSpin) {
+      if (tid == 0) add_dev(L.err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (tid < E) {
+    S.key[tid] = ((uint64_t)order_key(v) << 32) | (uint64_t)(~(uint32_t)tid);
+    S.rank[tid] = 0u;
+  } else {
+    S.key[tid] = 0u;  // below every real key: padding never outranks
+  }
+  if (tid < 16) S.key[kThreads + tid] = 0u;
+  __syncthreads();
+  {
+    // parts of 16-key chunks per candidate: every key read is a broadcast
+    // and 16 of them are in flight before the compares
+    const int chunks = (E + 15) / 16;
+    const int parts = min(kThreads / E, chunks);  // E <= kThreads
+    const int i = tid % E, part = tid / E;
+    if (part < parts) {
+      const uint64_t ki = S.key[i];
+      const int c0 = part * chunks / parts, c1 = (part + 1) * chunks / parts;
+      uint32_t r = 0;
+      for (int c = c0; c < c1; ++c) {
+        uint64_t kj[16];
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+          const ulonglong2 p2 = *(const ulonglong2 *)&S.key[16 * c + q];
+          kj[q] = p2.x;
+          kj[q + 1] = p2.y;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) r += kj[q] > ki ? 1u : 0u;
+      }
+      atomicAdd(&S.rank[i], r);
+    }
+  }
+  __syncthreads();
+  if (tid < E && S.rank[tid] < (uint32_t)k) S.sel[S.rank[tid]] = make_uint2(tid, __float_as_uint(v));
+  __syncthreads();
+  if (tid < 64) {
+    float myv = 0.0f;
+    int myi = 0;
+    if (lane < k) {
+      const uint2 r = S.sel[lane];
+      myi = (int)r.x;
+      myv = __uint_as_float(r.y);
+    }
+    const float m0 =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
+    const float z = lane < k ? expf(myv - m0) : 0.0f;
+    const float sum = wave_sum(z);
+    const float gate = z / sum;
+    if (lane < k) {
+      blob_out[lane] = (const uint8_t *)table[myi];
+      gate_out[lane] = gate;
+      if (report) {
+        if (L.ids_out) L.ids_out[(size_t)t * k + lane] = myi;
+        if (L.gates_out) L.gates_out[(size_t)t * k + lane] = gate;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+constexpr int kMaxBlockGroups = 16;  // gate/up column groups of one block (4 waves x 4)
+
+template <bool F16X, int M, int MAXC>
+__global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L) {
+  constexpr int MAXX = MAXC == 6 ? 2 : 4;  // 16-byte pieces of x per thread (router)
+  extern __shared__ __align__(16) uint8_t dsm[];
+  __shared__ float red[kNW][2][64];
+  __shared__ float hbuf[kNW][M][64];
+  __shared__ __align__(16) uint32_t s_xp[kMaxBlockGroups * 32];  // activation pairs
+  __shared__ float s_xs[kMaxBlockGroups];                        // 64-column sums
+  __shared__ const uint8_t *s_blob[2][kMaxK];  // [0]: gate/up token, [1]: down token
+  __shared__ float s_gate[2][kMaxK];
+  __shared__ SelectLds s_select;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x;
+  const int D = L.D, E = L.E, k = L.k, T = L.T;
+  const int G = D / 64, NB = D / 64;
+  const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
+  const int U = k * Gf + Gs;
+  const uint32_t tag = as_const(L.bep)[b] + 1u;
+  const uint16_t *x = (const uint16_t *)L.x;
+
+  // ---------------- roles of this block
+  const int nrb = (E + kRows - 1) / kRows;
+  const bool has_r = b < T * nrb;
+  const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
+
+  const bool has_g = b < L.n_gtiles * L.KSg;
+  const int tile = b / L.KSg, ks = b - tile * L.KSg;
+  Tile gt{};
+  if (has_g) gt = glu_tile(L, tile);
+  const bool g_routed = has_g && gt.j >= 0;
+  const int g0 = ks * G / L.KSg, g1 = (ks + 1) * G / L.KSg;
+
+  const bool has_d = b < T * NB * L.KSd;
+  const int ot = b / L.KSd, ksd = b - ot * L.KSd;
+  const int t_out = ot / NB, n = (ot - t_out * NB) * 64 + lane;
+  const int u0 = ksd * U / L.KSd, u1 = (ksd + 1) * U / L.KSd;
+  const bool d_routed = has_d && u0 < k * Gf;
+  const bool routed = g_routed || d_routed;
+
+  // ---------------- router logits; block (t, 0) selects token t's experts.
+  // The router blocks do this before anything else: it heads the chain of
+  // dependent steps, and its registers are free again before the expert loads.
+  const int nch = D / 16;
+  float *sx = (float *)dsm;   // router: x as fp32 [D]
+  float *sxs = sx + D;        // router: 16-column sums [D/16]
+  float *rred = sxs + nch;    // router: partial logits [kKL][kRows]
+  if (has_r) {
+    __builtin_amdgcn_s_setprio(1);
+    const int rr = tid % kRows, kl = tid / kRows;  // chunks kl, kl + kKL, ... of row rr
+    u32x4 xr[MAXX], rq[MAXC];
+    uint32_t rmw[MAXC];
+    const gptr<u32x4> xt = as_global((const u32x4 *)(x + (size_t)r_t * D));
+#pragma unroll
+    for (int i = 0; i < MAXX; ++i) xr[i] = xt[min(tid + i * kThreads, D / 8 - 1)];
+    const int e = min(r_e0 + rr, E - 1);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = min(kl + i * kKL, nch - 1);
+      rq[i] = as_global((const u32x4 *)L.rcodes)[(size_t)c * E + e];
+      rmw[i] = as_global(L.rmeta)[(size_t)c / 4 * E + e];
+    }
+#pragma unroll
+    for (int i = 0; i < MAXX; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < D / 8) {
+        const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          sx[8 * c + 2 * m] = x_to_f32<F16X>(w[m] & 0xFFFFu);
+          sx[8 * c + 2 * m + 1] = x_to_f32<F16X>(w[m] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nch; i += kThreads) {
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s += sx[16 * i + j];
+      sxs[i] = s;
+    }
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = kl + i * kKL;
+      if (c < nch) {
+        const float sc = f16_to_f32(rmw[i]), bi = f16_to_f32(rmw[i] >> 16);
+        const uint32_t w[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
+        const float *xv = sx + c * 16;
+        float d = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            d = fmaf(xv[4 * u + bb], (float)((w[u] >> (8 * bb)) & 0xFFu), d);
+        acc = fmaf(sc, d, acc);
+        acc = fmaf(bi, sxs[c], acc);
+      }
+    }
+    rred[kl * kRows + rr] = acc;
+    __syncthreads();
+    if (wave == 0 && lane < kRows) {
+      float s = 0.0f;
+      for (int j = 0; j < kKL; ++j) s += rred[j * kRows + lane];
+      const int e2 = r_e0 + lane;
+      if (e2 < E) {
+        if (L.logit_bias) s += L.logit_bias[e2];
+        st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // ---------------- loads that need no routing, in the order they are used
+  // (a wait on one of them then waits for the earlier ones only)
+  // 1. this block's gate/up columns of x: 8 columns per thread
+  const int n8 = (g1 - g0) * 8;
+  u32x4 xq = {0u, 0u, 0u, 0u};
+  if (has_g && tid < n8) xq = as_global((const u32x4 *)(x + (size_t)gt.t * D + 64 * g0))[tid];
+  // 2. the routed bank's blob table
+  constexpr int kTab = kMaxLayerE / kThreads;
+  const void *tb[kTab];
+  if (routed) {
+#pragma unroll
+    for (int i = 0; i < kTab; ++i) {
+      const int e = tid + i * kThreads;
+      tb[i] = e < E ? as_global(L.rblobs)[e] : nullptr;
+    }
+  }
+  // 3. shared-expert weights: gate/up tile, down units
+  u32x4 qg0[M], qg1[M], qu0[M], qu1[M];
+  uint32_t mg[M], mu[M];
+  auto load_glu = [&](const uint8_t *blob) {
+    const int F = gt.F, j = gt.rb * 64 + lane;
+    const BlobLayout BL = blob_layout(D, F);
+    const gptr<u32x4> gc = as_global((const u32x4 *)(blob + BL.gate_codes) + j);
+    const gptr<u32x4> uc = as_global((const u32x4 *)(blob + BL.up_codes) + j);
+    const gptr<uint32_t> gm = as_global((const uint32_t *)(blob + BL.gate_meta) + j);
+    const gptr<uint32_t> um = as_global((const uint32_t *)(blob + BL.up_meta) + j);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int g = min(g0 + wave + i * kNW, g1 - 1);
+      const size_t c0 = (size_t)(2 * g) * F;
+      qg0[i] = gc[c0];
+      qg1[i] = gc[c0 + F];
+      qu0[i] = uc[c0];
+      qu1[i] = uc[c0 + F];
+      mg[i] = gm[(size_t)g * F];
+      mu[i] = um[(size_t)g * F];
+    }
+  };
+  if (has_g && !g_routed) load_glu((const uint8_t *)L.sblobs[0]);
+  u32x4 dq0[M], dq1[M];
+  uint32_t dmw[M];
+  auto load_down = [&](int i, const uint8_t *blob, int Fb, int g) {
+    const BlobLayout BL = blob_layout(D, Fb);
+    const gptr<u32x4> dc = as_global((const u32x4 *)(blob + BL.down_codes) + n);
+    dq0[i] = dc[(size_t)(2 * g) * D];
+    dq1[i] = dc[(size_t)(2 * g + 1) * D];
+    dmw[i] = as_global((const uint32_t *)(blob + BL.down_meta))[(size_t)g * D + n];
+  };
+  if (has_d) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int u = min(u0 + wave + i * kNW, u1 - 1);
+      if (u >= k * Gf) load_down(i, (const uint8_t *)L.sblobs[0], L.Fs, u - k * Gf);
+    }
+  }
+
+  // ---------------- staging in LDS: activation pairs (x[8w + m], x[8w + m + 4])
+  // and 64-column sums of the gate/up groups, the blob table
+  if (has_g && tid < n8) {
+    const uint32_t a0 = xq.x, a1 = xq.y, a2 = xq.z, a3 = xq.w;
+    u32x4 pq;
+    pq.x = (a0 & 0xFFFFu) | (a2 << 16);
+    pq.y = (a0 >> 16) | (a2 & 0xFFFF0000u);
+    pq.z = (a1 & 0xFFFFu) | (a3 << 16);
+    pq.w = (a1 >> 16) | (a3 & 0xFFFF0000u);
+    *(u32x4 *)&s_xp[4 * tid] = pq;
+    const uint32_t w[4] = {a0, a1, a2, a3};
+    float s8 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s8 += x_to_f32<F16X>(w[m] & 0xFFFFu);
+      s8 += x_to_f32<F16X>(w[m] >> 16);
+    }
+    const float sg = sum8_lanes(s8);
+    if ((tid & 7) == 0) s_xs[tid / 8] = sg;
+  }
+  const void **s_table = (const void **)(dsm + L.table_off);
+  if (routed) {
+#pragma unroll
+    for (int i = 0; i < kTab; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < E) s_table[e] = tb[i];
+    }
+  }
+  __syncthreads();
+
+  // ---------------- gate/up arithmetic, split reduction (the last split to
+  // arrive holds the sums), hidden activations
+  auto glu = [&]() {
+    const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
+    float accg = 0.0f, accu = 0.0f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int gi = wave + i * kNW;  // group g0 + gi
+      // one group's activation pairs live at a time (keeps the registers of
+      // the in-flight weight loads free)
+      __builtin_amdgcn_sched_barrier(0);
+      if (g0 + gi < g1) {
+        uint32_t xg[32];
+        const u32x4 *xv = (const u32x4 *)&s_xp[32 * gi];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4 v4 = xv[c];
+          xg[4 * c] = v4.x;
+          xg[4 * c + 1] = v4.y;
+          xg[4 * c + 2] = v4.z;
+          xg[4 * c + 3] = v4.w;
+        }
+        const float xsg = s_xs[gi];
+        float dg = dot_chunk<F16X>(qg0[i], xg, 0.0f, magic);
+        dg = dot_chunk<F16X>(qg1[i], xg + 16, dg, magic);
+        float du = dot_chunk<F16X>(qu0[i], xg, 0.0f, magic);
+        du = dot_chunk<F16X>(qu1[i], xg + 16, du, magic);
+        const float sg = f16_to_f32(mg[i]), bg = f16_to_f32(mg[i] >> 16);
+        const float su = f16_to_f32(mu[i]), bu = f16_to_f32(mu[i] >> 16);
+        accg = fmaf(sg, dg, accg);
+        accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsg, accg);
+        accu = fmaf(su, du, accu);
+        accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsg, accu);
+      }
+    }
+    red[wave][0][lane] = accg;
+    red[wave][1][lane] = accu;
+    __syncthreads();
+    if (wave == 0) {
+      float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        v0 += red[w][0][lane];
+        v1 += red[w][1][lane];
+      }
+      bool last = true;
+      if (L.KSg > 1) {
+        const float pv[2] = {v0, v1};
+        float sv[2];
+        last = split_reduce_fixed<2>(L.gacc + (size_t)tile * 128,
+                                     L.gcnt + (size_t)tile * kCntStride, L.KSg, pv, sv);
+        v0 = sv[0];
+        v1 = sv[1];
+      }
+      if (last) {
+        const float h = gelu_tanh(v0) * v1;
+        st_dev64(L.h + gt.hoff + (size_t)gt.rb * 64 + lane, tagged(__float_as_uint(h), tag));
+      }
+    }
+  };
+
+  // ---------------- selected experts (and gates) of the token(s) of this block
+  if (routed) {
+    const bool report = g_routed && gt.j == 0 && gt.rb == 0 && ks == 0;  // first tile of a token
+    if (g_routed) block_select(L, gt.t, tag, s_select, s_table, s_blob[0], s_gate[0], report);
+    if (d_routed) {
+      if (g_routed && gt.t == t_out) {
+        if (tid < k) {
+          s_blob[1][tid] = s_blob[0][tid];
+          s_gate[1][tid] = s_gate[0][tid];
+        }
+        __syncthreads();
+      } else {
+        block_select(L, t_out, tag, s_select, s_table, s_blob[1], s_gate[1], false);
+      }
+    }
+  }
+
+  // ---------------- loads of the selected experts
+  if (g_routed) load_glu(s_blob[0][gt.j]);
+  if (d_routed) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int u = min(u0 + wave + i * kNW, u1 - 1);
+      if (u < k * Gf) {
+        const int jj = u / Gf;
+        load_down(i, s_blob[1][jj], L.F, u - jj * Gf);
+      }
+    }
+  }
+  // the shared expert's tiles compute after the routing (it needs the issue
+  // slots more) and before the routed tiles (their data comes later)
+  if (has_g) glu();
+
+  // ---------------- down projection and combine
+  if (has_d) {
+    const uint64_t *hp[M];
+    float gate[M];
+    bool use[M];
+    const uint64_t *hint = nullptr;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int u = u0 + wave + i * kNW;
+      use[i] = u < u1;
+      if (u < k * Gf) {
+        const int jj = u / Gf;
+        gate[i] = s_gate[1][jj];
+        hp[i] = L.h + (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
+      } else {
+        gate[i] = 1.0f;
+        hp[i] = L.h + (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)(u - k * Gf) * 64;
+      }
+      if (use[i] && lane == i) hint = hp[i];
+    }
+    // lane i polls one word of unit i, then the units' values are read (checked)
+    wait_hint(hint, tag, L.err);
+    float hv0[M];
+    for (long s = 0;; ++s) {
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        hv0[i] = 0.0f;
+        if (use[i]) {
+          const uint64_t w = ld_dev64(hp[i] + lane);
+          ok = ok && has_tag(w, tag);
+          hv0[i] = __uint_as_float((uint32_t)w);
+        }
+      }
+      if (__all(ok)) break;
+      if (s > kSpin) {
+        if (lane == 0) add_dev(L.err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    float hsum[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      hbuf[wave][i][lane] = hv0[i];
+      hsum[i] = wave_sum(hv0[i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (!use[i]) continue;
+      float hv[64];
+#pragma unroll
+      for (int j = 0; j < 64; j += 4) {
+        const float4 v4 = *(const float4 *)&hbuf[wave][i][j];
+        hv[j] = v4.x;
+        hv[j + 1] = v4.y;
+        hv[j + 2] = v4.z;
+        hv[j + 3] = v4.w;
+      }
+      const float d = dot_group_f32(dq0[i], dq1[i], hv);
+      const float v = fmaf(f16_to_f32(dmw[i]), d, f16_to_f32(dmw[i] >> 16) * hsum[i]);
+      acc = fmaf(gate[i], v, acc);
+    }
+    __syncthreads();  // red[] is reused
+    red[wave][0][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
+      bool last = true;
+      if (L.KSd > 1) {
+        const float pv[1] = {s};
+        float sv[1];
+        last = split_reduce_fixed<1>(L.dacc + (size_t)ot * 64, L.dcnt + (size_t)ot * kCntStride,
+                                     L.KSd, pv, sv);
+        s = sv[0];
+      }
+      if (last) {
+        const size_t idx = (size_t)t_out * D + n;
+        if (L.out_dtype == MOE_F32)
+          ((float *)L.out)[idx] = s;
+        else if (L.out_dtype == MOE_BF16)
+          ((uint16_t *)L.out)[idx] = (uint16_t)f32_to_bf16(s);
+        else
+          ((uint16_t *)L.out)[idx] = (uint16_t)f32_to_f16(s);
+      }
+    }
+  }
+
+  // ---------------- advance every copy of the epoch (block b: b, b + grid, ...)
+  if (tid == 0)
+    for (int j = b; j < kMaxLayerGrid; j += gridDim.x) st_dev(L.bep + j, tag);
+}
+
+using KernelFn = void (*)(LayerLaunch);
+template <bool F16X, int MAXC>
+KernelFn pick(int m) {
+  if (m == 2) return decode_layer_kernel<F16X, 2, MAXC>;
+  if (m == 3) return decode_layer_kernel<F16X, 3, MAXC>;
+  if (m == 4) return decode_layer_kernel<F16X, 4, MAXC>;
+  return nullptr;
+}
+KernelFn pick_layer(const LayerLaunch &L, int m) {
+  const bool small_d = L.D <= 3072;  // router chunks per thread: 6 (D <= 3072) or 16
+  if (L.f16x) return small_d ? pick<true, 6>(m) : pick<true, 16>(m);
+  return small_d ? pick<false, 6>(m) : pick<false, 16>(m);
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int g_layer_capacity[2][2][3][64];  // [f16x][MAXC 6/16][m - 2][device]
+
+}  // namespace
+
+int layer_m(const LayerLaunch &L) {
+  const int U = L.k * (L.F / 64) + (L.sblobs ? L.Fs / 64 : 0);
+  const int mg = ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
+  const int mu = ceil_div(ceil_div(U, L.KSd), kNW);
+  int m = mg > mu ? mg : mu;
+  return m < 2 ? 2 : m;
+}
+
+int layer_grid(const LayerLaunch &L) {
+  const int r = L.T * ((L.E + kRows - 1) / kRows);
+  const int g = L.n_gtiles * L.KSg;
+  const int d = L.T * (L.D / 64) * L.KSd;
+  int m = r > g ? r : g;
+  return m > d ? m : d;
+}
+
+size_t layer_smem(const LayerLaunch &L) {
+  // router staging: x as fp32, 16-column sums, partial logits; then the table
+  const size_t stage = sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads);
+  return align_up(stage) + sizeof(void *) * (size_t)L.E;
+}
+size_t layer_table_off(const LayerLaunch &L) {
+  return align_up(sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads));
+}
+
+hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
+  *cap = 0;
+  const int m = layer_m(L);
+  KernelFn k = pick_layer(L, m);
+  if (!k) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int &slot = g_layer_capacity[L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1][m - 2][dev];
+  const size_t smem = layer_smem(L);
+  if (smem > 64 * 1024) return hipSuccess;
+  if (!slot) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k, kThreads, smem);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    slot = per_cu * cus;
+  }
+  *cap = slot;
+  return hipSuccess;
+}
+
+hipError_t launch_layer(const LayerLaunch &L, hipStream_t s) {
+  KernelFn k = pick_layer(L, layer_m(L));
+  if (!k) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k, dim3(layer_grid(L)), dim3(kThreads), layer_smem(L), s, L);
+  return hipGetLastError();
+}
+
+}  // namespace moe

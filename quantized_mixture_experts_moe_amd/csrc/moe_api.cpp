@@ -49,16 +49,17 @@ struct Carver {
   }
 };
 
-// counters of the one-launch expert phase: tiles, output tiles, slots, and the
-// replicated slot-ready flags (one 32-word line per copy)
+// counters of the one-launch expert phase: slots, and the replicated
+// slot-ready flags (one 32-word line per copy)
 size_t fused_counter_words(const Dims &d) {
   const size_t slots = (size_t)d.T * (d.k + 1);
-  return 2 * (size_t)kMaxSplitBlocks + slots + slots * kFlagCopies * 32 + 64;
+  return slots + slots * kFlagCopies * 32 + 64;
 }
 
 Workspace carve(void *base, const Dims &d) {
   Carver c{(uint8_t *)base};
   Workspace w;
+  w.layer = c.take<uint8_t>(kLayerRegionBytes, 1);
   const size_t T = d.T, k = d.k;
   const size_t units = T * k * d.F + T * d.Fs;
   w.xp = c.take<uint32_t>(T * d.D / 2, 4);
@@ -108,6 +109,16 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HI
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Accumulators and counters of the deterministic split reductions: fixed
+// places in the workspace's layer region, zero between calls.
+void set_split_accumulators(const Workspace &w, uint64_t **gacc, uint64_t **dacc, uint32_t **gcnt,
+                            uint32_t **dcnt) {
+  *gacc = (uint64_t *)(w.layer + kAccGluOff);
+  *dacc = (uint64_t *)(w.layer + kAccOutOff);
+  *gcnt = (uint32_t *)(w.layer + kCntGluOff);
+  *dcnt = (uint32_t *)(w.layer + kCntOutOff);
+}
+
 // Choose the splits of the one-launch expert phase; false if its grid would
 // not be resident all at once (then the three-kernel path runs).
 bool plan_fused(const ExpertLaunch &a, const Workspace &w, FusedLaunch *f) {
@@ -132,18 +143,50 @@ bool plan_fused(const ExpertLaunch &a, const Workspace &w, FusedLaunch *f) {
   int cap = 0;
   if (fused_capacity(*f, &cap) != hipSuccess || cap <= 0) return false;
   const int grid = fused_grid(*f);
-  if (grid > cap || (long)n_gtiles * ksg > kMaxSplitBlocks || (long)a.T * NB * ksd > kMaxSplitBlocks)
-    return false;
-  // counters packed at the start of the region (cleared by the router kernel),
-  // then the flag lines
-  f->tile_cnt = w.fcounters;
-  f->out_cnt = f->tile_cnt + n_gtiles;
-  f->slot_cnt = f->out_cnt + a.T * NB;
-  f->slot_flag = w.fcounters + 2 * kMaxSplitBlocks + (size_t)a.T * (a.k + 1);
+  if (grid > cap || n_gtiles > kMaxAccTiles || a.T * NB > kMaxOutTiles) return false;
+  // slot counters (cleared by the router kernel), then the flag lines
+  f->slot_cnt = w.fcounters;
+  f->slot_flag = w.fcounters + (size_t)a.T * (a.k + 1);
   f->slot_flag += (32 - ((uintptr_t)f->slot_flag / 4) % 32) % 32;  // 128-byte lines
   f->err = w.err;
-  f->gpart = w.part;
-  f->dpart = w.dpart;
+  set_split_accumulators(w, &f->gacc, &f->dacc, &f->gcnt, &f->dcnt);
+  return true;
+}
+
+// Choose the splits of the one-launch decode layer and place its tagged words
+// in the workspace's fixed region; false if it does not apply (then the router
+// kernel and the expert kernels run).
+bool plan_layer(const Workspace &w, LayerLaunch *L) {
+  const int T = L->T, k = L->k, E = L->E, D = L->D, F = L->F;
+  const int Fs = L->sblobs ? L->Fs : 0;
+  if (!tuning().layer || T > kMaxLayerT || E > kMaxLayerE || k > kMaxK || D > 8192) return false;
+  const int G = D / 64, NB = D / 64;
+  const int n_gtiles = T * k * (F / 64) + T * (Fs / 64);
+  const int U = k * (F / 64) + Fs / 64;
+  // about two blocks per compute unit; at most 16 groups or units per block
+  const int target = 512;
+  int ksg = tuning().layer_ksg > 0 ? tuning().layer_ksg : (target + n_gtiles - 1) / n_gtiles;
+  ksg = clampi(ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
+  int ksd = tuning().layer_ksd > 0 ? tuning().layer_ksd
+                                   : (ksg * n_gtiles + T * NB - 1) / (T * NB);
+  ksd = clampi(ksd, (U + 15) / 16, U < kMaxFusedKSd ? U : kMaxFusedKSd);
+  L->KSg = ksg;
+  L->KSd = ksd;
+  L->n_gtiles = n_gtiles;
+  if (layer_m(*L) > 4) return false;
+  const int grid = layer_grid(*L);
+  int cap = 0;
+  if (layer_capacity(*L, &cap) != hipSuccess || grid > cap || grid > kMaxLayerGrid) return false;
+  if (n_gtiles > kMaxAccTiles || T * NB > kMaxOutTiles) return false;
+  L->bep = (uint32_t *)w.layer;
+  set_split_accumulators(w, &L->gacc, &L->dacc, &L->gcnt, &L->dcnt);
+  // tagged words: logits, hidden activations
+  Carver c{w.layer + kTaggedOff};
+  L->rlog = c.take<uint64_t>((size_t)T * E, 8);
+  L->h = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
+  if (kTaggedOff + c.off > kLayerRegionBytes) return false;
+  L->table_off = layer_table_off(*L);
+  L->err = w.err;
   return true;
 }
 
@@ -201,6 +244,12 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().fused_ksg = value;
   } else if (!strcmp(key, "fused_ksd")) {
     tuning().fused_ksd = value;
+  } else if (!strcmp(key, "layer")) {
+    tuning().layer = value;
+  } else if (!strcmp(key, "layer_ksg")) {
+    tuning().layer_ksg = value;
+  } else if (!strcmp(key, "layer_ksd")) {
+    tuning().layer_ksd = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
   } else {
@@ -307,6 +356,20 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   Workspace w = carve(ws, d);
   hipStream_t s = (hipStream_t)stream;
 
+  if (!pool) {
+    // decode: router, selection, experts and combine in one launch
+    LayerLaunch L{};
+    L.f16x = x_dtype == MOE_F16; L.T = T; L.k = k; L.E = E; L.D = D; L.F = F; L.Fs = Fs;
+    L.x = x; L.rcodes = (const uint8_t *)router->codes; L.rmeta = (const uint32_t *)router->meta;
+    L.logit_bias = logit_bias; L.rblobs = routed->blobs;
+    L.sblobs = shared ? shared->blobs : nullptr;
+    L.ids_out = ids_out; L.gates_out = gates_out; L.out = out; L.out_dtype = out_dtype;
+    if (plan_layer(w, &L)) {
+      const int pi = prof_begin(s);
+      return hip_status(prof_end(pi, s, launch_layer(L, s)));
+    }
+  }
+
   RouteLaunch r;
   r.zero = nullptr; r.zero_words = 0; r.zero2 = nullptr; r.zero2_count = 0; r.zero2_stride = 0;
   r.x = x; r.f16x = x_dtype == MOE_F16; r.T = T; r.D = D; r.E = E; r.k = k;
@@ -329,8 +392,8 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   FusedLaunch f;
   const bool fused = tuning().fused && plan_fused(a, w, &f);
   if (fused) {
-    r.zero = w.fcounters;
-    r.zero_words = (int)(f.slot_cnt + T * (k + 1) - w.fcounters);
+    r.zero = f.slot_cnt;
+    r.zero_words = T * (k + 1);
     r.zero2 = f.slot_flag;
     r.zero2_count = T * (k + 1) * kFlagCopies;
     r.zero2_stride = 32;

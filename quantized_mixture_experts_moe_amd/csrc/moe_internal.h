@@ -18,6 +18,27 @@ constexpr int kMaxSplitBlocks = 4096;  // blocks of a split launch (partial tile
 constexpr int kMaxFusedKSd = 16;       // output splits of the one-launch expert phase
 constexpr int kMaxDGroups = 128;       // model width / 64 handled by the prefill kernels
 constexpr int kMaxHGroups = 64;        // hidden width / 64 handled by the prefill kernels
+constexpr int kMaxLayerGrid = 4096;    // blocks of the one-launch decode layer
+constexpr int kMaxLayerT = 4;          // tokens of the one-launch decode layer
+constexpr int kMaxLayerE = 256;        // experts of the one-launch decode layer
+// Region at the start of every workspace that holds the tagged words of the
+// one-launch decode layer: the per-block epochs, then 64-bit (value, tag)
+// words only.  Its place and size do not depend on the call, so no other
+// kernel ever writes into it.
+constexpr size_t kLayerRegionBytes = size_t(8) << 20;
+constexpr size_t kLayerEpochBytes = sizeof(uint32_t) * kMaxLayerGrid;
+// Split-reduction accumulators and counters of the one-launch kernels, at
+// fixed places in that region (after the epochs): they are zero between calls
+// whatever the call's shape.  Gate/up tiles: 128 values each; output tiles:
+// 64 values each; one 64-byte line per counter.
+constexpr int kMaxAccTiles = 2048;
+constexpr int kMaxOutTiles = 512;
+constexpr size_t kAccGluOff = kLayerEpochBytes;
+constexpr size_t kAccOutOff = kAccGluOff + sizeof(uint64_t) * 128 * kMaxAccTiles;
+constexpr size_t kCntGluOff = kAccOutOff + sizeof(uint64_t) * 64 * kMaxOutTiles;
+constexpr size_t kCntOutOff = kCntGluOff + 64 * (size_t)kMaxAccTiles;
+constexpr size_t kTaggedOff = kCntOutOff + 64 * (size_t)kMaxOutTiles;
+constexpr int kCntStride = 16;  // u32 words per counter line
 
 __host__ __device__ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -53,11 +74,15 @@ struct Tuning {
   int fused_ksd = 0;
   int prefill_min_t = 16;  // tokens per call from which the grouped matrix-core path runs
   int route_rows = 8;  // experts per router block
+  int layer = 1;       // one launch for the whole decode layer when it fits
+  int layer_ksg = 0;   // its gate/up and down splits (0: chosen)
+  int layer_ksd = 0;
 };
 Tuning &tuning();
 
 // Workspace carve-up for one call.  Every region is 256-byte aligned.
 struct Workspace {
+  uint8_t *layer;      // the fixed region of the one-launch decode layer
   uint32_t *xp;        // x as dot2 pairs [T][D/2]
   float *xs;           // x group sums [T][D/64]
   float *logits;       // [T][E]
@@ -125,9 +150,11 @@ struct FusedLaunch {
   int KSg, KSd, n_gtiles;
   int tile_begin, tile_end; // gate/up tiles of this launch (routed tiles, then shared)
   int do_down;              // this launch also runs the down projection and combine
-  // counters and flags: zeroed by the router kernel launched just before
-  uint32_t *tile_cnt, *slot_cnt, *out_cnt, *slot_flag, *err;
-  float *gpart, *dpart;
+  // slot counters and flags: zeroed by the router kernel launched just before
+  uint32_t *slot_cnt, *slot_flag, *err;
+  // split reductions: accumulators and counters that are zero between calls
+  uint64_t *gacc, *dacc;
+  uint32_t *gcnt, *dcnt;
 };
 int fused_grid(const FusedLaunch &f);
 int fused_max_g(const FusedLaunch &f);
@@ -154,6 +181,31 @@ struct PrefillLaunch {
   void *out; int out_dtype;
 };
 hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s);
+
+// The whole decode layer in one launch (router, top-k, experts, combine).
+struct LayerLaunch {
+  int f16x, T, k, E, D, F, Fs;
+  const void *x;
+  const uint8_t *rcodes; const uint32_t *rmeta; const float *logit_bias;
+  const void *const *rblobs;          // routed bank [E]
+  const void *const *sblobs;          // shared bank (expert 0) or null
+  int KSg, KSd, n_gtiles;
+  size_t table_off;                   // LDS byte offset of the blob table
+  uint32_t *bep;                      // per-block epochs [kMaxLayerGrid]
+  uint64_t *rlog;                     // [T][E] tagged logits
+  uint64_t *h;                        // [T*k*F + T*Fs] tagged hidden activations
+  uint64_t *gacc, *dacc;              // split-reduction accumulators (zero between calls)
+  uint32_t *gcnt, *dcnt;              // and their counters
+  uint32_t *err;
+  int32_t *ids_out; float *gates_out; // optional
+  void *out; int out_dtype;
+};
+int layer_m(const LayerLaunch &L);
+int layer_grid(const LayerLaunch &L);
+size_t layer_smem(const LayerLaunch &L);
+size_t layer_table_off(const LayerLaunch &L);
+hipError_t layer_capacity(const LayerLaunch &L, int *cap);
+hipError_t launch_layer(const LayerLaunch &L, hipStream_t s);
 
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);

@@ -23,52 +23,37 @@ __device__ __forceinline__ float x_to_f32(uint16_t v) {
   return F16X ? f16_to_f32(v) : bf16_to_f32(v);
 }
 
-// Top-k over logits[0..E) of one token by one wave; larger logit first, equal
-// logits to the lower index; gates = softmax over the selected logits.  Each
-// round takes the wave maximum, then the lowest index holding it (DPP
-// reductions).  Optionally writes the blob address of every selected expert.
-__device__ void topk_wave(const float *lg, int E, int k, int32_t *ids, float *gates,
-                          const void *const *table, const void **slot_blob) {
+// Top-k over logits[0..E) of one token by one wave (see topk_regs); writes
+// ids, gates and optionally the blob address of every selected expert.
+template <int NV>
+__device__ void topk_wave_t(const float *lg, int E, int k, int32_t *ids, float *gates,
+                            const void *const *table, const void **slot_blob, uint2 *xch) {
   const int lane = threadIdx.x & 63;
-  const int nv = (E + 63) / 64;
-  float v[kMaxE / 64];
+  float v[NV];
 #pragma unroll
-  for (int j = 0; j < kMaxE / 64; ++j) {
+  for (int j = 0; j < NV; ++j) {
     const int idx = lane + 64 * j;
-    v[j] = (j < nv && idx < E) ? ld_dev(lg + idx) : -INFINITY;
+    v[j] = idx < E ? ld_dev(lg + idx) : -INFINITY;
   }
-  float myv = 0.0f;
-  int myi = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j) {
-      if (j >= nv) break;
-      const int idx = lane + 64 * j;
-      if (idx < E && v[j] > bv) {  // ascending j: ties keep the lower index
-        bv = v[j];
-        bi = idx;
-      }
-    }
-    const float m = wave_max(bv);
-    const int w = wave_min(bv == m ? bi : 0x7FFFFFFF);
-    if (lane == r) {
-      myv = m;
-      myi = w;
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxE / 64; ++j)
-      if (lane + 64 * j == w) v[j] = -INFINITY;  // taken
-  }
-  const float m0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
-  const float z = lane < k ? expf(myv - m0) : 0.0f;
-  const float sum = wave_sum(z);
+  int32_t id;
+  float gate;
+  topk_regs(v, k, xch, &id, &gate);
   if (lane < k) {
-    ids[lane] = myi;
-    gates[lane] = z / sum;
-    if (slot_blob) slot_blob[lane] = table[myi];
+    ids[lane] = id;
+    gates[lane] = gate;
+    if (slot_blob) slot_blob[lane] = table[id];
   }
+}
+__device__ void topk_wave(const float *lg, int E, int k, int32_t *ids, float *gates,
+                          const void *const *table, const void **slot_blob, uint2 *xch) {
+  if (E <= 128)
+    topk_wave_t<2>(lg, E, k, ids, gates, table, slot_blob, xch);
+  else if (E <= 256)
+    topk_wave_t<4>(lg, E, k, ids, gates, table, slot_blob, xch);
+  else if (E <= 512)
+    topk_wave_t<8>(lg, E, k, ids, gates, table, slot_blob, xch);
+  else
+    topk_wave_t<16>(lg, E, k, ids, gates, table, slot_blob, xch);
 }
 
 // Activations [nt][D] of fp16/bf16 bits into LDS as fp32: every thread issues
@@ -106,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
   float *sxs = sx + TT * D;          // [TT][D/16] chunk sums
   float *red = sxs + TT * nch;       // [KL][ROWS*TT]
   __shared__ int s_last;
+  __shared__ uint2 s_xch[TT][128];  // top-k exchange, one area per selecting wave
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,11 +145,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
         o[m] = lo | (hi << 16);
       }
     }
+    // 64-column sums: 8 threads per group, 8 columns each (sum8_lanes order)
     const int q0 = blockIdx.x * groups / gridDim.x, q1 = (blockIdx.x + 1) * groups / gridDim.x;
-    for (int i = wave; i < nt * (q1 - q0); i += kThreads / 64) {
-      const int tt = i / (q1 - q0), g = q0 + i - tt * (q1 - q0);
-      const float s = wave_sum(sx[(size_t)tt * D + 64 * g + lane]);
-      if (lane == 0) a.xs[(size_t)(t0 + tt) * (D / 64) + g] = s;
+    for (int i = tid; i < nt * (q1 - q0) * 8; i += kThreads) {
+      const int gi = i / 8, c = i - gi * 8;
+      const int tt = gi / (q1 - q0), g = q0 + gi - tt * (q1 - q0);
+      const float *xv = sx + (size_t)tt * D + 64 * g + 8 * c;
+      float s8 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s8 += xv[j];
+      const float s = sum8_lanes(s8);
+      if (c == 0) a.xs[(size_t)(t0 + tt) * (D / 64) + g] = s;
     }
   }
   __syncthreads();
@@ -219,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
     const int t = t0 + wave;
     topk_wave(a.logits + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k,
               a.gates + (size_t)t * a.k, a.table,
-              a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr);
+              a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr, s_xch[wave]);
   }
   if (tid == 0) st_dev(&a.counters[blockIdx.y], 0u);
 }
@@ -252,8 +244,14 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
   const int t = i / G, g = i - t * G;
   const uint16_t *xg = x + (size_t)t * D + 64 * g;
   uint32_t *o = xp + (size_t)t * (D / 2) + 32 * g;
-  float s = 0.0f;
-  for (int j = 0; j < 64; ++j) s += x_to_f32<F16X>(xg[j]);
+  // same order as sum8_lanes: eight in-order sums of 8, combined pairwise
+  float c8[8];
+  for (int c = 0; c < 8; ++c) {
+    float v = 0.0f;
+    for (int j = 0; j < 8; ++j) v += x_to_f32<F16X>(xg[8 * c + j]);
+    c8[c] = v;
+  }
+  const float s = ((c8[0] + c8[1]) + (c8[2] + c8[3])) + ((c8[4] + c8[5]) + (c8[6] + c8[7]));
   for (int w = 0; w < 8; ++w)
     for (int m = 0; m < 4; ++m)
       o[4 * w + m] = (uint32_t)xg[8 * w + m] | ((uint32_t)xg[8 * w + m + 4] << 16);

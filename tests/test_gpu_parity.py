@@ -101,6 +101,43 @@ def test_route_x_zero_closed_form():
     assert np.all(gates.cpu().numpy() == 1.0 / cfg.k)
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_selection_exact_ties(name):
+    """x = 0 makes the logits equal the per-expert bias exactly; a bias drawn
+    from four values gives many exact ties, the last selected slots among
+    them.  Both selection paths (the router
+    kernel and the one-launch layer) must order ties by the lower index, as
+    the oracle does, and give the same gates."""
+    _case(f"selection with exact ties ({name})")
+    L = dev_layer(name)
+    cfg = L.cfg
+    rng = np.random.default_rng(11)
+    T = 3
+    bias = rng.choice(np.array([-1.0, 0.0, 0.5], dtype=np.float32), size=cfg.E)
+    bias[rng.choice(cfg.E, cfg.k // 2, replace=False)] = 1.0  # the rest ties at 0.5
+    bias_d = torch.from_numpy(bias).cuda()
+    x = torch.zeros(T, cfg.D, dtype=torch.float16 if cfg.x_dtype == "fp16" else torch.bfloat16,
+                    device="cuda")
+    ref_ids, ref_gates = O.select_topk(np.tile(bias.astype(np.float64), (T, 1)), cfg.k)
+    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+    moe.moe_route(x, L.router, cfg.k, ids, gates, ws, bias_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(gates.cpu().numpy(), ref_gates, rtol=1e-6)
+    for t in range(T):  # one token per call: the one-launch layer
+        out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+        ids1 = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
+        gates1 = torch.empty(1, cfg.k, dtype=torch.float32, device="cuda")
+        moe.moe_layer_forward(x[t:t + 1], L.router, cfg.k, L.routed, L.shared, out, ws,
+                              logit_bias=bias_d, ids_out=ids1, gates_out=gates1)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids1.cpu().numpy()[0], ref_ids[t])
+        assert torch.equal(gates1[0], gates[t])
+        assert torch.all(out == 0)
+
+
 # ---------------------------------------------------------------- expert FFN
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 2)])
 def test_expert_ffn_parity(name, T):
@@ -309,13 +346,24 @@ def test_pool_streamed_equals_resident_and_trace():
     pool.close()
 
 
-@pytest.mark.parametrize("fused", [0, 1])
-def test_layer_forward_decode_both_expert_paths(fused):
-    """The one-launch expert phase and the three-kernel path both meet the bar."""
-    _case(f"layer_forward decode fused={fused}")
+_PATHS = {"layer": {"layer": 1}, "fused": {"layer": 0, "fused": 1},
+          "three": {"layer": 0, "fused": 0}}
+_DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0}
+
+
+def _tune(**kv):
+    for key, v in kv.items():
+        moe.moe_set_tuning(key, v)
+
+
+@pytest.mark.parametrize("path", ["layer", "fused", "three"])
+def test_layer_forward_decode_all_paths(path):
+    """The one-launch layer, the router + one-launch expert phase, and the
+    router + three expert kernels all meet the bar on decode tokens."""
+    _case(f"layer_forward decode path={path}")
     L = dev_layer("decode")
     cfg = L.cfg
-    moe.moe_set_tuning("fused", fused)
+    _tune(**_PATHS[path])
     try:
         for tok in range(3):
             xb = gen.activations(8, 0, tok, 1, cfg.D, cfg.x_dtype)
@@ -324,7 +372,54 @@ def test_layer_forward_decode_both_expert_paths(fused):
             again, _, _ = _layer_gpu(L, xb, cfg.k)
             assert torch.equal(out, again)
     finally:
-        moe.moe_set_tuning("fused", 1)
+        _tune(**_DEFAULTS)
+
+
+def test_layer_launch_equals_expert_phase_launch():
+    """Same splits, same summation order: the one-launch layer and the
+    router + one-launch expert phase agree bit for bit."""
+    _case("layer vs fused bitwise (decode, beta=6.5)")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    bias = gen.zipf_bias(0, 0, cfg.E, 6.5)
+    try:
+        for tok in range(4):
+            xb = gen.activations(9, 0, tok, 1, cfg.D, cfg.x_dtype)
+            _tune(layer=1)
+            a, ia, ga = _layer_gpu(L, xb, cfg.k, bias)
+            _tune(layer=0)
+            b, ib, gb = _layer_gpu(L, xb, cfg.k, bias)
+            assert np.array_equal(ia, ib) and np.array_equal(ga, gb)
+            assert torch.equal(a, b), tok
+    finally:
+        _tune(**_DEFAULTS)
+
+
+def test_layer_epochs_across_grid_sizes():
+    """One workspace, many calls, the grid changing between them: the per-block
+    epochs stay in step, every call meets the bar, and a repeated shape gives
+    the same bits."""
+    _case("layer epochs across grid sizes (decode)")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    xb = gen.activations(10, 0, 0, 1, cfg.D, cfg.x_dtype)
+    x = x_dev(xb, cfg.x_dtype)
+    first = {}
+    try:
+        for it, (ksg, ksd) in enumerate([(0, 0), (3, 8), (0, 0), (8, 16), (2, 0), (0, 0)] * 3):
+            _tune(layer_ksg=ksg, layer_ksd=ksd)
+            out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+            ids = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
+            moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, out, ws, ids_out=ids)
+            torch.cuda.synchronize()
+            if (ksg, ksd) in first:
+                assert torch.equal(first[(ksg, ksd)], out), (it, ksg, ksd)
+            else:
+                first[(ksg, ksd)] = out
+                _check_layer(L, xb, out.cpu().numpy(), ids.cpu().numpy(), cfg.k)
+    finally:
+        _tune(**_DEFAULTS)
 
 
 def test_layer_forward_prefill_ragged_chunk():
