@@ -14,10 +14,11 @@
 // bounded, and the last block to finish returns the counters to zero.
 //
 // Work split (decode, T = 1, k = 8, D = 2816, F = 704, F_s = 2112):
-//   gate/up: 121 tiles of 64 hidden rows (88 routed + 33 shared) x KSg = 4
-//            reduction splits of 11 column groups;
-//   down:    44 tiles of 64 output rows x KSd = 11 splits of 11 (slot, group)
-//            units, units ordered slot by slot, so a split waits for one slot.
+//   gate/up: 121 tiles of 64 hidden rows (88 routed + 33 shared) x KSg
+//            reduction splits over the 44 column groups;
+//   down:    44 tiles of 64 output rows x (KSdr splits of the 88 routed
+//            (slot, group) units + KSds splits of the 33 shared units), the
+//            splits of the one-launch layer kernel, so both agree bit for bit.
 // Block b owns gate/up item b and down item b.
 #include "device_common.h"
 #include "moe_internal.h"
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
 
   // ---------------- issue the down-projection loads of this block's output split
   const int Gf = a.F / 64, Gs = a.sblobs ? a.Fs / 64 : 0;
-  const int U = a.k * Gf + Gs;
+  const int Ur = a.k * Gf;  // units: routed (slot by slot), then shared
   int t_out = 0, n = 0, ksd = 0, u0 = 0, u1 = 0;
   u32x4 dq0[kMaxU], dq1[kMaxU];
   uint32_t dmw[kMaxU];
@@ -113,8 +114,13 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
     ksd = b - ot * f.KSd;
     t_out = ot / NB;
     n = (ot - t_out * NB) * 64 + lane;
-    u0 = ksd * U / f.KSd;
-    u1 = (ksd + 1) * U / f.KSd;
+    if (ksd < f.KSdr) {  // a split of the routed units, else of the shared units
+      u0 = ksd * Ur / f.KSdr;
+      u1 = (ksd + 1) * Ur / f.KSdr;
+    } else {
+      u0 = Ur + (ksd - f.KSdr) * Gs / f.KSds;
+      u1 = Ur + (ksd - f.KSdr + 1) * Gs / f.KSds;
+    }
 #pragma unroll
     for (int i = 0; i < kMaxU; ++i) {
       const int u = min(u0 + wave + i * kNW, u1 - 1);
@@ -314,8 +320,11 @@ int fused_max_g(const FusedLaunch &f) {
   return m < 2 ? 2 : m;
 }
 int fused_max_u(const FusedLaunch &f) {
-  const int U = f.a.k * (f.a.F / 64) + (f.a.sblobs ? f.a.Fs / 64 : 0);
-  const int m = ceil_div(ceil_div(U, f.KSd), kNW);
+  int m = ceil_div(ceil_div(f.a.k * (f.a.F / 64), f.KSdr), kNW);
+  if (f.KSds > 0) {
+    const int ms = ceil_div(ceil_div(f.a.Fs / 64, f.KSds), kNW);
+    m = m > ms ? m : ms;
+  }
   return m < 2 ? 2 : m;
 }
 

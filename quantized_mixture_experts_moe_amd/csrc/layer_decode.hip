@@ -6,30 +6,36 @@
 // the top 8, run the selected 4-bit experts and the resident shared expert,
 // and add the two outputs (es.news.hada.io, "Proceso de generacion de
 // tokens"; yodev.dev, "Por que funciona: el A4B del nombre").  Routing is a
-// short chain of dependent steps, while the shared expert and the router do
-// not depend on it, so one launch runs them side by side: the router blocks
-// publish their logits first, every block issues the loads that need no
-// routing (shared-expert tiles), and each block that works on routed experts
-// selects them from the logits itself and issues those loads at once.
+// short chain of dependent steps; the shared expert does not depend on it.
+// So the grid has two groups of blocks:
+//   routed blocks: the router rows (8 experts per block), then the routed
+//     gate/up tiles and the routed part of the down projection.  They issue no
+//     weight loads before the selection arrives, so their polls are not
+//     queued behind outstanding loads (a wave's loads complete in order).
+//   shared blocks: the shared expert's gate/up tiles and its part of the down
+//     projection; they stream from the first cycle, while routing runs.
+// Every router block of a token, once all logits of the token are published,
+// selects the experts (block-wide rank) and publishes ids and gates in its
+// own copy; each routed block polls one copy.
 //
 // Handoffs between blocks are tagged words: a 64-bit store of (value, tag)
 // with device scope, where the tag is the call's epoch.  A reader loads until
 // every word it needs carries the current tag, so nothing has to be reset
 // between calls and no full-cache fence is needed.  Each block keeps its own
 // copy of the epoch (bep[b]); every block advances all copies in lockstep, so
-// they agree for any grid size.  All blocks of the grid must be resident at
-// once (checked on the host); every wait is bounded and a timeout bumps an
-// error counter.
+// they agree for any grid size.  The split reductions (gate/up over column
+// groups, output over units) add fixed-point partials with integer atomics;
+// the last split to arrive finishes (deterministic in any arrival order).
+// All blocks of the grid must be resident at once (checked on the host);
+// every wait is bounded and a timeout bumps an error counter.
 //
 // Work split (one token, k = 8, D = 2816, F = 704, F_s = 2112):
-//   router:  E / 8 blocks of 8 experts; every block with routed work then
-//            selects the experts of its token from the published logits;
-//   gate/up: 121 tiles of 64 hidden rows (88 routed + 33 shared) x KSg
-//            reduction splits over the 44 column groups;
-//   down:    44 tiles of 64 output rows x KSd splits of the 121 (slot, group)
-//            units, units ordered slot by slot, the shared expert last.
-// Block b owns router item b, gate/up item b and down item b (those that
-// exist).
+//   router:  16 blocks of 8 experts;
+//   gate/up: 88 routed + 33 shared tiles of 64 hidden rows x KSg reduction
+//            splits over the 44 column groups;
+//   down:    44 tiles of 64 output rows x (KSdr splits of the 88 routed units
+//            + KSds splits of the 33 shared units); a unit is 64 hidden rows
+//            of one slot.
 #include <float.h>
 
 #include "device_common.h"
@@ -132,24 +138,22 @@ __device__ __forceinline__ Tile glu_tile(const LayerLaunch &L, int tile) {
   return g;
 }
 
-// Selection for token t by the whole block once every router block has
-// published its logits.  Thread i < E polls logit i; then every thread ranks
-// its candidate against a share of the others with unique 64-bit keys
-// (order-preserving logit bits, then the complemented index, so equal logits
-// rank the lower index first), the partial ranks add up in LDS, and the k
-// winners land in rank order.  Wave 0 computes the softmax gates as the
-// single-wave selection does (same order, same bits) and resolves the blob
-// of each selected expert.  Every block that works on routed experts selects
-// for itself, which saves a round of publishing and polling.
+// Selection for token t by a router block once every router block of the
+// token has published its logits.  Thread i < E polls logit i; then every
+// thread ranks its candidate against a share of the others with unique 64-bit
+// keys (order-preserving logit bits, then the complemented index, so equal
+// logits rank the lower index first), the partial ranks add up in LDS, and the
+// k winners land in rank order.  Wave 0 computes the softmax gates as the
+// single-wave selection does (same order, same bits) and publishes ids and
+// gates in this block's copy.
 struct __align__(16) SelectLds {
   uint64_t key[kThreads + 16];  // padded: rank loops read whole chunks of 16
   uint32_t rank[kThreads];
   uint2 sel[kMaxK];
 };
 
-__device__ void block_select(const LayerLaunch &L, int t, uint32_t tag, SelectLds &S,
-                             const void *const *table, const uint8_t **blob_out, float *gate_out,
-                             bool report) {
+__device__ void select_publish(const LayerLaunch &L, int t, int copy, uint32_t tag, SelectLds &S,
+                               bool report) {
   const int tid = threadIdx.x, lane = tid & 63, E = L.E, k = L.k;
   const uint64_t *lg = L.rlog + (size_t)t * E;
   float v = -INFINITY;
@@ -176,28 +180,28 @@ __device__ void block_select(const LayerLaunch &L, int t, uint32_t tag, SelectLd
   if (tid < 16) S.key[kThreads + tid] = 0u;
   __syncthreads();
   {
-    // parts of 16-key chunks per candidate: every key read is a broadcast
-    // and 16 of them are in flight before the compares
-    const int chunks = (E + 15) / 16;
-    const int parts = min(kThreads / E, chunks);  // E <= kThreads
-    const int i = tid % E, part = tid / E;
-    if (part < parts) {
-      const uint64_t ki = S.key[i];
-      const int c0 = part * chunks / parts, c1 = (part + 1) * chunks / parts;
-      uint32_t r = 0;
-      for (int c = c0; c < c1; ++c) {
-        uint64_t kj[16];
+    // E <= 128: thread (i, half) ranks candidate i against half of the keys;
+    // E <= 256: thread i against all.  Keys past E are zero (never larger).
+    // Every key read is a broadcast, 16 in flight before the compares.
+    const int P = E <= 128 ? 2 : 1;            // key parts per candidate
+    const int i = E <= 128 ? (tid & 127) : tid;
+    const int part = E <= 128 ? (tid >> 7) : 0;
+    const int nchunk = E <= 128 ? (E + 31) / 32 : (E + 15) / 16;  // chunks per part
+    const uint64_t ki = S.key[i];
+    uint32_t r = 0;
+    for (int c = part * nchunk; c < (part + 1) * nchunk; ++c) {
+      uint64_t kj[16];
 #pragma unroll
-        for (int q = 0; q < 16; q += 2) {
-          const ulonglong2 p2 = *(const ulonglong2 *)&S.key[16 * c + q];
-          kj[q] = p2.x;
-          kj[q + 1] = p2.y;
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) r += kj[q] > ki ? 1u : 0u;
+      for (int q = 0; q < 16; q += 2) {
+        const ulonglong2 p2 = *(const ulonglong2 *)&S.key[16 * c + q];
+        kj[q] = p2.x;
+        kj[q + 1] = p2.y;
       }
-      atomicAdd(&S.rank[i], r);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) r += kj[q] > ki ? 1u : 0u;
     }
+    (void)P;
+    if (i < E) atomicAdd(&S.rank[i], r);
   }
   __syncthreads();
   if (tid < E && S.rank[tid] < (uint32_t)k) S.sel[S.rank[tid]] = make_uint2(tid, __float_as_uint(v));
@@ -216,15 +220,43 @@ __device__ void block_select(const LayerLaunch &L, int t, uint32_t tag, SelectLd
     const float sum = wave_sum(z);
     const float gate = z / sum;
     if (lane < k) {
-      blob_out[lane] = (const uint8_t *)table[myi];
-      gate_out[lane] = gate;
+      uint64_t *line = L.sel + ((size_t)t * L.sel_copies + copy) * 2 * L.lid;
+      st_dev64(line + lane, tagged((uint32_t)myi, tag));
+      st_dev64(line + L.lid + lane, tagged(__float_as_uint(gate), tag));
       if (report) {
         if (L.ids_out) L.ids_out[(size_t)t * k + lane] = myi;
         if (L.gates_out) L.gates_out[(size_t)t * k + lane] = gate;
       }
     }
   }
-  __syncthreads();
+}
+
+// The selection of token t as published in one copy: lane r < k receives the
+// blob of the r-th expert and its gate (wave-wide, bounded wait).
+__device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t tag,
+                               const void *const *table, const uint8_t **blob_out,
+                               float *gate_out) {
+  const int lane = threadIdx.x & 63, k = L.k;
+  const uint64_t *line = L.sel + ((size_t)t * L.sel_copies + copy) * 2 * L.lid;
+  uint64_t wi = 0, wg = 0;
+  for (long s = 0;; ++s) {
+    bool ok = true;
+    if (lane < k) {
+      wi = ld_dev64(line + lane);
+      wg = ld_dev64(line + L.lid + lane);
+      ok = has_tag(wi, tag) && has_tag(wg, tag);
+    }
+    if (__all(ok)) break;
+    if (s > kSpin) {
+      if (lane == 0) add_dev(L.err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane < k) {
+    blob_out[lane] = (const uint8_t *)table[min((uint32_t)wi, (uint32_t)L.E - 1)];
+    gate_out[lane] = __uint_as_float((uint32_t)wg);
+  }
 }
 
 constexpr int kMaxBlockGroups = 16;  // gate/up column groups of one block (4 waves x 4)
@@ -247,32 +279,36 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   const int D = L.D, E = L.E, k = L.k, T = L.T;
   const int G = D / 64, NB = D / 64;
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
-  const int U = k * Gf + Gs;
   const uint32_t tag = as_const(L.bep)[b] + 1u;
   const uint16_t *x = (const uint16_t *)L.x;
 
-  // ---------------- roles of this block
+  // ---------------- roles of this block: routed blocks [0, NR), then shared
+  const bool shared_blk = b >= L.NR;
+  const int sb = shared_blk ? b - L.NR : b;
   const int nrb = (E + kRows - 1) / kRows;
-  const bool has_r = b < T * nrb;
+  const bool has_r = !shared_blk && b < T * nrb;
   const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
 
-  const bool has_g = b < L.n_gtiles * L.KSg;
-  const int tile = b / L.KSg, ks = b - tile * L.KSg;
+  const int n_rt = T * k * Gf;  // routed gate/up tiles, then the shared ones
+  const bool has_g = sb < (shared_blk ? L.n_gtiles - n_rt : n_rt) * L.KSg;
+  const int tile = (shared_blk ? n_rt : 0) + sb / L.KSg, ks = sb % L.KSg;
   Tile gt{};
   if (has_g) gt = glu_tile(L, tile);
-  const bool g_routed = has_g && gt.j >= 0;
+  const bool g_routed = has_g && !shared_blk;
   const int g0 = ks * G / L.KSg, g1 = (ks + 1) * G / L.KSg;
 
-  const bool has_d = b < T * NB * L.KSd;
-  const int ot = b / L.KSd, ksd = b - ot * L.KSd;
+  const int KSdx = shared_blk ? L.KSds : L.KSdr;  // splits of this block's unit range
+  const int Ux = shared_blk ? Gs : k * Gf;        // units of that range
+  const bool has_d = KSdx > 0 && sb < T * NB * KSdx;
+  const int ot = has_d ? sb / KSdx : 0, ksd = has_d ? sb % KSdx : 0;
   const int t_out = ot / NB, n = (ot - t_out * NB) * 64 + lane;
-  const int u0 = ksd * U / L.KSd, u1 = (ksd + 1) * U / L.KSd;
-  const bool d_routed = has_d && u0 < k * Gf;
+  const int u0 = ksd * Ux / max(KSdx, 1), u1 = (ksd + 1) * Ux / max(KSdx, 1);
+  const bool d_routed = has_d && !shared_blk;
   const bool routed = g_routed || d_routed;
 
-  // ---------------- router logits; block (t, 0) selects token t's experts.
-  // The router blocks do this before anything else: it heads the chain of
-  // dependent steps, and its registers are free again before the expert loads.
+  // ---------------- router logits, then the selection of the token (every
+  // router block publishes its own copy).  The router blocks do this before
+  // anything else: it heads the chain of dependent steps.
   const int nch = D / 16;
   float *sx = (float *)dsm;   // router: x as fp32 [D]
   float *sxs = sx + D;        // router: 16-column sums [D/16]
@@ -341,6 +377,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
         st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
       }
     }
+    __syncthreads();  // the selection reuses LDS
+    select_publish(L, r_t, b - r_t * nrb, tag, s_select, r_e0 == 0);
     __builtin_amdgcn_s_setprio(0);
   }
 
@@ -382,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       mu[i] = um[(size_t)g * F];
     }
   };
-  if (has_g && !g_routed) load_glu((const uint8_t *)L.sblobs[0]);
+  if (has_g && shared_blk) load_glu((const uint8_t *)L.sblobs[0]);
   u32x4 dq0[M], dq1[M];
   uint32_t dmw[M];
   auto load_down = [&](int i, const uint8_t *blob, int Fb, int g) {
@@ -392,11 +430,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     dq1[i] = dc[(size_t)(2 * g + 1) * D];
     dmw[i] = as_global((const uint32_t *)(blob + BL.down_meta))[(size_t)g * D + n];
   };
-  if (has_d) {
+  if (has_d && shared_blk) {
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       const int u = min(u0 + wave + i * kNW, u1 - 1);
-      if (u >= k * Gf) load_down(i, (const uint8_t *)L.sblobs[0], L.Fs, u - k * Gf);
+      load_down(i, (const uint8_t *)L.sblobs[0], L.Fs, u);
     }
   }
 
@@ -493,19 +531,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   // ---------------- selected experts (and gates) of the token(s) of this block
   if (routed) {
-    const bool report = g_routed && gt.j == 0 && gt.rb == 0 && ks == 0;  // first tile of a token
-    if (g_routed) block_select(L, gt.t, tag, s_select, s_table, s_blob[0], s_gate[0], report);
-    if (d_routed) {
-      if (g_routed && gt.t == t_out) {
-        if (tid < k) {
-          s_blob[1][tid] = s_blob[0][tid];
-          s_gate[1][tid] = s_gate[0][tid];
-        }
-        __syncthreads();
-      } else {
-        block_select(L, t_out, tag, s_select, s_table, s_blob[1], s_gate[1], false);
-      }
-    }
+    const int copy = b % nrb;
+    if (wave == 0 && g_routed) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0]);
+    if (wave == 1 && d_routed) wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1]);
+    __syncthreads();
   }
 
   // ---------------- loads of the selected experts
@@ -514,10 +543,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       const int u = min(u0 + wave + i * kNW, u1 - 1);
-      if (u < k * Gf) {
-        const int jj = u / Gf;
-        load_down(i, s_blob[1][jj], L.F, u - jj * Gf);
-      }
+      const int jj = u / Gf;
+      load_down(i, s_blob[1][jj], L.F, u - jj * Gf);
     }
   }
   // the shared expert's tiles compute after the routing (it needs the issue
@@ -532,15 +559,15 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     const uint64_t *hint = nullptr;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-      const int u = u0 + wave + i * kNW;
-      use[i] = u < u1;
-      if (u < k * Gf) {
+      const int u = min(u0 + wave + i * kNW, u1 - 1);
+      use[i] = u0 + wave + i * kNW < u1;
+      if (!shared_blk) {
         const int jj = u / Gf;
         gate[i] = s_gate[1][jj];
         hp[i] = L.h + (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
       } else {
         gate[i] = 1.0f;
-        hp[i] = L.h + (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)(u - k * Gf) * 64;
+        hp[i] = L.h + (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
       }
       if (use[i] && lane == i) hint = hp[i];
     }
@@ -597,11 +624,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 #pragma unroll
       for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
       bool last = true;
-      if (L.KSd > 1) {
+      if (L.KSdr + L.KSds > 1) {
         const float pv[1] = {s};
         float sv[1];
         last = split_reduce_fixed<1>(L.dacc + (size_t)ot * 64, L.dcnt + (size_t)ot * kCntStride,
-                                     L.KSd, pv, sv);
+                                     L.KSdr + L.KSds, pv, sv);
         s = sv[0];
       }
       if (last) {
@@ -642,20 +669,25 @@ int g_layer_capacity[2][2][3][64];  // [f16x][MAXC 6/16][m - 2][device]
 }  // namespace
 
 int layer_m(const LayerLaunch &L) {
-  const int U = L.k * (L.F / 64) + (L.sblobs ? L.Fs / 64 : 0);
-  const int mg = ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
-  const int mu = ceil_div(ceil_div(U, L.KSd), kNW);
-  int m = mg > mu ? mg : mu;
+  const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
+  int m = ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
+  m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), kNW));
+  if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), kNW));
   return m < 2 ? 2 : m;
 }
 
-int layer_grid(const LayerLaunch &L) {
+// routed blocks (router rows, routed gate/up tiles, routed down splits) and
+// shared blocks (shared gate/up tiles, shared down splits)
+int layer_routed_blocks(const LayerLaunch &L) {
+  const int n_rt = L.T * L.k * (L.F / 64);
   const int r = L.T * ((L.E + kRows - 1) / kRows);
-  const int g = L.n_gtiles * L.KSg;
-  const int d = L.T * (L.D / 64) * L.KSd;
-  int m = r > g ? r : g;
-  return m > d ? m : d;
+  return max(max(r, n_rt * L.KSg), L.T * (L.D / 64) * L.KSdr);
 }
+int layer_shared_blocks(const LayerLaunch &L) {
+  const int n_st = L.n_gtiles - L.T * L.k * (L.F / 64);
+  return max(n_st * L.KSg, L.T * (L.D / 64) * L.KSds);
+}
+int layer_grid(const LayerLaunch &L) { return layer_routed_blocks(L) + layer_shared_blocks(L); }
 
 size_t layer_smem(const LayerLaunch &L) {
   // router staging: x as fp32, 16-column sums, partial logits; then the table

@@ -119,23 +119,48 @@ void set_split_accumulators(const Workspace &w, uint64_t **gacc, uint64_t **dacc
   *dcnt = (uint32_t *)(w.layer + kCntOutOff);
 }
 
+// Reduction splits shared by both one-launch kernels (same splits, same
+// bits): gate/up splits over the column groups, aiming at about two blocks per
+// compute unit, and down splits over the routed units and over the shared
+// units, each at most 16 groups or units per block.
+struct Splits {
+  int ksg, ksdr, ksds;
+};
+Splits plan_splits(int T, int k, int D, int F, int Fs, int ksg_override, int ksd_override) {
+  const int G = D / 64, NB = D / 64;
+  const int n_rt = T * k * (F / 64), n_st = T * (Fs / 64);
+  const int Ur = k * (F / 64), Us = Fs / 64;
+  const int target = 512;
+  Splits sp;
+  sp.ksg = ksg_override > 0 ? ksg_override : (target + n_rt + n_st - 1) / (n_rt + n_st);
+  sp.ksg = clampi(sp.ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
+  // about one down item per gate/up item in each group of blocks
+  int ksdr = ksd_override > 0 ? ksd_override : (n_rt * sp.ksg + T * NB - 1) / (T * NB);
+  sp.ksdr = clampi(ksdr, (Ur + 15) / 16, Ur < kMaxFusedKSd ? Ur : kMaxFusedKSd);
+  sp.ksds = 0;
+  if (Us > 0) {
+    int ksds = ksd_override > 0 ? ksd_override : (n_st * sp.ksg + T * NB - 1) / (T * NB);
+    sp.ksds = clampi(ksds, (Us + 15) / 16, Us < kMaxFusedKSd ? Us : kMaxFusedKSd);
+  }
+  return sp;
+}
+
 // Choose the splits of the one-launch expert phase; false if its grid would
 // not be resident all at once (then the three-kernel path runs).
 bool plan_fused(const ExpertLaunch &a, const Workspace &w, FusedLaunch *f) {
   const int G = a.D / 64, NB = a.D / 64;
   const int n_gtiles = a.T * a.k * (a.F / 64) + (a.sblobs ? a.T * (a.Fs / 64) : 0);
-  const int U = a.k * (a.F / 64) + (a.sblobs ? a.Fs / 64 : 0);
-  // about two blocks per compute unit, each wave with at most 4 groups / units
-  const int target = 512;
-  int ksg = tuning().fused_ksg > 0 ? tuning().fused_ksg : (target + n_gtiles - 1) / n_gtiles;
-  ksg = clampi(ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
-  int ksd = tuning().fused_ksd > 0 ? tuning().fused_ksd
-                                   : (ksg * n_gtiles + a.T * NB - 1) / (a.T * NB);
-  ksd = clampi(ksd, (U + 15) / 16, U < kMaxFusedKSd ? U : kMaxFusedKSd);
-  if ((G + ksg - 1) / ksg > 16 || (U + ksd - 1) / ksd > 16) return false;
+  const Splits sp = plan_splits(a.T, a.k, a.D, a.F, a.sblobs ? a.Fs : 0, tuning().fused_ksg,
+                                tuning().fused_ksd);
+  const int Ur = a.k * (a.F / 64), Us = a.sblobs ? a.Fs / 64 : 0;
+  if ((G + sp.ksg - 1) / sp.ksg > 16 || (Ur + sp.ksdr - 1) / sp.ksdr > 16 ||
+      (sp.ksds > 0 && (Us + sp.ksds - 1) / sp.ksds > 16))
+    return false;
   f->a = a;
-  f->KSg = ksg;
-  f->KSd = ksd;
+  f->KSg = sp.ksg;
+  f->KSdr = sp.ksdr;
+  f->KSds = sp.ksds;
+  f->KSd = sp.ksdr + sp.ksds;
   f->n_gtiles = n_gtiles;
   f->tile_begin = 0;
   f->tile_end = n_gtiles;
@@ -160,19 +185,14 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   const int T = L->T, k = L->k, E = L->E, D = L->D, F = L->F;
   const int Fs = L->sblobs ? L->Fs : 0;
   if (!tuning().layer || T > kMaxLayerT || E > kMaxLayerE || k > kMaxK || D > 8192) return false;
-  const int G = D / 64, NB = D / 64;
+  const int NB = D / 64;
   const int n_gtiles = T * k * (F / 64) + T * (Fs / 64);
-  const int U = k * (F / 64) + Fs / 64;
-  // about two blocks per compute unit; at most 16 groups or units per block
-  const int target = 512;
-  int ksg = tuning().layer_ksg > 0 ? tuning().layer_ksg : (target + n_gtiles - 1) / n_gtiles;
-  ksg = clampi(ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
-  int ksd = tuning().layer_ksd > 0 ? tuning().layer_ksd
-                                   : (ksg * n_gtiles + T * NB - 1) / (T * NB);
-  ksd = clampi(ksd, (U + 15) / 16, U < kMaxFusedKSd ? U : kMaxFusedKSd);
-  L->KSg = ksg;
-  L->KSd = ksd;
+  const Splits sp = plan_splits(T, k, D, F, Fs, tuning().layer_ksg, tuning().layer_ksd);
+  L->KSg = sp.ksg;
+  L->KSdr = sp.ksdr;
+  L->KSds = sp.ksds;
   L->n_gtiles = n_gtiles;
+  L->NR = layer_routed_blocks(*L);
   if (layer_m(*L) > 4) return false;
   const int grid = layer_grid(*L);
   int cap = 0;
@@ -183,6 +203,9 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   // tagged words: logits, hidden activations
   Carver c{w.layer + kTaggedOff};
   L->rlog = c.take<uint64_t>((size_t)T * E, 8);
+  L->sel_copies = (E + 7) / 8;  // one per router block of a token
+  L->lid = (k + 15) / 16 * 16;
+  L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * 2 * L->lid, 8);
   L->h = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   if (kTaggedOff + c.off > kLayerRegionBytes) return false;
   L->table_off = layer_table_off(*L);

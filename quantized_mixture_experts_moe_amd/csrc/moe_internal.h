@@ -147,7 +147,8 @@ struct ExpertLaunch {
 constexpr int kFlagCopies = 16;  // replicas of each slot-ready flag (one 128-byte line each)
 struct FusedLaunch {
   ExpertLaunch a;           // needs slot_blob (resident experts)
-  int KSg, KSd, n_gtiles;
+  int KSg, KSd, n_gtiles;   // KSd = KSdr + KSds
+  int KSdr, KSds;           // down splits of the routed / shared units
   int tile_begin, tile_end; // gate/up tiles of this launch (routed tiles, then shared)
   int do_down;              // this launch also runs the down projection and combine
   // slot counters and flags: zeroed by the router kernel launched just before
@@ -189,10 +190,14 @@ struct LayerLaunch {
   const uint8_t *rcodes; const uint32_t *rmeta; const float *logit_bias;
   const void *const *rblobs;          // routed bank [E]
   const void *const *sblobs;          // shared bank (expert 0) or null
-  int KSg, KSd, n_gtiles;
+  int KSg, n_gtiles;
+  int KSdr, KSds;                     // down splits of the routed / shared units
+  int NR;                             // routed blocks (the shared blocks follow)
   size_t table_off;                   // LDS byte offset of the blob table
   uint32_t *bep;                      // per-block epochs [kMaxLayerGrid]
   uint64_t *rlog;                     // [T][E] tagged logits
+  uint64_t *sel;                      // [T][sel_copies][2][lid] tagged ids, gates
+  int sel_copies, lid;
   uint64_t *h;                        // [T*k*F + T*Fs] tagged hidden activations
   uint64_t *gacc, *dacc;              // split-reduction accumulators (zero between calls)
   uint32_t *gcnt, *dcnt;              // and their counters
@@ -201,6 +206,7 @@ struct LayerLaunch {
   void *out; int out_dtype;
 };
 int layer_m(const LayerLaunch &L);
+int layer_routed_blocks(const LayerLaunch &L);
 int layer_grid(const LayerLaunch &L);
 size_t layer_smem(const LayerLaunch &L);
 size_t layer_table_off(const LayerLaunch &L);
