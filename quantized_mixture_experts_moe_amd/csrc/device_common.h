@@ -109,6 +109,45 @@ __device__ __forceinline__ float dot_chunk_hilo(const u32x4 q, const uint32_t *x
   return acc;
 }
 
+// Matrix-core product v_mfma_f32_16x16x32_{bf16,f16}: D = A B + C with
+// A[row l % 16][k 8 (l / 16) + j], B[k 8 (l / 16) + j][col l % 16] (8 16-bit
+// values per lane in 4 registers, value j in half j % 2 of register j / 2)
+// and D[row 4 (l / 16) + i][col l % 16] in register i.
+typedef __bf16 mma_bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mma_f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mma_f16x8, a),
+                                                  __builtin_bit_cast(mma_f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mma_bf16x8, a),
+                                                   __builtin_bit_cast(mma_bf16x8, b), c, 0, 0,
+                                                   0);
+}
+
+// The 8 codes of one word as 16-bit pairs (offset + q_m, offset + q_{m+4}),
+// m = 0..3 (magic 0x43004300: bf16 128 + q; 0x64006400: fp16 1024 + q).
+__device__ __forceinline__ u32x4 code_pairs(uint32_t w, uint32_t magic) {
+  u32x4 r;
+  r.x = (w & 0x000F000Fu) | magic;
+  r.y = ((w >> 4) & 0x000F000Fu) | magic;
+  r.z = ((w >> 8) & 0x000F000Fu) | magic;
+  r.w = ((w >> 12) & 0x000F000Fu) | magic;
+  return r;
+}
+// The same pairs as bf16 1 + q / 16 (the nibble in mantissa bits 3..6 of
+// 1.0): a small offset, for products whose other factor has a large mean.
+__device__ __forceinline__ u32x4 code_pairs_unit(uint32_t w, uint32_t magic) {
+  u32x4 r;
+  r.x = ((w << 3) & 0x00780078u) | magic;
+  r.y = ((w >> 1) & 0x00780078u) | magic;
+  r.z = ((w >> 5) & 0x00780078u) | magic;
+  r.w = ((w >> 9) & 0x00780078u) | magic;
+  return r;
+}
+
 // View of global memory through the constant address space: wave-uniform
 // loads through it become scalar loads into SGPRs.  Only for data written by
 // an earlier kernel (the scalar cache does not see stores of the same kernel).

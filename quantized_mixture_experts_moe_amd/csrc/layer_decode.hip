@@ -8,10 +8,11 @@
 // tokens"; yodev.dev, "Por que funciona: el A4B del nombre").  Routing is a
 // short chain of dependent steps; the shared expert does not depend on it.
 // So the grid has two groups of blocks:
-//   routed blocks: the router rows (8 experts per block), then the routed
-//     gate/up tiles and the routed part of the down projection.  They issue no
-//     weight loads before the selection arrives, so their polls are not
-//     queued behind outstanding loads (a wave's loads complete in order).
+//   router blocks: the router rows (8 experts per block) and the selection;
+//   routed blocks: the routed gate/up tiles and the routed part of the down
+//     projection.  They issue no weight loads before the selection arrives,
+//     so their polls are not queued behind outstanding loads (a wave's loads
+//     complete in order).
 //   shared blocks: the shared expert's gate/up tiles and its part of the down
 //     projection; they stream from the first cycle, while routing runs.
 // Every router block of a token, once all logits of the token are published,
@@ -30,7 +31,7 @@
 // every wait is bounded and a timeout bumps an error counter.
 //
 // Work split (one token, k = 8, D = 2816, F = 704, F_s = 2112):
-//   router:  16 blocks of 8 experts;
+//   router:  16 blocks of 8 experts (they do nothing else);
 //   gate/up: 88 routed + 33 shared tiles of 64 hidden rows x KSg reduction
 //            splits over the 44 column groups;
 //   down:    44 tiles of 64 output rows x (KSdr splits of the 88 routed units
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   constexpr int MAXX = MAXC == 6 ? 2 : 4;  // 16-byte pieces of x per thread (router)
   extern __shared__ __align__(16) uint8_t dsm[];
   __shared__ float red[kNW][2][64];
-  __shared__ float hbuf[kNW][M][64];
+  __shared__ __align__(16) uint32_t hpl[kNW][M][3][32];  // h planes as bf16 pairs
   __shared__ __align__(16) uint32_t s_xp[kMaxBlockGroups * 32];  // activation pairs
   __shared__ float s_xs[kMaxBlockGroups];                        // 64-column sums
   __shared__ const uint8_t *s_blob[2][kMaxK];  // [0]: gate/up token, [1]: down token
@@ -275,19 +276,21 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x;
+  const int b = L.blk0 + blockIdx.x;
   const int D = L.D, E = L.E, k = L.k, T = L.T;
   const int G = D / 64, NB = D / 64;
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
   const uint32_t tag = as_const(L.bep)[b] + 1u;
   const uint16_t *x = (const uint16_t *)L.x;
 
-  // ---------------- roles of this block: routed blocks [0, NR), then shared
-  const bool shared_blk = b >= L.NR;
-  const int sb = shared_blk ? b - L.NR : b;
+  // ---------------- roles of this block: router blocks [0, T nrb), routed
+  // blocks [T nrb, NR), shared blocks [NR, grid)
   const int nrb = (E + kRows - 1) / kRows;
-  const bool has_r = !shared_blk && b < T * nrb;
+  const bool given = L.given_blob != nullptr;   // selection from the caller
+  const bool has_r = !given && b < T * nrb;
   const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
+  const bool shared_blk = b >= L.NR;
+  const int sb = shared_blk ? b - L.NR : (b < T * nrb ? 1 << 30 : b - T * nrb);  // item index
 
   const int n_rt = T * k * Gf;  // routed gate/up tiles, then the shared ones
   const bool has_g = sb < (shared_blk ? L.n_gtiles - n_rt : n_rt) * L.KSg;
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   const int KSdx = shared_blk ? L.KSds : L.KSdr;  // splits of this block's unit range
   const int Ux = shared_blk ? Gs : k * Gf;        // units of that range
-  const bool has_d = KSdx > 0 && sb < T * NB * KSdx;
+  const bool has_d = KSdx > 0 && sb < T * NB * KSdx;  // (router blocks: no items)
   const int ot = has_d ? sb / KSdx : 0, ksd = has_d ? sb % KSdx : 0;
   const int t_out = ot / NB, n = (ot - t_out * NB) * 64 + lane;
   const int u0 = ksd * Ux / max(KSdx, 1), u1 = (ksd + 1) * Ux / max(KSdx, 1);
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   // 2. the routed bank's blob table
   constexpr int kTab = kMaxLayerE / kThreads;
   const void *tb[kTab];
-  if (routed) {
+  if (routed && !given) {
 #pragma unroll
     for (int i = 0; i < kTab; ++i) {
       const int e = tid + i * kThreads;
@@ -459,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     if ((tid & 7) == 0) s_xs[tid / 8] = sg;
   }
   const void **s_table = (const void **)(dsm + L.table_off);
-  if (routed) {
+  if (routed && !given) {
 #pragma unroll
     for (int i = 0; i < kTab; ++i) {
       const int e = tid + i * kThreads;
@@ -470,36 +473,43 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   // ---------------- gate/up arithmetic, split reduction (the last split to
   // arrive holds the sums), hidden activations
+  // On the matrix cores: lane l holds word w (8 columns) of hidden row l as
+  // the B operand; lanes 0, 20, 40, 60 hold the activation pairs of word w
+  // as A rows 0, 4, 8, 12 (the other lanes zero), so D row 4q, column c --
+  // register 0 of lane 16q + c -- accumulates row l's dot product.
+  const bool xa_lane = (lane & 15) == 4 * (lane >> 4);
   auto glu = [&]() {
     const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
     float accg = 0.0f, accu = 0.0f;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       const int gi = wave + i * kNW;  // group g0 + gi
-      // one group's activation pairs live at a time (keeps the registers of
-      // the in-flight weight loads free)
-      __builtin_amdgcn_sched_barrier(0);
       if (g0 + gi < g1) {
-        uint32_t xg[32];
-        const u32x4 *xv = (const u32x4 *)&s_xp[32 * gi];
+        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t wg[8] = {qg0[i].x, qg0[i].y, qg0[i].z, qg0[i].w,
+                                qg1[i].x, qg1[i].y, qg1[i].z, qg1[i].w};
+        const uint32_t wu[8] = {qu0[i].x, qu0[i].y, qu0[i].z, qu0[i].w,
+                                qu1[i].x, qu1[i].y, qu1[i].z, qu1[i].w};
+        // the four A lanes read all 8 words at once (one masked region), the
+        // other lanes keep zeros
+        u32x4 a[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const u32x4 v4 = xv[c];
-          xg[4 * c] = v4.x;
-          xg[4 * c + 1] = v4.y;
-          xg[4 * c + 2] = v4.z;
-          xg[4 * c + 3] = v4.w;
+        for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
+        if (xa_lane) {
+#pragma unroll
+          for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&s_xp[32 * gi + 4 * w];
+        }
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          dg = mma16<F16X>(a[w], code_pairs(wg[w], magic), dg);
+          du = mma16<F16X>(a[w], code_pairs(wu[w], magic), du);
         }
         const float xsg = s_xs[gi];
-        float dg = dot_chunk<F16X>(qg0[i], xg, 0.0f, magic);
-        dg = dot_chunk<F16X>(qg1[i], xg + 16, dg, magic);
-        float du = dot_chunk<F16X>(qu0[i], xg, 0.0f, magic);
-        du = dot_chunk<F16X>(qu1[i], xg + 16, du, magic);
         const float sg = f16_to_f32(mg[i]), bg = f16_to_f32(mg[i] >> 16);
         const float su = f16_to_f32(mu[i]), bu = f16_to_f32(mu[i] >> 16);
-        accg = fmaf(sg, dg, accg);
+        accg = fmaf(sg, dg[0], accg);
         accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsg, accg);
-        accu = fmaf(su, du, accu);
+        accu = fmaf(su, du[0], accu);
         accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsg, accu);
       }
     }
@@ -531,9 +541,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   // ---------------- selected experts (and gates) of the token(s) of this block
   if (routed) {
-    const int copy = b % nrb;
-    if (wave == 0 && g_routed) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0]);
-    if (wave == 1 && d_routed) wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1]);
+    const int copy = sb % nrb;
+    if (given) {
+      if (tid < k) {  // written by earlier work on the stream: plain loads
+        s_blob[0][tid] = g_routed ? (const uint8_t *)L.given_blob[(size_t)gt.t * k + tid] : nullptr;
+        s_blob[1][tid] = d_routed ? (const uint8_t *)L.given_blob[(size_t)t_out * k + tid] : nullptr;
+        s_gate[1][tid] = d_routed ? L.given_gates[(size_t)t_out * k + tid] : 0.0f;
+      }
+    } else {
+      if (wave == 0 && g_routed) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0]);
+      if (wave == 1 && d_routed) wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1]);
+    }
     __syncthreads();
   }
 
@@ -592,28 +610,55 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
+    // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
     float hsum[M];
+    const int pos = 2 * (4 * (lane >> 3) + (lane & 3)) + ((lane >> 2) & 1);
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-      hbuf[wave][i][lane] = hv0[i];
-      hsum[i] = wave_sum(hv0[i]);
+      const float hv = hv0[i];
+      const uint32_t p0 = f32_to_bf16(hv);
+      const float r1 = hv - __uint_as_float(p0 << 16);
+      const uint32_t p1 = f32_to_bf16(r1);
+      const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
+      uint16_t *hp16 = (uint16_t *)&hpl[wave][i][0][0];
+      hp16[pos] = (uint16_t)p0;
+      hp16[64 + pos] = (uint16_t)p1;
+      hp16[128 + pos] = (uint16_t)p2;
+      hsum[i] = wave_sum(hv);
     }
     __builtin_amdgcn_wave_barrier();
+    // matrix cores: lane l holds word w (8 hidden rows) of output row l as
+    // B (codes as 1 + q / 16); lanes with l % 16 = 4 (l / 16) + p, p < 3,
+    // hold plane p of h as A row 4 (l / 16) + p, so registers 0..2 of lane l
+    // accumulate the three planes' dot products of output row l.
+    const int plane = (lane & 15) - 4 * (lane >> 4);
+    const bool ha_lane = plane >= 0 && plane < 3;
+    const uint32_t umagic = opaque_vgpr(0x3F803F80u);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       if (!use[i]) continue;
-      float hv[64];
+      const uint32_t wd[8] = {dq0[i].x, dq0[i].y, dq0[i].z, dq0[i].w,
+                              dq1[i].x, dq1[i].y, dq1[i].z, dq1[i].w};
+      u32x4 a[8];
 #pragma unroll
-      for (int j = 0; j < 64; j += 4) {
-        const float4 v4 = *(const float4 *)&hbuf[wave][i][j];
-        hv[j] = v4.x;
-        hv[j + 1] = v4.y;
-        hv[j + 2] = v4.z;
-        hv[j + 3] = v4.w;
+      for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
+      if (ha_lane) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&hpl[wave][i][plane][4 * w];
       }
-      const float d = dot_group_f32(dq0[i], dq1[i], hv);
-      const float v = fmaf(f16_to_f32(dmw[i]), d, f16_to_f32(dmw[i] >> 16) * hsum[i]);
+      // two accumulation chains (even and odd words)
+      f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < 8; w += 2) {
+        d0 = mma16<false>(a[w], code_pairs_unit(wd[w], umagic), d0);
+        d1 = mma16<false>(a[w + 1], code_pairs_unit(wd[w + 1], umagic), d1);
+      }
+      // sum (1 + q/16) h = sum h + sum q h / 16, three planes
+      const float dsum = ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2]);
+      const float sc = f16_to_f32(dmw[i]), bi = f16_to_f32(dmw[i] >> 16);
+      const float v = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum[i]);
       acc = fmaf(gate[i], v, acc);
     }
     __syncthreads();  // red[] is reused
@@ -645,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   // ---------------- advance every copy of the epoch (block b: b, b + grid, ...)
   if (tid == 0)
-    for (int j = b; j < kMaxLayerGrid; j += gridDim.x) st_dev(L.bep + j, tag);
+    for (int j = b; j < kMaxLayerGrid; j += L.grid_full) st_dev(L.bep + j, tag);
 }
 
 using KernelFn = void (*)(LayerLaunch);
@@ -680,8 +725,8 @@ int layer_m(const LayerLaunch &L) {
 // shared blocks (shared gate/up tiles, shared down splits)
 int layer_routed_blocks(const LayerLaunch &L) {
   const int n_rt = L.T * L.k * (L.F / 64);
-  const int r = L.T * ((L.E + kRows - 1) / kRows);
-  return max(max(r, n_rt * L.KSg), L.T * (L.D / 64) * L.KSdr);
+  const int r = L.T * ((L.E + kRows - 1) / kRows);  // router blocks come first
+  return r + max(n_rt * L.KSg, L.T * (L.D / 64) * L.KSdr);
 }
 int layer_shared_blocks(const LayerLaunch &L) {
   const int n_st = L.n_gtiles - L.T * L.k * (L.F / 64);
@@ -722,11 +767,18 @@ hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
   return hipSuccess;
 }
 
-hipError_t launch_layer(const LayerLaunch &L, hipStream_t s) {
+hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s) {
   KernelFn k = pick_layer(L, layer_m(L));
   if (!k) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k, dim3(layer_grid(L)), dim3(kThreads), layer_smem(L), s, L);
+  if (n <= 0) return hipSuccess;
+  L.blk0 = blk0;
+  L.grid_full = layer_grid(L);
+  hipLaunchKernelGGL(k, dim3(n), dim3(kThreads), layer_smem(L), s, L);
   return hipGetLastError();
+}
+
+hipError_t launch_layer(const LayerLaunch &L, hipStream_t s) {
+  return launch_layer_range(L, 0, layer_grid(L), s);
 }
 
 }  // namespace moe

@@ -379,18 +379,17 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   Workspace w = carve(ws, d);
   hipStream_t s = (hipStream_t)stream;
 
-  if (!pool) {
-    // decode: router, selection, experts and combine in one launch
-    LayerLaunch L{};
-    L.f16x = x_dtype == MOE_F16; L.T = T; L.k = k; L.E = E; L.D = D; L.F = F; L.Fs = Fs;
-    L.x = x; L.rcodes = (const uint8_t *)router->codes; L.rmeta = (const uint32_t *)router->meta;
-    L.logit_bias = logit_bias; L.rblobs = routed->blobs;
-    L.sblobs = shared ? shared->blobs : nullptr;
-    L.ids_out = ids_out; L.gates_out = gates_out; L.out = out; L.out_dtype = out_dtype;
-    if (plan_layer(w, &L)) {
-      const int pi = prof_begin(s);
-      return hip_status(prof_end(pi, s, launch_layer(L, s)));
-    }
+  // decode: router, selection, experts and combine in one launch
+  LayerLaunch L{};
+  L.f16x = x_dtype == MOE_F16; L.T = T; L.k = k; L.E = E; L.D = D; L.F = F; L.Fs = Fs;
+  L.x = x; L.rcodes = (const uint8_t *)router->codes; L.rmeta = (const uint32_t *)router->meta;
+  L.logit_bias = logit_bias; L.rblobs = pool ? nullptr : routed->blobs;
+  L.sblobs = shared ? shared->blobs : nullptr;
+  L.ids_out = ids_out; L.gates_out = gates_out; L.out = out; L.out_dtype = out_dtype;
+  const bool use_layer = plan_layer(w, &L);
+  if (use_layer && !pool) {
+    const int pi = prof_begin(s);
+    return hip_status(prof_end(pi, s, launch_layer(L, s)));
   }
 
   RouteLaunch r;
@@ -413,7 +412,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   a.h = w.h; a.hs = w.hs; a.part = w.part; a.counters = w.counters;
   a.y = nullptr; a.out = out; a.out_dtype = out_dtype;
   FusedLaunch f;
-  const bool fused = tuning().fused && plan_fused(a, w, &f);
+  const bool fused = !use_layer && tuning().fused && plan_fused(a, w, &f);
   if (fused) {
     r.zero = f.slot_cnt;
     r.zero_words = T * (k + 1);
@@ -422,6 +421,23 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     r.zero2_stride = 32;
   }
   if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
+  if (use_layer && pool) {
+    // Streamed experts: ids back to the host; the shared expert's blocks run
+    // while the host plans and the side stream copies the missing experts
+    // into HBM slots; then the routed blocks with that selection.  The
+    // splits are those of the resident launch, so results are bitwise equal.
+    st = pool_fetch_ids(pool, r.ids, T * k, s);
+    if (st) return st;
+    const int NR = L.NR, NS = layer_shared_blocks(L);
+    if (launch_layer_range(L, NR, NS, s) != hipSuccess) return MOE_E_HIP;
+    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, w.slot_blob);
+    if (st) return st;
+    L.given_blob = w.slot_blob;
+    L.given_gates = r.gates;
+    L.ids_out = nullptr;  // already written by the router kernel
+    L.gates_out = nullptr;
+    return hip_status(launch_layer_range(L, 0, NR, s));
+  }
   if (fused && !pool) {
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_fused(f, s)));

@@ -192,7 +192,12 @@ struct LayerLaunch {
   const void *const *sblobs;          // shared bank (expert 0) or null
   int KSg, n_gtiles;
   int KSdr, KSds;                     // down splits of the routed / shared units
-  int NR;                             // routed blocks (the shared blocks follow)
+  int NR;                             // router + routed blocks (the shared blocks follow)
+  int blk0, grid_full;                // this launch covers blocks [blk0, blk0 + grid)
+  // selection given by the caller (streamed experts: ids from an earlier
+  // routing, blobs from the pool): [T][k] blob addresses and gates, or null
+  const void *const *given_blob;
+  const float *given_gates;
   size_t table_off;                   // LDS byte offset of the blob table
   uint32_t *bep;                      // per-block epochs [kMaxLayerGrid]
   uint64_t *rlog;                     // [T][E] tagged logits
@@ -211,7 +216,11 @@ int layer_grid(const LayerLaunch &L);
 size_t layer_smem(const LayerLaunch &L);
 size_t layer_table_off(const LayerLaunch &L);
 hipError_t layer_capacity(const LayerLaunch &L, int *cap);
+int layer_shared_blocks(const LayerLaunch &L);
 hipError_t launch_layer(const LayerLaunch &L, hipStream_t s);
+// blocks [blk0, blk0 + n) of the grid only (streamed experts: shared blocks
+// first, then the rest once the pool has the selected experts)
+hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s);
 
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);

@@ -375,10 +375,11 @@ def test_layer_forward_decode_all_paths(path):
         _tune(**_DEFAULTS)
 
 
-def test_layer_launch_equals_expert_phase_launch():
-    """Same splits, same summation order: the one-launch layer and the
-    router + one-launch expert phase agree bit for bit."""
-    _case("layer vs fused bitwise (decode, beta=6.5)")
+def test_layer_launch_agrees_with_expert_phase_launch():
+    """The one-launch layer (matrix cores) and the router + one-launch expert
+    phase (dot products) select the same experts with the same gates, and
+    their outputs agree far inside the bar."""
+    _case("layer vs router + expert phase (decode, beta=6.5)")
     L = dev_layer("decode")
     cfg = L.cfg
     bias = gen.zipf_bias(0, 0, cfg.E, 6.5)
@@ -390,7 +391,9 @@ def test_layer_launch_equals_expert_phase_launch():
             _tune(layer=0)
             b, ib, gb = _layer_gpu(L, xb, cfg.k, bias)
             assert np.array_equal(ia, ib) and np.array_equal(ga, gb)
-            assert torch.equal(a, b), tok
+            r = rel_l2(a.cpu().numpy(), b.cpu().numpy())
+            print(f"    token {tok}: rel_l2(layer, expert phase) = {r:.2e}")
+            assert r < 1e-5, tok
     finally:
         _tune(**_DEFAULTS)
 
