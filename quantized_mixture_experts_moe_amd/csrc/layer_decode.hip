@@ -107,6 +107,23 @@ __device__ __forceinline__ int wait_hint(const uint64_t *p, uint32_t tag, uint32
   }
 }
 
+// Counted fixed-point reduction, one device-scope atomic per value: the
+// 64-bit word holds the sum of the partials, rounded to multiples of 2^-28,
+// in bits 8..63 and the number of partials added so far in bits 0..7.  The
+// returned word tells each lane whether its add completed the n partials;
+// that lane alone gets the sum (integer addition: the same for any arrival
+// order) and puts the word back to zero for the next call.  Sums must stay
+// below 2^27 in magnitude.
+__device__ __forceinline__ bool counted_add(uint64_t *word, float v, int n, float *sum) {
+  const uint64_t add = ((uint64_t)__double2ll_rn((double)v * 268435456.0) << 8) + 1u;
+  const uint64_t old =
+      __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old & 0xFFu) != (uint64_t)(n - 1)) return false;
+  *sum = (float)((double)((long long)(old + add) >> 8) * (1.0 / 268435456.0));
+  st_dev64(word, 0u);
+  return true;
+}
+
 template <bool F16X>
 __device__ __forceinline__ float x_to_f32(uint32_t v) {
   return F16X ? f16_to_f32(v) : bf16_to_f32(v);
@@ -433,10 +450,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     dq1[i] = dc[(size_t)(2 * g + 1) * D];
     dmw[i] = as_global((const uint32_t *)(blob + BL.down_meta))[(size_t)g * D + n];
   };
-  if (has_d && shared_blk) {
+  // down units: waves 1..3 take units u0 + (wave - 1) + 3 i; wave 0 has none,
+  // so its split reductions never wait behind outstanding weight loads
+  constexpr int kDW = kNW - 1;
+  const int dw = wave - 1;
+  if (has_d && shared_blk && wave > 0) {
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-      const int u = min(u0 + wave + i * kNW, u1 - 1);
+      const int u = min(u0 + dw + i * kDW, u1 - 1);
       load_down(i, (const uint8_t *)L.sblobs[0], L.Fs, u);
     }
   }
@@ -523,19 +544,15 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
         v0 += red[w][0][lane];
         v1 += red[w][1][lane];
       }
-      bool last = true;
-      if (L.KSg > 1) {
-        const float pv[2] = {v0, v1};
-        float sv[2];
-        last = split_reduce_fixed<2>(L.gacc + (size_t)tile * 128,
-                                     L.gcnt + (size_t)tile * kCntStride, L.KSg, pv, sv);
-        v0 = sv[0];
-        v1 = sv[1];
-      }
-      if (last) {
-        const float h = gelu_tanh(v0) * v1;
-        st_dev64(L.h + gt.hoff + (size_t)gt.rb * 64 + lane, tagged(__float_as_uint(h), tag));
-      }
+      // the split that completes a gate sum publishes gelu(gate), the one that
+      // completes an up sum publishes up; the consumer multiplies
+      const size_t ho = gt.hoff + (size_t)gt.rb * 64 + lane;
+      float g = v0, u = v1;
+      const bool last_g = L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + lane, v0, L.KSg, &g);
+      const bool last_u =
+          L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + 64 + lane, v1, L.KSg, &u);
+      if (last_g) st_dev64(L.hg + ho, tagged(__float_as_uint(gelu_tanh(g)), tag));
+      if (last_u) st_dev64(L.hu + ho, tagged(__float_as_uint(u), tag));
     }
   };
 
@@ -557,39 +574,46 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   // ---------------- loads of the selected experts
   if (g_routed) load_glu(s_blob[0][gt.j]);
-  if (d_routed) {
+  // routed down weights: with the gate/up tile (down_early) or after it
+  auto load_routed_down = [&]() {
+    if (d_routed && wave > 0) {
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int u = min(u0 + wave + i * kNW, u1 - 1);
-      const int jj = u / Gf;
-      load_down(i, s_blob[1][jj], L.F, u - jj * Gf);
+      for (int i = 0; i < M; ++i) {
+        const int u = min(u0 + dw + i * kDW, u1 - 1);
+        const int jj = u / Gf;
+        load_down(i, s_blob[1][jj], L.F, u - jj * Gf);
+      }
     }
-  }
+  };
+  if (L.down_early) load_routed_down();
   // the shared expert's tiles compute after the routing (it needs the issue
   // slots more) and before the routed tiles (their data comes later)
   if (has_g) glu();
+  if (!L.down_early) load_routed_down();
 
   // ---------------- down projection and combine
   if (has_d) {
-    const uint64_t *hp[M];
+    size_t hp[M];
     float gate[M];
     bool use[M];
     const uint64_t *hint = nullptr;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-      const int u = min(u0 + wave + i * kNW, u1 - 1);
-      use[i] = u0 + wave + i * kNW < u1;
+      const int u = min(u0 + dw + i * kDW, u1 - 1);
+      use[i] = wave > 0 && u0 + dw + i * kDW < u1;
       if (!shared_blk) {
         const int jj = u / Gf;
         gate[i] = s_gate[1][jj];
-        hp[i] = L.h + (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
+        hp[i] = (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
       } else {
         gate[i] = 1.0f;
-        hp[i] = L.h + (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
+        hp[i] = (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
       }
-      if (use[i] && lane == i) hint = hp[i];
+      if (use[i] && lane == 2 * i) hint = L.hg + hp[i];
+      if (use[i] && lane == 2 * i + 1) hint = L.hu + hp[i];
     }
-    // lane i polls one word of unit i, then the units' values are read (checked)
+    // lanes 2i, 2i + 1 poll one word of unit i's two rows, then the values
+    // are read (checked): h = gelu(gate) * up
     wait_hint(hint, tag, L.err);
     float hv0[M];
     for (long s = 0;; ++s) {
@@ -598,9 +622,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       for (int i = 0; i < M; ++i) {
         hv0[i] = 0.0f;
         if (use[i]) {
-          const uint64_t w = ld_dev64(hp[i] + lane);
-          ok = ok && has_tag(w, tag);
-          hv0[i] = __uint_as_float((uint32_t)w);
+          const uint64_t wg = ld_dev64(L.hg + hp[i] + lane);
+          const uint64_t wu = ld_dev64(L.hu + hp[i] + lane);
+          ok = ok && has_tag(wg, tag) && has_tag(wu, tag);
+          hv0[i] = __uint_as_float((uint32_t)wg) * __uint_as_float((uint32_t)wu);
         }
       }
       if (__all(ok)) break;
@@ -668,15 +693,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       float s = 0.0f;
 #pragma unroll
       for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
-      bool last = true;
-      if (L.KSdr + L.KSds > 1) {
-        const float pv[1] = {s};
-        float sv[1];
-        last = split_reduce_fixed<1>(L.dacc + (size_t)ot * 64, L.dcnt + (size_t)ot * kCntStride,
-                                     L.KSdr + L.KSds, pv, sv);
-        s = sv[0];
-      }
-      if (last) {
+      const int nsp = L.KSdr + L.KSds;
+      if (nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s)) {
         const size_t idx = (size_t)t_out * D + n;
         if (L.out_dtype == MOE_F32)
           ((float *)L.out)[idx] = s;
@@ -716,8 +734,8 @@ int g_layer_capacity[2][2][3][64];  // [f16x][MAXC 6/16][m - 2][device]
 int layer_m(const LayerLaunch &L) {
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
   int m = ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
-  m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), kNW));
-  if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), kNW));
+  m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), kNW - 1));  // down units: 3 waves
+  if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), kNW - 1));
   return m < 2 ? 2 : m;
 }
 

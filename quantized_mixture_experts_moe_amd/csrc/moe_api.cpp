@@ -122,7 +122,7 @@ void set_split_accumulators(const Workspace &w, uint64_t **gacc, uint64_t **dacc
 // Reduction splits shared by both one-launch kernels (same splits, same
 // bits): gate/up splits over the column groups, aiming at about two blocks per
 // compute unit, and down splits over the routed units and over the shared
-// units, each at most 16 groups or units per block.
+// units, at most 16 groups or 12 units per block.
 struct Splits {
   int ksg, ksdr, ksds;
 };
@@ -136,11 +136,11 @@ Splits plan_splits(int T, int k, int D, int F, int Fs, int ksg_override, int ksd
   sp.ksg = clampi(sp.ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
   // about one down item per gate/up item in each group of blocks
   int ksdr = ksd_override > 0 ? ksd_override : (n_rt * sp.ksg + T * NB - 1) / (T * NB);
-  sp.ksdr = clampi(ksdr, (Ur + 15) / 16, Ur < kMaxFusedKSd ? Ur : kMaxFusedKSd);
+  sp.ksdr = clampi(ksdr, (Ur + 11) / 12, Ur < kMaxFusedKSd ? Ur : kMaxFusedKSd);
   sp.ksds = 0;
   if (Us > 0) {
     int ksds = ksd_override > 0 ? ksd_override : (n_st * sp.ksg + T * NB - 1) / (T * NB);
-    sp.ksds = clampi(ksds, (Us + 15) / 16, Us < kMaxFusedKSd ? Us : kMaxFusedKSd);
+    sp.ksds = clampi(ksds, (Us + 11) / 12, Us < kMaxFusedKSd ? Us : kMaxFusedKSd);
   }
   return sp;
 }
@@ -185,18 +185,28 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   const int T = L->T, k = L->k, E = L->E, D = L->D, F = L->F;
   const int Fs = L->sblobs ? L->Fs : 0;
   if (!tuning().layer || T > kMaxLayerT || E > kMaxLayerE || k > kMaxK || D > 8192) return false;
-  const int NB = D / 64;
+  const int NB = D / 64, G = D / 64;
   const int n_gtiles = T * k * (F / 64) + T * (Fs / 64);
-  const Splits sp = plan_splits(T, k, D, F, Fs, tuning().layer_ksg, tuning().layer_ksd);
-  L->KSg = sp.ksg;
-  L->KSdr = sp.ksdr;
-  L->KSds = sp.ksds;
   L->n_gtiles = n_gtiles;
-  L->NR = layer_routed_blocks(*L);
-  if (layer_m(*L) > 4) return false;
-  const int grid = layer_grid(*L);
-  int cap = 0;
-  if (layer_capacity(*L, &cap) != hipSuccess || grid > cap || grid > kMaxLayerGrid) return false;
+  L->down_early = tuning().layer_down_early;
+  // the most gate/up splits (and with them down splits) whose grid is still
+  // resident all at once: more, smaller blocks overlap more of the transfer
+  bool found = false;
+  const int ksg_hi = tuning().layer_ksg > 0 ? tuning().layer_ksg : (G < kMaxKS ? G : kMaxKS);
+  const int ksg_lo = tuning().layer_ksg > 0 ? tuning().layer_ksg : 1;
+  for (int ksg = ksg_hi; ksg >= ksg_lo && !found; --ksg) {
+    const Splits sp = plan_splits(T, k, D, F, Fs, ksg, tuning().layer_ksd);
+    L->KSg = sp.ksg;
+    L->KSdr = sp.ksdr;
+    L->KSds = sp.ksds;
+    L->NR = layer_routed_blocks(*L);
+    if (layer_m(*L) > 4) continue;
+    const int grid = layer_grid(*L);
+    int cap = 0;
+    if (layer_capacity(*L, &cap) != hipSuccess) return false;
+    found = grid <= cap && grid <= kMaxLayerGrid;
+  }
+  if (!found) return false;
   if (n_gtiles > kMaxAccTiles || T * NB > kMaxOutTiles) return false;
   L->bep = (uint32_t *)w.layer;
   set_split_accumulators(w, &L->gacc, &L->dacc, &L->gcnt, &L->dcnt);
@@ -206,7 +216,8 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->sel_copies = (E + 7) / 8;  // one per router block of a token
   L->lid = (k + 15) / 16 * 16;
   L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * 2 * L->lid, 8);
-  L->h = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
+  L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
+  L->hu = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   if (kTaggedOff + c.off > kLayerRegionBytes) return false;
   L->table_off = layer_table_off(*L);
   L->err = w.err;
@@ -273,6 +284,8 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_ksg = value;
   } else if (!strcmp(key, "layer_ksd")) {
     tuning().layer_ksd = value;
+  } else if (!strcmp(key, "layer_down_early")) {
+    tuning().layer_down_early = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
   } else {

@@ -77,6 +77,7 @@ struct Tuning {
   int layer = 1;       // one launch for the whole decode layer when it fits
   int layer_ksg = 0;   // its gate/up and down splits (0: chosen)
   int layer_ksd = 0;
+  int layer_down_early = 0;
 };
 Tuning &tuning();
 
@@ -194,6 +195,7 @@ struct LayerLaunch {
   int KSdr, KSds;                     // down splits of the routed / shared units
   int NR;                             // router + routed blocks (the shared blocks follow)
   int blk0, grid_full;                // this launch covers blocks [blk0, blk0 + grid)
+  int down_early;                     // routed down weights with gate/up (else after)
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;
@@ -203,7 +205,7 @@ struct LayerLaunch {
   uint64_t *rlog;                     // [T][E] tagged logits
   uint64_t *sel;                      // [T][sel_copies][2][lid] tagged ids, gates
   int sel_copies, lid;
-  uint64_t *h;                        // [T*k*F + T*Fs] tagged hidden activations
+  uint64_t *hg, *hu;                  // [T*k*F + T*Fs] tagged gelu(gate) and up
   uint64_t *gacc, *dacc;              // split-reduction accumulators (zero between calls)
   uint32_t *gcnt, *dcnt;              // and their counters
   uint32_t *err;
