@@ -22,7 +22,9 @@
  * MOE_E_HIP reports a HIP runtime error from a launch or copy; device faults
  * surface at the caller's next synchronisation.  No call aborts and no C++
  * exception crosses this boundary.  Results are bitwise reproducible: every
- * reduction has a fixed order and no floating-point atomics are used.
+ * reduction has a fixed order and no floating-point atomics are used (where
+ * blocks add partial sums they add fixed-point integers, whose sum does not
+ * depend on the order of arrival).
  *
  * Quantised matrix storage (W[rows, cols], w = scale * q + bias per 64
  * consecutive columns of a row; codes unsigned, bits in {4, 8}):
@@ -89,10 +91,24 @@ size_t moe_blob_bytes(int32_t D, int32_t F);
 /* Scratch bytes `ws` must hold for calls with these sizes (F_shared = 0: no
  * shared expert).  The same workspace serves moe_route, moe_expert_ffn and
  * moe_layer_forward at or below these sizes.  It must be zero-filled before
- * its first use; every call leaves its synchronisation counters at zero.
- * Two calls that overlap in time must not share a workspace. */
+ * its first use; every call leaves its synchronisation counters at zero and
+ * its hand-off words tagged with a call counter, so one workspace serves calls
+ * of any shape in any order.  Two calls that overlap in time must not share a
+ * workspace. */
 size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t D, int32_t F,
                            int32_t F_shared);
+
+/* Number of bounded device-side waits that timed out in calls on `ws` since
+ * it was last zero-filled.  The one-launch kernels hand data between blocks
+ * that must all be resident; a wait that gives up (after about a second)
+ * counts here and lets the kernel finish with undefined results instead of
+ * hanging.  A nonzero count means the outputs of those calls are undefined
+ * and the workspace must be zero-filled again before further use.
+ *   ws      device workspace (as passed to the other calls), ws_bytes its size
+ *   count   host; receives the count
+ * Blocks the host: the word is copied after the work queued on `stream`. */
+moe_status moe_workspace_timeouts(const void *ws, size_t ws_bytes, uint32_t *count,
+                                  void *stream);
 
 /* Router and selection (es.news.hada.io, "Proceso de generacion de tokens":
  * top-8 expert IDs per layer; stork.ai blog, "Por que la mayor parte...":

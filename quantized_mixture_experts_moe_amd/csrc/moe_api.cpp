@@ -60,6 +60,7 @@ Workspace carve(void *base, const Dims &d) {
   Carver c{(uint8_t *)base};
   Workspace w;
   w.layer = c.take<uint8_t>(kLayerRegionBytes, 1);
+  w.err = base ? (uint32_t *)(w.layer + kErrOff) : nullptr;
   const size_t T = d.T, k = d.k;
   const size_t units = T * k * d.F + T * d.Fs;
   w.xp = c.take<uint32_t>(T * d.D / 2, 4);
@@ -74,7 +75,6 @@ Workspace carve(void *base, const Dims &d) {
   w.counters = c.take<uint32_t>((size_t)kMaxSplitBlocks + T, 4);
   w.dpart = c.take<float>((size_t)kMaxSplitBlocks * 64, 4);
   w.fcounters = c.take<uint32_t>(fused_counter_words(d), 4);
-  w.err = c.take<uint32_t>(1, 4);
   w.perm_counts = c.take<int32_t>(d.E, 4);
   w.perm_offsets = c.take<int32_t>(d.E + 1, 4);
   w.perm = c.take<int32_t>(T * k, 4);
@@ -218,7 +218,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * 2 * L->lid, 8);
   L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   L->hu = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
-  if (kTaggedOff + c.off > kLayerRegionBytes) return false;
+  if (kTaggedOff + c.off > kErrOff) return false;
   L->table_off = layer_table_off(*L);
   L->err = w.err;
   return true;
@@ -256,6 +256,20 @@ const char *moe_status_string(moe_status st) {
     case MOE_E_POOL: return "expert pool error";
     default: return "unknown status";
   }
+}
+
+moe_status moe_workspace_timeouts(const void *ws, size_t ws_bytes, uint32_t *count,
+                                  void *stream) {
+  if (!ws || !count || ws_bytes < kLayerRegionBytes) return !ws || !count ? MOE_E_INVALID
+                                                                          : MOE_E_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, (const uint8_t *)ws + kErrOff, sizeof(v),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return MOE_E_HIP;
+  *count = v;
+  return MOE_OK;
 }
 
 moe_status moe_set_profile_events(void *const *events, int32_t n_pairs) {

@@ -39,6 +39,9 @@ constexpr size_t kCntGluOff = kAccOutOff + sizeof(uint64_t) * 64 * kMaxOutTiles;
 constexpr size_t kCntOutOff = kCntGluOff + 64 * (size_t)kMaxAccTiles;
 constexpr size_t kTaggedOff = kCntOutOff + 64 * (size_t)kMaxOutTiles;
 constexpr int kCntStride = 16;  // u32 words per counter line
+// Sticky count of timed-out waits: the last line of the region, at the
+// same place for every call (read by moe_workspace_timeouts).
+constexpr size_t kErrOff = kLayerRegionBytes - kAlign;
 
 __host__ __device__ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 

@@ -35,7 +35,7 @@ EXPORTS = (
     "moe_blob_bytes", "moe_workspace_bytes", "moe_route", "moe_expert_ffn", "moe_combine",
     "moe_permute", "moe_layer_forward", "moe_pool_create", "moe_pool_destroy",
     "moe_pool_get_stats", "moe_pool_reset_stats", "moe_lfu_replay", "moe_set_tuning",
-    "moe_set_profile_events", "moe_status_string",
+    "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
 )
 
 
@@ -84,6 +84,7 @@ def _load() -> ctypes.CDLL:
         "moe_lfu_replay": (i32, [i32, i32, i32, i32, vp, vp]),
         "moe_set_tuning": (i32, [ctypes.c_char_p, i32]),
         "moe_set_profile_events": (i32, [vp, i32]),
+        "moe_workspace_timeouts": (i32, [vp, sz, P(ctypes.c_uint32), vp]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -195,6 +196,14 @@ class Workspace:
             raise ValueError("invalid workspace sizes")
         self.buf = torch.zeros(n, dtype=torch.uint8, device=device)
         self.nbytes = n
+
+    def timeouts(self, stream=None) -> int:
+        """Device-side waits that timed out since the buffer was zero-filled
+        (blocks the host until the stream's work is done)."""
+        c = ctypes.c_uint32(0)
+        _check(lib.moe_workspace_timeouts(_ptr(self.buf), self.nbytes, ctypes.byref(c),
+                                          _stream(stream)), "moe_workspace_timeouts")
+        return int(c.value)
 
 
 def _x_dtype(x: torch.Tensor) -> int:

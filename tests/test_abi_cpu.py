@@ -92,6 +92,10 @@ def test_argument_checks_launch_nothing():
     assert lib.moe_combine(ids, ids, None, 1, 1, 64, ids, 7, None) == moe.MOE_E_INVALID
     assert lib.moe_permute(ids, 65537, 1, 16, ids, ids, ids, ids, None) == moe.MOE_E_INVALID
     assert lib.moe_set_tuning(b"no_such_knob", 1) == moe.MOE_E_INVALID
+    cnt = ctypes.c_uint32(0)
+    assert lib.moe_workspace_timeouts(None, 1 << 30, ctypes.byref(cnt), None) == moe.MOE_E_INVALID
+    assert lib.moe_workspace_timeouts(ids, 1 << 30, None, None) == moe.MOE_E_INVALID
+    assert lib.moe_workspace_timeouts(ids, 4096, ctypes.byref(cnt), None) == moe.MOE_E_WORKSPACE
     # activations must be 16-byte aligned
     assert lib.moe_route(ctypes.c_void_p(258), moe.MOE_BF16, 1, ctypes.byref(q), None, 8, ids, ids,
                          None, ids, 1 << 30, None) == moe.MOE_E_INVALID

@@ -232,6 +232,7 @@ def _layer_gpu(L, xb, k, bias=None, T=None, out_dtype=torch.float32):
     moe.moe_layer_forward(x_dev(xb, cfg.x_dtype), L.router, k, L.routed, L.shared, out, ws,
                           logit_bias=bias_d, ids_out=ids, gates_out=gates)
     torch.cuda.synchronize()
+    assert ws.timeouts() == 0
     return out, ids.cpu().numpy(), gates.cpu().numpy()
 
 
@@ -421,6 +422,7 @@ def test_layer_epochs_across_grid_sizes():
             else:
                 first[(ksg, ksd)] = out
                 _check_layer(L, xb, out.cpu().numpy(), ids.cpu().numpy(), cfg.k)
+        assert ws.timeouts() == 0
     finally:
         _tune(**_DEFAULTS)
 
