@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kNW = 4;
 constexpr int kThreads = kNW * 64;
-constexpr int kRows = 8;                   // experts per router block
+constexpr int kRows = 4;                   // experts per router block
 constexpr int kKL = kThreads / kRows;      // threads splitting one router row
 constexpr long kSpin = 1L << 20;           // bounded waits, then the error counter
 
@@ -156,104 +156,77 @@ __device__ __forceinline__ Tile glu_tile(const LayerLaunch &L, int tile) {
   return g;
 }
 
-// Selection for token t by a router block once every router block of the
-// token has published its logits.  Thread i < E polls logit i; then every
-// thread ranks its candidate against a share of the others with unique 64-bit
-// keys (order-preserving logit bits, then the complemented index, so equal
-// logits rank the lower index first), the partial ranks add up in LDS, and the
-// k winners land in rank order.  Wave 0 computes the softmax gates as the
-// single-wave selection does (same order, same bits) and publishes ids and
-// gates in this block's copy.
+// Selection for token t, shared by the router blocks of the token: once every
+// logit of the token is published, each router block ranks its own kRows
+// candidates against all E logits and publishes every candidate that ranks
+// below k in that rank's place (in each copy of the selection line).  Keys
+// are unique 64-bit values (order-preserving logit bits, then the
+// complemented index), so the ranks of all candidates are a permutation and
+// equal logits rank the lower index first.  The line then holds, at place r,
+// the expert with the r-th largest logit and that logit; a consumer computes
+// the softmax gates itself.  The block's own keys are in own[] (written when
+// its logits were published); a rank is a count of set ballot bits.
 struct __align__(16) SelectLds {
-  uint64_t key[kThreads + 16];  // padded: rank loops read whole chunks of 16
-  uint32_t rank[kThreads];
-  uint2 sel[kMaxK];
+  uint64_t own[kRows];
 };
 
-__device__ void select_publish(const LayerLaunch &L, int t, int copy, uint32_t tag, SelectLds &S,
-                               bool report) {
-  const int tid = threadIdx.x, lane = tid & 63, E = L.E, k = L.k;
+// Wave 0 of a router block: polls the E logits of token t (lanes hold
+// experts lane, lane + 64, ...), ranks the own candidates with ballots and
+// publishes the winners.
+__device__ void select_publish(const LayerLaunch &L, int t, int e0, uint32_t tag,
+                               const SelectLds &S) {
+  constexpr int NV = kMaxLayerE / 64;
+  constexpr int LPC = 64 / kRows;  // lanes per candidate when publishing
+  const int lane = threadIdx.x & 63, E = L.E, k = L.k;
   const uint64_t *lg = L.rlog + (size_t)t * E;
-  float v = -INFINITY;
+  uint64_t key[NV];
   for (long s = 0;; ++s) {
     bool ok = true;
-    if (tid < E) {
-      const uint64_t w = ld_dev64(lg + tid);
-      ok = has_tag(w, tag);
-      v = __uint_as_float((uint32_t)w);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      key[j] = 0;
+      const int e = lane + 64 * j;
+      if (e < E) {
+        const uint64_t w = ld_dev64(lg + e);
+        ok = ok && has_tag(w, tag);
+        key[j] = ((uint64_t)order_key(__uint_as_float((uint32_t)w)) << 32) | (uint64_t)(~(uint32_t)e);
+      }
     }
-    if (__syncthreads_and(ok)) break;
+    if (__all(ok)) break;
     if (s > kSpin) {
-      if (tid == 0) add_dev(L.err, 1u);
+      if (lane == 0) add_dev(L.err, 1u);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  if (tid < E) {
-    S.key[tid] = ((uint64_t)order_key(v) << 32) | (uint64_t)(~(uint32_t)tid);
-    S.rank[tid] = 0u;
-  } else {
-    S.key[tid] = 0u;  // below every real key: padding never outranks
-  }
-  if (tid < 16) S.key[kThreads + tid] = 0u;
-  __syncthreads();
-  {
-    // E <= 128: thread (i, half) ranks candidate i against half of the keys;
-    // E <= 256: thread i against all.  Keys past E are zero (never larger).
-    // Every key read is a broadcast, 16 in flight before the compares.
-    const int P = E <= 128 ? 2 : 1;            // key parts per candidate
-    const int i = E <= 128 ? (tid & 127) : tid;
-    const int part = E <= 128 ? (tid >> 7) : 0;
-    const int nchunk = E <= 128 ? (E + 31) / 32 : (E + 15) / 16;  // chunks per part
-    const uint64_t ki = S.key[i];
-    uint32_t r = 0;
-    for (int c = part * nchunk; c < (part + 1) * nchunk; ++c) {
-      uint64_t kj[16];
+  // rank of candidate c = number of keys above its key (keys past E are 0)
+  const int c = lane / LPC, p = lane % LPC, e = e0 + c;
+  uint32_t r = 0;
 #pragma unroll
-      for (int q = 0; q < 16; q += 2) {
-        const ulonglong2 p2 = *(const ulonglong2 *)&S.key[16 * c + q];
-        kj[q] = p2.x;
-        kj[q + 1] = p2.y;
-      }
+  for (int cc = 0; cc < kRows; ++cc) {
+    const uint64_t kc = S.own[cc];
+    uint32_t cnt = 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) r += kj[q] > ki ? 1u : 0u;
-    }
-    (void)P;
-    if (i < E) atomicAdd(&S.rank[i], r);
+    for (int j = 0; j < NV; ++j) cnt += (uint32_t)__popcll(__ballot(key[j] > kc));
+    if (c == cc) r = cnt;
   }
-  __syncthreads();
-  if (tid < E && S.rank[tid] < (uint32_t)k) S.sel[S.rank[tid]] = make_uint2(tid, __float_as_uint(v));
-  __syncthreads();
-  if (tid < 64) {
-    float myv = 0.0f;
-    int myi = 0;
-    if (lane < k) {
-      const uint2 r = S.sel[lane];
-      myi = (int)r.x;
-      myv = __uint_as_float(r.y);
-    }
-    const float m0 =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
-    const float z = lane < k ? expf(myv - m0) : 0.0f;
-    const float sum = wave_sum(z);
-    const float gate = z / sum;
-    if (lane < k) {
-      uint64_t *line = L.sel + ((size_t)t * L.sel_copies + copy) * 2 * L.lid;
-      st_dev64(line + lane, tagged((uint32_t)myi, tag));
-      st_dev64(line + L.lid + lane, tagged(__float_as_uint(gate), tag));
-      if (report) {
-        if (L.ids_out) L.ids_out[(size_t)t * k + lane] = myi;
-        if (L.gates_out) L.gates_out[(size_t)t * k + lane] = gate;
-      }
+  if (e < E && r < (uint32_t)k) {
+    const uint32_t vbits = __float_as_uint(key_value((uint32_t)(S.own[c] >> 32)));
+    for (int cp = p; cp < L.sel_copies; cp += LPC) {
+      uint64_t *line = L.sel + ((size_t)t * L.sel_copies + cp) * 2 * L.lid;
+      st_dev64(line + r, tagged((uint32_t)e, tag));
+      st_dev64(line + L.lid + r, tagged(vbits, tag));
     }
   }
 }
 
-// The selection of token t as published in one copy: lane r < k receives the
-// blob of the r-th expert and its gate (wave-wide, bounded wait).
+// The selection of token t as published in one copy (wave-wide, bounded
+// wait): lane r < k receives the blob of the r-th expert and its softmax gate
+// (the max is the rank-0 logit; the same arithmetic, in the same order, as
+// the router kernel's selection).  `report`: also write ids_out / gates_out.
 __device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t tag,
                                const void *const *table, const uint8_t **blob_out,
-                               float *gate_out) {
+                               float *gate_out, bool report) {
   const int lane = threadIdx.x & 63, k = L.k;
   const uint64_t *line = L.sel + ((size_t)t * L.sel_copies + copy) * 2 * L.lid;
   uint64_t wi = 0, wg = 0;
@@ -271,17 +244,289 @@ __device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t t
     }
     __builtin_amdgcn_s_sleep(1);
   }
+  const uint32_t id = min((uint32_t)wi, (uint32_t)L.E - 1);
+  if (lane < k) blob_out[lane] = (const uint8_t *)table[id];
+  const float myv = lane < k ? __uint_as_float((uint32_t)wg) : 0.0f;
+  const float m0 =
+      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
+  const float z = lane < k ? expf(myv - m0) : 0.0f;
+  const float sum = wave_sum(z);
+  const float gate = z / sum;
   if (lane < k) {
-    blob_out[lane] = (const uint8_t *)table[min((uint32_t)wi, (uint32_t)L.E - 1)];
-    gate_out[lane] = __uint_as_float((uint32_t)wg);
+    gate_out[lane] = gate;
+    if (report) {
+      if (L.ids_out) L.ids_out[(size_t)t * k + lane] = (int32_t)id;
+      if (L.gates_out) L.gates_out[(size_t)t * k + lane] = gate;
+    }
   }
 }
 
 constexpr int kMaxBlockGroups = 16;  // gate/up column groups of one block (4 waves x 4)
+constexpr int kDW = kNW - 1;         // waves with down units (1..3)
+
+// Weights of one block, held in registers from issue to use.  Every load is
+// issued unconditionally (indices clamped into range where a block has less
+// work), so each wave's loads count the same on every path and the waits
+// the compiler places before a use cover exactly the loads that use needs
+// (a wave's loads complete in order).
+template <int M>
+struct GluRegs {
+  u32x4 qg0[M], qg1[M], qu0[M], qu1[M];
+  uint32_t mg[M], mu[M];
+};
+template <int M>
+struct DownRegs {
+  u32x4 dq0[M], dq1[M];
+  uint32_t dmw[M];
+};
+
+// gate/up rows rb*64 + lane of the 64-column groups g0 + wave + 4 i (clamped)
+template <int M>
+__device__ __forceinline__ void issue_glu(GluRegs<M> &R, const uint8_t *blob, int D, int F, int rb,
+                                          int g0, int g1, int wave, int lane) {
+  const int j = rb * 64 + lane;
+  const BlobLayout BL = blob_layout(D, F);
+  const gptr<u32x4> gc = as_global((const u32x4 *)(blob + BL.gate_codes) + j);
+  const gptr<u32x4> uc = as_global((const u32x4 *)(blob + BL.up_codes) + j);
+  const gptr<uint32_t> gm = as_global((const uint32_t *)(blob + BL.gate_meta) + j);
+  const gptr<uint32_t> um = as_global((const uint32_t *)(blob + BL.up_meta) + j);
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int g = min(g0 + wave + i * kNW, g1 - 1);
+    const size_t c0 = (size_t)(2 * g) * F;
+    R.qg0[i] = gc[c0];
+    R.qg1[i] = gc[c0 + F];
+    R.qu0[i] = uc[c0];
+    R.qu1[i] = uc[c0 + F];
+    R.mg[i] = gm[(size_t)g * F];
+    R.mu[i] = um[(size_t)g * F];
+  }
+}
+
+// down weights of output row n, hidden group g (64 hidden rows) of a blob
+template <int M>
+__device__ __forceinline__ void issue_down(DownRegs<M> &R, int i, const uint8_t *blob, int D,
+                                           int Fb, int g, int n) {
+  const BlobLayout BL = blob_layout(D, Fb);
+  const gptr<u32x4> dc = as_global((const u32x4 *)(blob + BL.down_codes) + n);
+  R.dq0[i] = dc[(size_t)(2 * g) * D];
+  R.dq1[i] = dc[(size_t)(2 * g + 1) * D];
+  R.dmw[i] = as_global((const uint32_t *)(blob + BL.down_meta))[(size_t)g * D + n];
+}
+
+// x of token t, columns [64 g0, 64 g1): thread i < 8 (g1 - g0) loads columns
+// 8i..8i+7 (clamped for the others)
+__device__ __forceinline__ u32x4 issue_x(const LayerLaunch &L, int t, int g0, int g1, int tid) {
+  const int c = min(tid, (g1 - g0) * 8 - 1);
+  return as_global((const u32x4 *)((const uint16_t *)L.x + (size_t)t * L.D + 64 * g0))[c];
+}
+
+// activation pairs (x[8w + m], x[8w + m + 4]) and 64-column sums into LDS
+template <bool F16X>
+__device__ __forceinline__ void stage_x(u32x4 xq, int n8, int tid, uint32_t *s_xp, float *s_xs) {
+  const uint32_t a0 = xq.x, a1 = xq.y, a2 = xq.z, a3 = xq.w;
+  u32x4 pq;
+  pq.x = (a0 & 0xFFFFu) | (a2 << 16);
+  pq.y = (a0 >> 16) | (a2 & 0xFFFF0000u);
+  pq.z = (a1 & 0xFFFFu) | (a3 << 16);
+  pq.w = (a1 >> 16) | (a3 & 0xFFFF0000u);
+  const uint32_t w[4] = {a0, a1, a2, a3};
+  float s8 = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    s8 += x_to_f32<F16X>(w[m] & 0xFFFFu);
+    s8 += x_to_f32<F16X>(w[m] >> 16);
+  }
+  const float sg = sum8_lanes(s8);
+  if (tid < n8) {
+    *(u32x4 *)&s_xp[4 * tid] = pq;
+    if ((tid & 7) == 0) s_xs[tid / 8] = sg;
+  }
+}
+
+// Gate/up dot products of hidden row l on the matrix cores: lane l holds
+// word w (8 columns) of row l as the B operand; lanes 0, 20, 40, 60 hold the
+// activation pairs of word w as A rows 0, 4, 8, 12 (the other lanes zero),
+// so D row 4q, column c -- register 0 of lane 16q + c -- accumulates row l's
+// dot product.  Per 64-column group the affine terms fold in fp32.
+template <bool F16X, int M>
+__device__ __forceinline__ void glu_dots(const GluRegs<M> &R, const uint32_t *s_xp,
+                                         const float *s_xs, int g0, int g1, int wave, int lane,
+                                         float &accg, float &accu) {
+  const bool xa_lane = (lane & 15) == 4 * (lane >> 4);
+  const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
+  accg = 0.0f;
+  accu = 0.0f;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int gi = wave + i * kNW;  // group g0 + gi
+    if (g0 + gi < g1) {
+      f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
+      const uint32_t wg[8] = {R.qg0[i].x, R.qg0[i].y, R.qg0[i].z, R.qg0[i].w,
+                              R.qg1[i].x, R.qg1[i].y, R.qg1[i].z, R.qg1[i].w};
+      const uint32_t wu[8] = {R.qu0[i].x, R.qu0[i].y, R.qu0[i].z, R.qu0[i].w,
+                              R.qu1[i].x, R.qu1[i].y, R.qu1[i].z, R.qu1[i].w};
+      // the four A lanes read all 8 words at once, the other lanes keep zeros
+      u32x4 a[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
+      if (xa_lane) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&s_xp[32 * gi + 4 * w];
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        dg = mma16<F16X>(a[w], code_pairs(wg[w], magic), dg);
+        du = mma16<F16X>(a[w], code_pairs(wu[w], magic), du);
+      }
+      const float xsg = s_xs[gi];
+      const float sg = f16_to_f32(R.mg[i]), bg = f16_to_f32(R.mg[i] >> 16);
+      const float su = f16_to_f32(R.mu[i]), bu = f16_to_f32(R.mu[i] >> 16);
+      accg = fmaf(sg, dg[0], accg);
+      accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsg, accg);
+      accu = fmaf(su, du[0], accu);
+      accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsg, accu);
+    }
+  }
+}
+
+// Block-wide sum of the gate/up partials, then the split reduction: the
+// split that completes a gate sum publishes gelu(gate), the one that
+// completes an up sum publishes up (the consumer multiplies).
+__device__ __forceinline__ void glu_publish(const LayerLaunch &L, float (&red)[kNW][2][64],
+                                            int tile, size_t ho, float accg, float accu,
+                                            int wave, int lane, uint32_t tag) {
+  red[wave][0][lane] = accg;
+  red[wave][1][lane] = accu;
+  __syncthreads();
+  if (wave == 0) {
+    float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      v0 += red[w][0][lane];
+      v1 += red[w][1][lane];
+    }
+    float g = v0, u = v1;
+    const bool last_g =
+        L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + lane, v0, L.KSg, &g);
+    const bool last_u =
+        L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + 64 + lane, v1, L.KSg, &u);
+    if (last_g) st_dev64(L.hg + ho + lane, tagged(__float_as_uint(gelu_tanh(g)), tag));
+    if (last_u) st_dev64(L.hu + ho + lane, tagged(__float_as_uint(u), tag));
+  }
+}
+
+// Down projection of output row n over this wave's units, then the split
+// reduction over the blocks of the output tile, which writes the output.
+// unit i: hidden rows hp[i] .. hp[i] + 63 (tagged words), weight gate[i].
+template <int M>
+__device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const DownRegs<M> &R,
+                                                 const size_t (&hp)[M], const float (&gate)[M],
+                                                 const bool (&use)[M], uint32_t (&hpl)[kNW][M][3][32],
+                                                 float (&red)[kNW][2][64], int ot, size_t out_idx,
+                                                 int wave, int lane, uint32_t tag) {
+  // lanes 2i, 2i + 1 poll one word of unit i's two rows, then the values
+  // are read (checked): h = gelu(gate) * up
+  const uint64_t *hint = nullptr;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    if (use[i] && lane == 2 * i) hint = L.hg + hp[i];
+    if (use[i] && lane == 2 * i + 1) hint = L.hu + hp[i];
+  }
+  wait_hint(hint, tag, L.err);
+  float hv0[M];
+  for (long s = 0;; ++s) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      hv0[i] = 0.0f;
+      if (use[i]) {
+        const uint64_t wg = ld_dev64(L.hg + hp[i] + lane);
+        const uint64_t wu = ld_dev64(L.hu + hp[i] + lane);
+        ok = ok && has_tag(wg, tag) && has_tag(wu, tag);
+        hv0[i] = __uint_as_float((uint32_t)wg) * __uint_as_float((uint32_t)wu);
+      }
+    }
+    if (__all(ok)) break;
+    if (s > kSpin) {
+      if (lane == 0) add_dev(L.err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
+  // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
+  float hsum[M];
+  const int pos = 2 * (4 * (lane >> 3) + (lane & 3)) + ((lane >> 2) & 1);
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const float hv = hv0[i];
+    const uint32_t p0 = f32_to_bf16(hv);
+    const float r1 = hv - __uint_as_float(p0 << 16);
+    const uint32_t p1 = f32_to_bf16(r1);
+    const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
+    uint16_t *hp16 = (uint16_t *)&hpl[wave][i][0][0];
+    hp16[pos] = (uint16_t)p0;
+    hp16[64 + pos] = (uint16_t)p1;
+    hp16[128 + pos] = (uint16_t)p2;
+    hsum[i] = wave_sum(hv);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // matrix cores: lane l holds word w (8 hidden rows) of output row l as
+  // B (codes as 1 + q / 16); lanes with l % 16 = 4 (l / 16) + p, p < 3,
+  // hold plane p of h as A row 4 (l / 16) + p, so registers 0..2 of lane l
+  // accumulate the three planes' dot products of output row l.
+  const int plane = (lane & 15) - 4 * (lane >> 4);
+  const bool ha_lane = plane >= 0 && plane < 3;
+  const uint32_t umagic = opaque_vgpr(0x3F803F80u);
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    if (!use[i]) continue;
+    const uint32_t wd[8] = {R.dq0[i].x, R.dq0[i].y, R.dq0[i].z, R.dq0[i].w,
+                            R.dq1[i].x, R.dq1[i].y, R.dq1[i].z, R.dq1[i].w};
+    u32x4 a[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
+    if (ha_lane) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&hpl[wave][i][plane][4 * w];
+    }
+    // two accumulation chains (even and odd words)
+    f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 8; w += 2) {
+      d0 = mma16<false>(a[w], code_pairs_unit(wd[w], umagic), d0);
+      d1 = mma16<false>(a[w + 1], code_pairs_unit(wd[w + 1], umagic), d1);
+    }
+    // sum (1 + q/16) h = sum h + sum q h / 16, three planes
+    const float dsum = ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2]);
+    const float sc = f16_to_f32(R.dmw[i]), bi = f16_to_f32(R.dmw[i] >> 16);
+    const float v = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum[i]);
+    acc = fmaf(gate[i], v, acc);
+  }
+  __syncthreads();  // red[] is reused
+  red[wave][0][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
+    const int nsp = L.KSdr + L.KSds;
+    if (nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s)) {
+      if (L.out_dtype == MOE_F32)
+        ((float *)L.out)[out_idx] = s;
+      else if (L.out_dtype == MOE_BF16)
+        ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_bf16(s);
+      else
+        ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_f16(s);
+    }
+  }
+}
 
 template <bool F16X, int M, int MAXC>
 __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L) {
-  constexpr int MAXX = MAXC == 6 ? 2 : 4;  // 16-byte pieces of x per thread (router)
+  constexpr int MAXX = MAXC == 3 ? 2 : 4;  // 16-byte pieces of x per thread (router)
   extern __shared__ __align__(16) uint8_t dsm[];
   __shared__ float red[kNW][2][64];
   __shared__ __align__(16) uint32_t hpl[kNW][M][3][32];  // h planes as bf16 pairs
@@ -298,411 +543,226 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   const int G = D / 64, NB = D / 64;
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
   const uint32_t tag = as_const(L.bep)[b] + 1u;
-  const uint16_t *x = (const uint16_t *)L.x;
 
-  // ---------------- roles of this block: router blocks [0, T nrb), routed
-  // blocks [T nrb, NR), shared blocks [NR, grid)
+  // roles: router blocks [0, T nrb), routed blocks [T nrb, NR), shared
+  // blocks [NR, grid).  Each role runs straight through its own code.
   const int nrb = (E + kRows - 1) / kRows;
-  const bool given = L.given_blob != nullptr;   // selection from the caller
-  const bool has_r = !given && b < T * nrb;
-  const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
-  const bool shared_blk = b >= L.NR;
-  const int sb = shared_blk ? b - L.NR : (b < T * nrb ? 1 << 30 : b - T * nrb);  // item index
+  const bool given = L.given_blob != nullptr;  // selection from the caller
+  const int n_rt = T * k * Gf;                 // routed gate/up tiles, then the shared ones
+  const int dw = max(wave - 1, 0);             // down units: waves 1..3 (wave 0 mirrors 1)
 
-  const int n_rt = T * k * Gf;  // routed gate/up tiles, then the shared ones
-  const bool has_g = sb < (shared_blk ? L.n_gtiles - n_rt : n_rt) * L.KSg;
-  const int tile = (shared_blk ? n_rt : 0) + sb / L.KSg, ks = sb % L.KSg;
-  Tile gt{};
-  if (has_g) gt = glu_tile(L, tile);
-  const bool g_routed = has_g && !shared_blk;
-  const int g0 = ks * G / L.KSg, g1 = (ks + 1) * G / L.KSg;
-
-  const int KSdx = shared_blk ? L.KSds : L.KSdr;  // splits of this block's unit range
-  const int Ux = shared_blk ? Gs : k * Gf;        // units of that range
-  const bool has_d = KSdx > 0 && sb < T * NB * KSdx;  // (router blocks: no items)
-  const int ot = has_d ? sb / KSdx : 0, ksd = has_d ? sb % KSdx : 0;
-  const int t_out = ot / NB, n = (ot - t_out * NB) * 64 + lane;
-  const int u0 = ksd * Ux / max(KSdx, 1), u1 = (ksd + 1) * Ux / max(KSdx, 1);
-  const bool d_routed = has_d && !shared_blk;
-  const bool routed = g_routed || d_routed;
-
-  // ---------------- router logits, then the selection of the token (every
-  // router block publishes its own copy).  The router blocks do this before
-  // anything else: it heads the chain of dependent steps.
-  const int nch = D / 16;
-  float *sx = (float *)dsm;   // router: x as fp32 [D]
-  float *sxs = sx + D;        // router: 16-column sums [D/16]
-  float *rred = sxs + nch;    // router: partial logits [kKL][kRows]
-  if (has_r) {
-    __builtin_amdgcn_s_setprio(1);
-    const int rr = tid % kRows, kl = tid / kRows;  // chunks kl, kl + kKL, ... of row rr
-    u32x4 xr[MAXX], rq[MAXC];
-    uint32_t rmw[MAXC];
-    const gptr<u32x4> xt = as_global((const u32x4 *)(x + (size_t)r_t * D));
+  if (b < T * nrb) {
+    // ---------------- router rows and the selection of the token.  They
+    // head the chain of dependent steps, so these blocks do nothing else.
+    if (!given) {
+      __builtin_amdgcn_s_setprio(1);
+      const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
+      const int nch = D / 16;
+      float *sx = (float *)dsm;   // x as fp32 [D]
+      float *sxs = sx + D;        // 16-column sums [D/16]
+      float *rred = sxs + nch;    // partial logits [kKL][kRows]
+      const int rr = tid % kRows, kl = tid / kRows;  // chunks kl, kl + kKL, ... of row rr
+      u32x4 xr[MAXX], rq[MAXC];
+      uint32_t rmw[MAXC];
+      const uint16_t *x = (const uint16_t *)L.x;
+      const gptr<u32x4> xt = as_global((const u32x4 *)(x + (size_t)r_t * D));
 #pragma unroll
-    for (int i = 0; i < MAXX; ++i) xr[i] = xt[min(tid + i * kThreads, D / 8 - 1)];
-    const int e = min(r_e0 + rr, E - 1);
+      for (int i = 0; i < MAXX; ++i) xr[i] = xt[min(tid + i * kThreads, D / 8 - 1)];
+      const int e = min(r_e0 + rr, E - 1);
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = min(kl + i * kKL, nch - 1);
-      rq[i] = as_global((const u32x4 *)L.rcodes)[(size_t)c * E + e];
-      rmw[i] = as_global(L.rmeta)[(size_t)c / 4 * E + e];
-    }
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = min(kl + i * kKL, nch - 1);
+        rq[i] = as_global((const u32x4 *)L.rcodes)[(size_t)c * E + e];
+        rmw[i] = as_global(L.rmeta)[(size_t)c / 4 * E + e];
+      }
 #pragma unroll
-    for (int i = 0; i < MAXX; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < D / 8) {
-        const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+      for (int i = 0; i < MAXX; ++i) {
+        const int c = tid + i * kThreads;
+        if (c < D / 8) {
+          const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          sx[8 * c + 2 * m] = x_to_f32<F16X>(w[m] & 0xFFFFu);
-          sx[8 * c + 2 * m + 1] = x_to_f32<F16X>(w[m] >> 16);
+          for (int m = 0; m < 4; ++m) {
+            sx[8 * c + 2 * m] = x_to_f32<F16X>(w[m] & 0xFFFFu);
+            sx[8 * c + 2 * m + 1] = x_to_f32<F16X>(w[m] >> 16);
+          }
         }
       }
-    }
-    __syncthreads();
-    for (int i = tid; i < nch; i += kThreads) {
-      float s = 0.0f;
+      __syncthreads();
+      for (int i = tid; i < nch; i += kThreads) {
+        float s = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s += sx[16 * i + j];
-      sxs[i] = s;
-    }
-    __syncthreads();
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = kl + i * kKL;
-      if (c < nch) {
-        const float sc = f16_to_f32(rmw[i]), bi = f16_to_f32(rmw[i] >> 16);
-        const uint32_t w[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
-        const float *xv = sx + c * 16;
-        float d = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
-            d = fmaf(xv[4 * u + bb], (float)((w[u] >> (8 * bb)) & 0xFFu), d);
-        acc = fmaf(sc, d, acc);
-        acc = fmaf(bi, sxs[c], acc);
+        for (int j = 0; j < 16; ++j) s += sx[16 * i + j];
+        sxs[i] = s;
       }
-    }
-    rred[kl * kRows + rr] = acc;
-    __syncthreads();
-    if (wave == 0 && lane < kRows) {
-      float s = 0.0f;
-      for (int j = 0; j < kKL; ++j) s += rred[j * kRows + lane];
-      const int e2 = r_e0 + lane;
-      if (e2 < E) {
-        if (L.logit_bias) s += L.logit_bias[e2];
-        st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
+      __syncthreads();
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = kl + i * kKL;
+        if (c < nch) {
+          const float sc = f16_to_f32(rmw[i]), bi = f16_to_f32(rmw[i] >> 16);
+          const uint32_t w[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
+          const float *xv = sx + c * 16;
+          float d = 0.0f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              d = fmaf(xv[4 * u + bb], (float)((w[u] >> (8 * bb)) & 0xFFu), d);
+          acc = fmaf(sc, d, acc);
+          acc = fmaf(bi, sxs[c], acc);
+        }
       }
+      rred[kl * kRows + rr] = acc;
+      __syncthreads();
+      if (wave == 0 && lane < kRows) {
+        float s = 0.0f;
+        for (int j = 0; j < kKL; ++j) s += rred[j * kRows + lane];
+        const int e2 = r_e0 + lane;
+        uint64_t own = 0;  // below every real key
+        if (e2 < E) {
+          if (L.logit_bias) s += L.logit_bias[e2];
+          st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
+          own = ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)e2);
+        }
+        s_select.own[lane] = own;
+      }
+      if (wave == 0) select_publish(L, r_t, r_e0, tag, s_select);
+      __builtin_amdgcn_s_setprio(0);
     }
-    __syncthreads();  // the selection reuses LDS
-    select_publish(L, r_t, b - r_t * nrb, tag, s_select, r_e0 == 0);
-    __builtin_amdgcn_s_setprio(0);
-  }
+  } else if (b >= L.NR) {
+    // ---------------- shared expert: its gate/up tiles and its part of the
+    // down projection; nothing waits on the routing
+    const int sb = b - L.NR;
+    const int n_st = L.n_gtiles - n_rt;
+    const bool has_g = sb < n_st * L.KSg;
+    const int gsb = min(sb, n_st * L.KSg - 1);
+    const int tile = n_rt + gsb / L.KSg, ks = gsb % L.KSg;
+    const Tile gt = glu_tile(L, tile);
+    const int g0 = ks * G / L.KSg, g1 = (ks + 1) * G / L.KSg;
+    const bool has_d = sb < T * NB * L.KSds;
+    const int dsb = min(sb, T * NB * L.KSds - 1);
+    const int ot = dsb / L.KSds, ksd = dsb % L.KSds;
+    const int t_out = ot / NB, n = (ot - t_out * NB) * 64 + lane;
+    const int u0 = ksd * Gs / L.KSds, u1 = (ksd + 1) * Gs / L.KSds;
 
-  // ---------------- loads that need no routing, in the order they are used
-  // (a wait on one of them then waits for the earlier ones only)
-  // 1. this block's gate/up columns of x: 8 columns per thread
-  const int n8 = (g1 - g0) * 8;
-  u32x4 xq = {0u, 0u, 0u, 0u};
-  if (has_g && tid < n8) xq = as_global((const u32x4 *)(x + (size_t)gt.t * D + 64 * g0))[tid];
-  // 2. the routed bank's blob table
-  constexpr int kTab = kMaxLayerE / kThreads;
-  const void *tb[kTab];
-  if (routed && !given) {
-#pragma unroll
-    for (int i = 0; i < kTab; ++i) {
-      const int e = tid + i * kThreads;
-      tb[i] = e < E ? as_global(L.rblobs)[e] : nullptr;
+    const uint8_t *sblob = (const uint8_t *)as_global(L.sblobs)[0];
+    const u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    if (L.shared_wait && !given) {
+      // hold the weight loads until the router logits are out: the router's
+      // loads head the chain of dependent steps
+      if (wave == 0) {
+        for (int base = 0; base < T * nrb; base += 64) {
+          const int q = base + lane;
+          const uint64_t *p =
+              q < T * nrb ? L.rlog + (size_t)(q / nrb) * E + (size_t)(q % nrb) * kRows : nullptr;
+          wait_hint(p, tag, L.err);
+        }
+      }
+      __syncthreads();
     }
-  }
-  // 3. shared-expert weights: gate/up tile, down units
-  u32x4 qg0[M], qg1[M], qu0[M], qu1[M];
-  uint32_t mg[M], mu[M];
-  auto load_glu = [&](const uint8_t *blob) {
-    const int F = gt.F, j = gt.rb * 64 + lane;
-    const BlobLayout BL = blob_layout(D, F);
-    const gptr<u32x4> gc = as_global((const u32x4 *)(blob + BL.gate_codes) + j);
-    const gptr<u32x4> uc = as_global((const u32x4 *)(blob + BL.up_codes) + j);
-    const gptr<uint32_t> gm = as_global((const uint32_t *)(blob + BL.gate_meta) + j);
-    const gptr<uint32_t> um = as_global((const uint32_t *)(blob + BL.up_meta) + j);
+    GluRegs<M> gr;
+    issue_glu(gr, sblob, D, L.Fs, gt.rb, g0, g1, wave, lane);
+    DownRegs<M> dr;
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int g = min(g0 + wave + i * kNW, g1 - 1);
-      const size_t c0 = (size_t)(2 * g) * F;
-      qg0[i] = gc[c0];
-      qg1[i] = gc[c0 + F];
-      qu0[i] = uc[c0];
-      qu1[i] = uc[c0 + F];
-      mg[i] = gm[(size_t)g * F];
-      mu[i] = um[(size_t)g * F];
+    for (int i = 0; i < M; ++i) issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * kDW, u1 - 1), n);
+    stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
+    __syncthreads();
+    if (has_g) {
+      float accg, accu;
+      glu_dots<F16X, M>(gr, s_xp, s_xs, g0, g1, wave, lane, accg, accu);
+      glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, accg, accu, wave, lane, tag);
     }
-  };
-  if (has_g && shared_blk) load_glu((const uint8_t *)L.sblobs[0]);
-  u32x4 dq0[M], dq1[M];
-  uint32_t dmw[M];
-  auto load_down = [&](int i, const uint8_t *blob, int Fb, int g) {
-    const BlobLayout BL = blob_layout(D, Fb);
-    const gptr<u32x4> dc = as_global((const u32x4 *)(blob + BL.down_codes) + n);
-    dq0[i] = dc[(size_t)(2 * g) * D];
-    dq1[i] = dc[(size_t)(2 * g + 1) * D];
-    dmw[i] = as_global((const uint32_t *)(blob + BL.down_meta))[(size_t)g * D + n];
-  };
-  // down units: waves 1..3 take units u0 + (wave - 1) + 3 i; wave 0 has none,
-  // so its split reductions never wait behind outstanding weight loads
-  constexpr int kDW = kNW - 1;
-  const int dw = wave - 1;
-  if (has_d && shared_blk && wave > 0) {
+    if (has_d) {
+      size_t hp[M];
+      float gate[M];
+      bool use[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int u = min(u0 + dw + i * kDW, u1 - 1);
+        use[i] = wave > 0 && u0 + dw + i * kDW < u1;
+        gate[i] = 1.0f;
+        hp[i] = (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
+      }
+      down_and_combine<M>(L, dr, hp, gate, use, hpl, red, ot, (size_t)t_out * D + n, wave, lane,
+                          tag);
+    }
+  } else {
+    // ---------------- routed blocks: gate/up tiles and the routed part of
+    // the down projection of the selected experts.  No weight load is issued
+    // before the selection arrives, so the polls do not queue behind loads.
+    const int sb = b - T * nrb;
+    const bool has_g = sb < n_rt * L.KSg;
+    const int gsb = min(sb, n_rt * L.KSg - 1);
+    const int tile = gsb / L.KSg, ks = gsb % L.KSg;
+    const Tile gt = glu_tile(L, tile);
+    const int g0 = ks * G / L.KSg, g1 = (ks + 1) * G / L.KSg;
+    const bool has_d = sb < T * NB * L.KSdr;
+    const int dsb = min(sb, T * NB * L.KSdr - 1);
+    const int ot = dsb / L.KSdr, ksd = dsb % L.KSdr;
+    const int t_out = ot / NB, n = (ot - t_out * NB) * 64 + lane;
+    const int Ur = k * Gf;
+    const int u0 = ksd * Ur / L.KSdr, u1 = (ksd + 1) * Ur / L.KSdr;
+
+    const u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    const void **s_table = (const void **)(dsm + L.table_off);
+    if (!given) {
+      constexpr int kTab = kMaxLayerE / kThreads;
+      const void *tb[kTab];
+#pragma unroll
+      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
+      stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
+#pragma unroll
+      for (int i = 0; i < kTab; ++i)
+        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
+      __syncthreads();
+      const int copy = sb % L.sel_copies;
+      // the first block of each token's first gate/up tile reports the selection
+      const bool report = has_g && gt.j == 0 && gt.rb == 0 && ks == 0;
+      if (wave == 0) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0], report);
+      if (wave == 1 && t_out != gt.t)
+        wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1], false);
+    } else {
+      stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
+      if (tid < k) {  // written by earlier work on the stream: plain loads
+        s_blob[0][tid] = (const uint8_t *)L.given_blob[(size_t)gt.t * k + tid];
+        s_gate[0][tid] = L.given_gates[(size_t)gt.t * k + tid];
+        s_blob[1][tid] = (const uint8_t *)L.given_blob[(size_t)t_out * k + tid];
+        s_gate[1][tid] = L.given_gates[(size_t)t_out * k + tid];
+      }
+    }
+    __syncthreads();
+    const int ds = t_out == gt.t ? 0 : 1;  // selection of the down token
+    // gate/up weights, then the down weights (every wave; wave 0 mirrors
+    // wave 1's units): the gate/up arithmetic waits for its own loads only
+    GluRegs<M> gr;
+    issue_glu(gr, s_blob[0][gt.j], D, L.F, gt.rb, g0, g1, wave, lane);
+    DownRegs<M> dr;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
       const int u = min(u0 + dw + i * kDW, u1 - 1);
-      load_down(i, (const uint8_t *)L.sblobs[0], L.Fs, u);
+      const int jj = u / Gf;
+      issue_down(dr, i, s_blob[ds][jj], D, L.F, u - jj * Gf, n);
     }
-  }
-
-  // ---------------- staging in LDS: activation pairs (x[8w + m], x[8w + m + 4])
-  // and 64-column sums of the gate/up groups, the blob table
-  if (has_g && tid < n8) {
-    const uint32_t a0 = xq.x, a1 = xq.y, a2 = xq.z, a3 = xq.w;
-    u32x4 pq;
-    pq.x = (a0 & 0xFFFFu) | (a2 << 16);
-    pq.y = (a0 >> 16) | (a2 & 0xFFFF0000u);
-    pq.z = (a1 & 0xFFFFu) | (a3 << 16);
-    pq.w = (a1 >> 16) | (a3 & 0xFFFF0000u);
-    *(u32x4 *)&s_xp[4 * tid] = pq;
-    const uint32_t w[4] = {a0, a1, a2, a3};
-    float s8 = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      s8 += x_to_f32<F16X>(w[m] & 0xFFFFu);
-      s8 += x_to_f32<F16X>(w[m] >> 16);
+    if (has_g) {
+      float accg, accu;
+      glu_dots<F16X, M>(gr, s_xp, s_xs, g0, g1, wave, lane, accg, accu);
+      glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, accg, accu, wave, lane, tag);
     }
-    const float sg = sum8_lanes(s8);
-    if ((tid & 7) == 0) s_xs[tid / 8] = sg;
-  }
-  const void **s_table = (const void **)(dsm + L.table_off);
-  if (routed && !given) {
-#pragma unroll
-    for (int i = 0; i < kTab; ++i) {
-      const int e = tid + i * kThreads;
-      if (e < E) s_table[e] = tb[i];
-    }
-  }
-  __syncthreads();
-
-  // ---------------- gate/up arithmetic, split reduction (the last split to
-  // arrive holds the sums), hidden activations
-  // On the matrix cores: lane l holds word w (8 columns) of hidden row l as
-  // the B operand; lanes 0, 20, 40, 60 hold the activation pairs of word w
-  // as A rows 0, 4, 8, 12 (the other lanes zero), so D row 4q, column c --
-  // register 0 of lane 16q + c -- accumulates row l's dot product.
-  const bool xa_lane = (lane & 15) == 4 * (lane >> 4);
-  auto glu = [&]() {
-    const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
-    float accg = 0.0f, accu = 0.0f;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int gi = wave + i * kNW;  // group g0 + gi
-      if (g0 + gi < g1) {
-        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
-        const uint32_t wg[8] = {qg0[i].x, qg0[i].y, qg0[i].z, qg0[i].w,
-                                qg1[i].x, qg1[i].y, qg1[i].z, qg1[i].w};
-        const uint32_t wu[8] = {qu0[i].x, qu0[i].y, qu0[i].z, qu0[i].w,
-                                qu1[i].x, qu1[i].y, qu1[i].z, qu1[i].w};
-        // the four A lanes read all 8 words at once (one masked region), the
-        // other lanes keep zeros
-        u32x4 a[8];
-#pragma unroll
-        for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
-        if (xa_lane) {
-#pragma unroll
-          for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&s_xp[32 * gi + 4 * w];
-        }
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          dg = mma16<F16X>(a[w], code_pairs(wg[w], magic), dg);
-          du = mma16<F16X>(a[w], code_pairs(wu[w], magic), du);
-        }
-        const float xsg = s_xs[gi];
-        const float sg = f16_to_f32(mg[i]), bg = f16_to_f32(mg[i] >> 16);
-        const float su = f16_to_f32(mu[i]), bu = f16_to_f32(mu[i] >> 16);
-        accg = fmaf(sg, dg[0], accg);
-        accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsg, accg);
-        accu = fmaf(su, du[0], accu);
-        accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsg, accu);
-      }
-    }
-    red[wave][0][lane] = accg;
-    red[wave][1][lane] = accu;
-    __syncthreads();
-    if (wave == 0) {
-      float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) {
-        v0 += red[w][0][lane];
-        v1 += red[w][1][lane];
-      }
-      // the split that completes a gate sum publishes gelu(gate), the one that
-      // completes an up sum publishes up; the consumer multiplies
-      const size_t ho = gt.hoff + (size_t)gt.rb * 64 + lane;
-      float g = v0, u = v1;
-      const bool last_g = L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + lane, v0, L.KSg, &g);
-      const bool last_u =
-          L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + 64 + lane, v1, L.KSg, &u);
-      if (last_g) st_dev64(L.hg + ho, tagged(__float_as_uint(gelu_tanh(g)), tag));
-      if (last_u) st_dev64(L.hu + ho, tagged(__float_as_uint(u), tag));
-    }
-  };
-
-  // ---------------- selected experts (and gates) of the token(s) of this block
-  if (routed) {
-    const int copy = sb % nrb;
-    if (given) {
-      if (tid < k) {  // written by earlier work on the stream: plain loads
-        s_blob[0][tid] = g_routed ? (const uint8_t *)L.given_blob[(size_t)gt.t * k + tid] : nullptr;
-        s_blob[1][tid] = d_routed ? (const uint8_t *)L.given_blob[(size_t)t_out * k + tid] : nullptr;
-        s_gate[1][tid] = d_routed ? L.given_gates[(size_t)t_out * k + tid] : 0.0f;
-      }
-    } else {
-      if (wave == 0 && g_routed) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0]);
-      if (wave == 1 && d_routed) wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1]);
-    }
-    __syncthreads();
-  }
-
-  // ---------------- loads of the selected experts
-  if (g_routed) load_glu(s_blob[0][gt.j]);
-  // routed down weights: with the gate/up tile (down_early) or after it
-  auto load_routed_down = [&]() {
-    if (d_routed && wave > 0) {
+    if (has_d) {
+      size_t hp[M];
+      float gate[M];
+      bool use[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) {
         const int u = min(u0 + dw + i * kDW, u1 - 1);
         const int jj = u / Gf;
-        load_down(i, s_blob[1][jj], L.F, u - jj * Gf);
-      }
-    }
-  };
-  if (L.down_early) load_routed_down();
-  // the shared expert's tiles compute after the routing (it needs the issue
-  // slots more) and before the routed tiles (their data comes later)
-  if (has_g) glu();
-  if (!L.down_early) load_routed_down();
-
-  // ---------------- down projection and combine
-  if (has_d) {
-    size_t hp[M];
-    float gate[M];
-    bool use[M];
-    const uint64_t *hint = nullptr;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int u = min(u0 + dw + i * kDW, u1 - 1);
-      use[i] = wave > 0 && u0 + dw + i * kDW < u1;
-      if (!shared_blk) {
-        const int jj = u / Gf;
-        gate[i] = s_gate[1][jj];
+        use[i] = wave > 0 && u0 + dw + i * kDW < u1;
+        gate[i] = s_gate[ds][jj];
         hp[i] = (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
-      } else {
-        gate[i] = 1.0f;
-        hp[i] = (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
       }
-      if (use[i] && lane == 2 * i) hint = L.hg + hp[i];
-      if (use[i] && lane == 2 * i + 1) hint = L.hu + hp[i];
-    }
-    // lanes 2i, 2i + 1 poll one word of unit i's two rows, then the values
-    // are read (checked): h = gelu(gate) * up
-    wait_hint(hint, tag, L.err);
-    float hv0[M];
-    for (long s = 0;; ++s) {
-      bool ok = true;
-#pragma unroll
-      for (int i = 0; i < M; ++i) {
-        hv0[i] = 0.0f;
-        if (use[i]) {
-          const uint64_t wg = ld_dev64(L.hg + hp[i] + lane);
-          const uint64_t wu = ld_dev64(L.hu + hp[i] + lane);
-          ok = ok && has_tag(wg, tag) && has_tag(wu, tag);
-          hv0[i] = __uint_as_float((uint32_t)wg) * __uint_as_float((uint32_t)wu);
-        }
-      }
-      if (__all(ok)) break;
-      if (s > kSpin) {
-        if (lane == 0) add_dev(L.err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
-    // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
-    float hsum[M];
-    const int pos = 2 * (4 * (lane >> 3) + (lane & 3)) + ((lane >> 2) & 1);
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const float hv = hv0[i];
-      const uint32_t p0 = f32_to_bf16(hv);
-      const float r1 = hv - __uint_as_float(p0 << 16);
-      const uint32_t p1 = f32_to_bf16(r1);
-      const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
-      uint16_t *hp16 = (uint16_t *)&hpl[wave][i][0][0];
-      hp16[pos] = (uint16_t)p0;
-      hp16[64 + pos] = (uint16_t)p1;
-      hp16[128 + pos] = (uint16_t)p2;
-      hsum[i] = wave_sum(hv);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // matrix cores: lane l holds word w (8 hidden rows) of output row l as
-    // B (codes as 1 + q / 16); lanes with l % 16 = 4 (l / 16) + p, p < 3,
-    // hold plane p of h as A row 4 (l / 16) + p, so registers 0..2 of lane l
-    // accumulate the three planes' dot products of output row l.
-    const int plane = (lane & 15) - 4 * (lane >> 4);
-    const bool ha_lane = plane >= 0 && plane < 3;
-    const uint32_t umagic = opaque_vgpr(0x3F803F80u);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      if (!use[i]) continue;
-      const uint32_t wd[8] = {dq0[i].x, dq0[i].y, dq0[i].z, dq0[i].w,
-                              dq1[i].x, dq1[i].y, dq1[i].z, dq1[i].w};
-      u32x4 a[8];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
-      if (ha_lane) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&hpl[wave][i][plane][4 * w];
-      }
-      // two accumulation chains (even and odd words)
-      f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int w = 0; w < 8; w += 2) {
-        d0 = mma16<false>(a[w], code_pairs_unit(wd[w], umagic), d0);
-        d1 = mma16<false>(a[w + 1], code_pairs_unit(wd[w + 1], umagic), d1);
-      }
-      // sum (1 + q/16) h = sum h + sum q h / 16, three planes
-      const float dsum = ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2]);
-      const float sc = f16_to_f32(dmw[i]), bi = f16_to_f32(dmw[i] >> 16);
-      const float v = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum[i]);
-      acc = fmaf(gate[i], v, acc);
-    }
-    __syncthreads();  // red[] is reused
-    red[wave][0][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
-      const int nsp = L.KSdr + L.KSds;
-      if (nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s)) {
-        const size_t idx = (size_t)t_out * D + n;
-        if (L.out_dtype == MOE_F32)
-          ((float *)L.out)[idx] = s;
-        else if (L.out_dtype == MOE_BF16)
-          ((uint16_t *)L.out)[idx] = (uint16_t)f32_to_bf16(s);
-        else
-          ((uint16_t *)L.out)[idx] = (uint16_t)f32_to_f16(s);
-      }
+      down_and_combine<M>(L, dr, hp, gate, use, hpl, red, ot, (size_t)t_out * D + n, wave, lane,
+                          tag);
     }
   }
 
@@ -720,14 +780,14 @@ KernelFn pick(int m) {
   return nullptr;
 }
 KernelFn pick_layer(const LayerLaunch &L, int m) {
-  const bool small_d = L.D <= 3072;  // router chunks per thread: 6 (D <= 3072) or 16
-  if (L.f16x) return small_d ? pick<true, 6>(m) : pick<true, 16>(m);
-  return small_d ? pick<false, 6>(m) : pick<false, 16>(m);
+  const bool small_d = L.D <= 3072;  // router chunks per thread: 3 (D <= 3072) or 8
+  if (L.f16x) return small_d ? pick<true, 3>(m) : pick<true, 8>(m);
+  return small_d ? pick<false, 3>(m) : pick<false, 8>(m);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int g_layer_capacity[2][2][3][64];  // [f16x][MAXC 6/16][m - 2][device]
+int g_layer_capacity[2][2][3][64];  // [f16x][MAXC 3/8][m - 2][device]
 
 }  // namespace
 

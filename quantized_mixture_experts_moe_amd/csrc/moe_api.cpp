@@ -188,7 +188,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   const int NB = D / 64, G = D / 64;
   const int n_gtiles = T * k * (F / 64) + T * (Fs / 64);
   L->n_gtiles = n_gtiles;
-  L->down_early = tuning().layer_down_early;
+  L->shared_wait = tuning().layer_shared_wait;
   // the most gate/up splits (and with them down splits) whose grid is still
   // resident all at once: more, smaller blocks overlap more of the transfer
   bool found = false;
@@ -213,7 +213,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   // tagged words: logits, hidden activations
   Carver c{w.layer + kTaggedOff};
   L->rlog = c.take<uint64_t>((size_t)T * E, 8);
-  L->sel_copies = (E + 7) / 8;  // one per router block of a token
+  L->sel_copies = 16;  // copies of each selection line (spread the polling)
   L->lid = (k + 15) / 16 * 16;
   L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * 2 * L->lid, 8);
   L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
@@ -298,8 +298,8 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_ksg = value;
   } else if (!strcmp(key, "layer_ksd")) {
     tuning().layer_ksd = value;
-  } else if (!strcmp(key, "layer_down_early")) {
-    tuning().layer_down_early = value;
+  } else if (!strcmp(key, "layer_shared_wait")) {
+    tuning().layer_shared_wait = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
   } else {

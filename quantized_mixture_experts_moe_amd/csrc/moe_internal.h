@@ -76,11 +76,10 @@ struct Tuning {
   int fused_ksg = 0;   // its gate/up and down splits (0: chosen)
   int fused_ksd = 0;
   int prefill_min_t = 16;  // tokens per call from which the grouped matrix-core path runs
-  int route_rows = 8;  // experts per router block
   int layer = 1;       // one launch for the whole decode layer when it fits
   int layer_ksg = 0;   // its gate/up and down splits (0: chosen)
   int layer_ksd = 0;
-  int layer_down_early = 0;
+  int layer_shared_wait = 0;
 };
 Tuning &tuning();
 
@@ -198,7 +197,7 @@ struct LayerLaunch {
   int KSdr, KSds;                     // down splits of the routed / shared units
   int NR;                             // router + routed blocks (the shared blocks follow)
   int blk0, grid_full;                // this launch covers blocks [blk0, blk0 + grid)
-  int down_early;                     // routed down weights with gate/up (else after)
+  int shared_wait;                    // shared blocks load after the router logits are out
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;

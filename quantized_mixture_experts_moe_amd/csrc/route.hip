@@ -275,16 +275,17 @@ hipError_t launch_prep_x(const void *x, int f16x, int T, int D, uint32_t *xp, fl
 
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
   // one token per block for decode; four tokens share each router load in
-  // prefill.  MAXC: 16-column chunks per thread (32 threads split a row).
+  // prefill.  MAXC: 16-column chunks per thread (64 threads split a row, the
+  // same split and order as the one-launch decode layer's router).
   const bool small_d = a.D <= 3072;
   if (a.T >= 16) {
     if (small_d)
-      return a.f16x ? launch_route_t<true, 8, 4, 6>(a, s) : launch_route_t<false, 8, 4, 6>(a, s);
-    return a.f16x ? launch_route_t<true, 8, 4, 16>(a, s) : launch_route_t<false, 8, 4, 16>(a, s);
+      return a.f16x ? launch_route_t<true, 4, 4, 3>(a, s) : launch_route_t<false, 4, 4, 3>(a, s);
+    return a.f16x ? launch_route_t<true, 4, 4, 8>(a, s) : launch_route_t<false, 4, 4, 8>(a, s);
   }
   if (small_d)
-    return a.f16x ? launch_route_t<true, 8, 1, 6>(a, s) : launch_route_t<false, 8, 1, 6>(a, s);
-  return a.f16x ? launch_route_t<true, 8, 1, 16>(a, s) : launch_route_t<false, 8, 1, 16>(a, s);
+    return a.f16x ? launch_route_t<true, 4, 1, 3>(a, s) : launch_route_t<false, 4, 1, 3>(a, s);
+  return a.f16x ? launch_route_t<true, 4, 1, 8>(a, s) : launch_route_t<false, 4, 1, 8>(a, s);
 }
 
 }  // namespace moe
