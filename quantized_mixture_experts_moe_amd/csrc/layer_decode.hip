@@ -390,14 +390,13 @@ __device__ __forceinline__ void glu_dots(const GluRegs<M> &R, const uint32_t *s_
   }
 }
 
-// Block-wide sum of the gate/up partials, then the split reduction: the
-// split that completes a gate sum publishes gelu(gate), the one that
-// completes an up sum publishes up (the consumer multiplies).
+// Block-wide sum of the gate/up partials (each wave has put its partials in
+// red[]), then the split reduction: the split that completes a gate sum
+// publishes gelu(gate), the one that completes an up sum publishes up (the
+// consumer multiplies).
 __device__ __forceinline__ void glu_publish(const LayerLaunch &L, float (&red)[kNW][2][64],
-                                            int tile, size_t ho, float accg, float accu,
-                                            int wave, int lane, uint32_t tag) {
-  red[wave][0][lane] = accg;
-  red[wave][1][lane] = accu;
+                                            int tile, size_t ho, int wave, int lane,
+                                            uint32_t tag) {
   __syncthreads();
   if (wave == 0) {
     float v0 = 0.0f, v1 = 0.0f;
@@ -664,15 +663,25 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     GluRegs<M> gr;
     issue_glu(gr, sblob, D, L.Fs, gt.rb, g0, g1, wave, lane);
     DownRegs<M> dr;
+    auto load_down = [&]() {
 #pragma unroll
-    for (int i = 0; i < M; ++i) issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * kDW, u1 - 1), n);
+      for (int i = 0; i < M; ++i)
+        issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * kDW, u1 - 1), n);
+    };
+    if (L.down_late == 0) load_down();
     stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
     __syncthreads();
     if (has_g) {
       float accg, accu;
       glu_dots<F16X, M>(gr, s_xp, s_xs, g0, g1, wave, lane, accg, accu);
-      glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, accg, accu, wave, lane, tag);
+      red[wave][0][lane] = accg;
+      red[wave][1][lane] = accu;
     }
+    // down weights of waves 1..3 once their gate/up data is in (2) or after
+    // the split reduction (1); wave 0 does the reduction's atomics
+    if (L.down_late == 2 && wave > 0) load_down();
+    if (has_g) glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, wave, lane, tag);
+    if (L.down_late == 1 && wave > 0) load_down();
     if (has_d) {
       size_t hp[M];
       float gate[M];
@@ -738,17 +747,26 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     GluRegs<M> gr;
     issue_glu(gr, s_blob[0][gt.j], D, L.F, gt.rb, g0, g1, wave, lane);
     DownRegs<M> dr;
+    auto load_down = [&]() {
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int u = min(u0 + dw + i * kDW, u1 - 1);
-      const int jj = u / Gf;
-      issue_down(dr, i, s_blob[ds][jj], D, L.F, u - jj * Gf, n);
-    }
+      for (int i = 0; i < M; ++i) {
+        const int u = min(u0 + dw + i * kDW, u1 - 1);
+        const int jj = u / Gf;
+        issue_down(dr, i, s_blob[ds][jj], D, L.F, u - jj * Gf, n);
+      }
+    };
+    if (L.down_late == 0) load_down();
     if (has_g) {
       float accg, accu;
       glu_dots<F16X, M>(gr, s_xp, s_xs, g0, g1, wave, lane, accg, accu);
-      glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, accg, accu, wave, lane, tag);
+      red[wave][0][lane] = accg;
+      red[wave][1][lane] = accu;
     }
+    // down weights of waves 1..3 once their gate/up data is in (2) or after
+    // the split reduction (1); wave 0 does the reduction's atomics
+    if (L.down_late == 2 && wave > 0) load_down();
+    if (has_g) glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, wave, lane, tag);
+    if (L.down_late == 1 && wave > 0) load_down();
     if (has_d) {
       size_t hp[M];
       float gate[M];

@@ -189,6 +189,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   const int n_gtiles = T * k * (F / 64) + T * (Fs / 64);
   L->n_gtiles = n_gtiles;
   L->shared_wait = tuning().layer_shared_wait;
+  L->down_late = tuning().layer_down_late;
   // the most gate/up splits (and with them down splits) whose grid is still
   // resident all at once: more, smaller blocks overlap more of the transfer
   bool found = false;
@@ -298,6 +299,8 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_ksg = value;
   } else if (!strcmp(key, "layer_ksd")) {
     tuning().layer_ksd = value;
+  } else if (!strcmp(key, "layer_down_late")) {
+    tuning().layer_down_late = value;
   } else if (!strcmp(key, "layer_shared_wait")) {
     tuning().layer_shared_wait = value;
   } else if (!strcmp(key, "prefill_min_t")) {

@@ -80,6 +80,7 @@ struct Tuning {
   int layer_ksg = 0;   // its gate/up and down splits (0: chosen)
   int layer_ksd = 0;
   int layer_shared_wait = 0;
+  int layer_down_late = 1;
 };
 Tuning &tuning();
 
@@ -198,6 +199,7 @@ struct LayerLaunch {
   int NR;                             // router + routed blocks (the shared blocks follow)
   int blk0, grid_full;                // this launch covers blocks [blk0, blk0 + grid)
   int shared_wait;                    // shared blocks load after the router logits are out
+  int down_late;                      // down weights: 0 with gate/up, 1 after its reduction, 2 after its arithmetic
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;

@@ -349,7 +349,7 @@ def test_pool_streamed_equals_resident_and_trace():
 
 _PATHS = {"layer": {"layer": 1}, "fused": {"layer": 0, "fused": 1},
           "three": {"layer": 0, "fused": 0}}
-_DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0}
+_DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1}
 
 
 def _tune(**kv):
