@@ -181,7 +181,7 @@ struct PrefillLaunch {
   const float *gates;
   const void *const *rblobs, *const *sblobs;
   const uint32_t *xp; const float *xs;
-  uint16_t *hp; size_t plane;         // three planes of `plane` elements
+  uint16_t *hp; size_t plane;         // h as three bf16 planes of `plane` elements
   float *hsum, *y, *ys;
   void *out; int out_dtype;
 };
