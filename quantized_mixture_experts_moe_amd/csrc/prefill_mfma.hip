@@ -28,9 +28,11 @@
 // down (down_mfma_kernel): block = (expert, 256 output rows, 32 group rows);
 //   per hidden group the block stages the down codes, their scale/bias words
 //   and the three planes of h (once for its 256 rows: wave w computes output
-//   rows 64w..64w+63).  B operand: exact codes (byte spread,
-//   v_cvt_f32_ubyte, packed to bf16); A operand: the planes, three products
-//   per step, so no offset or rounding of h enters the fp32 accumulation.
+//   rows 64w..64w+63).  B operand: codes as bf16 1 + q/16 (a nibble in the
+//   mantissa of 1.0, exact), pairs (q_m, q_{m+4}); A operand: the planes in
+//   the same pair order, three products per step; per group the fold is
+//   16 s * sum h (1 + q/16) + (b - 16 s) * sum h.  The small offset (1, not
+//   128) keeps the fp32 sums close to exact although h has a large mean.
 // combine (combine_prefill_kernel): out[t] = y_shared[t] + sum_j gate y[inv].
 #include "device_common.h"
 #include "moe_internal.h"
@@ -62,20 +64,6 @@ __device__ __forceinline__ u32x4_t unpack_magic(uint32_t w, uint32_t magic) {
   r.y = ((w >> 4) & 0x000F000Fu) | magic;
   r.z = ((w >> 8) & 0x000F000Fu) | magic;
   r.w = ((w >> 12) & 0x000F000Fu) | magic;
-  return r;
-}
-
-// 8 codes of one word -> exact bf16 values in natural column order
-__device__ __forceinline__ u32x4_t unpack_exact_bf16(uint32_t w) {
-  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-  u32x4_t r;
-  // integers 0..15 are exact in bf16: the top half of their fp32 pattern
-  r.x = (__float_as_uint((float)(ev & 0xFFu)) >> 16) | (__float_as_uint((float)(od & 0xFFu)) & 0xFFFF0000u);
-  r.y = (__float_as_uint((float)((ev >> 8) & 0xFFu)) >> 16) |
-        (__float_as_uint((float)((od >> 8) & 0xFFu)) & 0xFFFF0000u);
-  r.z = (__float_as_uint((float)((ev >> 16) & 0xFFu)) >> 16) |
-        (__float_as_uint((float)((od >> 16) & 0xFFu)) & 0xFFFF0000u);
-  r.w = (__float_as_uint((float)(ev >> 24)) >> 16) | (__float_as_uint((float)(od >> 24)) & 0xFFFF0000u);
   return r;
 }
 
@@ -113,13 +101,34 @@ __device__ __forceinline__ size_t hrow_off(const PrefillLaunch &p, int r) {
   return r < p.T * p.k ? (size_t)r * p.F : (size_t)p.T * p.k * p.F + (size_t)(r - p.T * p.k) * p.Fs;
 }
 
+// Direct global -> LDS loads (no registers): lane i's `size` bytes land at
+// dst + i * size; dst must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                   (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                   (void __attribute__((address_space(3))) *)dst, 4, 0, 0);
+}
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (they complete in order), then meet the other waves: the
+// staged data of every wave is then in LDS.  No fence: the loads in flight
+// for later stages stay in flight.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_s_barrier();
+}
+
 // 16-byte slot of (row t, vector v of 8) in a staged [32 rows][8 vectors]
 // tile: rows rotate their vectors so that 16 rows read at one v spread over
 // the banks
 __device__ __forceinline__ int xslot(int t, int v) { return t * 8 + (v ^ (t & 7)); }
 
 // ---------------------------------------------------------------- gate/up
-constexpr int kPg = 4;  // groups in flight per wave
+constexpr int kRg = 4;  // LDS stages of the gate/up ring (kRg - 1 groups in flight)
 
 struct GluBuf {
   u32x4_t w[4][64];        // (matrix, half): gate lo/hi chunk, up lo/hi; row = lane
@@ -127,35 +136,34 @@ struct GluBuf {
   u32x4_t x[kRows * 8];    // activation pairs of the 32 rows, xslot order
 };
 
-struct GluSlot {
-  u32x4_t w, x;
-  uint32_t m;
-};
-
 template <bool F16X, int NM>
 __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g, int nt, int m0,
                                          int nrow, const int *s_tok, const float *s_xs,
-                                         GluBuf (&buf)[2], float (*s_h)[65]) {
+                                         GluBuf &b0, GluBuf &b1, GluBuf &b2, GluBuf &b3,
+                                         float (*s_h)[65]) {
+  // one LDS object per stage, so that a read of one stage does not wait for
+  // the loads in flight into the others
+  auto buf = [&](int s) -> GluBuf & { return s == 0 ? b0 : s == 1 ? b1 : s == 2 ? b2 : b3; };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int D = p.D, G = D / 64, F = g.F;
   const int col = lane & 15, kb = lane >> 4;
   const BlobLayout L = blob_layout(D, F);
-  // this wave's loads: weight piece (matrix wave/2, half wave%2), meta of
-  // matrix wave%2, activation pairs of rows 8 wave .. 8 wave + 7
-  const gptr<u32x4_t> wsrc = as_global(
-      (const u32x4_t *)(g.blob + ((wave >> 1) ? L.up_codes : L.gate_codes)) + (size_t)(wave & 1) * F +
-      nt * 64 + lane);
-  const gptr<uint32_t> msrc =
-      as_global((const uint32_t *)(g.blob + ((wave & 1) ? L.up_meta : L.gate_meta)) + nt * 64 + lane);
-  const int xt = 8 * wave + (lane >> 3), xv = lane & 7;
-  const gptr<u32x4_t> xsrc =
-      as_global((const u32x4_t *)(p.xp + (size_t)s_tok[xt] * (D / 2)) + xv);
-  auto issue = [&](GluSlot &S, int gi) {
+  // this wave stages, per group: one code piece (matrix wave / 2, half
+  // wave % 2; row = lane), the scale/bias words of matrix wave % 2, and the
+  // activation pairs of rows 8 wave .. 8 wave + 7 (lane p: row t = 8 wave +
+  // p / 8, vector (p % 8) ^ (t & 7), so that it lands in its xslot)
+  const u32x4_t *wsrc = (const u32x4_t *)(g.blob + ((wave >> 1) ? L.up_codes : L.gate_codes)) +
+                        (size_t)(wave & 1) * F + nt * 64 + lane;
+  const uint32_t *msrc =
+      (const uint32_t *)(g.blob + ((wave & 1) ? L.up_meta : L.gate_meta)) + nt * 64 + lane;
+  const int xt = 8 * wave + (lane >> 3), xv = (lane & 7) ^ (xt & 7);
+  const u32x4_t *xsrc = (const u32x4_t *)(p.xp + (size_t)s_tok[xt] * (D / 2)) + xv;
+  auto issue = [&](GluBuf &B, int gi) {
     gi = min(gi, G - 1);  // past the end: a repeat of the last group, folded with weight 0
-    S.w = wsrc[(size_t)(2 * gi) * F];
-    S.m = msrc[(size_t)gi * F];
-    S.x = xsrc[gi * 8];
+    dma16(wsrc + (size_t)(2 * gi) * F, &B.w[wave][0]);
+    dma4(msrc + (size_t)gi * F, &B.m[wave][0]);
+    dma16(xsrc + gi * 8, &B.x[64 * wave]);
   };
   const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
 
@@ -165,19 +173,17 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
     tg[mt] = f32x4_t{0, 0, 0, 0};
     tu[mt] = f32x4_t{0, 0, 0, 0};
   }
-  GluSlot ring[kPg];
 #pragma unroll
-  for (int s = 0; s < kPg; ++s) issue(ring[s], s);
-  for (int g0 = 0; g0 < G; g0 += kPg) {
+  for (int s = 0; s < kRg - 1; ++s) issue(buf(s), s);
+  for (int g0 = 0; g0 < G; g0 += kRg) {
 #pragma unroll
-    for (int s = 0; s < kPg; ++s) {
+    for (int s = 0; s < kRg; ++s) {
       const int gi = g0 + s;
-      GluBuf &B = buf[s & 1];
-      B.w[wave][lane] = ring[s].w;
-      B.m[wave][lane] = ring[s].m;
-      B.x[xslot(xt, xv)] = ring[s].x;
-      issue(ring[s], gi + kPg);
-      __syncthreads();
+      // this group's stage is in (3 loads per stage per wave; kRg - 2 later
+      // stages may stay in flight), and every wave is done with group gi - 1
+      stage_barrier<3 * (kRg - 2)>();
+      issue(buf((s + kRg - 1) % kRg), gi + kRg - 1);
+      const GluBuf &B = buf(s);
       const bool live = gi < G;
       f32x4_t ag[NM], au[NM];
 #pragma unroll
@@ -213,6 +219,8 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
       }
     }
   }
+  // the stages past the end are still landing in LDS: let them finish
+  stage_barrier<0>();
   // h into LDS [row][hidden col of the tile]
 #pragma unroll
   for (int mt = 0; mt < NM; ++mt) {
@@ -221,7 +229,8 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
       s_h[mt * 16 + kb * 4 + i][wave * 16 + col] = gelu_tanh(tg[mt][i]) * tu[mt][i];
   }
   __syncthreads();
-  // three bf16 planes and the 64-unit sum of every valid row
+  // three bf16 planes (in the pair order (h[8v + m], h[8v + m + 4]) of the
+  // down kernel's code pairs) and the 64-unit sum of every valid row
   for (int idx = threadIdx.x; idx < nrow * 64; idx += 256) {
     const int m = idx >> 6, c = idx & 63;
     const float h = s_h[m][c];
@@ -229,7 +238,8 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
     const float r1 = h - bf16_to_f32(hi);
     const uint32_t mid = f32_to_bf16(r1);
     const uint32_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-    const size_t o = hrow_off(p, g.off + m0 + m) + (size_t)nt * 64 + c;
+    const int u = c & 7, pos = (c & ~7) | (u < 4 ? 2 * u : 2 * (u - 4) + 1);
+    const size_t o = hrow_off(p, g.off + m0 + m) + (size_t)nt * 64 + pos;
     p.hp[o] = (uint16_t)hi;
     p.hp[p.plane + o] = (uint16_t)mid;
     p.hp[2 * p.plane + o] = (uint16_t)lo;
@@ -246,7 +256,8 @@ template <bool F16X>
 __global__ __launch_bounds__(256) void glu_mfma_kernel(PrefillLaunch p) {
   extern __shared__ float s_dyn[];  // [kRows][G] 64-column sums of x
   __shared__ int s_tok[kRows];
-  __shared__ GluBuf buf[2];
+  __shared__ GluBuf b0, b1, b2, b3;
+  static_assert(kRg == 4, "one LDS object per stage");
   __shared__ float s_h[kRows][65];
   const int NT = p.F / 64;
   const int bid = blockIdx.x;
@@ -268,73 +279,79 @@ __global__ __launch_bounds__(256) void glu_mfma_kernel(PrefillLaunch p) {
   }
   __syncthreads();
   if (nrow <= 16)
-    glu_body<F16X, 1>(p, g, nt, m0, nrow, s_tok, s_dyn, buf, s_h);
+    glu_body<F16X, 1>(p, g, nt, m0, nrow, s_tok, s_dyn, b0, b1, b2, b3, s_h);
   else
-    glu_body<F16X, 2>(p, g, nt, m0, nrow, s_tok, s_dyn, buf, s_h);
+    glu_body<F16X, 2>(p, g, nt, m0, nrow, s_tok, s_dyn, b0, b1, b2, b3, s_h);
 }
 
 // ---------------------------------------------------------------- down
-constexpr int kPd = 2;   // hidden groups in flight per wave
+constexpr int kRd = 3;   // LDS stages of the down ring (kRd - 1 groups in flight)
 constexpr int kDT = 4;   // 16-row output tiles per wave (a block covers 256 output rows)
 
 struct DownBuf {
-  u32x4_t pl[3][kRows * 8];   // planes of h for the 32 rows, 64 units, xslot order
+  u32x4_t pl[3][kRows * 8];   // planes of h (pair order) for the 32 rows, xslot order
   u32x4_t w[2][4 * 64];       // down codes, chunks 2gi and 2gi + 1; row = 64 wave + lane
   uint32_t m[4 * 64];         // scale/bias words of the 256 rows
-};
-
-struct DownSlot {
-  u32x4_t pl[3];  // plane q of rows 8 wave .. 8 wave + 7
-  u32x4_t w[2];   // chunks 2gi, 2gi + 1 of output row 64 wave + lane
-  uint32_t m;     // its scale/bias word
 };
 
 template <int NM>
 __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g, int nb, int m0,
                                           int nrow, const int *s_row, const float *s_hs,
-                                          DownBuf (&buf)[2]) {
+                                          DownBuf &b0, DownBuf &b1, DownBuf &b2) {
+  // one LDS object per stage, so that a read of one stage does not wait for
+  // the loads in flight into the others
+  auto buf = [&](int s) -> DownBuf & { return s == 0 ? b0 : s == 1 ? b1 : b2; };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int D = p.D, F = g.F, GH = F / 64;
   const int col = lane & 15, kb = lane >> 4;
   const BlobLayout L = blob_layout(D, F);
-  const int xt = 8 * wave + (lane >> 3), xv = lane & 7;
-  const gptr<u32x4_t> hsrc = as_global((const u32x4_t *)(p.hp + hrow_off(p, s_row[xt])) + xv);
+  // this wave stages, per hidden group: the three planes of rows 8 wave ..
+  // 8 wave + 7 (lane p: row t = 8 wave + p / 8, vector (p % 8) ^ (t & 7), so
+  // that it lands in its xslot), the two code chunks and the scale/bias word
+  // of output row 64 wave + lane
+  const int xt = 8 * wave + (lane >> 3), xv = (lane & 7) ^ (xt & 7);
+  const u32x4_t *hsrc = (const u32x4_t *)(p.hp + hrow_off(p, s_row[xt])) + xv;
   const size_t plane_v = p.plane / 8;  // plane size in 16-byte vectors
-  const int wrow = min(nb * 256 + wave * 64 + lane, D - 1);  // output row this lane loads
-  const gptr<u32x4_t> wsrc = as_global((const u32x4_t *)(g.blob + L.down_codes) + wrow);
-  const gptr<uint32_t> msrc = as_global((const uint32_t *)(g.blob + L.down_meta) + wrow);
-  auto issue = [&](DownSlot &S, int gi) {
+  const int wrow = min(nb * 256 + wave * 64 + lane, D - 1);
+  const u32x4_t *wsrc = (const u32x4_t *)(g.blob + L.down_codes) + wrow;
+  const uint32_t *msrc = (const uint32_t *)(g.blob + L.down_meta) + wrow;
+  auto issue = [&](DownBuf &B, int gi) {
     gi = min(gi, GH - 1);  // past the end: a repeat of the last group, folded with weight 0
 #pragma unroll
-    for (int q = 0; q < 3; ++q) S.pl[q] = hsrc[q * plane_v + gi * 8];
-    S.w[0] = wsrc[(size_t)(2 * gi) * D];
-    S.w[1] = wsrc[(size_t)(2 * gi + 1) * D];
-    S.m = msrc[(size_t)gi * D];
+    for (int q = 0; q < 3; ++q) dma16(hsrc + q * plane_v + gi * 8, &B.pl[q][64 * wave]);
+    dma16(wsrc + (size_t)(2 * gi) * D, &B.w[0][64 * wave]);
+    dma16(wsrc + (size_t)(2 * gi + 1) * D, &B.w[1][64 * wave]);
+    dma4(msrc + (size_t)gi * D, &B.m[64 * wave]);
   };
+  const uint32_t umagic = opaque_vgpr(0x3F803F80u);  // bf16 1.0 pairs
 
   f32x4_t t[NM][kDT];
 #pragma unroll
   for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
     for (int j = 0; j < kDT; ++j) t[mt][j] = f32x4_t{0, 0, 0, 0};
-  DownSlot ring[kPd];
 #pragma unroll
-  for (int s = 0; s < kPd; ++s) issue(ring[s], s);
-  for (int g0 = 0; g0 < GH; g0 += kPd) {
+  for (int s = 0; s < kRd - 1; ++s) issue(buf(s), s);
+  for (int g0 = 0; g0 < GH; g0 += kRd) {
 #pragma unroll
-    for (int s = 0; s < kPd; ++s) {
+    for (int s = 0; s < kRd; ++s) {
       const int gi = g0 + s;
-      DownBuf &B = buf[(gi) & 1];
-#pragma unroll
-      for (int q = 0; q < 3; ++q) B.pl[q][xslot(xt, xv)] = ring[s].pl[q];
-      B.w[0][wave * 64 + lane] = ring[s].w[0];
-      B.w[1][wave * 64 + lane] = ring[s].w[1];
-      B.m[wave * 64 + lane] = ring[s].m;
-      issue(ring[s], gi + kPd);
-      __syncthreads();
+      // this group's stage is in (6 loads per stage per wave; kRd - 2 later
+      // stages may stay in flight), and every wave is done with group gi - 1
+      stage_barrier<6 * (kRd - 2)>();
+      issue(buf((s + kRd - 1) % kRd), gi + kRd - 1);
+      const DownBuf &B = buf(s);
       const bool live = gi < GH;
       const int gx = min(gi, GH - 1);
+      // the planes of this wave's rows, shared by its kDT output tiles
+      u32x4_t a_in[NM][2][3];
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int q = 0; q < 3; ++q) a_in[mt][half][q] = B.pl[q][xslot(mt * 16 + col, half * 4 + kb)];
 #pragma unroll
       for (int j = 0; j < kDT; ++j) {
         // output tile j of this wave: rows 64 wave + 16 j + col
@@ -344,26 +361,29 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
         for (int mt = 0; mt < NM; ++mt) a[mt] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const u32x4_t b = unpack_exact_bf16(((const uint32_t *)&B.w[half][r])[kb]);
+          const u32x4_t b = code_pairs_unit(((const uint32_t *)&B.w[half][r])[kb], umagic);
 #pragma unroll
           for (int mt = 0; mt < NM; ++mt) {
-            const int sl = xslot(mt * 16 + col, half * 4 + kb);
-            a[mt] = mfma<false>(B.pl[0][sl], b, a[mt]);
-            a[mt] = mfma<false>(B.pl[1][sl], b, a[mt]);
-            a[mt] = mfma<false>(B.pl[2][sl], b, a[mt]);
+            a[mt] = mfma<false>(a_in[mt][half][0], b, a[mt]);
+            a[mt] = mfma<false>(a_in[mt][half][1], b, a[mt]);
+            a[mt] = mfma<false>(a_in[mt][half][2], b, a[mt]);
           }
         }
+        // sum h (1 + q/16) = sum h + sum h q / 16: fold s q + b per group
         const uint32_t mw = B.m[r];
         const float sd = live ? f16_to_f32(mw) : 0.0f, bd = live ? f16_to_f32(mw >> 16) : 0.0f;
+        const float s16 = 16.0f * sd, c16 = fmaf(-16.0f, sd, bd);
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            t[mt][j][i] = fmaf(sd, a[mt][i], fmaf(bd, s_hs[(mt * 16 + kb * 4 + i) * GH + gx], t[mt][j][i]));
+            t[mt][j][i] = fmaf(s16, a[mt][i], fmaf(c16, s_hs[(mt * 16 + kb * 4 + i) * GH + gx], t[mt][j][i]));
         }
       }
     }
   }
+  // the stages past the end are still landing in LDS: let them finish
+  stage_barrier<0>();
 #pragma unroll
   for (int j = 0; j < kDT; ++j) {
     const int n = nb * 256 + wave * 64 + j * 16 + col;  // output row of this lane's column
@@ -385,7 +405,8 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
 __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
   __shared__ int s_row[kRows];
   __shared__ float s_hs[kRows * kMaxHGroups];
-  __shared__ DownBuf buf[2];
+  __shared__ DownBuf b0, b1, b2;
+  static_assert(kRd == 3, "one LDS object per stage");
   const int D = p.D, NB = (D + 255) / 256;
   const int bid = blockIdx.x;
   const int g_idx = bid < p.E * NB ? bid / NB : p.E;
@@ -403,9 +424,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
   }
   __syncthreads();
   if (nrow <= 16)
-    down_body<1>(p, g, nb, m0, nrow, s_row, s_hs, buf);
+    down_body<1>(p, g, nb, m0, nrow, s_row, s_hs, b0, b1, b2);
   else
-    down_body<2>(p, g, nb, m0, nrow, s_row, s_hs, buf);
+    down_body<2>(p, g, nb, m0, nrow, s_row, s_hs, b0, b1, b2);
 }
 
 __global__ void combine_prefill_kernel(PrefillLaunch p) {
