@@ -418,21 +418,31 @@ __device__ __forceinline__ void glu_publish(const LayerLaunch &L, float (&red)[k
 // Down projection of output row n over this wave's units, then the split
 // reduction over the blocks of the output tile, which writes the output.
 // unit i: hidden rows hp[i] .. hp[i] + 63 (tagged words), weight gate[i].
-template <int M>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// With L.hu null the hidden activations are single tagged words h in L.hg
+// (gelu(gate) * up, finished by one block); otherwise gelu(gate) in L.hg and
+// up in L.hu.  on_hint runs once the units' first words are seen.
+template <int M, class OnHint = NoHook>
 __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const DownRegs<M> &R,
                                                  const size_t (&hp)[M], const float (&gate)[M],
                                                  const bool (&use)[M], uint32_t (&hpl)[kNW][M][3][32],
                                                  float (&red)[kNW][2][64], int ot, size_t out_idx,
-                                                 int wave, int lane, uint32_t tag) {
-  // lanes 2i, 2i + 1 poll one word of unit i's two rows, then the values
-  // are read (checked): h = gelu(gate) * up
+                                                 int wave, int lane, uint32_t tag,
+                                                 OnHint on_hint = OnHint()) {
+  // lanes 2i, 2i + 1 poll one word of unit i's rows, then the values are
+  // read (checked)
+  const bool single = L.hu == nullptr;
   const uint64_t *hint = nullptr;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     if (use[i] && lane == 2 * i) hint = L.hg + hp[i];
-    if (use[i] && lane == 2 * i + 1) hint = L.hu + hp[i];
+    if (use[i] && lane == 2 * i + 1 && !single) hint = L.hu + hp[i];
   }
   wait_hint(hint, tag, L.err);
+  on_hint();
   float hv0[M];
   for (long s = 0;; ++s) {
     bool ok = true;
@@ -441,9 +451,13 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
       hv0[i] = 0.0f;
       if (use[i]) {
         const uint64_t wg = ld_dev64(L.hg + hp[i] + lane);
-        const uint64_t wu = ld_dev64(L.hu + hp[i] + lane);
-        ok = ok && has_tag(wg, tag) && has_tag(wu, tag);
-        hv0[i] = __uint_as_float((uint32_t)wg) * __uint_as_float((uint32_t)wu);
+        ok = ok && has_tag(wg, tag);
+        hv0[i] = __uint_as_float((uint32_t)wg);
+        if (!single) {
+          const uint64_t wu = ld_dev64(L.hu + hp[i] + lane);
+          ok = ok && has_tag(wu, tag);
+          hv0[i] *= __uint_as_float((uint32_t)wu);
+        }
       }
     }
     if (__all(ok)) break;
@@ -523,9 +537,95 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
   }
 }
 
+// Router rows e0 .. e0 + kRows - 1 of token r_t and the selection of the
+// token (every router block publishes its winners).  They head the chain of
+// dependent steps, so these blocks do nothing else.
+template <bool F16X, int MAXC>
+__device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_t tag, uint8_t *dsm,
+                                            SelectLds &s_select) {
+  constexpr int MAXX = MAXC == 3 ? 2 : 4;  // 16-byte pieces of x per thread
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int D = L.D, E = L.E;
+  const int nrb = (E + kRows - 1) / kRows;
+  const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
+  __builtin_amdgcn_s_setprio(1);
+  const int nch = D / 16;
+  float *sx = (float *)dsm;   // x as fp32 [D]
+  float *sxs = sx + D;        // 16-column sums [D/16]
+  float *rred = sxs + nch;    // partial logits [kKL][kRows]
+  const int rr = tid % kRows, kl = tid / kRows;  // chunks kl, kl + kKL, ... of row rr
+  u32x4 xr[MAXX], rq[MAXC];
+  uint32_t rmw[MAXC];
+  const uint16_t *x = (const uint16_t *)L.x;
+  const gptr<u32x4> xt = as_global((const u32x4 *)(x + (size_t)r_t * D));
+#pragma unroll
+  for (int i = 0; i < MAXX; ++i) xr[i] = xt[min(tid + i * kThreads, D / 8 - 1)];
+  const int e = min(r_e0 + rr, E - 1);
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = min(kl + i * kKL, nch - 1);
+    rq[i] = as_global((const u32x4 *)L.rcodes)[(size_t)c * E + e];
+    rmw[i] = as_global(L.rmeta)[(size_t)c / 4 * E + e];
+  }
+#pragma unroll
+  for (int i = 0; i < MAXX; ++i) {
+    const int c = tid + i * kThreads;
+    if (c < D / 8) {
+      const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        sx[8 * c + 2 * m] = x_to_f32<F16X>(w[m] & 0xFFFFu);
+        sx[8 * c + 2 * m + 1] = x_to_f32<F16X>(w[m] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nch; i += kThreads) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += sx[16 * i + j];
+    sxs[i] = s;
+  }
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = kl + i * kKL;
+    if (c < nch) {
+      const float sc = f16_to_f32(rmw[i]), bi = f16_to_f32(rmw[i] >> 16);
+      const uint32_t w[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
+      const float *xv = sx + c * 16;
+      float d = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+          d = fmaf(xv[4 * u + bb], (float)((w[u] >> (8 * bb)) & 0xFFu), d);
+      acc = fmaf(sc, d, acc);
+      acc = fmaf(bi, sxs[c], acc);
+    }
+  }
+  rred[kl * kRows + rr] = acc;
+  __syncthreads();
+  if (wave == 0 && lane < kRows) {
+    float s = 0.0f;
+    for (int j = 0; j < kKL; ++j) s += rred[j * kRows + lane];
+    const int e2 = r_e0 + lane;
+    uint64_t own = 0;  // below every real key
+    if (e2 < E) {
+      if (L.logit_bias) s += L.logit_bias[e2];
+      st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
+      own = ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)e2);
+    }
+    s_select.own[lane] = own;
+  }
+  if (wave == 0) select_publish(L, r_t, r_e0, tag, s_select);
+  __builtin_amdgcn_s_setprio(0);
+}
+
 template <bool F16X, int M, int MAXC>
 __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L) {
-  constexpr int MAXX = MAXC == 3 ? 2 : 4;  // 16-byte pieces of x per thread (router)
   extern __shared__ __align__(16) uint8_t dsm[];
   __shared__ float red[kNW][2][64];
   __shared__ __align__(16) uint32_t hpl[kNW][M][3][32];  // h planes as bf16 pairs
@@ -553,82 +653,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   if (b < T * nrb) {
     // ---------------- router rows and the selection of the token.  They
     // head the chain of dependent steps, so these blocks do nothing else.
-    if (!given) {
-      __builtin_amdgcn_s_setprio(1);
-      const int r_t = b / nrb, r_e0 = (b - r_t * nrb) * kRows;
-      const int nch = D / 16;
-      float *sx = (float *)dsm;   // x as fp32 [D]
-      float *sxs = sx + D;        // 16-column sums [D/16]
-      float *rred = sxs + nch;    // partial logits [kKL][kRows]
-      const int rr = tid % kRows, kl = tid / kRows;  // chunks kl, kl + kKL, ... of row rr
-      u32x4 xr[MAXX], rq[MAXC];
-      uint32_t rmw[MAXC];
-      const uint16_t *x = (const uint16_t *)L.x;
-      const gptr<u32x4> xt = as_global((const u32x4 *)(x + (size_t)r_t * D));
-#pragma unroll
-      for (int i = 0; i < MAXX; ++i) xr[i] = xt[min(tid + i * kThreads, D / 8 - 1)];
-      const int e = min(r_e0 + rr, E - 1);
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        const int c = min(kl + i * kKL, nch - 1);
-        rq[i] = as_global((const u32x4 *)L.rcodes)[(size_t)c * E + e];
-        rmw[i] = as_global(L.rmeta)[(size_t)c / 4 * E + e];
-      }
-#pragma unroll
-      for (int i = 0; i < MAXX; ++i) {
-        const int c = tid + i * kThreads;
-        if (c < D / 8) {
-          const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            sx[8 * c + 2 * m] = x_to_f32<F16X>(w[m] & 0xFFFFu);
-            sx[8 * c + 2 * m + 1] = x_to_f32<F16X>(w[m] >> 16);
-          }
-        }
-      }
-      __syncthreads();
-      for (int i = tid; i < nch; i += kThreads) {
-        float s = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s += sx[16 * i + j];
-        sxs[i] = s;
-      }
-      __syncthreads();
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        const int c = kl + i * kKL;
-        if (c < nch) {
-          const float sc = f16_to_f32(rmw[i]), bi = f16_to_f32(rmw[i] >> 16);
-          const uint32_t w[4] = {rq[i].x, rq[i].y, rq[i].z, rq[i].w};
-          const float *xv = sx + c * 16;
-          float d = 0.0f;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-              d = fmaf(xv[4 * u + bb], (float)((w[u] >> (8 * bb)) & 0xFFu), d);
-          acc = fmaf(sc, d, acc);
-          acc = fmaf(bi, sxs[c], acc);
-        }
-      }
-      rred[kl * kRows + rr] = acc;
-      __syncthreads();
-      if (wave == 0 && lane < kRows) {
-        float s = 0.0f;
-        for (int j = 0; j < kKL; ++j) s += rred[j * kRows + lane];
-        const int e2 = r_e0 + lane;
-        uint64_t own = 0;  // below every real key
-        if (e2 < E) {
-          if (L.logit_bias) s += L.logit_bias[e2];
-          st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
-          own = ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)e2);
-        }
-        s_select.own[lane] = own;
-      }
-      if (wave == 0) select_publish(L, r_t, r_e0, tag, s_select);
-      __builtin_amdgcn_s_setprio(0);
-    }
+    if (!given) router_role<F16X, MAXC>(L, b, tag, dsm, s_select);
   } else if (b >= L.NR) {
     // ---------------- shared expert: its gate/up tiles and its part of the
     // down projection; nothing waits on the routing
@@ -789,9 +814,264 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     for (int j = b; j < kMaxLayerGrid; j += L.grid_full) st_dev(L.bep + j, tag);
 }
 
+// ---------------------------------------------------------------- one token, full-K gate/up blocks
+//
+// The variant for one token.  Each gate/up block owns a whole hidden tile
+// (64 rows of one selected expert or of the shared expert, all column
+// groups), so it finishes h = gelu(gate) * up itself: no split reduction
+// and no hand-off of partial sums.  Its waves stream groups wave, wave + 4,
+// ... through a register ring (kRs groups per wave, the next kRs - 1 in
+// flight), which bounds the bytes in flight per block instead of requesting
+// everything at once: a queue of tens of megabytes in front of the memory
+// controllers would delay every hand-off behind it.
+//   router blocks [0, nR);  routed gate/up [nR, nR + n_rt);  routed down
+//   splits [.., NR);  shared gate/up [NR, NR + n_st);  shared down splits.
+constexpr int kRs = 4;
+
+struct GluStage {
+  u32x4 g0, g1, u0, u1;
+  uint32_t mg, mu;
+};
+
+// full-K gate/up of hidden rows rb * 64 + lane of `blob` (hidden width F);
+// the activation pairs and 64-column sums of all groups are in s_xp, s_xs.
+// NG > 0: exactly NG groups per wave, straight-line code (the waits then
+// cover exactly the group each step needs); NG = 0: any count, a loop.
+template <bool F16X, int NG>
+__device__ __forceinline__ void glu_full(const LayerLaunch &L, const uint8_t *blob, int F, int rb,
+                                         size_t hrow, const uint32_t *s_xp, const float *s_xs,
+                                         float (&red)[kNW][2][64], int wave, int lane,
+                                         uint32_t tag) {
+  const int D = L.D, G = D / 64;
+  const int j = rb * 64 + lane;
+  const BlobLayout BL = blob_layout(D, F);
+  const gptr<u32x4> gc = as_global((const u32x4 *)(blob + BL.gate_codes) + j);
+  const gptr<u32x4> uc = as_global((const u32x4 *)(blob + BL.up_codes) + j);
+  const gptr<uint32_t> gm = as_global((const uint32_t *)(blob + BL.gate_meta) + j);
+  const gptr<uint32_t> um = as_global((const uint32_t *)(blob + BL.up_meta) + j);
+  const int ng = NG > 0 ? NG : (G - wave + kNW - 1) / kNW;  // groups wave, wave + 4, ...
+  auto issue = [&](GluStage &S, int i) {
+    const int g = wave + kNW * min(i, ng - 1);  // past the end: repeat, weight 0
+    const size_t c0 = (size_t)(2 * g) * F;
+    S.g0 = gc[c0];
+    S.g1 = gc[c0 + F];
+    S.u0 = uc[c0];
+    S.u1 = uc[c0 + F];
+    S.mg = gm[(size_t)g * F];
+    S.mu = um[(size_t)g * F];
+  };
+  const bool xa_lane = (lane & 15) == 4 * (lane >> 4);
+  const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
+  float accg = 0.0f, accu = 0.0f;
+  GluStage ring[kRs];
+#pragma unroll
+  for (int s = 0; s < kRs - 1; ++s) issue(ring[s], s);
+  constexpr int kRounds = NG > 0 ? (NG + kRs - 1) / kRs : 1;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+  for (int i0 = r * kRs; i0 < (NG > 0 ? (r + 1) * kRs : ng); i0 += kRs) {
+#pragma unroll
+    for (int s = 0; s < kRs; ++s) {
+      const int i = i0 + s;
+      if (NG > 0 && i >= NG) break;  // straight-line form: no steps past the last group
+      if (NG == 0 || i + kRs - 1 < NG) issue(ring[(s + kRs - 1) % kRs], i + kRs - 1);
+      const GluStage &S = ring[s];
+      const bool live = i < ng;
+      const int g = wave + kNW * min(i, ng - 1);
+      f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
+      const uint32_t wg[8] = {S.g0.x, S.g0.y, S.g0.z, S.g0.w, S.g1.x, S.g1.y, S.g1.z, S.g1.w};
+      const uint32_t wu[8] = {S.u0.x, S.u0.y, S.u0.z, S.u0.w, S.u1.x, S.u1.y, S.u1.z, S.u1.w};
+      u32x4 a[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
+      if (xa_lane) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&s_xp[32 * g + 4 * w];
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        dg = mma16<F16X>(a[w], code_pairs(wg[w], magic), dg);
+        du = mma16<F16X>(a[w], code_pairs(wu[w], magic), du);
+      }
+      const float xsg = s_xs[g];
+      const float sg = live ? f16_to_f32(S.mg) : 0.0f, bg = live ? f16_to_f32(S.mg >> 16) : 0.0f;
+      const float su = live ? f16_to_f32(S.mu) : 0.0f, bu = live ? f16_to_f32(S.mu >> 16) : 0.0f;
+      accg = fmaf(sg, dg[0], accg);
+      accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsg, accg);
+      accu = fmaf(su, du[0], accu);
+      accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsg, accu);
+    }
+  }
+  red[wave][0][lane] = accg;
+  red[wave][1][lane] = accu;
+  __syncthreads();
+  if (wave == 0) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      g += red[w][0][lane];
+      u += red[w][1][lane];
+    }
+    st_dev64(L.hg + hrow + lane, tagged(__float_as_uint(gelu_tanh(g) * u), tag));
+  }
+}
+
+// activation pairs (x[8w + m], x[8w + m + 4]) and 64-column sums of all
+// column groups of token t into s_xp [G][32], s_xs [G]
+template <bool F16X>
+__device__ __forceinline__ void stage_x_all(const LayerLaunch &L, int t, uint32_t *s_xp,
+                                            float *s_xs) {
+  const int tid = threadIdx.x, D = L.D;
+  constexpr int kMaxXV = 8192 / 8 / kThreads;  // 16-byte pieces of x per thread
+  const gptr<u32x4> xr = as_global((const u32x4 *)((const uint16_t *)L.x + (size_t)t * D));
+  u32x4 xq[kMaxXV];
+#pragma unroll
+  for (int i = 0; i < kMaxXV; ++i) xq[i] = xr[min(tid + i * kThreads, D / 8 - 1)];
+  // piece i: 8-column blocks i * kThreads + tid (8 threads per group)
+#pragma unroll
+  for (int i = 0; i < kMaxXV; ++i)
+    if (i * kThreads < D / 8)
+      stage_x<F16X>(xq[i], D / 8 - i * kThreads, tid, s_xp + 4 * i * kThreads, s_xs + i * kThreads / 8);
+}
+
+template <bool F16X, int M, int MAXC>
+__global__ __launch_bounds__(kThreads, 3) void decode_stream_kernel(LayerLaunch L) {
+  extern __shared__ __align__(16) uint8_t dsm[];
+  __shared__ float red[kNW][2][64];
+  __shared__ __align__(16) uint32_t hpl[kNW][M][3][32];
+  __shared__ const uint8_t *s_blob[kMaxK];
+  __shared__ float s_gate[kMaxK];
+  __shared__ SelectLds s_select;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = L.blk0 + blockIdx.x;
+  const int D = L.D, E = L.E, k = L.k;
+  const int NB = D / 64, G = D / 64;
+  const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
+  const uint32_t tag = as_const(L.bep)[b] + 1u;
+  const bool given = L.given_blob != nullptr;
+  const int nR = (E + kRows - 1) / kRows;
+  const int n_rt = k * Gf;
+  const int r_down0 = nR + n_rt;
+  const int dw = max(wave - 1, 0);  // down units: waves 1..3
+
+  uint32_t *s_xp = (uint32_t *)dsm;           // gate/up blocks: [G][32]
+  float *s_xs = (float *)(dsm + 128 * G);     // [G]
+  const void **s_table = (const void **)(dsm + L.table_off);
+
+  if (b < nR) {
+    if (!given) router_role<F16X, MAXC>(L, b, tag, dsm, s_select);
+  } else if (b < r_down0 || (b >= L.NR && b < L.NR + Gs)) {
+    // ---------------- a whole gate/up tile
+    const bool routed = b < r_down0;
+    const int tile = routed ? b - nR : n_rt + (b - L.NR);
+    const Tile gt = glu_tile(L, tile);
+    const uint8_t *blob = nullptr;
+    if (routed && !given) {
+      constexpr int kTab = kMaxLayerE / kThreads;
+      const void *tb[kTab];
+#pragma unroll
+      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
+      stage_x_all<F16X>(L, 0, s_xp, s_xs);
+#pragma unroll
+      for (int i = 0; i < kTab; ++i)
+        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
+      __syncthreads();
+      const bool report = gt.j == 0 && gt.rb == 0;
+      if (wave == 0) wait_selection(L, 0, tile % L.sel_copies, tag, s_table, s_blob, s_gate, report);
+      __syncthreads();
+      blob = s_blob[gt.j];
+    } else {
+      stage_x_all<F16X>(L, 0, s_xp, s_xs);
+      blob = routed ? (const uint8_t *)L.given_blob[gt.j] : (const uint8_t *)as_global(L.sblobs)[0];
+      __syncthreads();
+    }
+    if (G == 44)
+      glu_full<F16X, 11>(L, blob, gt.F, gt.rb, gt.hoff + (size_t)gt.rb * 64, s_xp, s_xs, red, wave,
+                         lane, tag);
+    else
+      glu_full<F16X, 0>(L, blob, gt.F, gt.rb, gt.hoff + (size_t)gt.rb * 64, s_xp, s_xs, red, wave,
+                        lane, tag);
+  } else {
+    // ---------------- a split of the down projection (routed or shared)
+    const bool routed = b < L.NR;
+    const int sb = routed ? b - r_down0 : b - L.NR - Gs;
+    const int KSx = routed ? L.KSdr : L.KSds;
+    const int Ux = routed ? k * Gf : Gs;
+    const int ot = sb / KSx, ksd = sb % KSx;
+    const int n = ot * 64 + lane;
+    const int u0 = ksd * Ux / KSx, u1 = (ksd + 1) * Ux / KSx;
+    const uint8_t *sblob = routed ? nullptr : (const uint8_t *)as_global(L.sblobs)[0];
+    if (routed) {
+      if (!given) {
+        constexpr int kTab = kMaxLayerE / kThreads;
+        const void *tb[kTab];
+#pragma unroll
+        for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
+#pragma unroll
+        for (int i = 0; i < kTab; ++i)
+          if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
+        __syncthreads();
+        if (wave == 0) wait_selection(L, 0, sb % L.sel_copies, tag, s_table, s_blob, s_gate, false);
+      } else if (tid < k) {
+        s_blob[tid] = (const uint8_t *)L.given_blob[tid];
+        s_gate[tid] = L.given_gates[tid];
+      }
+      __syncthreads();
+    }
+    DownRegs<M> dr;
+    auto load_down = [&]() {
+      if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+          const int u = min(u0 + dw + i * kDW, u1 - 1);
+          if (routed) {
+            const int jj = u / Gf;
+            issue_down(dr, i, s_blob[jj], D, L.F, u - jj * Gf, n);
+          } else {
+            issue_down(dr, i, sblob, D, L.Fs, u, n);
+          }
+        }
+      }
+    };
+    size_t hp[M];
+    float gate[M];
+    bool use[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const int u = min(u0 + dw + i * kDW, u1 - 1);
+      use[i] = wave > 0 && u0 + dw + i * kDW < u1;
+      if (routed) {
+        const int jj = u / Gf;
+        gate[i] = s_gate[jj];
+        hp[i] = (size_t)jj * L.F + (size_t)(u - jj * Gf) * 64;
+      } else {
+        gate[i] = 1.0f;
+        hp[i] = (size_t)k * L.F + (size_t)u * 64;
+      }
+    }
+    if (!L.down_late) load_down();
+    auto late = [&]() {
+      if (L.down_late) load_down();
+    };
+    down_and_combine<M>(L, dr, hp, gate, use, hpl, red, ot, (size_t)n, wave, lane, tag, late);
+  }
+
+  // ---------------- advance every copy of the epoch (block b: b, b + grid, ...)
+  if (tid == 0)
+    for (int j = b; j < kMaxLayerGrid; j += L.grid_full) st_dev(L.bep + j, tag);
+}
+
 using KernelFn = void (*)(LayerLaunch);
 template <bool F16X, int MAXC>
-KernelFn pick(int m) {
+KernelFn pick(int m, bool stream) {
+  if (stream) {
+    if (m == 2) return decode_stream_kernel<F16X, 2, MAXC>;
+    if (m == 3) return decode_stream_kernel<F16X, 3, MAXC>;
+    if (m == 4) return decode_stream_kernel<F16X, 4, MAXC>;
+    return nullptr;
+  }
   if (m == 2) return decode_layer_kernel<F16X, 2, MAXC>;
   if (m == 3) return decode_layer_kernel<F16X, 3, MAXC>;
   if (m == 4) return decode_layer_kernel<F16X, 4, MAXC>;
@@ -799,19 +1079,20 @@ KernelFn pick(int m) {
 }
 KernelFn pick_layer(const LayerLaunch &L, int m) {
   const bool small_d = L.D <= 3072;  // router chunks per thread: 3 (D <= 3072) or 8
-  if (L.f16x) return small_d ? pick<true, 3>(m) : pick<true, 8>(m);
-  return small_d ? pick<false, 3>(m) : pick<false, 8>(m);
+  const bool st = L.stream != 0;
+  if (L.f16x) return small_d ? pick<true, 3>(m, st) : pick<true, 8>(m, st);
+  return small_d ? pick<false, 3>(m, st) : pick<false, 8>(m, st);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int g_layer_capacity[2][2][3][64];  // [f16x][MAXC 3/8][m - 2][device]
+int g_layer_capacity[2][2][2][3][64];  // [stream][f16x][MAXC 3/8][m - 2][device]
 
 }  // namespace
 
 int layer_m(const LayerLaunch &L) {
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
-  int m = ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
+  int m = L.stream ? 2 : ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
   m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), kNW - 1));  // down units: 3 waves
   if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), kNW - 1));
   return m < 2 ? 2 : m;
@@ -822,22 +1103,24 @@ int layer_m(const LayerLaunch &L) {
 int layer_routed_blocks(const LayerLaunch &L) {
   const int n_rt = L.T * L.k * (L.F / 64);
   const int r = L.T * ((L.E + kRows - 1) / kRows);  // router blocks come first
+  if (L.stream) return r + n_rt + L.T * (L.D / 64) * L.KSdr;
   return r + max(n_rt * L.KSg, L.T * (L.D / 64) * L.KSdr);
 }
 int layer_shared_blocks(const LayerLaunch &L) {
   const int n_st = L.n_gtiles - L.T * L.k * (L.F / 64);
+  if (L.stream) return n_st + L.T * (L.D / 64) * L.KSds;
   return max(n_st * L.KSg, L.T * (L.D / 64) * L.KSds);
 }
 int layer_grid(const LayerLaunch &L) { return layer_routed_blocks(L) + layer_shared_blocks(L); }
 
-size_t layer_smem(const LayerLaunch &L) {
-  // router staging: x as fp32, 16-column sums, partial logits; then the table
-  const size_t stage = sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads);
-  return align_up(stage) + sizeof(void *) * (size_t)L.E;
-}
 size_t layer_table_off(const LayerLaunch &L) {
-  return align_up(sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads));
+  // router staging: x as fp32, 16-column sums, partial logits; full-K gate/up
+  // blocks: activation pairs and 64-column sums of every group
+  size_t stage = sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads);
+  if (L.stream) stage = max(stage, (size_t)132 * (L.D / 64));
+  return align_up(stage);
 }
+size_t layer_smem(const LayerLaunch &L) { return layer_table_off(L) + sizeof(void *) * (size_t)L.E; }
 
 hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
   *cap = 0;
@@ -848,7 +1131,7 @@ hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int &slot = g_layer_capacity[L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1][m - 2][dev];
+  int &slot = g_layer_capacity[L.stream ? 1 : 0][L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1][m - 2][dev];
   const size_t smem = layer_smem(L);
   if (smem > 64 * 1024) return hipSuccess;
   if (!slot) {

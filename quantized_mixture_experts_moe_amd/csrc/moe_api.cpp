@@ -190,9 +190,29 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->n_gtiles = n_gtiles;
   L->shared_wait = tuning().layer_shared_wait;
   L->down_late = tuning().layer_down_late;
+  bool found = false;
+  L->stream = tuning().layer == 2 && T == 1;
+  if (L->stream) {
+    // one token: whole gate/up tiles per block; the most down splits whose
+    // grid is still resident
+    const int U = k * (F / 64), Us = Fs / 64;
+    const int hi = tuning().layer_ksd > 0 ? tuning().layer_ksd : (U < 16 ? U : 16);
+    const int lo = tuning().layer_ksd > 0 ? tuning().layer_ksd : 1;
+    for (int ksdr = hi; ksdr >= lo && !found; --ksdr) {
+      L->KSg = 1;
+      L->KSdr = ksdr;
+      L->KSds = Us ? (ksdr * Us + U - 1) / U : 0;
+      L->NR = layer_routed_blocks(*L);
+      if (layer_m(*L) > 4) break;  // fewer splits only make it larger
+      const int grid = layer_grid(*L);
+      int cap = 0;
+      if (layer_capacity(*L, &cap) != hipSuccess) return false;
+      found = grid <= cap && grid <= kMaxLayerGrid;
+    }
+    if (!found) L->stream = 0;
+  }
   // the most gate/up splits (and with them down splits) whose grid is still
   // resident all at once: more, smaller blocks overlap more of the transfer
-  bool found = false;
   const int ksg_hi = tuning().layer_ksg > 0 ? tuning().layer_ksg : (G < kMaxKS ? G : kMaxKS);
   const int ksg_lo = tuning().layer_ksg > 0 ? tuning().layer_ksg : 1;
   for (int ksg = ksg_hi; ksg >= ksg_lo && !found; --ksg) {
@@ -218,7 +238,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->lid = (k + 15) / 16 * 16;
   L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * 2 * L->lid, 8);
   L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
-  L->hu = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
+  L->hu = L->stream ? nullptr : c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   if (kTaggedOff + c.off > kErrOff) return false;
   L->table_off = layer_table_off(*L);
   L->err = w.err;

@@ -200,6 +200,7 @@ struct LayerLaunch {
   int blk0, grid_full;                // this launch covers blocks [blk0, blk0 + grid)
   int shared_wait;                    // shared blocks load after the router logits are out
   int down_late;                      // down weights: 0 with gate/up, 1 after its reduction, 2 after its arithmetic
+  int stream;                         // one token, whole gate/up tiles per block (hu unused)
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;

@@ -347,7 +347,7 @@ def test_pool_streamed_equals_resident_and_trace():
     pool.close()
 
 
-_PATHS = {"layer": {"layer": 1}, "fused": {"layer": 0, "fused": 1},
+_PATHS = {"layer": {"layer": 1}, "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
           "three": {"layer": 0, "fused": 0}}
 _DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1}
 
@@ -357,10 +357,11 @@ def _tune(**kv):
         moe.moe_set_tuning(key, v)
 
 
-@pytest.mark.parametrize("path", ["layer", "fused", "three"])
+@pytest.mark.parametrize("path", ["layer", "stream", "fused", "three"])
 def test_layer_forward_decode_all_paths(path):
-    """The one-launch layer, the router + one-launch expert phase, and the
-    router + three expert kernels all meet the bar on decode tokens."""
+    """The one-launch layer (split or whole gate/up tiles), the router +
+    one-launch expert phase, and the router + three expert kernels all meet
+    the bar on decode tokens."""
     _case(f"layer_forward decode path={path}")
     L = dev_layer("decode")
     cfg = L.cfg
@@ -387,14 +388,15 @@ def test_layer_launch_agrees_with_expert_phase_launch():
     try:
         for tok in range(4):
             xb = gen.activations(9, 0, tok, 1, cfg.D, cfg.x_dtype)
-            _tune(layer=1)
-            a, ia, ga = _layer_gpu(L, xb, cfg.k, bias)
             _tune(layer=0)
             b, ib, gb = _layer_gpu(L, xb, cfg.k, bias)
-            assert np.array_equal(ia, ib) and np.array_equal(ga, gb)
-            r = rel_l2(a.cpu().numpy(), b.cpu().numpy())
-            print(f"    token {tok}: rel_l2(layer, expert phase) = {r:.2e}")
-            assert r < 1e-5, tok
+            for variant in (1, 2):
+                _tune(layer=variant)
+                a, ia, ga = _layer_gpu(L, xb, cfg.k, bias)
+                assert np.array_equal(ia, ib) and np.array_equal(ga, gb)
+                r = rel_l2(a.cpu().numpy(), b.cpu().numpy())
+                print(f"    token {tok}: rel_l2(layer {variant}, expert phase) = {r:.2e}")
+                assert r < 1e-5, tok
     finally:
         _tune(**_DEFAULTS)
 
@@ -411,16 +413,17 @@ def test_layer_epochs_across_grid_sizes():
     x = x_dev(xb, cfg.x_dtype)
     first = {}
     try:
-        for it, (ksg, ksd) in enumerate([(0, 0), (3, 8), (0, 0), (8, 16), (2, 0), (0, 0)] * 3):
-            _tune(layer_ksg=ksg, layer_ksd=ksd)
+        plan = [(1, 0, 0), (1, 3, 8), (2, 0, 0), (1, 8, 16), (2, 0, 6), (1, 2, 0), (2, 0, 0)] * 3
+        for it, (variant, ksg, ksd) in enumerate(plan):
+            _tune(layer=variant, layer_ksg=ksg, layer_ksd=ksd)
             out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
             ids = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
             moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, out, ws, ids_out=ids)
             torch.cuda.synchronize()
-            if (ksg, ksd) in first:
-                assert torch.equal(first[(ksg, ksd)], out), (it, ksg, ksd)
+            if (variant, ksg, ksd) in first:
+                assert torch.equal(first[(variant, ksg, ksd)], out), (it, variant, ksg, ksd)
             else:
-                first[(ksg, ksd)] = out
+                first[(variant, ksg, ksd)] = out
                 _check_layer(L, xb, out.cpu().numpy(), ids.cpu().numpy(), cfg.k)
         assert ws.timeouts() == 0
     finally:
@@ -442,11 +445,13 @@ def test_layer_forward_prefill_ragged_chunk():
     _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=toks[:6] + toks[-6:] + [76])
 
 
-def test_pool_decode_shapes_streamed_equals_resident():
+@pytest.mark.parametrize("variant", [1, 2])
+def test_pool_decode_shapes_streamed_equals_resident(variant):
     """Decode-shaped layers, 16 HBM slots each: streamed output is bitwise the
     resident output, the pool's hit/miss counts follow the LFU model, and a
-    sampled token matches the oracle."""
-    _case("pool streamed vs resident (decode shapes, 2 layers, 16 slots)")
+    sampled token matches the oracle (both one-launch layer variants)."""
+    _case(f"pool streamed vs resident (decode shapes, 2 layers, 16 slots, layer {variant})")
+    _tune(layer=variant)
     cfg = gen.CONFIGS["decode"]
     layers = [dev_layer("decode", seed=0, layer=l) for l in range(2)]
     host = [torch.from_numpy(L.lw.experts).pin_memory() for L in layers]
@@ -476,3 +481,4 @@ def test_pool_decode_shapes_streamed_equals_resident():
     st = pool.stats()
     assert st["misses"] == misses and st["lookups"] == 10 * 2 * cfg.k
     pool.close()
+    _tune(**_DEFAULTS)
