@@ -94,16 +94,23 @@ __device__ __forceinline__ int wait_rows(const uint64_t *p, size_t stride, int n
 // Wave-wide: polls one word per lane (p, or nothing where p is null) until
 // each carries `tag`.  Waiting on one word per producer store keeps the
 // polling traffic small; the data is read (and checked) afterwards.
-__device__ __forceinline__ int wait_hint(const uint64_t *p, uint32_t tag, uint32_t *err) {
+// Two polls are in flight: the next one is issued before the previous one is
+// checked, so a store is seen about half a round trip after it lands rather
+// than a whole one.  Lanes with `active` false poll p too (any valid word)
+// and count as done.
+__device__ __forceinline__ int wait_hint(const uint64_t *p, bool active, uint32_t tag,
+                                         uint32_t *err) {
   const int lane = threadIdx.x & 63;
+  uint64_t w = ld_dev64(p);
   for (long s = 0;; ++s) {
-    const bool ok = !p || has_tag(ld_dev64(p), tag);
-    if (__all(ok)) return (int)s;
+    __builtin_amdgcn_s_sleep(1);
+    const uint64_t nx = ld_dev64(p);
+    if (__all(!active || has_tag(w, tag))) return (int)s;
     if (s > kSpin) {
       if (lane == 0) add_dev(err, 1u);
       return (int)s;
     }
-    __builtin_amdgcn_s_sleep(2);
+    w = nx;
   }
 }
 
@@ -179,25 +186,32 @@ __device__ void select_publish(const LayerLaunch &L, int t, int e0, uint32_t tag
   constexpr int LPC = 64 / kRows;  // lanes per candidate when publishing
   const int lane = threadIdx.x & 63, E = L.E, k = L.k;
   const uint64_t *lg = L.rlog + (size_t)t * E;
-  uint64_t key[NV];
+  // two polls in flight (see wait_hint); lanes past E poll expert E - 1
+  uint64_t w[NV], nx[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) w[j] = ld_dev64(lg + min(lane + 64 * j, E - 1));
   for (long s = 0;; ++s) {
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) nx[j] = ld_dev64(lg + min(lane + 64 * j, E - 1));
     bool ok = true;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      key[j] = 0;
-      const int e = lane + 64 * j;
-      if (e < E) {
-        const uint64_t w = ld_dev64(lg + e);
-        ok = ok && has_tag(w, tag);
-        key[j] = ((uint64_t)order_key(__uint_as_float((uint32_t)w)) << 32) | (uint64_t)(~(uint32_t)e);
-      }
-    }
+    for (int j = 0; j < NV; ++j) ok = ok && (lane + 64 * j >= E || has_tag(w[j], tag));
     if (__all(ok)) break;
     if (s > kSpin) {
       if (lane == 0) add_dev(L.err, 1u);
       break;
     }
-    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) w[j] = nx[j];
+  }
+  uint64_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? ((uint64_t)order_key(__uint_as_float((uint32_t)w[j])) << 32) |
+                         (uint64_t)(~(uint32_t)e)
+                   : 0;
   }
   // rank of candidate c = number of keys above its key (keys past E are 0)
   const int c = lane / LPC, p = lane % LPC, e = e0 + c;
@@ -213,7 +227,7 @@ __device__ void select_publish(const LayerLaunch &L, int t, int e0, uint32_t tag
   if (e < E && r < (uint32_t)k) {
     const uint32_t vbits = __float_as_uint(key_value((uint32_t)(S.own[c] >> 32)));
     for (int cp = p; cp < L.sel_copies; cp += LPC) {
-      uint64_t *line = L.sel + ((size_t)t * L.sel_copies + cp) * 2 * L.lid;
+      uint64_t *line = L.sel + ((size_t)t * L.sel_copies + cp) * L.sel_stride;
       st_dev64(line + r, tagged((uint32_t)e, tag));
       st_dev64(line + L.lid + r, tagged(vbits, tag));
     }
@@ -228,21 +242,20 @@ __device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t t
                                const void *const *table, const uint8_t **blob_out,
                                float *gate_out, bool report) {
   const int lane = threadIdx.x & 63, k = L.k;
-  const uint64_t *line = L.sel + ((size_t)t * L.sel_copies + copy) * 2 * L.lid;
-  uint64_t wi = 0, wg = 0;
+  const uint64_t *line = L.sel + ((size_t)t * L.sel_copies + copy) * L.sel_stride;
+  // two polls in flight (see wait_hint); lanes past k poll place k - 1
+  const int r = min(lane, k - 1);
+  uint64_t wi = ld_dev64(line + r), wg = ld_dev64(line + L.lid + r);
   for (long s = 0;; ++s) {
-    bool ok = true;
-    if (lane < k) {
-      wi = ld_dev64(line + lane);
-      wg = ld_dev64(line + L.lid + lane);
-      ok = has_tag(wi, tag) && has_tag(wg, tag);
-    }
-    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(1);
+    const uint64_t ni = ld_dev64(line + r), ng = ld_dev64(line + L.lid + r);
+    if (__all(lane >= k || (has_tag(wi, tag) && has_tag(wg, tag)))) break;
     if (s > kSpin) {
       if (lane == 0) add_dev(L.err, 1u);
       break;
     }
-    __builtin_amdgcn_s_sleep(1);
+    wi = ni;
+    wg = ng;
   }
   const uint32_t id = min((uint32_t)wi, (uint32_t)L.E - 1);
   if (lane < k) blob_out[lane] = (const uint8_t *)table[id];
@@ -435,13 +448,14 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
   // lanes 2i, 2i + 1 poll one word of unit i's rows, then the values are
   // read (checked)
   const bool single = L.hu == nullptr;
-  const uint64_t *hint = nullptr;
+  const uint64_t *hint = L.hg + hp[0];
+  bool active = false;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
-    if (use[i] && lane == 2 * i) hint = L.hg + hp[i];
-    if (use[i] && lane == 2 * i + 1 && !single) hint = L.hu + hp[i];
+    if (use[i] && lane == 2 * i) hint = L.hg + hp[i], active = true;
+    if (use[i] && lane == 2 * i + 1 && !single) hint = L.hu + hp[i], active = true;
   }
-  wait_hint(hint, tag, L.err);
+  wait_hint(hint, active, tag, L.err);
   on_hint();
   float hv0[M];
   for (long s = 0;; ++s) {
@@ -541,7 +555,7 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
 // token (every router block publishes its winners).  They head the chain of
 // dependent steps, so these blocks do nothing else.
 template <bool F16X, int MAXC>
-__device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_t tag, uint8_t *dsm,
+__device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_t &tag, uint8_t *dsm,
                                             SelectLds &s_select) {
   constexpr int MAXX = MAXC == 3 ? 2 : 4;  // 16-byte pieces of x per thread
   const int tid = threadIdx.x, lane = tid & 63;
@@ -568,6 +582,10 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
     rq[i] = as_global((const u32x4 *)L.rcodes)[(size_t)c * E + e];
     rmw[i] = as_global(L.rmeta)[(size_t)c / 4 * E + e];
   }
+  // the epoch (a vector load, after the loads above) and the logit bias
+  tag = __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
+  float lbias = 0.0f;
+  if (L.logit_bias && wave == 0 && lane < kRows) lbias = L.logit_bias[min(r_e0 + lane, E - 1)];
 #pragma unroll
   for (int i = 0; i < MAXX; ++i) {
     const int c = tid + i * kThreads;
@@ -614,7 +632,7 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
     const int e2 = r_e0 + lane;
     uint64_t own = 0;  // below every real key
     if (e2 < E) {
-      if (L.logit_bias) s += L.logit_bias[e2];
+      if (L.logit_bias) s += lbias;
       st_dev64(L.rlog + (size_t)r_t * E + e2, tagged(__float_as_uint(s), tag));
       own = ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)e2);
     }
@@ -637,15 +655,23 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = L.blk0 + blockIdx.x;
   const int D = L.D, E = L.E, k = L.k, T = L.T;
   const int G = D / 64, NB = D / 64;
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
-  const uint32_t tag = as_const(L.bep)[b] + 1u;
-
   // roles: router blocks [0, T nrb), routed blocks [T nrb, NR), shared
-  // blocks [NR, grid).  Each role runs straight through its own code.
+  // blocks [NR, grid).  Each role runs straight through its own code.  With
+  // order 1 the shared blocks are dispatched right after the router blocks
+  // (their loads depend on nothing and then drain before the routing's
+  // hand-offs); b is the logical index either way.
   const int nrb = (E + kRows - 1) / kRows;
+  const int p = blockIdx.x, nr0 = T * nrb, ns = L.grid_full - L.NR;
+  const int b = !L.order ? L.blk0 + p : p < nr0 ? p : p < nr0 + ns ? L.NR + (p - nr0) : p - ns;
+  // the epoch is read by each role after its first loads are issued, with a
+  // vector load (an atomic one): nothing waits for it before its first use
+  uint32_t tag = 0;
+  auto load_tag = [&]() {
+    tag = __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
+  };
   const bool given = L.given_blob != nullptr;  // selection from the caller
   const int n_rt = T * k * Gf;                 // routed gate/up tiles, then the shared ones
   const int dw = max(wave - 1, 0);             // down units: waves 1..3 (wave 0 mirrors 1)
@@ -653,7 +679,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   if (b < T * nrb) {
     // ---------------- router rows and the selection of the token.  They
     // head the chain of dependent steps, so these blocks do nothing else.
-    if (!given) router_role<F16X, MAXC>(L, b, tag, dsm, s_select);
+    if (!given)
+      router_role<F16X, MAXC>(L, b, tag, dsm, s_select);
+    else
+      load_tag();
   } else if (b >= L.NR) {
     // ---------------- shared expert: its gate/up tiles and its part of the
     // down projection; nothing waits on the routing
@@ -672,15 +701,16 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
 
     const uint8_t *sblob = (const uint8_t *)as_global(L.sblobs)[0];
     const u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    load_tag();
     if (L.shared_wait && !given) {
       // hold the weight loads until the router logits are out: the router's
       // loads head the chain of dependent steps
       if (wave == 0) {
         for (int base = 0; base < T * nrb; base += 64) {
           const int q = base + lane;
-          const uint64_t *p =
-              q < T * nrb ? L.rlog + (size_t)(q / nrb) * E + (size_t)(q % nrb) * kRows : nullptr;
-          wait_hint(p, tag, L.err);
+          const int qq = min(q, T * nrb - 1);
+          wait_hint(L.rlog + (size_t)(qq / nrb) * E + (size_t)(qq % nrb) * kRows, q < T * nrb, tag,
+                    L.err);
         }
       }
       __syncthreads();
@@ -739,6 +769,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     const int u0 = ksd * Ur / L.KSdr, u1 = (ksd + 1) * Ur / L.KSdr;
 
     const u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    load_tag();
     const void **s_table = (const void **)(dsm + L.table_off);
     if (!given) {
       constexpr int kTab = kMaxLayerE / kThreads;
@@ -949,7 +980,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_stream_kernel(LayerLaunch 
   const int D = L.D, E = L.E, k = L.k;
   const int NB = D / 64, G = D / 64;
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
-  const uint32_t tag = as_const(L.bep)[b] + 1u;
+  uint32_t tag =
+      __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
   const bool given = L.given_blob != nullptr;
   const int nR = (E + kRows - 1) / kRows;
   const int n_rt = k * Gf;
@@ -1152,6 +1184,8 @@ hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   L.blk0 = blk0;
   L.grid_full = layer_grid(L);
+  // the block order applies to whole-grid launches only (ranges are logical)
+  if (blk0 != 0 || n != L.grid_full || L.stream) L.order = 0;
   hipLaunchKernelGGL(k, dim3(n), dim3(kThreads), layer_smem(L), s, L);
   return hipGetLastError();
 }

@@ -190,6 +190,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->n_gtiles = n_gtiles;
   L->shared_wait = tuning().layer_shared_wait;
   L->down_late = tuning().layer_down_late;
+  L->order = tuning().layer_order;
   bool found = false;
   L->stream = tuning().layer == 2 && T == 1;
   if (L->stream) {
@@ -234,9 +235,12 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   // tagged words: logits, hidden activations
   Carver c{w.layer + kTaggedOff};
   L->rlog = c.take<uint64_t>((size_t)T * E, 8);
-  L->sel_copies = 16;  // copies of each selection line (spread the polling)
+  // copies of each selection line (spread the polling)
+  L->sel_copies = min(max(tuning().layer_sel_copies, 1), 256);
   L->lid = (k + 15) / 16 * 16;
-  L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * 2 * L->lid, 8);
+  L->sel_stride = max(tuning().layer_sel_stride, 2 * L->lid);
+  if (L->sel_stride > 4096) L->sel_stride = 4096;
+  L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * L->sel_stride, 8);
   L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   L->hu = L->stream ? nullptr : c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   if (kTaggedOff + c.off > kErrOff) return false;
@@ -321,6 +325,12 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_ksd = value;
   } else if (!strcmp(key, "layer_down_late")) {
     tuning().layer_down_late = value;
+  } else if (!strcmp(key, "layer_order")) {
+    tuning().layer_order = value;
+  } else if (!strcmp(key, "layer_sel_copies")) {
+    tuning().layer_sel_copies = value;
+  } else if (!strcmp(key, "layer_sel_stride")) {
+    tuning().layer_sel_stride = value;
   } else if (!strcmp(key, "layer_shared_wait")) {
     tuning().layer_shared_wait = value;
   } else if (!strcmp(key, "prefill_min_t")) {

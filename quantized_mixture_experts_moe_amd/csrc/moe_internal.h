@@ -81,6 +81,9 @@ struct Tuning {
   int layer_ksd = 0;
   int layer_shared_wait = 0;
   int layer_down_late = 1;
+  int layer_order = 1;
+  int layer_sel_copies = 16;
+  int layer_sel_stride = 0;  // words between selection lines; 0: packed
 };
 Tuning &tuning();
 
@@ -201,6 +204,7 @@ struct LayerLaunch {
   int shared_wait;                    // shared blocks load after the router logits are out
   int down_late;                      // down weights: 0 with gate/up, 1 after its reduction, 2 after its arithmetic
   int stream;                         // one token, whole gate/up tiles per block (hu unused)
+  int order;                          // dispatch order: 0 router, routed, shared; 1 router, shared, routed
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;
@@ -208,8 +212,8 @@ struct LayerLaunch {
   size_t table_off;                   // LDS byte offset of the blob table
   uint32_t *bep;                      // per-block epochs [kMaxLayerGrid]
   uint64_t *rlog;                     // [T][E] tagged logits
-  uint64_t *sel;                      // [T][sel_copies][2][lid] tagged ids, gates
-  int sel_copies, lid;
+  uint64_t *sel;                      // [T][sel_copies] lines of [2][lid] tagged ids, gates
+  int sel_copies, lid, sel_stride;    // sel_stride: words from one line to the next
   uint64_t *hg, *hu;                  // [T*k*F + T*Fs] tagged gelu(gate) and up
   uint64_t *gacc, *dacc;              // split-reduction accumulators (zero between calls)
   uint32_t *gcnt, *dcnt;              // and their counters

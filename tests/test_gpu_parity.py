@@ -347,9 +347,11 @@ def test_pool_streamed_equals_resident_and_trace():
     pool.close()
 
 
-_PATHS = {"layer": {"layer": 1}, "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
+_PATHS = {"layer": {"layer": 1}, "order0": {"layer": 1, "layer_order": 0},
+          "order1": {"layer": 1, "layer_order": 1}, "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
           "three": {"layer": 0, "fused": 0}}
-_DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1}
+_DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1,
+             "layer_order": 1}
 
 
 def _tune(**kv):
@@ -357,7 +359,7 @@ def _tune(**kv):
         moe.moe_set_tuning(key, v)
 
 
-@pytest.mark.parametrize("path", ["layer", "stream", "fused", "three"])
+@pytest.mark.parametrize("path", ["layer", "order0", "order1", "stream", "fused", "three"])
 def test_layer_forward_decode_all_paths(path):
     """The one-launch layer (split or whole gate/up tiles), the router +
     one-launch expert phase, and the router + three expert kernels all meet
@@ -415,7 +417,8 @@ def test_layer_epochs_across_grid_sizes():
     try:
         plan = [(1, 0, 0), (1, 3, 8), (2, 0, 0), (1, 8, 16), (2, 0, 6), (1, 2, 0), (2, 0, 0)] * 3
         for it, (variant, ksg, ksd) in enumerate(plan):
-            _tune(layer=variant, layer_ksg=ksg, layer_ksd=ksd)
+            # the block order changes between calls too (epochs are per logical block)
+            _tune(layer=variant, layer_ksg=ksg, layer_ksd=ksd, layer_order=it % 2)
             out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
             ids = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
             moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, out, ws, ids_out=ids)
