@@ -82,7 +82,7 @@ Workspace carve(void *base, const Dims &d) {
   w.hplanes = c.take<uint16_t>(3 * units, 2);
   w.hsum = c.take<float>(units / 64 + 1, 4);
   w.y = c.take<float>(T * k * (size_t)d.D, 4);
-  w.ys = c.take<float>(T * (size_t)d.D, 4);
+  w.ys = c.take<float>(kMaxSharedSplits * T * (size_t)d.D, 4);
   w.total = c.off;
   return w;
 }
@@ -335,6 +335,8 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_shared_wait = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
+  } else if (!strcmp(key, "route_mfma")) {
+    tuning().route_mfma = value;
   } else {
     return MOE_E_INVALID;
   }
@@ -534,6 +536,9 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     pl.xp = w.xp; pl.xs = w.xs;
     pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;
     pl.hsum = w.hsum; pl.y = w.y; pl.ys = w.ys; pl.out = out; pl.out_dtype = out_dtype;
+    // the shared down projection in as many splits as make its blocks no
+    // longer than a routed expert's
+    pl.sks = shared ? min(kMaxSharedSplits, max(1, (Fs / 64 + F / 64 - 1) / (F / 64))) : 1;
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_prefill_experts(pl, s)));
   }

@@ -76,6 +76,7 @@ struct Tuning {
   int fused_ksg = 0;   // its gate/up and down splits (0: chosen)
   int fused_ksd = 0;
   int prefill_min_t = 16;  // tokens per call from which the grouped matrix-core path runs
+  int route_mfma = 1;      // router of 16 or more tokens on the matrix cores
   int layer = 1;       // one launch for the whole decode layer when it fits
   int layer_ksg = 0;   // its gate/up and down splits (0: chosen)
   int layer_ksd = 0;
@@ -185,9 +186,11 @@ struct PrefillLaunch {
   const void *const *rblobs, *const *sblobs;
   const uint32_t *xp; const float *xs;
   uint16_t *hp; size_t plane;         // h as three bf16 planes of `plane` elements
-  float *hsum, *y, *ys;
+  float *hsum, *y, *ys;                // ys: sks partial sums of the shared expert, [sks][T][D]
+  int sks;                            // splits of the shared down projection over its hidden groups
   void *out; int out_dtype;
 };
+constexpr int kMaxSharedSplits = 4;
 hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s);
 
 // The whole decode layer in one launch (router, top-k, experts, combine).

@@ -259,13 +259,27 @@ __global__ __launch_bounds__(256) void glu_mfma_kernel(PrefillLaunch p) {
   __shared__ GluBuf b0, b1, b2, b3;
   static_assert(kRg == 4, "one LDS object per stage");
   __shared__ float s_h[kRows][65];
-  const int NT = p.F / 64;
+  // blocks: the shared expert's (every row chunk of it has rows, and each
+  // runs as long as a routed one) first, so that they do not form the tail;
+  // then (row chunk, expert, tile), most of them past their expert's rows
+  const int NT = p.F / 64, NTs = p.sblobs ? p.Fs / 64 : 0;
+  const int mch = (p.T + kRows - 1) / kRows;
   const int bid = blockIdx.x;
-  const int g_idx = bid < p.E * NT ? bid / NT : p.E;
-  const int nt = bid < p.E * NT ? bid - g_idx * NT : bid - p.E * NT;
+  int g_idx, nt, yc;
+  if (bid < NTs * mch) {
+    g_idx = p.E;
+    yc = bid / NTs;
+    nt = bid - yc * NTs;
+  } else {
+    const int r = bid - NTs * mch;
+    yc = r / (p.E * NT);
+    const int rem = r - yc * (p.E * NT);
+    g_idx = rem / NT;
+    nt = rem - g_idx * NT;
+  }
   const Group g = group_of(p, g_idx);
-  const int m0 = blockIdx.y * kRows;
-  if (g.count <= m0 || (g.shared && !p.sblobs)) return;
+  const int m0 = yc * kRows;
+  if (g.count <= m0) return;
   const int nrow = min(kRows, g.count - m0);
   const int G = p.D / 64;
   for (int i = threadIdx.x; i < kRows; i += 256) {
@@ -296,14 +310,16 @@ struct DownBuf {
 
 template <int NM>
 __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g, int nb, int m0,
-                                          int nrow, const int *s_row, const float *s_hs,
-                                          DownBuf &b0, DownBuf &b1, DownBuf &b2) {
+                                          int nrow, int gbeg, int GH, float *dst, int row0,
+                                          const int *s_row, const float *s_hs, DownBuf &b0,
+                                          DownBuf &b1, DownBuf &b2) {
   // one LDS object per stage, so that a read of one stage does not wait for
   // the loads in flight into the others
   auto buf = [&](int s) -> DownBuf & { return s == 0 ? b0 : s == 1 ? b1 : b2; };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int D = p.D, F = g.F, GH = F / 64;
+  // hidden groups gbeg .. gbeg + GH - 1 of the expert (GHa in all)
+  const int D = p.D, F = g.F, GHa = F / 64;
   const int col = lane & 15, kb = lane >> 4;
   const BlobLayout L = blob_layout(D, F);
   // this wave stages, per hidden group: the three planes of rows 8 wave ..
@@ -317,7 +333,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   const u32x4_t *wsrc = (const u32x4_t *)(g.blob + L.down_codes) + wrow;
   const uint32_t *msrc = (const uint32_t *)(g.blob + L.down_meta) + wrow;
   auto issue = [&](DownBuf &B, int gi) {
-    gi = min(gi, GH - 1);  // past the end: a repeat of the last group, folded with weight 0
+    gi = gbeg + min(gi, GH - 1);  // past the end: a repeat of the last group, folded with weight 0
 #pragma unroll
     for (int q = 0; q < 3; ++q) dma16(hsrc + q * plane_v + gi * 8, &B.pl[q][64 * wave]);
     dma16(wsrc + (size_t)(2 * gi) * D, &B.w[0][64 * wave]);
@@ -343,7 +359,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
       issue(buf((s + kRd - 1) % kRd), gi + kRd - 1);
       const DownBuf &B = buf(s);
       const bool live = gi < GH;
-      const int gx = min(gi, GH - 1);
+      const int gx = gbeg + min(gi, GH - 1);
       // the planes of this wave's rows, shared by its kDT output tiles
       u32x4_t a_in[NM][2][3];
 #pragma unroll
@@ -377,7 +393,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
         for (int mt = 0; mt < NM; ++mt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            t[mt][j][i] = fmaf(s16, a[mt][i], fmaf(c16, s_hs[(mt * 16 + kb * 4 + i) * GH + gx], t[mt][j][i]));
+            t[mt][j][i] = fmaf(s16, a[mt][i], fmaf(c16, s_hs[(mt * 16 + kb * 4 + i) * GHa + gx], t[mt][j][i]));
         }
       }
     }
@@ -392,11 +408,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mt * 16 + kb * 4 + i;
-        if (m < nrow && n < D) {
-          const int rr = g.off + m0 + m;
-          float *dst = rr < p.T * p.k ? p.y + (size_t)rr * D : p.ys + (size_t)(rr - p.T * p.k) * D;
-          dst[n] = t[mt][j][i];
-        }
+        if (m < nrow && n < D) dst[(size_t)(row0 + m0 + m) * D + n] = t[mt][j][i];
       }
     }
   }
@@ -407,15 +419,35 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
   __shared__ float s_hs[kRows * kMaxHGroups];
   __shared__ DownBuf b0, b1, b2;
   static_assert(kRd == 3, "one LDS object per stage");
+  // blocks: the shared expert's first, its hidden groups split sks ways (as
+  // many groups per block as a routed expert has), then (row chunk, expert,
+  // 256 output rows)
   const int D = p.D, NB = (D + 255) / 256;
+  const int mch = (p.T + kRows - 1) / kRows, nsh = p.sblobs ? p.sks * mch * NB : 0;
   const int bid = blockIdx.x;
-  const int g_idx = bid < p.E * NB ? bid / NB : p.E;
-  const int nb = bid < p.E * NB ? bid - g_idx * NB : bid - p.E * NB;
+  int g_idx, nb, yc, ks = 0;
+  if (bid < nsh) {
+    g_idx = p.E;
+    ks = bid / (mch * NB);
+    const int r = bid - ks * (mch * NB);
+    yc = r / NB;
+    nb = r - yc * NB;
+  } else {
+    const int r = bid - nsh;
+    yc = r / (p.E * NB);
+    const int rem = r - yc * (p.E * NB);
+    g_idx = rem / NB;
+    nb = rem - g_idx * NB;
+  }
   const Group g = group_of(p, g_idx);
-  const int m0 = blockIdx.y * kRows;
-  if (g.count <= m0 || (g.shared && !p.sblobs)) return;
+  const int m0 = yc * kRows;
+  if (g.count <= m0) return;
   const int nrow = min(kRows, g.count - m0);
   const int GH = g.F / 64;
+  const int gbeg = g.shared ? ks * GH / p.sks : 0, gend = g.shared ? (ks + 1) * GH / p.sks : GH;
+  // routed rows into y (at their pair row), shared rows into partial ks of ys
+  float *dst = g.shared ? p.ys + (size_t)ks * p.T * D : p.y;
+  const int row0 = g.shared ? 0 : g.off;
   for (int i = threadIdx.x; i < kRows; i += 256) s_row[i] = g.off + m0 + min(i, nrow - 1);
   __syncthreads();
   for (int i = threadIdx.x; i < kRows * GH; i += 256) {
@@ -424,9 +456,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
   }
   __syncthreads();
   if (nrow <= 16)
-    down_body<1>(p, g, nb, m0, nrow, s_row, s_hs, b0, b1, b2);
+    down_body<1>(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
   else
-    down_body<2>(p, g, nb, m0, nrow, s_row, s_hs, b0, b1, b2);
+    down_body<2>(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
 }
 
 __global__ void combine_prefill_kernel(PrefillLaunch p) {
@@ -434,7 +466,9 @@ __global__ void combine_prefill_kernel(PrefillLaunch p) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t t = i / p.D, d = i - t * p.D;
-    float s = p.sblobs ? p.ys[i] : 0.0f;
+    float s = 0.0f;
+    if (p.sblobs)
+      for (int ks = 0; ks < p.sks; ++ks) s += p.ys[(size_t)ks * total + i];
     for (int j = 0; j < p.k; ++j)
       s = fmaf(p.gates[t * p.k + j], p.y[(size_t)p.inv[t * p.k + j] * p.D + d], s);
     if (p.out_dtype == MOE_F32)
@@ -451,8 +485,9 @@ __global__ void combine_prefill_kernel(PrefillLaunch p) {
 hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   if (p.D / 64 > kMaxDGroups || p.F / 64 > kMaxHGroups || p.Fs / 64 > kMaxHGroups)
     return hipErrorInvalidValue;
+  if (p.sblobs && (p.sks < 1 || p.sks > kMaxSharedSplits)) return hipErrorInvalidValue;
   const int mchunks = (p.T + kRows - 1) / kRows;
-  dim3 g1(p.E * (p.F / 64) + (p.sblobs ? p.Fs / 64 : 0), mchunks);
+  dim3 g1((p.E * (p.F / 64) + (p.sblobs ? p.Fs / 64 : 0)) * mchunks);
   const size_t smem = sizeof(float) * kRows * (p.D / 64);
   if (p.f16x)
     hipLaunchKernelGGL(glu_mfma_kernel<true>, g1, dim3(256), smem, s, p);
@@ -461,7 +496,7 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb4 = (p.D + 255) / 256;  // 256 output rows per down block
-  dim3 g2(p.E * nb4 + (p.sblobs ? nb4 : 0), mchunks);
+  dim3 g2((p.E * nb4 + (p.sblobs ? p.sks * nb4 : 0)) * mchunks);
   hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -233,6 +233,237 @@ hipError_t launch_route_t(const RouteLaunch &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Router of a prefill chunk on the matrix cores.  One block scores 16 tokens
+// against every expert, so the selection needs no second block: the logits
+// of a token are the 16 x E product of the tokens' activations with the
+// router weights, accumulated per 64-column group (the affine scale and bias
+// are per group): logit[t][e] = sum_g s[g][e] P[t][e][g] + b[g][e] X[t][g],
+// P = sum over the group of x q, X = sum over the group of x (the same
+// algebra as the row-by-row router; pages: hndistilled.com, "Enfoque
+// tecnico", 8-bit router).  P comes from v_mfma_f32_16x16x32 with the codes
+// as exact 16-bit integers (bf16 for bf16 activations: q < 256 has 8
+// significant bits; fp16 for fp16 activations) and fp32 accumulation, so its
+// only rounding is the fp32 summation.
+constexpr int kRTok = 16;               // tokens per block (matrix rows)
+constexpr int kRWaves = 8;              // waves per block; wave w takes expert tiles w, w + 8, ...
+constexpr int kRThr = kRWaves * 64;
+constexpr int kRMaxWords = 16;          // 8-column words of x per thread (D <= 4096)
+
+// The 16 codes of one chunk (columns 16 c + 0..15 of an expert) as the B
+// operands of two products (values 0..7 and 8..15), each register holding
+// two consecutive values.
+template <bool F16>
+__device__ __forceinline__ void codes_b(u32x4 q, u32x4 &b0, u32x4 &b1) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t wd = w[i / 2], sh = 16 * (i % 2);
+    if constexpr (F16) {
+      // fp16 bits 0x6400 | q = 1024 + q exactly; minus 1024 is exact
+      const uint32_t m = __builtin_amdgcn_perm(0x64646464u, wd >> sh, 0x04010400u);
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 v = __builtin_bit_cast(h2, m) - h2{(_Float16)1024.0f, (_Float16)1024.0f};
+      r[i] = __builtin_bit_cast(uint32_t, v);
+    } else {
+      // fp32 of a byte is exact and its upper half is the bf16 value
+      const float f0 = (float)((wd >> sh) & 0xFFu), f1 = (float)((wd >> (sh + 8)) & 0xFFu);
+      r[i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    }
+  }
+  b0 = u32x4{r[0], r[1], r[2], r[3]};
+  b1 = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+template <int NV>
+__device__ void topk_lds(const float *lg, int E, int k, int32_t *ids, float *gates,
+                         const void *const *table, const void **slot_blob, uint2 *xch) {
+  const int lane = threadIdx.x & 63;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int idx = lane + 64 * j;
+    v[j] = idx < E ? lg[idx] : -INFINITY;
+  }
+  int32_t id;
+  float gate;
+  topk_regs(v, k, xch, &id, &gate);
+  if (lane < k) {
+    ids[lane] = id;
+    gates[lane] = gate;
+    if (slot_blob) slot_blob[lane] = table[id];
+  }
+}
+
+// One group of one expert tile: the two products and the affine fold.
+template <bool F16X>
+__device__ __forceinline__ void group_fold(u32x4 q, uint32_t mw, const uint16_t *xa,
+                                           const float *sX, int g, int g4, float (&acc)[4]) {
+  u32x4 b0, b1;
+  codes_b<F16X>(q, b0, b1);
+  const u32x4 a0 = *(const u32x4 *)(xa + 64 * g);
+  const u32x4 a1 = *(const u32x4 *)(xa + 64 * g + 8);
+  f32x4 P = {0.0f, 0.0f, 0.0f, 0.0f};
+  P = mma16<F16X>(a0, b0, P);
+  P = mma16<F16X>(a1, b1, P);
+  const float sc = f16_to_f32(mw & 0xFFFFu), bi = f16_to_f32(mw >> 16);
+  const f32x4 X = *(const f32x4 *)(sX + g * kRTok + 4 * g4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(bi, X[i], fmaf(sc, P[i], acc[i]));
+}
+
+// Groups of one expert tile through a ring of R groups of loads in flight:
+// slot j holds groups j, j + R, ... and is refilled right after its use, so
+// every wait covers exactly the group it needs (G is a multiple of R).  A
+// group's address is a scalar base plus the lane's 32-bit offset.
+template <bool F16X, int R>
+__device__ __forceinline__ void tile_logits(const RouteLaunch &a, int G, int e, int g4,
+                                            const uint16_t *xa, const float *sX,
+                                            float (&acc)[4]) {
+  const int E = a.E;
+  const uint8_t *cb = (const uint8_t *)a.codes, *mb = (const uint8_t *)a.meta;
+  const uint32_t vq = (uint32_t)(g4 * E + e) * 16u, vm = (uint32_t)e * 4u;
+  const size_t cs = (size_t)E * 64, ms = (size_t)E * 4;  // bytes per group
+  u32x4 q[R];
+  uint32_t mw[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    q[j] = *(const u32x4 *)(cb + j * cs + vq);
+    mw[j] = *(const uint32_t *)(mb + j * ms + vm);
+    __builtin_amdgcn_sched_barrier(0);  // issued in slot order
+  }
+  for (int gb = 0; gb < G; gb += R) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      group_fold<F16X>(q[j], mw[j], xa, sX, gb + j, g4, acc);
+      const int gn = min(gb + R + j, G - 1);  // past the end: the last group again
+      q[j] = *(const u32x4 *)(cb + gn * cs + vq);
+      mw[j] = *(const uint32_t *)(mb + gn * ms + vm);
+      __builtin_amdgcn_sched_barrier(0);  // the refill stays right after its use
+    }
+  }
+}
+
+size_t route_mfma_smem(int D, int E) {
+  return (size_t)kRTok * (D + 8) * 2 + (size_t)(D / 64) * kRTok * 4 + (size_t)kRTok * E * 4 +
+         (size_t)kRWaves * 128 * 8;
+}
+
+template <bool F16X, int NV, int R>
+__global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a) {
+  extern __shared__ __align__(16) uint8_t rsm[];
+  const int D = a.D, E = a.E, G = D / 64, ldx = D + 8, W8 = D / 8;
+  uint16_t *sx = (uint16_t *)rsm;                       // [16][ldx] activation bits
+  float *sX = (float *)(rsm + (size_t)kRTok * ldx * 2);  // [G][16] 64-column sums
+  float *slog = sX + G * kRTok;                         // [16][E] logits
+  uint2 *xch = (uint2 *)(slog + kRTok * E);             // [waves][128] top-k exchange
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * kRTok, nt = min(kRTok, a.T - t0);
+
+  // clear the counters of the kernel that follows
+  if (a.zero) {
+    for (int i = blockIdx.x * kRThr + tid; i < a.zero_words; i += gridDim.x * kRThr) a.zero[i] = 0u;
+    for (int i = blockIdx.x * kRThr + tid; i < a.zero2_count; i += gridDim.x * kRThr)
+      a.zero2[(size_t)i * a.zero2_stride] = 0u;
+  }
+
+  // activations: 8-column words into LDS as they are, the pairs and 64-column
+  // sums the 4-bit expert kernels read (sum8_lanes order, as the row router)
+  const uint16_t *x = (const uint16_t *)a.x;
+  u32x4 xv[kRMaxWords];
+#pragma unroll
+  for (int r = 0; r < kRMaxWords; ++r) {
+    const int i = min(tid + r * kRThr, kRTok * W8 - 1);
+    const int tt = min(i / W8, nt - 1), w = i % W8;
+    xv[r] = *(const u32x4 *)(x + (size_t)(t0 + tt) * D + 8 * w);
+  }
+#pragma unroll
+  for (int r = 0; r < kRMaxWords; ++r) {
+    const int i = tid + r * kRThr;
+    if (r * kRThr >= kRTok * W8) break;  // uniform over the block
+    const bool in = i < kRTok * W8;
+    const int tt = i / W8, w = i - tt * W8;
+    const bool tok = in && tt < nt;
+    const uint32_t wd[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
+    if (in) {
+      // zeros for the rows past the chunk's tokens
+      u32x4 z = tok ? xv[r] : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4 *)(sx + (size_t)tt * ldx + 8 * w) = z;
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (wd[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
+    float s8 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s8 += x_to_f32<F16X>(h[j]);
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) o[m] = h[m] | (h[m + 4] << 16);
+    const float gs = sum8_lanes(tok ? s8 : 0.0f);
+    if (tok) {
+      uint32_t *xo = a.xp + (size_t)(t0 + tt) * (D / 2) + 4 * w;
+      *(u32x4 *)xo = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    if (in && (w & 7) == 0) {
+      sX[(w >> 3) * kRTok + tt] = tok ? gs : 0.0f;
+      if (tok) a.xs[(size_t)(t0 + tt) * G + (w >> 3)] = gs;
+    }
+  }
+  __syncthreads();
+
+  // logits: wave w, expert tiles w, w + 8, ...; lane l supplies expert
+  // 16 tile + l % 16 and the 16-column chunk l / 16 of each group
+  const int NT = (E + 15) / 16, g4 = lane >> 4, col = lane & 15;
+  for (int et = wave; et < NT; et += kRWaves) {
+    const int e = min(et * 16 + col, E - 1);
+    const uint16_t *xa = sx + (size_t)col * ldx + 16 * g4;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    tile_logits<F16X, R>(a, G, e, g4, xa, sX, acc);
+    const int ee = et * 16 + col;
+    const float lb = (a.logit_bias && ee < E) ? a.logit_bias[ee] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g4 + i;
+      float s = acc[i];
+      if (a.logit_bias) s += lb;
+      if (ee < E) {
+        slog[row * E + ee] = s;
+        if (row < nt) a.logits[(size_t)(t0 + row) * E + ee] = s;
+      }
+    }
+  }
+  __syncthreads();
+  for (int row = wave; row < nt; row += kRWaves) {
+    const int t = t0 + row;
+    topk_lds<NV>(slog + row * E, E, a.k, a.ids + (size_t)t * a.k, a.gates + (size_t)t * a.k,
+                 a.table, a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr,
+                 xch + wave * 128);
+  }
+}
+
+template <bool F16X, int NV, int R>
+hipError_t launch_route_mfma_r(const RouteLaunch &a, hipStream_t s) {
+  const size_t smem = route_mfma_smem(a.D, a.E);
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void *)route_mfma_kernel<F16X, NV, R>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((route_mfma_kernel<F16X, NV, R>), dim3((a.T + kRTok - 1) / kRTok),
+                     dim3(kRThr), smem, s, a);
+  return hipGetLastError();
+}
+// the deepest ring that divides the groups (d_model 2816: 44 = 4 x 11)
+template <bool F16X, int NV>
+hipError_t launch_route_mfma_t(const RouteLaunch &a, hipStream_t s) {
+  const int G = a.D / 64;
+  if (G % 11 == 0) return launch_route_mfma_r<F16X, NV, 11>(a, s);
+  if (G % 8 == 0) return launch_route_mfma_r<F16X, NV, 8>(a, s);
+  return launch_route_mfma_r<F16X, NV, 4>(a, s);
+}
+
 template <bool F16X>
 __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict__ x, int T, int D,
                                                      uint32_t *__restrict__ xp,
@@ -278,6 +509,12 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
   // prefill.  MAXC: 16-column chunks per thread (64 threads split a row, the
   // same split and order as the one-launch decode layer's router).
   const bool small_d = a.D <= 3072;
+  if (a.T >= 16 && tuning().route_mfma && a.E <= 256 && a.D <= 4096 && (a.D / 64) % 4 == 0 &&
+      route_mfma_smem(a.D, a.E) <= 160 * 1024) {
+    if (a.E <= 128)
+      return a.f16x ? launch_route_mfma_t<true, 2>(a, s) : launch_route_mfma_t<false, 2>(a, s);
+    return a.f16x ? launch_route_mfma_t<true, 4>(a, s) : launch_route_mfma_t<false, 4>(a, s);
+  }
   if (a.T >= 16) {
     if (small_d)
       return a.f16x ? launch_route_t<true, 4, 4, 3>(a, s) : launch_route_t<false, 4, 4, 3>(a, s);
