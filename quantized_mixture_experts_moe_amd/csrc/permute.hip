@@ -6,12 +6,19 @@
 // (integer LDS atomics, order-free), an exclusive scan, then a stable
 // placement in which wave 0 walks the pairs 64 at a time and ranks equal
 // experts inside the wave with ballots, so equal experts keep token order and
-// the result is the same on every run.
+// the result is the same on every run.  The expert ids are read from memory
+// once, by all threads, and kept in LDS (up to kStageIds pairs).  When every
+// chunk of 64 pairs has a wave of its own, the chunks are placed in parallel:
+// a chunk's pairs of expert e follow the pairs of e in the earlier chunks
+// (counted per chunk, summed in chunk order), which is the same placement.
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+constexpr int kStageIds = 8192;  // pairs whose ids the walk reads from LDS
+constexpr int kChunkHist = 8192; // chunk x expert counts for the parallel placement
 
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict__ ids, int n,
                                                        int E, int32_t *__restrict__ counts,
@@ -19,12 +26,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
                                                        int32_t *__restrict__ perm,
                                                        int32_t *__restrict__ inv) {
   extern __shared__ int sm[];
-  int *cnt = sm, *fill = sm + E;
+  int *cnt = sm, *fill = sm + E, *sid = sm + 2 * E;
+  const bool staged = n <= kStageIds;
   const int tid = threadIdx.x, lane = tid & 63;
   for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
     const int e = ids[i];
+    if (staged) sid[i] = e;
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
@@ -50,12 +59,61 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
     if (lane == 63) offsets[E] = incl;
   }
   __syncthreads();
-  if (tid >= 64) return;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  const int nch = (n + 63) / 64;
+  if (staged && nch <= 16 && nch * E <= kChunkHist) {  // 16 waves
+    // one wave per chunk of 64 pairs: ranks inside the chunk by ballots, the
+    // chunk's count of each of its experts, then (per expert, over the
+    // chunks in order) the pairs of that expert in earlier chunks
+    int *hist = sid + n;  // [nch][E]
+    for (int i = tid; i < nch * E; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const int c = tid >> 6, i = 64 * c + lane;
+    int e = -1, rank = 0, cnt_e = 0;
+    if (c < nch) {
+      e = i < n ? sid[i] : -1;
+      const bool valid = e >= 0 && e < E;
+      unsigned long long mask = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long bal = __ballot(valid && bit);
+        mask &= bit ? bal : ~bal;
+      }
+      if (valid) {
+        rank = __popcll(mask & ((1ull << lane) - 1ull));
+        cnt_e = __popcll(mask);
+        if (rank == 0) hist[c * E + e] = cnt_e;
+      } else {
+        e = -1;
+      }
+    }
+    __syncthreads();
+    // exclusive prefix over the chunks, per expert, from the expert's offset
+    for (int x = tid; x < E; x += blockDim.x) {
+      int run = fill[x];
+      for (int cc = 0; cc < nch; ++cc) {
+        const int v = hist[cc * E + x];
+        hist[cc * E + x] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    if (c < nch && i < n) {
+      if (e >= 0) {
+        const int pos = hist[c * E + e] + rank;
+        perm[pos] = i;
+        inv[i] = pos;
+      } else {
+        inv[i] = -1;
+      }
+    }
+    return;
+  }
+  if (tid >= 64) return;
   for (int base = 0; base < n; base += 64) {
     const int i = base + lane;
-    const int e = i < n ? ids[i] : -1;
+    const int e = i < n ? (staged ? sid[i] : ids[i]) : -1;
     const bool valid = e >= 0 && e < E;
     unsigned long long mask = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
@@ -80,8 +138,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
 
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), sizeof(int) * 2 * E, s, ids, T * k, E,
-                     counts, offsets, perm, inv);
+  const int n = T * k;
+  const int nch = (n + 63) / 64;
+  const bool par = n <= kStageIds && nch <= 16 && nch * E <= kChunkHist;  // as the kernel decides
+  const size_t smem =
+      sizeof(int) * (2 * (size_t)E + (n <= kStageIds ? n : 0) + (par ? (size_t)nch * E : 0));
+  if (smem > 64 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), smem, s, ids, n, E, counts, offsets,
+                     perm, inv);
   return hipGetLastError();
 }
 

@@ -461,22 +461,48 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
     down_body<2>(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
 }
 
+// four consecutive outputs per thread (16-byte loads of y), the k routed
+// rows in fixed j order after the shared expert's partial sums
 __global__ void combine_prefill_kernel(PrefillLaunch p) {
-  const size_t total = (size_t)p.T * p.D;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
+  const size_t total = (size_t)p.T * p.D, total4 = total / 4;
+  const int D4 = p.D / 4;
+  const bool aligned = ((uintptr_t)p.out & 15) == 0;  // else element by element
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total4;
        i += (size_t)gridDim.x * blockDim.x) {
-    const size_t t = i / p.D, d = i - t * p.D;
-    float s = 0.0f;
+    const size_t t = i / D4, d = (i - t * D4) * 4;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (p.sblobs)
-      for (int ks = 0; ks < p.sks; ++ks) s += p.ys[(size_t)ks * total + i];
-    for (int j = 0; j < p.k; ++j)
-      s = fmaf(p.gates[t * p.k + j], p.y[(size_t)p.inv[t * p.k + j] * p.D + d], s);
-    if (p.out_dtype == MOE_F32)
-      ((float *)p.out)[i] = s;
-    else if (p.out_dtype == MOE_BF16)
-      ((uint16_t *)p.out)[i] = (uint16_t)f32_to_bf16(s);
-    else
-      ((uint16_t *)p.out)[i] = (uint16_t)f32_to_f16(s);
+      for (int ks = 0; ks < p.sks; ++ks) {
+        const float4 v = *(const float4 *)(p.ys + (size_t)ks * total + t * p.D + d);
+        s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+      }
+    for (int j = 0; j < p.k; ++j) {
+      const float gt = p.gates[t * p.k + j];
+      const float4 v = *(const float4 *)(p.y + (size_t)p.inv[t * p.k + j] * p.D + d);
+      s.x = fmaf(gt, v.x, s.x), s.y = fmaf(gt, v.y, s.y);
+      s.z = fmaf(gt, v.z, s.z), s.w = fmaf(gt, v.w, s.w);
+    }
+    const size_t o = t * p.D + d;
+    if (!aligned) {
+      const float v[4] = {s.x, s.y, s.z, s.w};
+      for (int u = 0; u < 4; ++u) {
+        if (p.out_dtype == MOE_F32)
+          ((float *)p.out)[o + u] = v[u];
+        else if (p.out_dtype == MOE_BF16)
+          ((uint16_t *)p.out)[o + u] = (uint16_t)f32_to_bf16(v[u]);
+        else
+          ((uint16_t *)p.out)[o + u] = (uint16_t)f32_to_f16(v[u]);
+      }
+    } else if (p.out_dtype == MOE_F32) {
+      *(float4 *)((float *)p.out + o) = s;
+    } else {
+      const bool bf = p.out_dtype == MOE_BF16;
+      const uint32_t c0 = bf ? f32_to_bf16(s.x) : f32_to_f16(s.x);
+      const uint32_t c1 = bf ? f32_to_bf16(s.y) : f32_to_f16(s.y);
+      const uint32_t c2 = bf ? f32_to_bf16(s.z) : f32_to_f16(s.z);
+      const uint32_t c3 = bf ? f32_to_bf16(s.w) : f32_to_f16(s.w);
+      *(uint2 *)((uint16_t *)p.out + o) = make_uint2(c0 | (c1 << 16), c2 | (c3 << 16));
+    }
   }
 }
 
@@ -500,7 +526,7 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t total = (size_t)p.T * p.D;
+  const size_t total = (size_t)p.T * p.D / 4;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(combine_prefill_kernel, dim3(blocks), dim3(256), 0, s, p);

@@ -466,6 +466,27 @@ def test_layer_forward_prefill_ragged_chunk():
     _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=toks[:6] + toks[-6:] + [76])
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_layer_forward_prefill_out_dtypes(out_dtype):
+    """The prefill combine writes 16-bit outputs four at a time; into an
+    output that is not 16-byte aligned it writes them one by one.  Both are
+    the fp32 output rounded to nearest even."""
+    _case(f"layer_forward prefill T=40 out={out_dtype}")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    T = 40
+    xb = gen.activations(0, 2, 0, T, cfg.D, cfg.x_dtype)
+    ref, ids, _ = _layer_gpu(L, xb, cfg.k)
+    want = ref.to(out_dtype)
+    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    buf = torch.empty(T * cfg.D + 8, dtype=out_dtype, device="cuda")
+    for off in (0, 1):  # byte offset 0 and 2
+        out = buf[off:off + T * cfg.D].view(T, cfg.D)
+        moe.moe_layer_forward(x_dev(xb, cfg.x_dtype), L.router, cfg.k, L.routed, L.shared, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), off
+
+
 @pytest.mark.parametrize("variant", [1, 2])
 def test_pool_decode_shapes_streamed_equals_resident(variant):
     """Decode-shaped layers, 16 HBM slots each: streamed output is bitwise the
