@@ -455,32 +455,58 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
     if (use[i] && lane == 2 * i) hint = L.hg + hp[i], active = true;
     if (use[i] && lane == 2 * i + 1 && !single) hint = L.hu + hp[i], active = true;
   }
-  wait_hint(hint, active, tag, L.err);
+  if (L.direct_h != 1) wait_hint(hint, active, tag, L.err);
   on_hint();
-  float hv0[M];
-  for (long s = 0;; ++s) {
-    bool ok = true;
+  // the values: with a hint first (direct_h 0, 2) or polled directly
+  // (direct_h 1); direct_h 2 keeps two rounds of loads in flight (see
+  // wait_hint).  Units a wave does not use are loaded too (valid rows) and
+  // not checked.
+  const uint64_t *hu = single ? L.hg : L.hu;
+  uint64_t wg[M], wu[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      hv0[i] = 0.0f;
-      if (use[i]) {
-        const uint64_t wg = ld_dev64(L.hg + hp[i] + lane);
-        ok = ok && has_tag(wg, tag);
-        hv0[i] = __uint_as_float((uint32_t)wg);
-        if (!single) {
-          const uint64_t wu = ld_dev64(L.hu + hp[i] + lane);
-          ok = ok && has_tag(wu, tag);
-          hv0[i] *= __uint_as_float((uint32_t)wu);
-        }
+  for (int i = 0; i < M; ++i) {
+    wg[i] = ld_dev64(L.hg + hp[i] + lane);
+    wu[i] = ld_dev64(hu + hp[i] + lane);
+  }
+  for (long s = 0;; ++s) {
+    uint64_t ng[M], nu[M];
+    if (L.direct_h == 2) {
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        ng[i] = ld_dev64(L.hg + hp[i] + lane);
+        nu[i] = ld_dev64(hu + hp[i] + lane);
       }
     }
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < M; ++i) ok = ok && (!use[i] || (has_tag(wg[i], tag) && has_tag(wu[i], tag)));
     if (__all(ok)) break;
     if (s > kSpin) {
       if (lane == 0) add_dev(L.err, 1u);
       break;
     }
-    __builtin_amdgcn_s_sleep(1);
+    if (L.direct_h == 2) {
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        wg[i] = ng[i];
+        wu[i] = nu[i];
+      }
+    } else {
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        wg[i] = ld_dev64(L.hg + hp[i] + lane);
+        wu[i] = ld_dev64(hu + hp[i] + lane);
+      }
+    }
   }
+  float hv0[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+    hv0[i] = use[i] ? __uint_as_float((uint32_t)wg[i]) *
+                          (single ? 1.0f : __uint_as_float((uint32_t)wu[i]))
+                    : 0.0f;
   // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
   // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
   float hsum[M];

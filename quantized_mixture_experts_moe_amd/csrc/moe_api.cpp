@@ -191,6 +191,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->shared_wait = tuning().layer_shared_wait;
   L->down_late = tuning().layer_down_late;
   L->order = tuning().layer_order;
+  L->direct_h = tuning().layer_direct_h;
   bool found = false;
   L->stream = tuning().layer == 2 && T == 1;
   if (L->stream) {
@@ -327,6 +328,8 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_down_late = value;
   } else if (!strcmp(key, "layer_order")) {
     tuning().layer_order = value;
+  } else if (!strcmp(key, "layer_direct_h")) {
+    tuning().layer_direct_h = value;
   } else if (!strcmp(key, "layer_sel_copies")) {
     tuning().layer_sel_copies = value;
   } else if (!strcmp(key, "layer_sel_stride")) {

@@ -83,6 +83,7 @@ struct Tuning {
   int layer_shared_wait = 0;
   int layer_down_late = 1;
   int layer_order = 1;
+  int layer_direct_h = 0;
   int layer_sel_copies = 16;
   int layer_sel_stride = 0;  // words between selection lines; 0: packed
 };
@@ -208,6 +209,7 @@ struct LayerLaunch {
   int down_late;                      // down weights: 0 with gate/up, 1 after its reduction, 2 after its arithmetic
   int stream;                         // one token, whole gate/up tiles per block (hu unused)
   int order;                          // dispatch order: 0 router, routed, shared; 1 router, shared, routed
+  int direct_h;                       // down waves poll the hidden values, not a hint word first
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;

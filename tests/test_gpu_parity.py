@@ -366,10 +366,12 @@ def test_pool_streamed_equals_resident_and_trace():
 
 
 _PATHS = {"layer": {"layer": 1}, "order0": {"layer": 1, "layer_order": 0},
-          "order1": {"layer": 1, "layer_order": 1}, "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
+          "order1": {"layer": 1, "layer_order": 1}, "hint0": {"layer": 1, "layer_direct_h": 0},
+          "hint1": {"layer": 1, "layer_direct_h": 1}, "hint2": {"layer": 1, "layer_direct_h": 2},
+          "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
           "three": {"layer": 0, "fused": 0}}
 _DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1,
-             "layer_order": 1}
+             "layer_order": 1, "layer_direct_h": 0}
 
 
 def _tune(**kv):
@@ -377,7 +379,8 @@ def _tune(**kv):
         moe.moe_set_tuning(key, v)
 
 
-@pytest.mark.parametrize("path", ["layer", "order0", "order1", "stream", "fused", "three"])
+@pytest.mark.parametrize("path", ["layer", "order0", "order1", "hint0", "hint1", "hint2", "stream",
+                                  "fused", "three"])
 def test_layer_forward_decode_all_paths(path):
     """The one-launch layer (split or whole gate/up tiles), the router +
     one-launch expert phase, and the router + three expert kernels all meet
