@@ -74,11 +74,16 @@ def cpu_baseline(cfg, seed, budget_s):
                       f"host cpu_count {os.cpu_count()})"}
 
 
-def source_hash() -> str:
+# sources that build (and launch) the decode layer kernel: its counters are
+# stale once any of them changes
+DECODE_LAYER_SOURCES = ("device_common.h", "layer_decode.hip", "moe_api.cpp", "moe_internal.h")
+
+
+def source_hash(files=DECODE_LAYER_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "quantized_mixture_experts_moe_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(files):
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
@@ -294,17 +299,23 @@ def main():
     log(f"{steps} steps in {ms:.2f} ms: {ms_step * 1e3:.2f} us/step, {tokens_per_s:,.0f} tokens/s"
         + (f", {gbps:,.0f} GB/s" if gbps else ""))
 
-    # duration of the dominant kernel, measured with events the library records
-    # around that launch on its own stream (eager steps): the one-launch layer
-    # for a decode token, else the expert phase
-    n_prof = min(512, steps)
-    with moe.ProfileEvents(n_prof) as pe, torch.cuda.stream(stream):
-        for i in range(n_prof):
-            step(i)
-        torch.cuda.synchronize()
-        kms = pe.elapsed_ms(n_prof)
-    k_us = 1e3 * float(np.mean(kms))
+    # duration of the dominant kernel.  A decode step on the one-launch path
+    # is exactly one launch of the layer kernel, so its average duration is
+    # the timed region's (HIP events on the stream the graphs replay on) per
+    # step.  Otherwise (the expert phase of a prefill chunk, or of a decode
+    # step on the router + expert-phase path) the library records events
+    # around that phase's launches on the same stream, in eager steps.
     layer_path = T == 1 and "layer=0" not in a.tune
+    if layer_path:
+        k_us = ms_step * 1e3
+    else:
+        n_prof = min(512, steps)
+        with moe.ProfileEvents(n_prof) as pe, torch.cuda.stream(stream):
+            for i in range(n_prof):
+                step(i)
+            torch.cuda.synchronize()
+            kms = pe.elapsed_ms(n_prof)
+        k_us = 1e3 * float(np.mean(kms))
     if layer_path:
         k_bytes = gen.algorithmic_decode_bytes(cfg)
         k_name = ("decode_layer_kernel (router, top-8, gate/up, down and combine of the 8 "
@@ -316,8 +327,22 @@ def main():
         k_name = "experts_fused_kernel (gate/up + down + combine of the 8 routed and the shared expert)"
         traffic = stored_traffic("decode_expert_phase_traffic.json")
     else:
-        k_bytes = None
-        k_name = "grouped prefill expert kernels"
+        # the expert phase of a chunk reads every selected expert's blob once
+        # (experts chosen by several tokens serve all their rows from one
+        # read), the shared expert, the activation pairs and the outputs
+        ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+        gates = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+        uniq = []
+        for i in range(n_x):
+            router, routed, shared, bias = layers[i % n_layers]
+            moe.moe_route(x_all[i], router, cfg.k, ids, gates, ws, bias)
+            torch.cuda.synchronize()
+            uniq.append(len(np.unique(ids.cpu().numpy())))
+        k_bytes = (float(np.mean(uniq)) * gen.blob_bytes(cfg.D, cfg.F)
+                   + (gen.blob_bytes(cfg.D, cfg.F_shared) if cfg.F_shared else 0)
+                   + T * cfg.D * 2 + T * cfg.D * 4)
+        k_name = (f"grouped prefill expert kernels (gate/up, down, combine; "
+                  f"{np.mean(uniq):.1f} distinct experts per chunk)")
         traffic = None
     k_gbps = k_bytes / (k_us * 1e-6) / 1e9 if k_bytes else None
     log(f"timed kernel: {k_us:.2f} us per launch" + (f", {k_gbps:,.0f} GB/s" if k_gbps else ""))
