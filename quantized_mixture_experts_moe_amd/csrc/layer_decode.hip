@@ -274,6 +274,53 @@ __device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t t
   }
 }
 
+// The selection of token t from its E logits in one copy (wave-wide, bounded
+// wait, two polls in flight): the top k and their softmax gates by the same
+// selection (larger logit first, ties to the lower index) and the same gate
+// arithmetic as the router kernel's; lane r < k receives the blob of the
+// r-th expert and its gate.  `report`: also write ids_out / gates_out.
+__device__ void select_from_logits(const LayerLaunch &L, int t, int copy, uint32_t tag,
+                                   const void *const *table, const uint8_t **blob_out,
+                                   float *gate_out, bool report, uint2 *xch) {
+  constexpr int NV = kMaxLayerE / 64;
+  const int lane = threadIdx.x & 63, E = L.E, k = L.k;
+  const uint64_t *lg = L.rlog + ((size_t)copy * L.T + t) * E;
+  uint64_t w[NV], nx[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) w[j] = ld_dev64(lg + min(lane + 64 * j, E - 1));
+  for (long s = 0;; ++s) {
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) nx[j] = ld_dev64(lg + min(lane + 64 * j, E - 1));
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ok = ok && (lane + 64 * j >= E || has_tag(w[j], tag));
+    if (__all(ok)) break;
+    if (s > kSpin) {
+      if (lane == 0) add_dev(L.err, 1u);
+      break;
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) w[j] = nx[j];
+  }
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    v[j] = lane + 64 * j < E ? __uint_as_float((uint32_t)w[j]) : -INFINITY;
+  int32_t id;
+  float gate;
+  topk_regs(v, k, xch, &id, &gate);
+  const uint32_t ids = min((uint32_t)id, (uint32_t)E - 1);
+  if (lane < k) {
+    blob_out[lane] = (const uint8_t *)table[ids];
+    gate_out[lane] = gate;
+    if (report) {
+      if (L.ids_out) L.ids_out[(size_t)t * k + lane] = (int32_t)ids;
+      if (L.gates_out) L.gates_out[(size_t)t * k + lane] = gate;
+    }
+  }
+}
+
 constexpr int kMaxBlockGroups = 16;  // gate/up column groups of one block (4 waves x 4)
 constexpr int kDW = kNW - 1;         // waves with down units (1..3)
 
@@ -652,6 +699,22 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
   }
   rred[kl * kRows + rr] = acc;
   __syncthreads();
+  if (L.select == 1) {
+    // the routed blocks rank the logits themselves: publish this block's
+    // logits into every copy (lane: row lane % kRows, copy lane / kRows)
+    if (wave == 0) {
+      float s = 0.0f;
+      const int r = lane % kRows;
+      for (int j = 0; j < kKL; ++j) s += rred[j * kRows + r];
+      if (L.logit_bias) s += __shfl(lbias, r, 64);
+      const int e2 = r_e0 + r;
+      for (int cp = lane / kRows; cp < L.log_copies; cp += 64 / kRows)
+        if (e2 < E)
+          st_dev64(L.rlog + ((size_t)cp * L.T + r_t) * E + e2, tagged(__float_as_uint(s), tag));
+    }
+    __builtin_amdgcn_s_setprio(0);
+    return;
+  }
   if (wave == 0 && lane < kRows) {
     float s = 0.0f;
     for (int j = 0; j < kKL; ++j) s += rred[j * kRows + lane];
@@ -678,6 +741,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   __shared__ const uint8_t *s_blob[2][kMaxK];  // [0]: gate/up token, [1]: down token
   __shared__ float s_gate[2][kMaxK];
   __shared__ SelectLds s_select;
+  __shared__ uint2 s_xch[2][128];  // top-k exchange of the selecting waves
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -810,9 +874,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       const int copy = sb % L.sel_copies;
       // the first block of each token's first gate/up tile reports the selection
       const bool report = has_g && gt.j == 0 && gt.rb == 0 && ks == 0;
-      if (wave == 0) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0], report);
-      if (wave == 1 && t_out != gt.t)
-        wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1], false);
+      if (L.select == 1) {
+        const int lc = sb % L.log_copies;
+        if (wave == 0)
+          select_from_logits(L, gt.t, lc, tag, s_table, s_blob[0], s_gate[0], report, s_xch[0]);
+        if (wave == 1 && t_out != gt.t)
+          select_from_logits(L, t_out, lc, tag, s_table, s_blob[1], s_gate[1], false, s_xch[1]);
+      } else {
+        if (wave == 0) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0], report);
+        if (wave == 1 && t_out != gt.t)
+          wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1], false);
+      }
     } else {
       stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
       if (tid < k) {  // written by earlier work on the stream: plain loads

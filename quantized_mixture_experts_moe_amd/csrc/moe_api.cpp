@@ -192,6 +192,8 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->down_late = tuning().layer_down_late;
   L->order = tuning().layer_order;
   L->direct_h = tuning().layer_direct_h;
+  L->select = tuning().layer_select == 1 ? 1 : 0;
+  L->log_copies = L->select ? min(max(tuning().layer_log_copies, 1), 64) : 1;
   bool found = false;
   L->stream = tuning().layer == 2 && T == 1;
   if (L->stream) {
@@ -230,12 +232,16 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
     found = grid <= cap && grid <= kMaxLayerGrid;
   }
   if (!found) return false;
+  if (L->stream) {  // the whole-tile variant reads the published selection
+    L->select = 0;
+    L->log_copies = 1;
+  }
   if (n_gtiles > kMaxAccTiles || T * NB > kMaxOutTiles) return false;
   L->bep = (uint32_t *)w.layer;
   set_split_accumulators(w, &L->gacc, &L->dacc, &L->gcnt, &L->dcnt);
   // tagged words: logits, hidden activations
   Carver c{w.layer + kTaggedOff};
-  L->rlog = c.take<uint64_t>((size_t)T * E, 8);
+  L->rlog = c.take<uint64_t>((size_t)L->log_copies * T * E, 8);
   // copies of each selection line (spread the polling)
   L->sel_copies = min(max(tuning().layer_sel_copies, 1), 256);
   L->lid = (k + 15) / 16 * 16;
@@ -330,6 +336,10 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_order = value;
   } else if (!strcmp(key, "layer_direct_h")) {
     tuning().layer_direct_h = value;
+  } else if (!strcmp(key, "layer_select")) {
+    tuning().layer_select = value;
+  } else if (!strcmp(key, "layer_log_copies")) {
+    tuning().layer_log_copies = value;
   } else if (!strcmp(key, "layer_sel_copies")) {
     tuning().layer_sel_copies = value;
   } else if (!strcmp(key, "layer_sel_stride")) {

@@ -84,6 +84,8 @@ struct Tuning {
   int layer_down_late = 1;
   int layer_order = 1;
   int layer_direct_h = 0;
+  int layer_select = 0;
+  int layer_log_copies = 16;
   int layer_sel_copies = 16;
   int layer_sel_stride = 0;  // words between selection lines; 0: packed
 };
@@ -210,13 +212,15 @@ struct LayerLaunch {
   int stream;                         // one token, whole gate/up tiles per block (hu unused)
   int order;                          // dispatch order: 0 router, routed, shared; 1 router, shared, routed
   int direct_h;                       // down waves poll the hidden values, not a hint word first
+  int select;                         // 0: router blocks rank and publish the selection; 1: routed blocks rank the logits
+  int log_copies;                     // copies of the logits (select 1)
   // selection given by the caller (streamed experts: ids from an earlier
   // routing, blobs from the pool): [T][k] blob addresses and gates, or null
   const void *const *given_blob;
   const float *given_gates;
   size_t table_off;                   // LDS byte offset of the blob table
   uint32_t *bep;                      // per-block epochs [kMaxLayerGrid]
-  uint64_t *rlog;                     // [T][E] tagged logits
+  uint64_t *rlog;                     // [log_copies][T][E] tagged logits
   uint64_t *sel;                      // [T][sel_copies] lines of [2][lid] tagged ids, gates
   int sel_copies, lid, sel_stride;    // sel_stride: words from one line to the next
   uint64_t *hg, *hu;                  // [T*k*F + T*Fs] tagged gelu(gate) and up

@@ -144,16 +144,24 @@ def test_selection_exact_ties(name, T):
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     np.testing.assert_allclose(gates.cpu().numpy(), ref_gates, rtol=1e-6)
-    for t in range(T):  # one token per call: the one-launch layer
-        out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
-        ids1 = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
-        gates1 = torch.empty(1, cfg.k, dtype=torch.float32, device="cuda")
-        moe.moe_layer_forward(x[t:t + 1], L.router, cfg.k, L.routed, L.shared, out, ws,
-                              logit_bias=bias_d, ids_out=ids1, gates_out=gates1)
-        torch.cuda.synchronize()
-        assert np.array_equal(ids1.cpu().numpy()[0], ref_ids[t])
-        assert torch.equal(gates1[0], gates[t])
-        assert torch.all(out == 0)
+    # one token per call: the one-launch layer, with the selection ranked by
+    # the router blocks (0) or by every routed block from the logits (1)
+    try:
+        for sel in (0, 1):
+            _tune(layer_select=sel)
+            for t in range(T):
+                out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+                ids1 = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
+                gates1 = torch.empty(1, cfg.k, dtype=torch.float32, device="cuda")
+                moe.moe_layer_forward(x[t:t + 1], L.router, cfg.k, L.routed, L.shared, out, ws,
+                                      logit_bias=bias_d, ids_out=ids1, gates_out=gates1)
+                torch.cuda.synchronize()
+                assert np.array_equal(ids1.cpu().numpy()[0], ref_ids[t]), (sel, t)
+                assert torch.equal(gates1[0], gates[t]), (sel, t)
+                assert torch.all(out == 0)
+        assert ws.timeouts() == 0
+    finally:
+        _tune(**_DEFAULTS)
 
 
 # ---------------------------------------------------------------- expert FFN
@@ -368,10 +376,11 @@ def test_pool_streamed_equals_resident_and_trace():
 _PATHS = {"layer": {"layer": 1}, "order0": {"layer": 1, "layer_order": 0},
           "order1": {"layer": 1, "layer_order": 1}, "hint0": {"layer": 1, "layer_direct_h": 0},
           "hint1": {"layer": 1, "layer_direct_h": 1}, "hint2": {"layer": 1, "layer_direct_h": 2},
+          "select0": {"layer": 1, "layer_select": 0}, "select1": {"layer": 1, "layer_select": 1},
           "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
           "three": {"layer": 0, "fused": 0}}
 _DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1,
-             "layer_order": 1, "layer_direct_h": 0}
+             "layer_order": 1, "layer_direct_h": 0, "layer_select": 0}
 
 
 def _tune(**kv):
@@ -379,8 +388,8 @@ def _tune(**kv):
         moe.moe_set_tuning(key, v)
 
 
-@pytest.mark.parametrize("path", ["layer", "order0", "order1", "hint0", "hint1", "hint2", "stream",
-                                  "fused", "three"])
+@pytest.mark.parametrize("path", ["layer", "order0", "order1", "hint0", "hint1", "hint2", "select0",
+                                  "select1", "stream", "fused", "three"])
 def test_layer_forward_decode_all_paths(path):
     """The one-launch layer (split or whole gate/up tiles), the router +
     one-launch expert phase, and the router + three expert kernels all meet
@@ -438,8 +447,10 @@ def test_layer_epochs_across_grid_sizes():
     try:
         plan = [(1, 0, 0), (1, 3, 8), (2, 0, 0), (1, 8, 16), (2, 0, 6), (1, 2, 0), (2, 0, 0)] * 3
         for it, (variant, ksg, ksd) in enumerate(plan):
-            # the block order changes between calls too (epochs are per logical block)
-            _tune(layer=variant, layer_ksg=ksg, layer_ksd=ksd, layer_order=it % 2)
+            # the block order and the selection mode change between calls too
+            # (epochs are per logical block)
+            _tune(layer=variant, layer_ksg=ksg, layer_ksd=ksd, layer_order=it % 2,
+                  layer_select=(it // 2) % 2)
             out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
             ids = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
             moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, out, ws, ids_out=ids)
