@@ -77,6 +77,9 @@ Workspace carve(void *base, const Dims &d) {
   w.fcounters = c.take<uint32_t>(fused_counter_words(d), 4);
   w.perm_counts = c.take<int32_t>(d.E, 4);
   w.perm_offsets = c.take<int32_t>(d.E + 1, 4);
+  // at most one partial chunk per expert: sum ceil(c / R) <= E + T k / R
+  w.perm_items = c.take<int32_t>((size_t)d.E + (T * k + kPrefillRows - 1) / kPrefillRows, 4);
+  w.perm_n_items = c.take<int32_t>(1, 4);
   w.perm = c.take<int32_t>(T * k, 4);
   w.perm_inv = c.take<int32_t>(T * k, 4);
   w.hplanes = c.take<uint16_t>(3 * units, 2);
@@ -417,8 +420,8 @@ moe_status moe_permute(const int32_t *ids, int32_t T, int32_t k, int32_t E, int3
                        int32_t *offsets, int32_t *perm, int32_t *inv, void *stream) {
   if (!ids || !counts || !offsets || !perm || !inv) return MOE_E_INVALID;
   if (T < 1 || k < 1 || E < 1 || E > kMaxE || (long)T * k > 65536) return MOE_E_INVALID;
-  return hip_status(launch_permute(ids, T, k, E, counts, offsets, perm, inv,
-                                   (hipStream_t)stream));
+  return hip_status(launch_permute(ids, T, k, E, counts, offsets, perm, inv, nullptr, nullptr,
+                                   0, (hipStream_t)stream));
 }
 
 moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *router,
@@ -539,12 +542,14 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   // prefill chunk: group the (token, slot) pairs by expert, then matrix cores
   if (!pool && T >= tuning().prefill_min_t && T * k <= 65536 && D / 64 <= kMaxDGroups &&
       F / 64 <= kMaxHGroups && Fs / 64 <= kMaxHGroups) {
-    if (launch_permute(r.ids, T, k, E, w.perm_counts, w.perm_offsets, w.perm, w.perm_inv, s) !=
+    if (launch_permute(r.ids, T, k, E, w.perm_counts, w.perm_offsets, w.perm, w.perm_inv,
+                       w.perm_items, w.perm_n_items, kPrefillRows, s) !=
         hipSuccess)
       return MOE_E_HIP;
     PrefillLaunch pl;
     pl.f16x = r.f16x; pl.T = T; pl.k = k; pl.E = E; pl.D = D; pl.F = F; pl.Fs = Fs;
     pl.counts = w.perm_counts; pl.offsets = w.perm_offsets; pl.perm = w.perm; pl.inv = w.perm_inv;
+    pl.items = w.perm_items; pl.n_items = w.perm_n_items;
     pl.gates = r.gates; pl.rblobs = routed->blobs; pl.sblobs = shared ? shared->blobs : nullptr;
     pl.xp = w.xp; pl.xs = w.xs;
     pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;

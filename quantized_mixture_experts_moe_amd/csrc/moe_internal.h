@@ -12,6 +12,7 @@ namespace moe {
 constexpr int kGroup = 64;      // columns per scale/bias pair (MLX affine group 64)
 constexpr size_t kAlign = 256;  // section alignment inside a blob and the workspace
 constexpr int kMaxE = 1024;     // router width handled by the top-k wave
+constexpr int kPrefillRows = 32; // token rows per block of the grouped prefill kernels
 constexpr int kMaxK = 64;       // experts per token
 constexpr int kMaxKS = 16;      // split of a reduction over blocks
 constexpr int kMaxSplitBlocks = 4096;  // blocks of a split launch (partial tiles)
@@ -107,7 +108,7 @@ struct Workspace {
   float *dpart;        // output-split partials of the one-launch expert phase
   uint32_t *fcounters; // its counters (zero between calls)
   uint32_t *err;       // sticky count of timed-out waits
-  int32_t *perm_counts, *perm_offsets, *perm, *perm_inv;
+  int32_t *perm_counts, *perm_offsets, *perm, *perm_inv, *perm_items, *perm_n_items;
   uint16_t *hplanes;   // prefill: hidden activations as three bf16 planes
   float *hsum;         // prefill: 64-unit sums of the hidden activations
   float *y, *ys;       // prefill: routed outputs per pair, shared outputs per token
@@ -185,6 +186,7 @@ hipError_t launch_combine(const float *y, const float *gates, const float *ys, i
 struct PrefillLaunch {
   int f16x, T, k, E, D, F, Fs;
   const int32_t *counts, *offsets, *perm, *inv;
+  const int32_t *items, *n_items;    // work list: expert | row chunk << 16, longest first
   const float *gates;
   const void *const *rblobs, *const *sblobs;
   const uint32_t *xp; const float *xs;
@@ -242,7 +244,11 @@ hipError_t launch_layer(const LayerLaunch &L, hipStream_t s);
 // first, then the rest once the pool has the selected experts)
 hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s);
 
+// items (optional, [E * ceil(T k / chunk_rows)]): the grouped kernels' work
+// list, expert | chunk << 16, experts by count (most first, ties by index);
+// n_items: its length
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
-                          int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);
+                          int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *items,
+                          int32_t *n_items, int chunk_rows, hipStream_t s);
 
 }  // namespace moe

@@ -24,8 +24,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
                                                        int E, int32_t *__restrict__ counts,
                                                        int32_t *__restrict__ offsets,
                                                        int32_t *__restrict__ perm,
-                                                       int32_t *__restrict__ inv) {
+                                                       int32_t *__restrict__ inv,
+                                                       int32_t *__restrict__ items,
+                                                       int32_t *__restrict__ n_items,
+                                                       int chunk_rows) {
   extern __shared__ int sm[];
+  __shared__ int s_ord[kMaxE];
   int *cnt = sm, *fill = sm + E, *sid = sm + 2 * E;
   const bool staged = n <= kStageIds;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -59,6 +63,38 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
     if (lane == 63) offsets[E] = incl;
   }
   __syncthreads();
+  // work list of the grouped kernels: (expert, chunk of chunk_rows rows)
+  // items, experts by count with the most rows first (ties by index), so that
+  // the longest blocks start first and no block is spent on an empty chunk
+  if (items) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      const int c = cnt[e];
+      int r = 0;
+      for (int j = 0; j < E; ++j) r += (cnt[j] > c || (cnt[j] == c && j < e)) ? 1 : 0;
+      s_ord[r] = e;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int per = (E + 63) / 64, base = lane * per;
+      int s = 0;
+      for (int j = 0; j < per; ++j)
+        if (base + j < E) s += (cnt[s_ord[base + j]] + chunk_rows - 1) / chunk_rows;
+      int incl = s;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      int at = incl - s;
+      for (int j = 0; j < per; ++j) {
+        if (base + j < E) {
+          const int e = s_ord[base + j], nc = (cnt[e] + chunk_rows - 1) / chunk_rows;
+          for (int yc = 0; yc < nc; ++yc) items[at + yc] = e | (yc << 16);
+          at += nc;
+        }
+      }
+      if (lane == 63) *n_items = incl;
+    }
+  }
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const int nch = (n + 63) / 64;
@@ -137,7 +173,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
 }  // namespace
 
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
-                          int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s) {
+                          int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *items,
+                          int32_t *n_items, int chunk_rows, hipStream_t s) {
+  if (E > kMaxE || (items && (!n_items || chunk_rows < 1))) return hipErrorInvalidValue;
   const int n = T * k;
   const int nch = (n + 63) / 64;
   const bool par = n <= kStageIds && nch <= 16 && nch * E <= kChunkHist;  // as the kernel decides
@@ -145,7 +183,7 @@ hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *coun
       sizeof(int) * (2 * (size_t)E + (n <= kStageIds ? n : 0) + (par ? (size_t)nch * E : 0));
   if (smem > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), smem, s, ids, n, E, counts, offsets,
-                     perm, inv);
+                     perm, inv, items, n_items, chunk_rows);
   return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@
 //   16 s * sum h (1 + q/16) + (b - 16 s) * sum h.  The small offset (1, not
 //   128) keeps the fp32 sums close to exact although h has a large mean.
 // combine (combine_prefill_kernel): out[t] = y_shared[t] + sum_j gate y[inv].
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -45,7 +47,8 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 32;  // group rows per block (one or two 16-row tiles)
+constexpr int kRows = kPrefillRows;  // group rows per block (one or two 16-row tiles)
+static_assert(kRows == 32, "one or two 16-row tiles");
 
 template <bool F16>
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -118,8 +121,11 @@ __device__ __forceinline__ void dma4(const void *src, void *dst) {
 template <int N>
 __device__ __forceinline__ void stage_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  // compiler barriers: no LDS access moves across the wait and the barrier
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // 16-byte slot of (row t, vector v of 8) in a staged [32 rows][8 vectors]
@@ -132,15 +138,17 @@ constexpr int kRg = 4;  // LDS stages of the gate/up ring (kRg - 1 groups in fli
 
 struct GluBuf {
   u32x4_t w[4][64];        // (matrix, half): gate lo/hi chunk, up lo/hi; row = lane
-  uint32_t m[4][64];       // gate meta, up meta (rows 2, 3: unused copies)
+  uint32_t m[2][64];       // gate meta (staged by waves 0, 2), up meta (waves 1, 3)
   u32x4_t x[kRows * 8];    // activation pairs of the 32 rows, xslot order
 };
+// h of the tile [row][hidden col], in the first stage's buffer once the ring
+// is drained (so that four blocks fit in a CU's LDS)
+static_assert(sizeof(float) * kRows * 65 <= sizeof(GluBuf), "h fits in one stage");
 
 template <bool F16X, int NM>
 __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g, int nt, int m0,
                                          int nrow, const int *s_tok, const float *s_xs,
-                                         GluBuf &b0, GluBuf &b1, GluBuf &b2, GluBuf &b3,
-                                         float (*s_h)[65]) {
+                                         GluBuf &b0, GluBuf &b1, GluBuf &b2, GluBuf &b3) {
   // one LDS object per stage, so that a read of one stage does not wait for
   // the loads in flight into the others
   auto buf = [&](int s) -> GluBuf & { return s == 0 ? b0 : s == 1 ? b1 : s == 2 ? b2 : b3; };
@@ -150,9 +158,11 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
   const int col = lane & 15, kb = lane >> 4;
   const BlobLayout L = blob_layout(D, F);
   // this wave stages, per group: one code piece (matrix wave / 2, half
-  // wave % 2; row = lane), the scale/bias words of matrix wave % 2, and the
-  // activation pairs of rows 8 wave .. 8 wave + 7 (lane p: row t = 8 wave +
-  // p / 8, vector (p % 8) ^ (t & 7), so that it lands in its xslot)
+  // wave % 2; row = lane), the scale/bias words of matrix wave % 2 (waves 2
+  // and 3 write the same words as waves 0 and 1: loads are issued
+  // unconditionally, so the waits stay exact), and the activation pairs of
+  // rows 8 wave .. 8 wave + 7 (lane p: row t = 8 wave + p / 8, vector
+  // (p % 8) ^ (t & 7), so that it lands in its xslot)
   const u32x4_t *wsrc = (const u32x4_t *)(g.blob + ((wave >> 1) ? L.up_codes : L.gate_codes)) +
                         (size_t)(wave & 1) * F + nt * 64 + lane;
   const uint32_t *msrc =
@@ -162,7 +172,7 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
   auto issue = [&](GluBuf &B, int gi) {
     gi = min(gi, G - 1);  // past the end: a repeat of the last group, folded with weight 0
     dma16(wsrc + (size_t)(2 * gi) * F, &B.w[wave][0]);
-    dma4(msrc + (size_t)gi * F, &B.m[wave][0]);
+    dma4(msrc + (size_t)gi * F, &B.m[wave & 1][0]);  // waves 2, 3: the same words again
     dma16(xsrc + gi * 8, &B.x[64 * wave]);
   };
   const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
@@ -219,8 +229,10 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
       }
     }
   }
-  // the stages past the end are still landing in LDS: let them finish
+  // the stages past the end are still landing in LDS: let them finish (and
+  // every wave is past its last read of the ring)
   stage_barrier<0>();
+  float (*s_h)[65] = reinterpret_cast<float (*)[65]>(&b0);
   // h into LDS [row][hidden col of the tile]
 #pragma unroll
   for (int mt = 0; mt < NM; ++mt) {
@@ -253,15 +265,15 @@ __device__ __forceinline__ void glu_body(const PrefillLaunch &p, const Group &g,
 }
 
 template <bool F16X>
-__global__ __launch_bounds__(256) void glu_mfma_kernel(PrefillLaunch p) {
+__global__ __launch_bounds__(256, 4) void glu_mfma_kernel(PrefillLaunch p) {
   extern __shared__ float s_dyn[];  // [kRows][G] 64-column sums of x
   __shared__ int s_tok[kRows];
   __shared__ GluBuf b0, b1, b2, b3;
   static_assert(kRg == 4, "one LDS object per stage");
-  __shared__ float s_h[kRows][65];
-  // blocks: the shared expert's (every row chunk of it has rows, and each
-  // runs as long as a routed one) first, so that they do not form the tail;
-  // then (row chunk, expert, tile), most of them past their expert's rows
+  // blocks, longest first so that they do not form the tail: the shared
+  // expert's (every row chunk of it has rows), then the work list's items
+  // (expert by count, most rows first, and row chunk) x tiles; the blocks
+  // past the list's end return at once
   const int NT = p.F / 64, NTs = p.sblobs ? p.Fs / 64 : 0;
   const int mch = (p.T + kRows - 1) / kRows;
   const int bid = blockIdx.x;
@@ -271,11 +283,12 @@ __global__ __launch_bounds__(256) void glu_mfma_kernel(PrefillLaunch p) {
     yc = bid / NTs;
     nt = bid - yc * NTs;
   } else {
-    const int r = bid - NTs * mch;
-    yc = r / (p.E * NT);
-    const int rem = r - yc * (p.E * NT);
-    g_idx = rem / NT;
-    nt = rem - g_idx * NT;
+    const int r = bid - NTs * mch, item = r / NT;
+    if (item >= *p.n_items) return;
+    const int it = p.items[item];
+    g_idx = it & 0xFFFF;
+    yc = it >> 16;
+    nt = r - item * NT;
   }
   const Group g = group_of(p, g_idx);
   const int m0 = yc * kRows;
@@ -293,9 +306,9 @@ __global__ __launch_bounds__(256) void glu_mfma_kernel(PrefillLaunch p) {
   }
   __syncthreads();
   if (nrow <= 16)
-    glu_body<F16X, 1>(p, g, nt, m0, nrow, s_tok, s_dyn, b0, b1, b2, b3, s_h);
+    glu_body<F16X, 1>(p, g, nt, m0, nrow, s_tok, s_dyn, b0, b1, b2, b3);
   else
-    glu_body<F16X, 2>(p, g, nt, m0, nrow, s_tok, s_dyn, b0, b1, b2, b3, s_h);
+    glu_body<F16X, 2>(p, g, nt, m0, nrow, s_tok, s_dyn, b0, b1, b2, b3);
 }
 
 // ---------------------------------------------------------------- down
@@ -420,8 +433,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
   __shared__ DownBuf b0, b1, b2;
   static_assert(kRd == 3, "one LDS object per stage");
   // blocks: the shared expert's first, its hidden groups split sks ways (as
-  // many groups per block as a routed expert has), then (row chunk, expert,
-  // 256 output rows)
+  // many groups per block as a routed expert has), then the work list's
+  // items x 256 output rows
   const int D = p.D, NB = (D + 255) / 256;
   const int mch = (p.T + kRows - 1) / kRows, nsh = p.sblobs ? p.sks * mch * NB : 0;
   const int bid = blockIdx.x;
@@ -433,11 +446,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
     yc = r / NB;
     nb = r - yc * NB;
   } else {
-    const int r = bid - nsh;
-    yc = r / (p.E * NB);
-    const int rem = r - yc * (p.E * NB);
-    g_idx = rem / NB;
-    nb = rem - g_idx * NB;
+    const int r = bid - nsh, item = r / NB;
+    if (item >= *p.n_items) return;
+    const int it = p.items[item];
+    g_idx = it & 0xFFFF;
+    yc = it >> 16;
+    nb = r - item * NB;
   }
   const Group g = group_of(p, g_idx);
   const int m0 = yc * kRows;
@@ -513,7 +527,9 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
     return hipErrorInvalidValue;
   if (p.sblobs && (p.sks < 1 || p.sks > kMaxSharedSplits)) return hipErrorInvalidValue;
   const int mchunks = (p.T + kRows - 1) / kRows;
-  dim3 g1((p.E * (p.F / 64) + (p.sblobs ? p.Fs / 64 : 0)) * mchunks);
+  // routed blocks: the work list has at most one partial chunk per expert
+  const int max_items = std::min(p.E * mchunks, p.E + (p.T * p.k + kRows - 1) / kRows);
+  dim3 g1(max_items * (p.F / 64) + (p.sblobs ? (p.Fs / 64) * mchunks : 0));
   const size_t smem = sizeof(float) * kRows * (p.D / 64);
   if (p.f16x)
     hipLaunchKernelGGL(glu_mfma_kernel<true>, g1, dim3(256), smem, s, p);
@@ -522,7 +538,7 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb4 = (p.D + 255) / 256;  // 256 output rows per down block
-  dim3 g2((p.E * nb4 + (p.sblobs ? p.sks * nb4 : 0)) * mchunks);
+  dim3 g2(max_items * nb4 + (p.sblobs ? p.sks * nb4 * mchunks : 0));
   hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -234,19 +234,24 @@ hipError_t launch_route_t(const RouteLaunch &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Router of a prefill chunk on the matrix cores.  One block scores 16 tokens
-// against every expert, so the selection needs no second block: the logits
-// of a token are the 16 x E product of the tokens' activations with the
-// router weights, accumulated per 64-column group (the affine scale and bias
-// are per group): logit[t][e] = sum_g s[g][e] P[t][e][g] + b[g][e] X[t][g],
+// Router of a prefill chunk on the matrix cores.  The logits of 16 tokens
+// against 16 experts are a 16 x 16 product of the tokens' activations with
+// the router weights, accumulated per 64-column group (the affine scale and
+// bias are per group): logit[t][e] = sum_g s[g][e] P[t][e][g] + b[g][e] X[t][g],
 // P = sum over the group of x q, X = sum over the group of x (the same
 // algebra as the row-by-row router; pages: hndistilled.com, "Enfoque
 // tecnico", 8-bit router).  P comes from v_mfma_f32_16x16x32 with the codes
 // as exact 16-bit integers (bf16 for bf16 activations: q < 256 has 8
 // significant bits; fp16 for fp16 activations) and fp32 accumulation, so its
 // only rounding is the fp32 summation.
+//
+// Grid: (expert splits, 16-token tiles).  A block takes tpb expert tiles of
+// its token tile, each over kp parts of the groups (one wave per tile and
+// part, kp * tpb = 8 waves); the parts are added in part order in LDS.  The
+// blocks of a token tile publish their logits, and the last one to finish
+// (a counter) selects the top k of the tile's tokens.
 constexpr int kRTok = 16;               // tokens per block (matrix rows)
-constexpr int kRWaves = 8;              // waves per block; wave w takes expert tiles w, w + 8, ...
+constexpr int kRWaves = 8;
 constexpr int kRThr = kRWaves * 64;
 constexpr int kRMaxWords = 16;          // 8-column words of x per thread (D <= 4096)
 
@@ -276,26 +281,6 @@ __device__ __forceinline__ void codes_b(u32x4 q, u32x4 &b0, u32x4 &b1) {
   b1 = u32x4{r[4], r[5], r[6], r[7]};
 }
 
-template <int NV>
-__device__ void topk_lds(const float *lg, int E, int k, int32_t *ids, float *gates,
-                         const void *const *table, const void **slot_blob, uint2 *xch) {
-  const int lane = threadIdx.x & 63;
-  float v[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int idx = lane + 64 * j;
-    v[j] = idx < E ? lg[idx] : -INFINITY;
-  }
-  int32_t id;
-  float gate;
-  topk_regs(v, k, xch, &id, &gate);
-  if (lane < k) {
-    ids[lane] = id;
-    gates[lane] = gate;
-    if (slot_blob) slot_blob[lane] = table[id];
-  }
-}
-
 // One group of one expert tile: the two products and the affine fold.
 template <bool F16X>
 __device__ __forceinline__ void group_fold(u32x4 q, uint32_t mw, const uint16_t *xa,
@@ -313,15 +298,16 @@ __device__ __forceinline__ void group_fold(u32x4 q, uint32_t mw, const uint16_t 
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(bi, X[i], fmaf(sc, P[i], acc[i]));
 }
 
-// Groups of one expert tile through a ring of R groups of loads in flight:
-// slot j holds groups j, j + R, ... and is refilled right after its use, so
-// every wait covers exactly the group it needs (G is a multiple of R).  A
-// group's address is a scalar base plus the lane's 32-bit offset.
+// Groups g0 .. g0 + ng - 1 of one expert tile through a ring of R groups of
+// loads in flight: slot j holds groups g0 + j, g0 + j + R, ... and is
+// refilled right after its use, so every wait covers exactly the group it
+// needs (ng is a multiple of R).  A group's address is a scalar base plus
+// the lane's 32-bit offset.
 template <bool F16X, int R>
-__device__ __forceinline__ void tile_logits(const RouteLaunch &a, int G, int e, int g4,
+__device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng, int e, int g4,
                                             const uint16_t *xa, const float *sX,
                                             float (&acc)[4]) {
-  const int E = a.E;
+  const int E = a.E, gl = g0 + ng - 1;
   const uint8_t *cb = (const uint8_t *)a.codes, *mb = (const uint8_t *)a.meta;
   const uint32_t vq = (uint32_t)(g4 * E + e) * 16u, vm = (uint32_t)e * 4u;
   const size_t cs = (size_t)E * 64, ms = (size_t)E * 4;  // bytes per group
@@ -329,15 +315,15 @@ __device__ __forceinline__ void tile_logits(const RouteLaunch &a, int G, int e, 
   uint32_t mw[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    q[j] = *(const u32x4 *)(cb + j * cs + vq);
-    mw[j] = *(const uint32_t *)(mb + j * ms + vm);
+    q[j] = *(const u32x4 *)(cb + (g0 + j) * cs + vq);
+    mw[j] = *(const uint32_t *)(mb + (g0 + j) * ms + vm);
     __builtin_amdgcn_sched_barrier(0);  // issued in slot order
   }
-  for (int gb = 0; gb < G; gb += R) {
+  for (int gb = g0; gb <= gl; gb += R) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       group_fold<F16X>(q[j], mw[j], xa, sX, gb + j, g4, acc);
-      const int gn = min(gb + R + j, G - 1);  // past the end: the last group again
+      const int gn = min(gb + R + j, gl);  // past the end: the last group again
       q[j] = *(const u32x4 *)(cb + gn * cs + vq);
       mw[j] = *(const uint32_t *)(mb + gn * ms + vm);
       __builtin_amdgcn_sched_barrier(0);  // the refill stays right after its use
@@ -345,123 +331,161 @@ __device__ __forceinline__ void tile_logits(const RouteLaunch &a, int G, int e, 
   }
 }
 
-size_t route_mfma_smem(int D, int E) {
-  return (size_t)kRTok * (D + 8) * 2 + (size_t)(D / 64) * kRTok * 4 + (size_t)kRTok * E * 4 +
-         (size_t)kRWaves * 128 * 8;
+size_t route_mfma_smem(int D) {
+  return (size_t)kRTok * (D + 8) * 2 + (size_t)(D / 64) * kRTok * 4 +
+         (size_t)kRWaves * 4 * 64 * 4 + (size_t)kRWaves * 128 * 8;
 }
 
 template <bool F16X, int NV, int R>
-__global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a) {
+__global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp, int tpb) {
   extern __shared__ __align__(16) uint8_t rsm[];
+  __shared__ int s_last;
   const int D = a.D, E = a.E, G = D / 64, ldx = D + 8, W8 = D / 8;
   uint16_t *sx = (uint16_t *)rsm;                       // [16][ldx] activation bits
   float *sX = (float *)(rsm + (size_t)kRTok * ldx * 2);  // [G][16] 64-column sums
-  float *slog = sX + G * kRTok;                         // [16][E] logits
-  uint2 *xch = (uint2 *)(slog + kRTok * E);             // [waves][128] top-k exchange
+  float *red = sX + G * kRTok;                          // [waves][4][64] partial logits
+  uint2 *xch = (uint2 *)(red + kRWaves * 4 * 64);       // [waves][128] top-k exchange
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = blockIdx.x * kRTok, nt = min(kRTok, a.T - t0);
+  const int es = blockIdx.x, ES = gridDim.x, tt = blockIdx.y;
+  const int t0 = tt * kRTok, nt = min(kRTok, a.T - t0);
 
   // clear the counters of the kernel that follows
   if (a.zero) {
-    for (int i = blockIdx.x * kRThr + tid; i < a.zero_words; i += gridDim.x * kRThr) a.zero[i] = 0u;
-    for (int i = blockIdx.x * kRThr + tid; i < a.zero2_count; i += gridDim.x * kRThr)
+    const int bl = tt * ES + es, nbl = ES * gridDim.y;
+    for (int i = bl * kRThr + tid; i < a.zero_words; i += nbl * kRThr) a.zero[i] = 0u;
+    for (int i = bl * kRThr + tid; i < a.zero2_count; i += nbl * kRThr)
       a.zero2[(size_t)i * a.zero2_stride] = 0u;
   }
 
-  // activations: 8-column words into LDS as they are, the pairs and 64-column
-  // sums the 4-bit expert kernels read (sum8_lanes order, as the row router)
+  // activations: 8-column words into LDS as they are, 64-column sums
+  // (sum8_lanes order, as the row router).  No global store here: a store
+  // in the loop would make each later wait for a load also wait for it.
   const uint16_t *x = (const uint16_t *)a.x;
+  const int gw0 = es * G / ES, gw1 = (es + 1) * G / ES;
   u32x4 xv[kRMaxWords];
 #pragma unroll
   for (int r = 0; r < kRMaxWords; ++r) {
     const int i = min(tid + r * kRThr, kRTok * W8 - 1);
-    const int tt = min(i / W8, nt - 1), w = i % W8;
-    xv[r] = *(const u32x4 *)(x + (size_t)(t0 + tt) * D + 8 * w);
+    const int tk = min(i / W8, nt - 1), w = i % W8;
+    xv[r] = *(const u32x4 *)(x + (size_t)(t0 + tk) * D + 8 * w);
   }
 #pragma unroll
   for (int r = 0; r < kRMaxWords; ++r) {
     const int i = tid + r * kRThr;
     if (r * kRThr >= kRTok * W8) break;  // uniform over the block
     const bool in = i < kRTok * W8;
-    const int tt = i / W8, w = i - tt * W8;
-    const bool tok = in && tt < nt;
+    const int tk = i / W8, w = i - tk * W8;
+    const bool tok = in && tk < nt;
     const uint32_t wd[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
-    if (in) {
-      // zeros for the rows past the chunk's tokens
-      u32x4 z = tok ? xv[r] : u32x4{0u, 0u, 0u, 0u};
-      *(u32x4 *)(sx + (size_t)tt * ldx + 8 * w) = z;
-    }
-    uint32_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = (wd[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
+    if (in) *(u32x4 *)(sx + (size_t)tk * ldx + 8 * w) = tok ? xv[r] : u32x4{0u, 0u, 0u, 0u};
     float s8 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s8 += x_to_f32<F16X>(h[j]);
-    uint32_t o[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) o[m] = h[m] | (h[m + 4] << 16);
+    for (int j = 0; j < 8; ++j) s8 += x_to_f32<F16X>((wd[j / 2] >> (16 * (j % 2))) & 0xFFFFu);
     const float gs = sum8_lanes(tok ? s8 : 0.0f);
-    if (tok) {
-      uint32_t *xo = a.xp + (size_t)(t0 + tt) * (D / 2) + 4 * w;
-      *(u32x4 *)xo = u32x4{o[0], o[1], o[2], o[3]};
-    }
-    if (in && (w & 7) == 0) {
-      sX[(w >> 3) * kRTok + tt] = tok ? gs : 0.0f;
-      if (tok) a.xs[(size_t)(t0 + tt) * G + (w >> 3)] = gs;
-    }
+    if (in && (w & 7) == 0) sX[(w >> 3) * kRTok + tk] = tok ? gs : 0.0f;
   }
   __syncthreads();
+  // block es writes the pairs and sums the 4-bit expert kernels read, for
+  // its share of the groups, from LDS
+  for (int i = tid; i < nt * (gw1 - gw0) * 8; i += kRThr) {
+    const int tk = i / ((gw1 - gw0) * 8), w = gw0 * 8 + (i - tk * (gw1 - gw0) * 8);
+    const u32x4 v = *(const u32x4 *)(sx + (size_t)tk * ldx + 8 * w);
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[m] = ((wd[m / 2] >> (16 * (m % 2))) & 0xFFFFu) | (((wd[2 + m / 2] >> (16 * (m % 2))) & 0xFFFFu) << 16);
+    *(u32x4 *)(a.xp + (size_t)(t0 + tk) * (D / 2) + 4 * w) = u32x4{o[0], o[1], o[2], o[3]};
+    if ((w & 7) == 0) a.xs[(size_t)(t0 + tk) * G + (w >> 3)] = sX[(w >> 3) * kRTok + tk];
+  }
 
-  // logits: wave w, expert tiles w, w + 8, ...; lane l supplies expert
-  // 16 tile + l % 16 and the 16-column chunk l / 16 of each group
+  // wave w: expert tile es tpb + w / kp, groups of part w % kp; lane l
+  // supplies expert 16 tile + l % 16 and the 16-column chunk l / 16
   const int NT = (E + 15) / 16, g4 = lane >> 4, col = lane & 15;
-  for (int et = wave; et < NT; et += kRWaves) {
+  const int tl = wave / kp, part = wave - tl * kp, et = es * tpb + tl;
+  const bool live = tl < tpb && et < NT;
+  const int P = G / kp;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (live) {
     const int e = min(et * 16 + col, E - 1);
-    const uint16_t *xa = sx + (size_t)col * ldx + 16 * g4;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    tile_logits<F16X, R>(a, G, e, g4, xa, sX, acc);
+    tile_logits<F16X, R>(a, part * P, P, e, g4, sx + (size_t)col * ldx + 16 * g4, sX, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  if (live && part == 0) {
     const int ee = et * 16 + col;
     const float lb = (a.logit_bias && ee < E) ? a.logit_bias[ee] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      float v = red[(wave * 4 + i) * 64 + lane];
+      for (int pp = 1; pp < kp; ++pp) v += red[((wave + pp) * 4 + i) * 64 + lane];
+      if (a.logit_bias) v += lb;
       const int row = 4 * g4 + i;
-      float s = acc[i];
-      if (a.logit_bias) s += lb;
-      if (ee < E) {
-        slog[row * E + ee] = s;
-        if (row < nt) a.logits[(size_t)(t0 + row) * E + ee] = s;
-      }
+      if (ee < E && row < nt) st_dev(a.logits + (size_t)(t0 + row) * E + ee, v);
     }
   }
+  // the last block of the token tile selects
+  wait_all_memory();
   __syncthreads();
-  for (int row = wave; row < nt; row += kRWaves) {
-    const int t = t0 + row;
-    topk_lds<NV>(slog + row * E, E, a.k, a.ids + (size_t)t * a.k, a.gates + (size_t)t * a.k,
-                 a.table, a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr,
-                 xch + wave * 128);
+  if (tid == 0) s_last = add_dev(&a.counters[tt], 1u) == (uint32_t)(ES - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // wave w selects rows w and w + 8, both rows' logits requested first
+  static_assert(kRTok == 2 * kRWaves, "two rows per wave");
+  float v[2][NV];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = min(wave + kRWaves * rr, nt - 1);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      v[rr][j] = ld_dev(a.logits + (size_t)(t0 + row) * E + min(lane + 64 * j, E - 1));
   }
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = wave + kRWaves * rr;
+    if (row >= nt) break;  // uniform over the wave
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (lane + 64 * j >= E) v[rr][j] = -INFINITY;
+    int32_t id;
+    float gate;
+    topk_regs(v[rr], a.k, xch + wave * 128, &id, &gate);
+    const size_t o = (size_t)(t0 + row) * a.k + lane;
+    if (lane < a.k) {
+      a.ids[o] = id;
+      a.gates[o] = gate;
+      if (a.slot_blob) a.slot_blob[o] = a.table[id];
+    }
+  }
+  if (tid == 0) st_dev(&a.counters[tt], 0u);
 }
 
 template <bool F16X, int NV, int R>
-hipError_t launch_route_mfma_r(const RouteLaunch &a, hipStream_t s) {
-  const size_t smem = route_mfma_smem(a.D, a.E);
+hipError_t launch_route_mfma_r(const RouteLaunch &a, int kp, hipStream_t s) {
+  const size_t smem = route_mfma_smem(a.D);
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void *)route_mfma_kernel<F16X, NV, R>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((route_mfma_kernel<F16X, NV, R>), dim3((a.T + kRTok - 1) / kRTok),
-                     dim3(kRThr), smem, s, a);
+  const int tpb = kRWaves / kp, NT = (a.E + 15) / 16;
+  const dim3 grid((NT + tpb - 1) / tpb, (a.T + kRTok - 1) / kRTok);
+  hipLaunchKernelGGL((route_mfma_kernel<F16X, NV, R>), grid, dim3(kRThr), smem, s, a, kp, tpb);
   return hipGetLastError();
 }
-// the deepest ring that divides the groups (d_model 2816: 44 = 4 x 11)
+// kp parts of the groups per expert tile (4 when they divide, so that more
+// blocks share the work), and the deepest ring that divides a part
 template <bool F16X, int NV>
 hipError_t launch_route_mfma_t(const RouteLaunch &a, hipStream_t s) {
   const int G = a.D / 64;
-  if (G % 11 == 0) return launch_route_mfma_r<F16X, NV, 11>(a, s);
-  if (G % 8 == 0) return launch_route_mfma_r<F16X, NV, 8>(a, s);
-  return launch_route_mfma_r<F16X, NV, 4>(a, s);
+  const int kp = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1, P = G / kp;
+  if (P % 11 == 0) return launch_route_mfma_r<F16X, NV, 11>(a, kp, s);
+  if (P % 8 == 0) return launch_route_mfma_r<F16X, NV, 8>(a, kp, s);
+  if (P % 4 == 0) return launch_route_mfma_r<F16X, NV, 4>(a, kp, s);
+  if (P % 2 == 0) return launch_route_mfma_r<F16X, NV, 2>(a, kp, s);
+  return launch_route_mfma_r<F16X, NV, 1>(a, kp, s);
 }
 
 template <bool F16X>
@@ -509,8 +533,8 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
   // prefill.  MAXC: 16-column chunks per thread (64 threads split a row, the
   // same split and order as the one-launch decode layer's router).
   const bool small_d = a.D <= 3072;
-  if (a.T >= 16 && tuning().route_mfma && a.E <= 256 && a.D <= 4096 && (a.D / 64) % 4 == 0 &&
-      route_mfma_smem(a.D, a.E) <= 160 * 1024) {
+  if (a.T >= 16 && tuning().route_mfma && a.E <= 256 && a.D <= 4096 &&
+      route_mfma_smem(a.D) <= 160 * 1024) {
     if (a.E <= 128)
       return a.f16x ? launch_route_mfma_t<true, 2>(a, s) : launch_route_mfma_t<false, 2>(a, s);
     return a.f16x ? launch_route_mfma_t<true, 4>(a, s) : launch_route_mfma_t<false, 4>(a, s);
