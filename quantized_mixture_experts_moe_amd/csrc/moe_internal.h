@@ -43,6 +43,18 @@ constexpr int kCntStride = 16;  // u32 words per counter line
 // Sticky count of timed-out waits: the last line of the region, at the
 // same place for every call (read by moe_workspace_timeouts).
 constexpr size_t kErrOff = kLayerRegionBytes - kAlign;
+// Epochs of the matrix-core router, one per 16-token tile, at a fixed place
+// below that line: every call advances all of them in step, so the tagged
+// partial logits of a call carry one epoch, above every older word's.
+constexpr int kMaxRouteTiles = 4096;  // 65536 tokens
+constexpr size_t kRouteEpochOff = kErrOff - sizeof(uint32_t) * kMaxRouteTiles;
+static_assert(kRouteEpochOff % kAlign == 0, "aligned");
+// and its tagged partial logits [kRouteParts][tokens][E], below them: a
+// launch routes at most kRouteTagBytes / (8 kRouteParts E) tokens (longer
+// calls are routed in windows of that many)
+constexpr int kRouteParts = 4;
+constexpr size_t kRouteTagBytes = size_t(4) << 20;
+constexpr size_t kRouteTagOff = kRouteEpochOff - kRouteTagBytes;
 
 __host__ __device__ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -135,6 +147,10 @@ struct RouteLaunch {
   // zero2_stride-th word of zero2, zero2_count of them
   uint32_t *zero; int zero_words;
   uint32_t *zero2; int zero2_count, zero2_stride;
+  // 16 or more tokens (matrix-core router): tagged partial logits
+  // [kRouteParts][T][E] and the epochs [kMaxRouteTiles], in the fixed
+  // region (zero-filled once)
+  uint64_t *rtag; uint32_t *rep;
 };
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 // x pairs and 64-column sums for the expert kernels without routing

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
                                                        int32_t *__restrict__ n_items,
                                                        int chunk_rows) {
   extern __shared__ int sm[];
-  __shared__ int s_ord[kMaxE];
+  __shared__ int s_bkt[kMaxE], s_bst[kMaxE];
   int *cnt = sm, *fill = sm + E, *sid = sm + 2 * E;
   const bool staged = n <= kStageIds;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -64,31 +64,65 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
   }
   __syncthreads();
   // work list of the grouped kernels: (expert, chunk of chunk_rows rows)
-  // items, experts by count with the most rows first (ties by index), so that
-  // the longest blocks start first and no block is spent on an empty chunk
+  // items, experts in buckets of chunk_rows / 2 rows, the fullest first, so
+  // that the longest blocks start first and no block is spent on an empty
+  // chunk.  All experts of a bucket have the same number of chunks; the
+  // order inside a bucket is whatever the LDS atomics give: every item is
+  // computed on its own, so the results do not depend on it.
   if (items) {
-    for (int e = tid; e < E; e += blockDim.x) {
-      const int c = cnt[e];
-      int r = 0;
-      for (int j = 0; j < E; ++j) r += (cnt[j] > c || (cnt[j] == c && j < e)) ? 1 : 0;
-      s_ord[r] = e;
-    }
-    __syncthreads();
-    if (tid < 64) {
+    const int half = (chunk_rows + 1) / 2;
+    const int nb = (n + half - 1) / half + 1;  // buckets 0 .. ceil(max count / half)
+    auto chunks = [&](int b) { return (b * half + chunk_rows - 1) / chunk_rows; };
+    if (nb <= kMaxE) {
+      for (int i = tid; i < nb; i += blockDim.x) s_bkt[i] = 0, s_bst[i] = 0;
+      __syncthreads();
+      for (int e = tid; e < E; e += blockDim.x) atomicAdd(&s_bkt[(cnt[e] + half - 1) / half], 1);
+      __syncthreads();
+      if (tid < 64) {  // first item of each bucket, fullest first (one wave scan)
+        const int per = (nb + 63) / 64, base = lane * per;
+        int sum = 0;
+        for (int j = 0; j < per; ++j) {
+          const int b = nb - 1 - (base + j);
+          if (b >= 0) sum += s_bkt[b] * chunks(b);
+        }
+        int incl = sum;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += v;
+        }
+        int at = incl - sum;
+        for (int j = 0; j < per; ++j) {
+          const int b = nb - 1 - (base + j);
+          if (b >= 0) {
+            s_bst[b] = at;
+            at += s_bkt[b] * chunks(b);
+            s_bkt[b] = 0;  // now the bucket's fill count
+          }
+        }
+        if (lane == 63) *n_items = incl;
+      }
+      __syncthreads();
+      for (int e = tid; e < E; e += blockDim.x) {
+        const int b = (cnt[e] + half - 1) / half, nc = chunks(b);
+        if (nc == 0) continue;
+        const int at = s_bst[b] + atomicAdd(&s_bkt[b], 1) * nc;
+        for (int yc = 0; yc < nc; ++yc) items[at + yc] = e | (yc << 16);
+      }
+    } else if (tid < 64) {  // too many buckets: experts in index order
       const int per = (E + 63) / 64, base = lane * per;
-      int s = 0;
+      int sum = 0;
       for (int j = 0; j < per; ++j)
-        if (base + j < E) s += (cnt[s_ord[base + j]] + chunk_rows - 1) / chunk_rows;
-      int incl = s;
+        if (base + j < E) sum += (cnt[base + j] + chunk_rows - 1) / chunk_rows;
+      int incl = sum;
       for (int off = 1; off < 64; off <<= 1) {
         const int v = __shfl_up(incl, off, 64);
         if (lane >= off) incl += v;
       }
-      int at = incl - s;
+      int at = incl - sum;
       for (int j = 0; j < per; ++j) {
         if (base + j < E) {
-          const int e = s_ord[base + j], nc = (cnt[e] + chunk_rows - 1) / chunk_rows;
-          for (int yc = 0; yc < nc; ++yc) items[at + yc] = e | (yc << 16);
+          const int nc = (cnt[base + j] + chunk_rows - 1) / chunk_rows;
+          for (int yc = 0; yc < nc; ++yc) items[at + yc] = (base + j) | (yc << 16);
           at += nc;
         }
       }

@@ -10,6 +10,8 @@
 // pair layout the 4-bit expert kernels read (dot2 pairs and 64-column sums).
 #include <float.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -245,15 +247,18 @@ hipError_t launch_route_t(const RouteLaunch &a, hipStream_t s) {
 // significant bits; fp16 for fp16 activations) and fp32 accumulation, so its
 // only rounding is the fp32 summation.
 //
-// Grid: (expert splits, 16-token tiles).  A block takes tpb expert tiles of
-// its token tile, each over kp parts of the groups (one wave per tile and
-// part, kp * tpb = 8 waves); the parts are added in part order in LDS.  The
-// blocks of a token tile publish their logits, and the last one to finish
-// (a counter) selects the top k of the tile's tokens.
+// Grid: (parts of the groups, 16-token tiles).  Block (part, tile) stages
+// only its part of the tokens' activations and sums, over that part, the
+// logits of every expert (one 16-expert tile per wave).  It publishes them
+// as tagged words (value, epoch of the token tile); then each block selects
+// 16 / parts of the tile's tokens: a wave polls the parts' words of its
+// token, adds them in part order and runs the top k.  No block waits for
+// another's stores to drain and no counter is taken.
 constexpr int kRTok = 16;               // tokens per block (matrix rows)
 constexpr int kRWaves = 8;
 constexpr int kRThr = kRWaves * 64;
-constexpr int kRMaxWords = 16;          // 8-column words of x per thread (D <= 4096)
+constexpr int kRMaxWords = 16;          // 8-column words of x per thread and part (D <= 4096)
+constexpr long kRSpin = 1L << 20;       // bounded waits, then the tokens are marked
 
 // The 16 codes of one chunk (columns 16 c + 0..15 of an expert) as the B
 // operands of two products (values 0..7 and 8..15), each register holding
@@ -298,11 +303,11 @@ __device__ __forceinline__ void group_fold(u32x4 q, uint32_t mw, const uint16_t 
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(bi, X[i], fmaf(sc, P[i], acc[i]));
 }
 
-// Groups g0 .. g0 + ng - 1 of one expert tile through a ring of R groups of
-// loads in flight: slot j holds groups g0 + j, g0 + j + R, ... and is
-// refilled right after its use, so every wait covers exactly the group it
-// needs (ng is a multiple of R).  A group's address is a scalar base plus
-// the lane's 32-bit offset.
+// Groups g0 .. g0 + ng - 1 of one expert tile (xa and sX hold those groups
+// only) through a ring of R groups of loads in flight: slot j holds groups
+// g0 + j, g0 + j + R, ... and is refilled right after its use, so every wait
+// covers exactly the group it needs (ng is a multiple of R).  A group's
+// address is a scalar base plus the lane's 32-bit offset.
 template <bool F16X, int R>
 __device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng, int e, int g4,
                                             const uint16_t *xa, const float *sX,
@@ -322,7 +327,7 @@ __device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng
   for (int gb = g0; gb <= gl; gb += R) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      group_fold<F16X>(q[j], mw[j], xa, sX, gb + j, g4, acc);
+      group_fold<F16X>(q[j], mw[j], xa, sX, gb + j - g0, g4, acc);  // LDS holds g0 ..
       const int gn = min(gb + R + j, gl);  // past the end: the last group again
       q[j] = *(const u32x4 *)(cb + gn * cs + vq);
       mw[j] = *(const uint32_t *)(mb + gn * ms + vm);
@@ -331,51 +336,53 @@ __device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng
   }
 }
 
-size_t route_mfma_smem(int D) {
-  return (size_t)kRTok * (D + 8) * 2 + (size_t)(D / 64) * kRTok * 4 +
-         (size_t)kRWaves * 4 * 64 * 4 + (size_t)kRWaves * 128 * 8;
+size_t route_mfma_smem(int D, int kp) {
+  const int P = D / 64 / kp;
+  return (size_t)kRTok * (P * 64 + 8) * 2 + (size_t)P * kRTok * 4 + (size_t)kRWaves * 128 * 8;
 }
 
 template <bool F16X, int NV, int R>
-__global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp, int tpb) {
+__global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp) {
   extern __shared__ __align__(16) uint8_t rsm[];
-  __shared__ int s_last;
-  const int D = a.D, E = a.E, G = D / 64, ldx = D + 8, W8 = D / 8;
-  uint16_t *sx = (uint16_t *)rsm;                       // [16][ldx] activation bits
-  float *sX = (float *)(rsm + (size_t)kRTok * ldx * 2);  // [G][16] 64-column sums
-  float *red = sX + G * kRTok;                          // [waves][4][64] partial logits
-  uint2 *xch = (uint2 *)(red + kRWaves * 4 * 64);       // [waves][128] top-k exchange
+  const int D = a.D, E = a.E, G = D / 64, W8 = D / 8;
+  const int part = blockIdx.x, tt = blockIdx.y;
+  const int P = G / kp, g0 = part * P, ldx = P * 64 + 8, PW = P * 8;
+  uint16_t *sx = (uint16_t *)rsm;                       // [16][ldx] this part's activation bits
+  float *sX = (float *)(rsm + (size_t)kRTok * ldx * 2);  // [P][16] 64-column sums
+  uint2 *xch = (uint2 *)(sX + P * kRTok);               // [waves][128] top-k exchange
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int es = blockIdx.x, ES = gridDim.x, tt = blockIdx.y;
   const int t0 = tt * kRTok, nt = min(kRTok, a.T - t0);
+  // the token tile's epoch, read with a vector load: nothing waits for it
+  // before the logits are published
+  const uint32_t tag =
+      __hip_atomic_load(a.rep + tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
   // clear the counters of the kernel that follows
   if (a.zero) {
-    const int bl = tt * ES + es, nbl = ES * gridDim.y;
+    const int bl = tt * gridDim.x + part, nbl = gridDim.x * gridDim.y;
     for (int i = bl * kRThr + tid; i < a.zero_words; i += nbl * kRThr) a.zero[i] = 0u;
     for (int i = bl * kRThr + tid; i < a.zero2_count; i += nbl * kRThr)
       a.zero2[(size_t)i * a.zero2_stride] = 0u;
   }
 
-  // activations: 8-column words into LDS as they are, 64-column sums
-  // (sum8_lanes order, as the row router).  No global store here: a store
-  // in the loop would make each later wait for a load also wait for it.
+  // this part's activations: 8-column words into LDS as they are, 64-column
+  // sums (sum8_lanes order, as the row router).  No global store in this
+  // loop: a store would make each later wait for a load also wait for it.
   const uint16_t *x = (const uint16_t *)a.x;
-  const int gw0 = es * G / ES, gw1 = (es + 1) * G / ES;
   u32x4 xv[kRMaxWords];
 #pragma unroll
   for (int r = 0; r < kRMaxWords; ++r) {
-    const int i = min(tid + r * kRThr, kRTok * W8 - 1);
-    const int tk = min(i / W8, nt - 1), w = i % W8;
-    xv[r] = *(const u32x4 *)(x + (size_t)(t0 + tk) * D + 8 * w);
+    const int i = min(tid + r * kRThr, kRTok * PW - 1);
+    const int tk = min(i / PW, nt - 1), w = i % PW;
+    xv[r] = *(const u32x4 *)(x + (size_t)(t0 + tk) * D + 64 * g0 + 8 * w);
   }
 #pragma unroll
   for (int r = 0; r < kRMaxWords; ++r) {
     const int i = tid + r * kRThr;
-    if (r * kRThr >= kRTok * W8) break;  // uniform over the block
-    const bool in = i < kRTok * W8;
-    const int tk = i / W8, w = i - tk * W8;
+    if (r * kRThr >= kRTok * PW) break;  // uniform over the block
+    const bool in = i < kRTok * PW;
+    const int tk = i / PW, w = i - tk * PW;
     const bool tok = in && tk < nt;
     const uint32_t wd[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
     if (in) *(u32x4 *)(sx + (size_t)tk * ldx + 8 * w) = tok ? xv[r] : u32x4{0u, 0u, 0u, 0u};
@@ -386,97 +393,112 @@ __global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp
     if (in && (w & 7) == 0) sX[(w >> 3) * kRTok + tk] = tok ? gs : 0.0f;
   }
   __syncthreads();
-  // block es writes the pairs and sums the 4-bit expert kernels read, for
-  // its share of the groups, from LDS
-  for (int i = tid; i < nt * (gw1 - gw0) * 8; i += kRThr) {
-    const int tk = i / ((gw1 - gw0) * 8), w = gw0 * 8 + (i - tk * (gw1 - gw0) * 8);
+  // the pairs and sums the 4-bit expert kernels read, for this part's groups
+  for (int i = tid; i < nt * PW; i += kRThr) {
+    const int tk = i / PW, w = i - tk * PW;
     const u32x4 v = *(const u32x4 *)(sx + (size_t)tk * ldx + 8 * w);
     const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      o[m] = ((wd[m / 2] >> (16 * (m % 2))) & 0xFFFFu) | (((wd[2 + m / 2] >> (16 * (m % 2))) & 0xFFFFu) << 16);
-    *(u32x4 *)(a.xp + (size_t)(t0 + tk) * (D / 2) + 4 * w) = u32x4{o[0], o[1], o[2], o[3]};
-    if ((w & 7) == 0) a.xs[(size_t)(t0 + tk) * G + (w >> 3)] = sX[(w >> 3) * kRTok + tk];
+      o[m] = ((wd[m / 2] >> (16 * (m % 2))) & 0xFFFFu) |
+             (((wd[2 + m / 2] >> (16 * (m % 2))) & 0xFFFFu) << 16);
+    *(u32x4 *)(a.xp + (size_t)(t0 + tk) * (D / 2) + 32 * g0 + 4 * w) = u32x4{o[0], o[1], o[2], o[3]};
+    if ((w & 7) == 0) a.xs[(size_t)(t0 + tk) * G + g0 + (w >> 3)] = sX[(w >> 3) * kRTok + tk];
   }
 
-  // wave w: expert tile es tpb + w / kp, groups of part w % kp; lane l
-  // supplies expert 16 tile + l % 16 and the 16-column chunk l / 16
+  // this part's sums of the logits: wave w takes expert tiles w, w + 8, ...;
+  // lane l supplies expert 16 tile + l % 16 and the 16-column chunk l / 16
   const int NT = (E + 15) / 16, g4 = lane >> 4, col = lane & 15;
-  const int tl = wave / kp, part = wave - tl * kp, et = es * tpb + tl;
-  const bool live = tl < tpb && et < NT;
-  const int P = G / kp;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (live) {
+  uint64_t *mine = a.rtag + (size_t)part * a.T * E;
+  for (int et = wave; et < NT; et += kRWaves) {
     const int e = min(et * 16 + col, E - 1);
-    tile_logits<F16X, R>(a, part * P, P, e, g4, sx + (size_t)col * ldx + 16 * g4, sX, acc);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 64 + lane] = acc[i];
-  __syncthreads();
-  if (live && part == 0) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    tile_logits<F16X, R>(a, g0, P, e, g4, sx + (size_t)col * ldx + 16 * g4, sX, acc);
     const int ee = et * 16 + col;
-    const float lb = (a.logit_bias && ee < E) ? a.logit_bias[ee] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = red[(wave * 4 + i) * 64 + lane];
-      for (int pp = 1; pp < kp; ++pp) v += red[((wave + pp) * 4 + i) * 64 + lane];
-      if (a.logit_bias) v += lb;
       const int row = 4 * g4 + i;
-      if (ee < E && row < nt) st_dev(a.logits + (size_t)(t0 + row) * E + ee, v);
+      if (ee < E && row < nt)
+        st_dev(mine + (size_t)(t0 + row) * E + ee,
+               (uint64_t)__float_as_uint(acc[i]) | ((uint64_t)tag << 32));
     }
   }
-  // the last block of the token tile selects
-  wait_all_memory();
-  __syncthreads();
-  if (tid == 0) s_last = add_dev(&a.counters[tt], 1u) == (uint32_t)(ES - 1);
-  __syncthreads();
-  if (!s_last) return;
-  // wave w selects rows w and w + 8, both rows' logits requested first
-  static_assert(kRTok == 2 * kRWaves, "two rows per wave");
-  float v[2][NV];
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int row = min(wave + kRWaves * rr, nt - 1);
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-      v[rr][j] = ld_dev(a.logits + (size_t)(t0 + row) * E + min(lane + 64 * j, E - 1));
-  }
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int row = wave + kRWaves * rr;
+
+  // selection: this block's share of the tile's tokens, one per wave
+  const int per = (kRTok + kp - 1) / kp;
+  for (int j = wave; j < per; j += kRWaves) {
+    const int row = part * per + j;
     if (row >= nt) break;  // uniform over the wave
+    const int t = t0 + row;
+    // every part's words of the token in one round trip per try
+    uint64_t w[kRouteParts][NV];
+    for (long sp = 0;; ++sp) {
+      bool ok = true;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if (lane + 64 * j >= E) v[rr][j] = -INFINITY;
+      for (int pp = 0; pp < kRouteParts; ++pp) {
+        const uint64_t *src = a.rtag + ((size_t)min(pp, kp - 1) * a.T + t) * E;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+          w[pp][q] = ld_dev(src + min(lane + 64 * q, E - 1));
+          ok = ok && (pp >= kp || (uint32_t)(w[pp][q] >> 32) == tag);
+        }
+      }
+      if (__all(ok) || sp > kRSpin) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    float v[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      v[q] = 0.0f;
+#pragma unroll
+      for (int pp = 0; pp < kRouteParts; ++pp)  // part order
+        if (pp < kp) v[q] += __uint_as_float((uint32_t)w[pp][q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) {
+        if (a.logit_bias) v[q] += a.logit_bias[e];
+        a.logits[(size_t)t * E + e] = v[q];
+      } else {
+        v[q] = -INFINITY;
+      }
+    }
     int32_t id;
     float gate;
-    topk_regs(v[rr], a.k, xch + wave * 128, &id, &gate);
-    const size_t o = (size_t)(t0 + row) * a.k + lane;
+    topk_regs(v, a.k, xch + wave * 128, &id, &gate);
+    const size_t o = (size_t)t * a.k + lane;
     if (lane < a.k) {
       a.ids[o] = id;
       a.gates[o] = gate;
       if (a.slot_blob) a.slot_blob[o] = a.table[id];
     }
   }
-  if (tid == 0) st_dev(&a.counters[tt], 0u);
+  // every block of the tile has read its epoch (their logits are in), so
+  // part 0 can advance it, and the copies tt + j ntt with it, once its own
+  // selection is done: all copies move in step whatever the next call's T
+  __syncthreads();
+  const int ntt = gridDim.y;
+  if (part == 0)
+    for (int j = tt + tid * ntt; j < kMaxRouteTiles; j += kRThr * ntt)
+      __hip_atomic_store(a.rep + j, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool F16X, int NV, int R>
 hipError_t launch_route_mfma_r(const RouteLaunch &a, int kp, hipStream_t s) {
-  const size_t smem = route_mfma_smem(a.D);
+  const size_t smem = route_mfma_smem(a.D, kp);
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void *)route_mfma_kernel<F16X, NV, R>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  const int tpb = kRWaves / kp, NT = (a.E + 15) / 16;
-  const dim3 grid((NT + tpb - 1) / tpb, (a.T + kRTok - 1) / kRTok);
-  hipLaunchKernelGGL((route_mfma_kernel<F16X, NV, R>), grid, dim3(kRThr), smem, s, a, kp, tpb);
+  const dim3 grid(kp, (a.T + kRTok - 1) / kRTok);
+  hipLaunchKernelGGL((route_mfma_kernel<F16X, NV, R>), grid, dim3(kRThr), smem, s, a, kp);
   return hipGetLastError();
 }
-// kp parts of the groups per expert tile (4 when they divide, so that more
-// blocks share the work), and the deepest ring that divides a part
+// kp parts of the groups (4 when they divide), and the deepest ring that
+// divides a part
 template <bool F16X, int NV>
 hipError_t launch_route_mfma_t(const RouteLaunch &a, hipStream_t s) {
   const int G = a.D / 64;
@@ -533,11 +555,29 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
   // prefill.  MAXC: 16-column chunks per thread (64 threads split a row, the
   // same split and order as the one-launch decode layer's router).
   const bool small_d = a.D <= 3072;
-  if (a.T >= 16 && tuning().route_mfma && a.E <= 256 && a.D <= 4096 &&
-      route_mfma_smem(a.D) <= 160 * 1024) {
-    if (a.E <= 128)
-      return a.f16x ? launch_route_mfma_t<true, 2>(a, s) : launch_route_mfma_t<false, 2>(a, s);
-    return a.f16x ? launch_route_mfma_t<true, 4>(a, s) : launch_route_mfma_t<false, 4>(a, s);
+  if (a.T >= 16 && tuning().route_mfma && a.E <= 256 && a.D <= 4096 && a.rtag && a.rep) {
+    // windows of as many tokens as the tagged area holds (whole 16-token tiles)
+    const int win = (int)(kRouteTagBytes / (sizeof(uint64_t) * kRouteParts * a.E)) / kRTok * kRTok;
+    for (int t0 = 0; t0 < a.T; t0 += win) {
+      RouteLaunch b = a;
+      const int n = std::min(win, a.T - t0);
+      b.T = n;
+      b.x = (const uint16_t *)a.x + (size_t)t0 * a.D;
+      b.logits = a.logits + (size_t)t0 * a.E;
+      b.ids = a.ids + (size_t)t0 * a.k;
+      b.gates = a.gates + (size_t)t0 * a.k;
+      if (a.slot_blob) b.slot_blob = a.slot_blob + (size_t)t0 * a.k;
+      b.xp = a.xp + (size_t)t0 * (a.D / 2);
+      b.xs = a.xs + (size_t)t0 * (a.D / 64);
+      if (t0 > 0) b.zero = nullptr, b.zero_words = 0, b.zero2 = nullptr, b.zero2_count = 0;
+      hipError_t e;
+      if (a.E <= 128)
+        e = a.f16x ? launch_route_mfma_t<true, 2>(b, s) : launch_route_mfma_t<false, 2>(b, s);
+      else
+        e = a.f16x ? launch_route_mfma_t<true, 4>(b, s) : launch_route_mfma_t<false, 4>(b, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (a.T >= 16) {
     if (small_d)
