@@ -62,7 +62,7 @@ def oracle_layer(L, xf, k, bias=None, ids=None):
 @pytest.mark.parametrize("name,T,beta,mfma", [("tiny", 4, 0.0, 1), ("tiny", 37, 1.0, 1),
                                               ("decode", 1, 0.0, 1), ("decode", 5, 6.5, 1),
                                               ("decode", 128, 1.5, 1), ("decode", 77, 1.5, 1),
-                                              ("decode", 128, 1.5, 0)])
+                                              ("decode", 128, 1.5, 0), ("decode", 2100, 1.5, 1)])
 def test_route_parity(name, T, beta, mfma):
     """Row router (fewer than 16 tokens, or route_mfma=0) and the matrix-core
     router (16 or more tokens per call; 77 leaves a ragged last block)."""
@@ -229,8 +229,12 @@ def test_combine_parity(out_dtype):
 
 # ---------------------------------------------------------------- permutation
 @pytest.mark.parametrize("T,k,E,beta", [(128, 8, 128, 1.5), (77, 8, 128, 0.0), (4, 4, 16, 0.0),
-                                        (1, 8, 128, 0.0), (128, 8, 128, 8.0)])
+                                        (1, 8, 128, 0.0), (128, 8, 128, 8.0),
+                                        (200, 8, 128, 1.5), (1100, 8, 128, 1.5)])
 def test_permute_bit_exact(T, k, E, beta):
+    """One wave per 64-pair chunk (up to 16 chunks), one wave walking the
+    chunks in order (200 tokens: 25 chunks), and ids read from memory
+    instead of LDS (1100 tokens: 8,800 pairs)."""
     _case(f"permute T={T} k={k} E={E}")
     rng = np.random.default_rng(T + E)
     w = np.exp(-beta * 1.1 * np.log(1 + rng.permutation(E)))
@@ -478,6 +482,31 @@ def test_layer_forward_prefill_ragged_chunk():
     busiest = int(np.argmax(counts))
     toks = sorted(set(np.nonzero(ids == busiest)[0].tolist()))
     _check_layer(L, xb, out.cpu().numpy(), ids, cfg.k, bias, tokens=toks[:6] + toks[-6:] + [76])
+
+
+def test_layer_forward_prefill_long_call():
+    """2,100 tokens in one call: the matrix-core router's tagged partial
+    logits in three windows of 1,024 tokens, the permutation with ids read
+    from memory, and the work list in expert order (more row buckets than
+    its table holds).  Sampled tokens at the window edges and the busiest
+    expert's rows against the oracle; one token against its own decode."""
+    T = 2100
+    _case(f"layer_forward prefill T={T} beta=1.5")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    xb = gen.activations(0, 3, 0, T, cfg.D, cfg.x_dtype)
+    bias = gen.zipf_bias(0, 3, cfg.E, 1.5)
+    out, ids, _ = _layer_gpu(L, xb, cfg.k, bias)
+    got = out.cpu().numpy()
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    assert counts.sum() == T * cfg.k and counts.max() > 32
+    busiest = int(np.argmax(counts))
+    toks = sorted(set(np.nonzero(ids == busiest)[0].tolist()))
+    edge = [0, 1, 1023, 1024, 1025, 2047, 2048, 2099]
+    _check_layer(L, xb, got, ids, cfg.k, bias, tokens=sorted(set(edge + toks[:4] + toks[-4:])))
+    o1, i1, _ = _layer_gpu(L, xb[1500:1501], cfg.k, bias)
+    assert np.array_equal(i1[0], ids[1500])
+    assert rel_l2(o1.cpu().numpy()[0], got[1500]) < 1e-5
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
