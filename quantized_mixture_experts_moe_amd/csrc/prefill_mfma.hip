@@ -25,7 +25,7 @@
 //   group; the affine terms fold per group as s * acc + (b - 128 s) * sum(x).
 //   h = gelu(gate) * up is written as three bf16 planes (hi + mid + lo, 24
 //   bits) and 64-unit sums.
-// down (down_mfma_kernel): block = (expert, 256 output rows, 32 group rows);
+// down (down_mfma_kernel): block = (expert, 256 output rows, 16 group rows);
 //   per hidden group the block stages the down codes, their scale/bias words
 //   and the three planes of h (once for its 256 rows: wave w computes output
 //   rows 64w..64w+63).  B operand: codes as bf16 1 + q/16 (a nibble in the
@@ -312,16 +312,16 @@ __global__ __launch_bounds__(256, 4) void glu_mfma_kernel(PrefillLaunch p) {
 }
 
 // ---------------------------------------------------------------- down
-constexpr int kRd = 3;   // LDS stages of the down ring (kRd - 1 groups in flight)
-constexpr int kDT = 4;   // 16-row output tiles per wave (a block covers 256 output rows)
+constexpr int kRd = 3;    // LDS stages of the down ring (kRd - 1 groups in flight)
+constexpr int kDT = 4;    // 16-row output tiles per wave (a block covers 256 output rows)
+constexpr int kDRows = 16;  // group rows per down block (one matrix tile)
 
 struct DownBuf {
-  u32x4_t pl[3][kRows * 8];   // planes of h (pair order) for the 32 rows, xslot order
+  u32x4_t pl[3][kDRows * 8];  // planes of h (pair order) for the 16 rows, xslot order
   u32x4_t w[2][4 * 64];       // down codes, chunks 2gi and 2gi + 1; row = 64 wave + lane
   uint32_t m[4 * 64];         // scale/bias words of the 256 rows
 };
 
-template <int NM>
 __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g, int nb, int m0,
                                           int nrow, int gbeg, int GH, float *dst, int row0,
                                           const int *s_row, const float *s_hs, DownBuf &b0,
@@ -335,79 +335,74 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   const int D = p.D, F = g.F, GHa = F / 64;
   const int col = lane & 15, kb = lane >> 4;
   const BlobLayout L = blob_layout(D, F);
-  // this wave stages, per hidden group: the three planes of rows 8 wave ..
-  // 8 wave + 7 (lane p: row t = 8 wave + p / 8, vector (p % 8) ^ (t & 7), so
-  // that it lands in its xslot), the two code chunks and the scale/bias word
-  // of output row 64 wave + lane
-  const int xt = 8 * wave + (lane >> 3), xv = (lane & 7) ^ (xt & 7);
-  const u32x4_t *hsrc = (const u32x4_t *)(p.hp + hrow_off(p, s_row[xt])) + xv;
+  // this wave stages, per hidden group: plane wave % 3 of the 16 rows (two
+  // loads of 8 rows; wave 3 loads plane 0 again, onto the same words, so
+  // that every wave issues the same loads and the waits stay exact; lane p:
+  // row t = 8 j + p / 8, vector (p % 8) ^ (t & 7), so that it lands in its
+  // xslot), the two code chunks and the scale/bias word of output row
+  // 64 wave + lane
+  const int pq = wave % 3;
+  const int xv = (lane & 7) ^ ((lane >> 3) & 7);
   const size_t plane_v = p.plane / 8;  // plane size in 16-byte vectors
+  const u32x4_t *hsrc0 = (const u32x4_t *)(p.hp + hrow_off(p, s_row[lane >> 3])) + pq * plane_v + xv;
+  const u32x4_t *hsrc1 =
+      (const u32x4_t *)(p.hp + hrow_off(p, s_row[8 + (lane >> 3)])) + pq * plane_v + xv;
   const int wrow = min(nb * 256 + wave * 64 + lane, D - 1);
   const u32x4_t *wsrc = (const u32x4_t *)(g.blob + L.down_codes) + wrow;
   const uint32_t *msrc = (const uint32_t *)(g.blob + L.down_meta) + wrow;
   auto issue = [&](DownBuf &B, int gi) {
     gi = gbeg + min(gi, GH - 1);  // past the end: a repeat of the last group, folded with weight 0
-#pragma unroll
-    for (int q = 0; q < 3; ++q) dma16(hsrc + q * plane_v + gi * 8, &B.pl[q][64 * wave]);
+    dma16(hsrc0 + gi * 8, &B.pl[pq][0]);
+    dma16(hsrc1 + gi * 8, &B.pl[pq][64]);
     dma16(wsrc + (size_t)(2 * gi) * D, &B.w[0][64 * wave]);
     dma16(wsrc + (size_t)(2 * gi + 1) * D, &B.w[1][64 * wave]);
     dma4(msrc + (size_t)gi * D, &B.m[64 * wave]);
   };
   const uint32_t umagic = opaque_vgpr(0x3F803F80u);  // bf16 1.0 pairs
 
-  f32x4_t t[NM][kDT];
+  f32x4_t t[kDT];
 #pragma unroll
-  for (int mt = 0; mt < NM; ++mt)
-#pragma unroll
-    for (int j = 0; j < kDT; ++j) t[mt][j] = f32x4_t{0, 0, 0, 0};
+  for (int j = 0; j < kDT; ++j) t[j] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
   for (int s = 0; s < kRd - 1; ++s) issue(buf(s), s);
   for (int g0 = 0; g0 < GH; g0 += kRd) {
 #pragma unroll
     for (int s = 0; s < kRd; ++s) {
       const int gi = g0 + s;
-      // this group's stage is in (6 loads per stage per wave; kRd - 2 later
+      // this group's stage is in (5 loads per stage per wave; kRd - 2 later
       // stages may stay in flight), and every wave is done with group gi - 1
-      stage_barrier<6 * (kRd - 2)>();
+      stage_barrier<5 * (kRd - 2)>();
       issue(buf((s + kRd - 1) % kRd), gi + kRd - 1);
       const DownBuf &B = buf(s);
       const bool live = gi < GH;
       const int gx = gbeg + min(gi, GH - 1);
-      // the planes of this wave's rows, shared by its kDT output tiles
-      u32x4_t a_in[NM][2][3];
+      // the planes of the block's rows, shared by the wave's kDT output tiles
+      u32x4_t a_in[2][3];
 #pragma unroll
-      for (int mt = 0; mt < NM; ++mt)
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int q = 0; q < 3; ++q) a_in[half][q] = B.pl[q][xslot(col, half * 4 + kb)];
+      float hs[4];
 #pragma unroll
-          for (int q = 0; q < 3; ++q) a_in[mt][half][q] = B.pl[q][xslot(mt * 16 + col, half * 4 + kb)];
+      for (int i = 0; i < 4; ++i) hs[i] = s_hs[(kb * 4 + i) * GHa + gx];
 #pragma unroll
       for (int j = 0; j < kDT; ++j) {
         // output tile j of this wave: rows 64 wave + 16 j + col
         const int r = wave * 64 + j * 16 + col;
-        f32x4_t a[NM];
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) a[mt] = f32x4_t{0, 0, 0, 0};
+        f32x4_t a = f32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const u32x4_t b = code_pairs_unit(((const uint32_t *)&B.w[half][r])[kb], umagic);
-#pragma unroll
-          for (int mt = 0; mt < NM; ++mt) {
-            a[mt] = mfma<false>(a_in[mt][half][0], b, a[mt]);
-            a[mt] = mfma<false>(a_in[mt][half][1], b, a[mt]);
-            a[mt] = mfma<false>(a_in[mt][half][2], b, a[mt]);
-          }
+          a = mfma<false>(a_in[half][0], b, a);
+          a = mfma<false>(a_in[half][1], b, a);
+          a = mfma<false>(a_in[half][2], b, a);
         }
         // sum h (1 + q/16) = sum h + sum h q / 16: fold s q + b per group
         const uint32_t mw = B.m[r];
         const float sd = live ? f16_to_f32(mw) : 0.0f, bd = live ? f16_to_f32(mw >> 16) : 0.0f;
         const float s16 = 16.0f * sd, c16 = fmaf(-16.0f, sd, bd);
 #pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            t[mt][j][i] = fmaf(s16, a[mt][i], fmaf(c16, s_hs[(mt * 16 + kb * 4 + i) * GHa + gx], t[mt][j][i]));
-        }
+        for (int i = 0; i < 4; ++i) t[j][i] = fmaf(s16, a[i], fmaf(c16, hs[i], t[j][i]));
       }
     }
   }
@@ -417,26 +412,25 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   for (int j = 0; j < kDT; ++j) {
     const int n = nb * 256 + wave * 64 + j * 16 + col;  // output row of this lane's column
 #pragma unroll
-    for (int mt = 0; mt < NM; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + kb * 4 + i;
-        if (m < nrow && n < D) dst[(size_t)(row0 + m0 + m) * D + n] = t[mt][j][i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int m = kb * 4 + i;
+      if (m < nrow && n < D) dst[(size_t)(row0 + m0 + m) * D + n] = t[j][i];
     }
   }
 }
 
-__global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
-  __shared__ int s_row[kRows];
-  __shared__ float s_hs[kRows * kMaxHGroups];
+__global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
+  __shared__ int s_row[kDRows];
+  __shared__ float s_hs[kDRows * kMaxHGroups];
   __shared__ DownBuf b0, b1, b2;
   static_assert(kRd == 3, "one LDS object per stage");
+  static_assert(kRows == 2 * kDRows, "two down row chunks per work-list item");
   // blocks: the shared expert's first, its hidden groups split sks ways (as
   // many groups per block as a routed expert has), then the work list's
-  // items x 256 output rows
+  // items x their two 16-row halves x 256 output rows (the second half of
+  // an item with 16 rows or fewer returns at once)
   const int D = p.D, NB = (D + 255) / 256;
-  const int mch = (p.T + kRows - 1) / kRows, nsh = p.sblobs ? p.sks * mch * NB : 0;
+  const int mch = (p.T + kDRows - 1) / kDRows, nsh = p.sblobs ? p.sks * mch * NB : 0;
   const int bid = blockIdx.x;
   int g_idx, nb, yc, ks = 0;
   if (bid < nsh) {
@@ -446,33 +440,31 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(PrefillLaunch p) {
     yc = r / NB;
     nb = r - yc * NB;
   } else {
-    const int r = bid - nsh, item = r / NB;
+    const int r = bid - nsh, item = r / (2 * NB);
     if (item >= *p.n_items) return;
     const int it = p.items[item];
+    const int rr = r - item * 2 * NB, half = rr / NB;
     g_idx = it & 0xFFFF;
-    yc = it >> 16;
-    nb = r - item * NB;
+    yc = 2 * (it >> 16) + half;
+    nb = rr - half * NB;
   }
   const Group g = group_of(p, g_idx);
-  const int m0 = yc * kRows;
+  const int m0 = yc * kDRows;
   if (g.count <= m0) return;
-  const int nrow = min(kRows, g.count - m0);
+  const int nrow = min(kDRows, g.count - m0);
   const int GH = g.F / 64;
   const int gbeg = g.shared ? ks * GH / p.sks : 0, gend = g.shared ? (ks + 1) * GH / p.sks : GH;
   // routed rows into y (at their pair row), shared rows into partial ks of ys
   float *dst = g.shared ? p.ys + (size_t)ks * p.T * D : p.y;
   const int row0 = g.shared ? 0 : g.off;
-  for (int i = threadIdx.x; i < kRows; i += 256) s_row[i] = g.off + m0 + min(i, nrow - 1);
+  for (int i = threadIdx.x; i < kDRows; i += 256) s_row[i] = g.off + m0 + min(i, nrow - 1);
   __syncthreads();
-  for (int i = threadIdx.x; i < kRows * GH; i += 256) {
+  for (int i = threadIdx.x; i < kDRows * GH; i += 256) {
     const int m = i / GH, gg = i - m * GH;
     s_hs[i] = p.hsum[hrow_off(p, s_row[m]) / 64 + gg];
   }
   __syncthreads();
-  if (nrow <= 16)
-    down_body<1>(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
-  else
-    down_body<2>(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
+  down_body(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
 }
 
 // four consecutive outputs per thread (16-byte loads of y), the k routed
@@ -538,7 +530,8 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb4 = (p.D + 255) / 256;  // 256 output rows per down block
-  dim3 g2(max_items * nb4 + (p.sblobs ? p.sks * nb4 * mchunks : 0));
+  const int mch16 = (p.T + 15) / 16;  // 16-row chunks of the shared expert
+  dim3 g2(2 * max_items * nb4 + (p.sblobs ? p.sks * nb4 * mch16 : 0));
   hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
