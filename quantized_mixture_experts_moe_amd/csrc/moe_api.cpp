@@ -371,7 +371,7 @@ moe_status moe_route(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *
   const Dims d{T, k, E, D, 64, 0};
   if (ws_bytes < workspace_bytes(d)) return MOE_E_WORKSPACE;
   Workspace w = carve(ws, d);
-  RouteLaunch a;
+  RouteLaunch a{};
   a.x = x; a.f16x = x_dtype == MOE_F16; a.T = T; a.D = D; a.E = E; a.k = k;
   a.codes = (const uint8_t *)router->codes; a.meta = (const uint32_t *)router->meta;
   a.logit_bias = logit_bias;
@@ -471,7 +471,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     return hip_status(prof_end(pi, s, launch_layer(L, s)));
   }
 
-  RouteLaunch r;
+  RouteLaunch r{};
   r.zero = nullptr; r.zero_words = 0; r.zero2 = nullptr; r.zero2_count = 0; r.zero2_stride = 0;
   r.x = x; r.f16x = x_dtype == MOE_F16; r.T = T; r.D = D; r.E = E; r.k = k;
   r.codes = (const uint8_t *)router->codes; r.meta = (const uint32_t *)router->meta;
@@ -483,6 +483,10 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   // streamed experts: the pool writes the slot addresses after its copies
   r.table = pool ? nullptr : routed->blobs;
   r.slot_blob = pool ? nullptr : w.slot_blob;
+  if (pool) {
+    st = pool_route_ids(pool, T, k, &r.host_ids, &r.host_flag, &r.host_epoch);
+    if (st) return st;
+  }
 
   ExpertLaunch a{};
   a.f16x = r.f16x; a.T = T; a.k = k; a.D = D; a.E = E;
@@ -510,13 +514,15 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     if (st) return st;
     const int NR = L.NR, NS = layer_shared_blocks(L);
     if (launch_layer_range(L, NR, NS, s) != hipSuccess) return MOE_E_HIP;
-    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, w.slot_blob);
+    const void *const *slots = nullptr;
+    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, &slots);
     if (st) return st;
-    L.given_blob = w.slot_blob;
+    L.given_blob = slots;
     L.given_gates = r.gates;
     L.ids_out = nullptr;  // already written by the router kernel
     L.gates_out = nullptr;
-    return hip_status(launch_layer_range(L, 0, NR, s));
+    if (launch_layer_range(L, 0, NR, s) != hipSuccess) return MOE_E_HIP;
+    return pool_slots_read(pool, s);
   }
   if (fused && !pool) {
     const int pi = prof_begin(s);
@@ -535,11 +541,14 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     fs.tile_begin = n_routed_tiles;
     fs.do_down = 0;
     if (launch_fused(fs, s) != hipSuccess) return MOE_E_HIP;
-    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, w.slot_blob);
+    const void *const *slots = nullptr;
+    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, &slots);
     if (st) return st;
     FusedLaunch fr = f;
+    fr.a.slot_blob = slots;
     fr.tile_end = n_routed_tiles;
-    return hip_status(launch_fused(fr, s));
+    if (launch_fused(fr, s) != hipSuccess) return MOE_E_HIP;
+    return pool_slots_read(pool, s);
   }
   // prefill chunk: group the (token, slot) pairs by expert, then matrix cores
   if (!pool && T >= tuning().prefill_min_t && T * k <= 65536 && D / 64 <= kMaxDGroups &&

@@ -151,6 +151,10 @@ struct RouteLaunch {
   // [kRouteParts][T][E] and the epochs [kMaxRouteTiles], in the fixed
   // region (zero-filled once)
   uint64_t *rtag; uint32_t *rep;
+  // fewer than 16 tokens, streamed experts: the ids also go to pinned host
+  // memory (device-readable addresses), then host_flag[t] = host_epoch per
+  // token, so that the host reads them without a copy; null otherwise
+  int32_t *host_ids; uint32_t *host_flag; uint32_t host_epoch;
 };
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 // x pairs and 64-column sums for the expert kernels without routing

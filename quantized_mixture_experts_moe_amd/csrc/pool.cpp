@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <new>
 
 namespace moe {
@@ -72,10 +73,20 @@ struct moe_pool {
   const void **d_tables = nullptr;            // device [n_layers][E] blob pointers
   const void **h_tables = nullptr;            // pinned host mirror of d_tables
   int32_t *h_ids = nullptr;                   // pinned host ids of the last call
-  const void **h_slot = nullptr;              // pinned staging of per-pair slot addresses
+  const void **h_slot = nullptr;              // pinned per-pair slot addresses, read by the kernels
+  const void *const *d_slot = nullptr;        // the device's address of h_slot
   int ids_cap = 0;
   hipStream_t side = nullptr;
   hipEvent_t ev_ids = nullptr, ev_copies = nullptr;
+  hipEvent_t ev_slot = nullptr;               // after the last kernel that reads h_slot
+  bool slot_pending = false;
+  // ids written by the router kernel straight into host memory (fewer than
+  // 16 tokens): per-token flags carry the call's epoch
+  uint32_t *h_flag = nullptr;                 // pinned [ids_cap]
+  int32_t *d_ids_host = nullptr;              // device addresses of h_ids and h_flag
+  uint32_t *d_flag_host = nullptr;
+  uint32_t epoch = 0;
+  bool ids_direct = false;                    // the current call's ids come that way
   moe_pool_stats stats{};
 };
 
@@ -90,22 +101,69 @@ moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k) {
 
 int pool_F(const moe_pool *p) { return p->F; }
 
-moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s) {
+static moe_status ensure_ids(moe_pool *p, int n) {
   if (n > p->ids_cap) {
-    // earlier copies from the staging buffers have completed: every call
-    // waits on its id readback, which follows the previous call's kernels
+    // the kernels of earlier calls may still read h_slot
+    if (p->slot_pending && hipEventSynchronize(p->ev_slot) != hipSuccess) return MOE_E_HIP;
+    p->slot_pending = false;
+    // and every earlier router kernel that writes h_ids and h_flag
+    if (hipEventSynchronize(p->ev_ids) != hipSuccess) return MOE_E_HIP;
     if (p->h_ids) (void)hipHostFree(p->h_ids);
     if (p->h_slot) (void)hipHostFree(p->h_slot);
+    if (p->h_flag) (void)hipHostFree(p->h_flag);
     p->h_ids = nullptr;
     p->h_slot = nullptr;
+    p->h_flag = nullptr;
     p->ids_cap = 0;
-    if (hipHostMalloc((void **)&p->h_ids, sizeof(int32_t) * n, hipHostMallocDefault) !=
-            hipSuccess ||
-        hipHostMalloc((void **)&p->h_slot, sizeof(void *) * n, hipHostMallocDefault) !=
-            hipSuccess)
+    // coherent (uncached on the device): the kernels read what the host
+    // wrote before their launch, and the host polls what they write
+    const unsigned fl = hipHostMallocCoherent;
+    if (hipHostMalloc((void **)&p->h_ids, sizeof(int32_t) * n, fl) != hipSuccess ||
+        hipHostMalloc((void **)&p->h_slot, sizeof(void *) * n, fl) != hipSuccess ||
+        hipHostMalloc((void **)&p->h_flag, sizeof(uint32_t) * n, fl) != hipSuccess)
       return MOE_E_HIP;
+    for (int i = 0; i < n; ++i) p->h_flag[i] = 0u;
+    p->epoch = 0;
+    void *dv = nullptr, *di = nullptr, *df = nullptr;
+    if (hipHostGetDevicePointer(&dv, p->h_slot, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&di, p->h_ids, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&df, p->h_flag, 0) != hipSuccess)
+      return MOE_E_HIP;
+    p->d_slot = (const void *const *)dv;
+    p->d_ids_host = (int32_t *)di;
+    p->d_flag_host = (uint32_t *)df;
     p->ids_cap = n;
   }
+  return MOE_OK;
+}
+
+moe_status pool_route_ids(moe_pool *p, int T, int k, int32_t **host_ids, uint32_t **host_flag,
+                          uint32_t *epoch) {
+  *host_ids = nullptr;
+  *host_flag = nullptr;
+  *epoch = 0;
+  p->ids_direct = false;
+  if (T >= 16) return MOE_OK;  // the matrix-core router: ids copied back
+  const moe_status st = ensure_ids(p, T * k);
+  if (st) return st;
+  if (++p->epoch == 0) {  // wrapped: no flag may hold the new epoch already
+    for (int i = 0; i < p->ids_cap; ++i) p->h_flag[i] = 0u;
+    p->epoch = 1;
+  }
+  *host_ids = p->d_ids_host;
+  *host_flag = p->d_flag_host;
+  *epoch = p->epoch;
+  p->ids_direct = true;
+  return MOE_OK;
+}
+
+moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s) {
+  if (p->ids_direct) {
+    // the router kernel writes them; the event is the fallback wait
+    return hipEventRecord(p->ev_ids, s) == hipSuccess ? MOE_OK : MOE_E_HIP;
+  }
+  const moe_status st = ensure_ids(p, n);
+  if (st) return st;
   if (hipMemcpyAsync(p->h_ids, d_ids, sizeof(int32_t) * n, hipMemcpyDeviceToHost, s) !=
       hipSuccess)
     return MOE_E_HIP;
@@ -113,9 +171,31 @@ moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t 
   return MOE_OK;
 }
 
+// Waits until the router kernel's per-token flags carry the call's epoch:
+// a short spin (the ids arrive a few microseconds after the kernel ends),
+// then a blocking wait for the kernel, after which they must be there.
+static moe_status wait_direct_ids(moe_pool *p, int T) {
+  auto ready = [&]() {
+    for (int t = 0; t < T; ++t)
+      if (__atomic_load_n(p->h_flag + t, __ATOMIC_ACQUIRE) != p->epoch) return false;
+    return true;
+  };
+  const auto t0 = std::chrono::steady_clock::now();
+  while (!ready()) {
+    if (std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(2000)) {
+      if (hipEventSynchronize(p->ev_ids) != hipSuccess) return MOE_E_HIP;
+      return ready() ? MOE_OK : MOE_E_HIP;
+    }
+  }
+  return MOE_OK;
+}
+
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
-                              const void *const **table, const void **slot_blob) {
-  if (hipEventSynchronize(p->ev_ids) != hipSuccess) return MOE_E_HIP;
+                              const void *const **table, const void *const **slot_blob) {
+  const moe_status ws = p->ids_direct ? wait_direct_ids(p, T)
+                                      : (hipEventSynchronize(p->ev_ids) == hipSuccess ? MOE_OK
+                                                                                       : MOE_E_HIP);
+  if (ws) return ws;
   // distinct experts of the call in first-use order
   std::vector<int> need;
   need.reserve(T * k);
@@ -155,17 +235,25 @@ moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t 
       return MOE_E_HIP;
   }
   if (slot_blob) {
+    // the kernels read the addresses from pinned host memory: no copy, and
+    // with every expert resident nothing for stream s to wait on.  The
+    // previous reader has finished (it precedes this call's id readback on
+    // the stream; the event covers callers that switch streams).
+    if (p->slot_pending && hipEventSynchronize(p->ev_slot) != hipSuccess) return MOE_E_HIP;
     for (int i = 0; i < T * k; ++i) p->h_slot[i] = tab[p->h_ids[i]];
-    if (hipMemcpyAsync(slot_blob, p->h_slot, sizeof(void *) * T * k, hipMemcpyHostToDevice,
-                       p->side) != hipSuccess)
-      return MOE_E_HIP;
-    queued = true;
+    *slot_blob = p->d_slot;
   }
   if (queued) {
     if (hipEventRecord(p->ev_copies, p->side) != hipSuccess) return MOE_E_HIP;
     if (hipStreamWaitEvent(s, p->ev_copies, 0) != hipSuccess) return MOE_E_HIP;
   }
   if (table) *table = p->d_tables + (size_t)layer * p->E;
+  return MOE_OK;
+}
+
+moe_status pool_slots_read(moe_pool *p, hipStream_t s) {
+  if (hipEventRecord(p->ev_slot, s) != hipSuccess) return MOE_E_HIP;
+  p->slot_pending = true;
   return MOE_OK;
 }
 
@@ -221,6 +309,7 @@ moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int3
   ok = ok && hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_ids, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_copies, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->ev_slot, hipEventDisableTiming) == hipSuccess;
   if (ok) {
     // every table entry starts at the layer's first slot (nothing resident yet)
     for (int l = 0; l < n_layers; ++l)
@@ -240,13 +329,16 @@ moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int3
 moe_status moe_pool_destroy(moe_pool *p) {
   if (!p) return MOE_E_INVALID;
   if (p->side) (void)hipStreamSynchronize(p->side);
+  if (p->slot_pending) (void)hipEventSynchronize(p->ev_slot);
   if (p->slot_mem) (void)hipFree(p->slot_mem);
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->h_tables) (void)hipHostFree(p->h_tables);
   if (p->h_ids) (void)hipHostFree(p->h_ids);
   if (p->h_slot) (void)hipHostFree(p->h_slot);
+  if (p->h_flag) (void)hipHostFree(p->h_flag);
   if (p->ev_ids) (void)hipEventDestroy(p->ev_ids);
   if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
+  if (p->ev_slot) (void)hipEventDestroy(p->ev_slot);
   if (p->side) (void)hipStreamDestroy(p->side);
   delete p;
   return MOE_OK;

@@ -31,12 +31,20 @@ class LfuPlanner {
 
 moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k);
 int pool_F(const moe_pool *p);
+// Before the router kernel: with fewer than 16 tokens, where it writes the
+// ids in host memory and the epoch of this call's flags (null otherwise).
+moe_status pool_route_ids(moe_pool *p, int T, int k, int32_t **host_ids, uint32_t **host_flag,
+                          uint32_t *epoch);
+// After it: the ids back to the host (a copy, unless the kernel writes them).
 moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s);
 // Plans the call's experts, copies the misses into HBM slots on the side
 // stream and makes stream s wait for them.  Publishes the layer's device
-// pointer table (*table, if non-null) and, if slot_blob is non-null, the slot
-// address of every (token, slot) pair into that device array.
+// pointer table (*table, if non-null) and, if slot_blob is non-null, a
+// device-readable array (pinned host memory) with the slot address of every
+// (token, slot) pair; the caller reports the kernels that read it with
+// pool_slots_read once they are enqueued.
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
-                              const void *const **table, const void **slot_blob);
+                              const void *const **table, const void *const **slot_blob);
+moe_status pool_slots_read(moe_pool *p, hipStream_t s);
 
 }  // namespace moe

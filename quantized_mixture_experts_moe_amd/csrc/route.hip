@@ -29,7 +29,8 @@ __device__ __forceinline__ float x_to_f32(uint16_t v) {
 // ids, gates and optionally the blob address of every selected expert.
 template <int NV>
 __device__ void topk_wave_t(const float *lg, int E, int k, int32_t *ids, float *gates,
-                            const void *const *table, const void **slot_blob, uint2 *xch) {
+                            const void *const *table, const void **slot_blob, uint2 *xch,
+                            int32_t *host_ids) {
   const int lane = threadIdx.x & 63;
   float v[NV];
 #pragma unroll
@@ -44,18 +45,20 @@ __device__ void topk_wave_t(const float *lg, int E, int k, int32_t *ids, float *
     ids[lane] = id;
     gates[lane] = gate;
     if (slot_blob) slot_blob[lane] = table[id];
+    if (host_ids) host_ids[lane] = id;
   }
 }
 __device__ void topk_wave(const float *lg, int E, int k, int32_t *ids, float *gates,
-                          const void *const *table, const void **slot_blob, uint2 *xch) {
+                          const void *const *table, const void **slot_blob, uint2 *xch,
+                          int32_t *host_ids = nullptr) {
   if (E <= 128)
-    topk_wave_t<2>(lg, E, k, ids, gates, table, slot_blob, xch);
+    topk_wave_t<2>(lg, E, k, ids, gates, table, slot_blob, xch, host_ids);
   else if (E <= 256)
-    topk_wave_t<4>(lg, E, k, ids, gates, table, slot_blob, xch);
+    topk_wave_t<4>(lg, E, k, ids, gates, table, slot_blob, xch, host_ids);
   else if (E <= 512)
-    topk_wave_t<8>(lg, E, k, ids, gates, table, slot_blob, xch);
+    topk_wave_t<8>(lg, E, k, ids, gates, table, slot_blob, xch, host_ids);
   else
-    topk_wave_t<16>(lg, E, k, ids, gates, table, slot_blob, xch);
+    topk_wave_t<16>(lg, E, k, ids, gates, table, slot_blob, xch, host_ids);
 }
 
 // Activations [nt][D] of fp16/bf16 bits into LDS as fp32: every thread issues
@@ -213,7 +216,17 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
     const int t = t0 + wave;
     topk_wave(a.logits + (size_t)t * E, E, a.k, a.ids + (size_t)t * a.k,
               a.gates + (size_t)t * a.k, a.table,
-              a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr, s_xch[wave]);
+              a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr, s_xch[wave],
+              a.host_ids ? a.host_ids + (size_t)t * a.k : nullptr);
+  }
+  if (a.host_ids) {
+    // the ids in host memory, then the tokens' flags (release at system
+    // scope: the host reads the ids once it sees its epoch)
+    __threadfence_system();
+    __syncthreads();
+    if (tid < nt)
+      __hip_atomic_store(a.host_flag + t0 + tid, a.host_epoch, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if (tid == 0) st_dev(&a.counters[blockIdx.y], 0u);
 }
@@ -555,6 +568,7 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s) {
   // prefill.  MAXC: 16-column chunks per thread (64 threads split a row, the
   // same split and order as the one-launch decode layer's router).
   const bool small_d = a.D <= 3072;
+  if (a.T >= 16 && a.host_ids) return hipErrorInvalidValue;  // ids to the host: row router only
   if (a.T >= 16 && tuning().route_mfma && a.E <= 256 && a.D <= 4096 && a.rtag && a.rep) {
     // windows of as many tokens as the tagged area holds (whole 16-token tiles)
     const int win = (int)(kRouteTagBytes / (sizeof(uint64_t) * kRouteParts * a.E)) / kRTok * kRTok;
