@@ -180,6 +180,7 @@ struct __align__(16) SelectLds {
 // Wave 0 of a router block: polls the E logits of token t (lanes hold
 // experts lane, lane + 64, ...), ranks the own candidates with ballots and
 // publishes the winners.
+template <bool HS>
 __device__ void select_publish(const LayerLaunch &L, int t, int e0, uint32_t tag,
                                const SelectLds &S) {
   constexpr int NV = kMaxLayerE / 64;
@@ -231,6 +232,11 @@ __device__ void select_publish(const LayerLaunch &L, int t, int e0, uint32_t tag
       st_dev64(line + r, tagged((uint32_t)e, tag));
       st_dev64(line + L.lid + r, tagged(vbits, tag));
     }
+    if constexpr (HS) {
+      if (p == 0)  // the host's copy of the selection (one 64-bit word)
+        __hip_atomic_store(L.host_sel + (size_t)t * k + r, tagged((uint32_t)e, L.host_epoch),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
@@ -238,6 +244,7 @@ __device__ void select_publish(const LayerLaunch &L, int t, int e0, uint32_t tag
 // wait): lane r < k receives the blob of the r-th expert and its softmax gate
 // (the max is the rank-0 logit; the same arithmetic, in the same order, as
 // the router kernel's selection).  `report`: also write ids_out / gates_out.
+template <bool BY_RANK = false>
 __device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t tag,
                                const void *const *table, const uint8_t **blob_out,
                                float *gate_out, bool report) {
@@ -258,7 +265,7 @@ __device__ void wait_selection(const LayerLaunch &L, int t, int copy, uint32_t t
     wg = ng;
   }
   const uint32_t id = min((uint32_t)wi, (uint32_t)L.E - 1);
-  if (lane < k) blob_out[lane] = (const uint8_t *)table[id];
+  if (lane < k) blob_out[lane] = (const uint8_t *)table[BY_RANK ? (uint32_t)lane : id];
   const float myv = lane < k ? __uint_as_float((uint32_t)wg) : 0.0f;
   const float m0 =
       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
@@ -627,7 +634,7 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
 // Router rows e0 .. e0 + kRows - 1 of token r_t and the selection of the
 // token (every router block publishes its winners).  They head the chain of
 // dependent steps, so these blocks do nothing else.
-template <bool F16X, int MAXC>
+template <bool F16X, int MAXC, bool HS = false>
 __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_t &tag, uint8_t *dsm,
                                             SelectLds &s_select) {
   constexpr int MAXX = MAXC == 3 ? 2 : 4;  // 16-byte pieces of x per thread
@@ -727,11 +734,14 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
     }
     s_select.own[lane] = own;
   }
-  if (wave == 0) select_publish(L, r_t, r_e0, tag, s_select);
+  if (wave == 0) select_publish<HS>(L, r_t, r_e0, tag, s_select);
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <bool F16X, int M, int MAXC>
+// TWO: the streamed variant in two launches (router and shared blocks, then
+// the routed blocks); its router blocks also store the selection into host
+// memory and its routed blocks take each rank's blob from given_blob
+template <bool F16X, int M, int MAXC, bool TWO>
 __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L) {
   extern __shared__ __align__(16) uint8_t dsm[];
   __shared__ float red[kNW][2][64];
@@ -754,15 +764,18 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   // (their loads depend on nothing and then drain before the routing's
   // hand-offs); b is the logical index either way.
   const int nrb = (E + kRows - 1) / kRows;
-  const int p = blockIdx.x, nr0 = T * nrb, ns = L.grid_full - L.NR;
-  const int b = !L.order ? L.blk0 + p : p < nr0 ? p : p < nr0 + ns ? L.NR + (p - nr0) : p - ns;
+  const int p = TWO ? L.blk0 + blockIdx.x : blockIdx.x, nr0 = T * nrb, ns = L.grid_full - L.NR;
+  const int b = !L.order ? (TWO ? p : L.blk0 + p)
+                         : p < nr0 ? p : p < nr0 + ns ? L.NR + (p - nr0) : p - ns;
   // the epoch is read by each role after its first loads are issued, with a
   // vector load (an atomic one): nothing waits for it before its first use
   uint32_t tag = 0;
   auto load_tag = [&]() {
     tag = __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
   };
-  const bool given = L.given_blob != nullptr;  // selection from the caller
+  // selection from the caller (blob addresses by rank alone: the selection
+  // lines still give the ids and gates)
+  const bool given = !TWO && L.given_blob != nullptr;
   const int n_rt = T * k * Gf;                 // routed gate/up tiles, then the shared ones
   const int dw = max(wave - 1, 0);             // down units: waves 1..3 (wave 0 mirrors 1)
 
@@ -770,7 +783,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     // ---------------- router rows and the selection of the token.  They
     // head the chain of dependent steps, so these blocks do nothing else.
     if (!given)
-      router_role<F16X, MAXC>(L, b, tag, dsm, s_select);
+      router_role<F16X, MAXC, TWO>(L, b, tag, dsm, s_select);
     else
       load_tag();
   } else if (b >= L.NR) {
@@ -862,28 +875,36 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     load_tag();
     const void **s_table = (const void **)(dsm + L.table_off);
     if (!given) {
-      constexpr int kTab = kMaxLayerE / kThreads;
-      const void *tb[kTab];
+      if constexpr (!TWO) {
+        constexpr int kTab = kMaxLayerE / kThreads;
+        const void *tb[kTab];
 #pragma unroll
-      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
-      stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
+        for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
+        stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
 #pragma unroll
-      for (int i = 0; i < kTab; ++i)
-        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
+        for (int i = 0; i < kTab; ++i)
+          if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
+      } else {
+        stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
+      }
       __syncthreads();
       const int copy = sb % L.sel_copies;
       // the first block of each token's first gate/up tile reports the selection
       const bool report = has_g && gt.j == 0 && gt.rb == 0 && ks == 0;
-      if (L.select == 1) {
+      if (!TWO && L.select == 1) {
         const int lc = sb % L.log_copies;
         if (wave == 0)
           select_from_logits(L, gt.t, lc, tag, s_table, s_blob[0], s_gate[0], report, s_xch[0]);
         if (wave == 1 && t_out != gt.t)
           select_from_logits(L, t_out, lc, tag, s_table, s_blob[1], s_gate[1], false, s_xch[1]);
       } else {
-        if (wave == 0) wait_selection(L, gt.t, copy, tag, s_table, s_blob[0], s_gate[0], report);
+        // the blob table: by expert id, or (two launches) by rank per token
+        const void *const *t0 = TWO ? L.given_blob + (size_t)gt.t * k : s_table;
+        const void *const *t1 = TWO ? L.given_blob + (size_t)t_out * k : s_table;
+        if (wave == 0)
+          wait_selection<TWO>(L, gt.t, copy, tag, t0, s_blob[0], s_gate[0], report);
         if (wave == 1 && t_out != gt.t)
-          wait_selection(L, t_out, copy, tag, s_table, s_blob[1], s_gate[1], false);
+          wait_selection<TWO>(L, t_out, copy, tag, t1, s_blob[1], s_gate[1], false);
       }
     } else {
       stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
@@ -1195,28 +1216,34 @@ __global__ __launch_bounds__(kThreads, 3) void decode_stream_kernel(LayerLaunch 
 
 using KernelFn = void (*)(LayerLaunch);
 template <bool F16X, int MAXC>
-KernelFn pick(int m, bool stream) {
+KernelFn pick(int m, bool stream, bool two) {
   if (stream) {
     if (m == 2) return decode_stream_kernel<F16X, 2, MAXC>;
     if (m == 3) return decode_stream_kernel<F16X, 3, MAXC>;
     if (m == 4) return decode_stream_kernel<F16X, 4, MAXC>;
     return nullptr;
   }
-  if (m == 2) return decode_layer_kernel<F16X, 2, MAXC>;
-  if (m == 3) return decode_layer_kernel<F16X, 3, MAXC>;
-  if (m == 4) return decode_layer_kernel<F16X, 4, MAXC>;
+  if (two) {
+    if (m == 2) return decode_layer_kernel<F16X, 2, MAXC, true>;
+    if (m == 3) return decode_layer_kernel<F16X, 3, MAXC, true>;
+    if (m == 4) return decode_layer_kernel<F16X, 4, MAXC, true>;
+    return nullptr;
+  }
+  if (m == 2) return decode_layer_kernel<F16X, 2, MAXC, false>;
+  if (m == 3) return decode_layer_kernel<F16X, 3, MAXC, false>;
+  if (m == 4) return decode_layer_kernel<F16X, 4, MAXC, false>;
   return nullptr;
 }
 KernelFn pick_layer(const LayerLaunch &L, int m) {
   const bool small_d = L.D <= 3072;  // router chunks per thread: 3 (D <= 3072) or 8
-  const bool st = L.stream != 0;
-  if (L.f16x) return small_d ? pick<true, 3>(m, st) : pick<true, 8>(m, st);
-  return small_d ? pick<false, 3>(m, st) : pick<false, 8>(m, st);
+  const bool st = L.stream != 0, two = L.two != 0;
+  if (L.f16x) return small_d ? pick<true, 3>(m, st, two) : pick<true, 8>(m, st, two);
+  return small_d ? pick<false, 3>(m, st, two) : pick<false, 8>(m, st, two);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int g_layer_capacity[2][2][2][3][64];  // [stream][f16x][MAXC 3/8][m - 2][device]
+int g_layer_capacity[3][2][2][3][64];  // [resident, stream, two][f16x][MAXC 3/8][m - 2][device]
 
 }  // namespace
 
@@ -1227,6 +1254,8 @@ int layer_m(const LayerLaunch &L) {
   if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), kNW - 1));
   return m < 2 ? 2 : m;
 }
+
+int layer_router_blocks(const LayerLaunch &L) { return L.T * ((L.E + kRows - 1) / kRows); }
 
 // routed blocks (router rows, routed gate/up tiles, routed down splits) and
 // shared blocks (shared gate/up tiles, shared down splits)
@@ -1261,7 +1290,8 @@ hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int &slot = g_layer_capacity[L.stream ? 1 : 0][L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1][m - 2][dev];
+  int &slot = g_layer_capacity[L.stream ? 1 : L.two ? 2 : 0][L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1]
+                              [m - 2][dev];
   const size_t smem = layer_smem(L);
   if (smem > 64 * 1024) return hipSuccess;
   if (!slot) {
@@ -1290,6 +1320,17 @@ hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s) {
 
 hipError_t launch_layer(const LayerLaunch &L, hipStream_t s) {
   return launch_layer_range(L, 0, layer_grid(L), s);
+}
+
+hipError_t launch_layer_ordered(LayerLaunch L, int first, int n, hipStream_t s) {
+  KernelFn k = pick_layer(L, layer_m(L));
+  if (!k || L.stream || !L.two) return hipErrorInvalidValue;
+  L.grid_full = layer_grid(L);
+  if (first < 0 || n < 0 || first + n > L.grid_full) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  L.blk0 = first;
+  hipLaunchKernelGGL(k, dim3(n), dim3(kThreads), layer_smem(L), s, L);
+  return hipGetLastError();
 }
 
 }  // namespace moe

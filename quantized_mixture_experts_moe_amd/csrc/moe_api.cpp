@@ -465,10 +465,38 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   L.logit_bias = logit_bias; L.rblobs = pool ? nullptr : routed->blobs;
   L.sblobs = shared ? shared->blobs : nullptr;
   L.ids_out = ids_out; L.gates_out = gates_out; L.out = out; L.out_dtype = out_dtype;
+  L.two = pool != nullptr;  // streamed experts: the two-launch variant (its occupancy)
   const bool use_layer = plan_layer(w, &L);
   if (use_layer && !pool) {
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_layer(L, s)));
+  }
+
+  if (use_layer && pool && !L.stream) {
+    // Streamed experts, two launches of the layer kernel.  First its router
+    // blocks and the shared expert's blocks (dispatch order 1: router,
+    // shared, routed); the ranking waves also store the selection into host
+    // memory.  The host plans the slots from it and the side stream copies
+    // the missing experts while the shared blocks run; then the routed
+    // blocks take the ids and gates from the selection lines, as in the
+    // resident launch, and each rank's blob from the pool.  Same blocks,
+    // same splits: the output is bitwise the resident one.
+    L.select = 0;
+    L.order = 1;
+    st = pool_layer_sel(pool, T, k, &L.host_sel, &L.host_epoch);
+    if (st) return st;
+    const int grid = layer_grid(L);
+    const int first = layer_router_blocks(L) + layer_shared_blocks(L);
+    if (launch_layer_ordered(L, 0, first, s) != hipSuccess) return MOE_E_HIP;
+    st = pool_fetch_ids(pool, nullptr, T * k, s);
+    if (st) return st;
+    const void *const *slots = nullptr;
+    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, &slots);
+    if (st) return st;
+    L.host_sel = nullptr;
+    L.given_blob = slots;
+    if (launch_layer_ordered(L, first, grid - first, s) != hipSuccess) return MOE_E_HIP;
+    return pool_slots_read(pool, s);
   }
 
   RouteLaunch r{};

@@ -251,15 +251,25 @@ struct LayerLaunch {
   uint32_t *err;
   int32_t *ids_out; float *gates_out; // optional
   void *out; int out_dtype;
+  // streamed experts in two launches of this kernel (router and shared
+  // blocks, then the routed blocks): the router blocks also store each
+  // selected expert as (id, host_epoch) into host_sel [T][k] (pinned host
+  // memory); the routed blocks take the selection and gates from the
+  // selection lines as usual and the blob of rank r from given_blob[t][r]
+  uint64_t *host_sel; uint32_t host_epoch;
+  int two;                            // that variant of the kernel (set before planning)
 };
 int layer_m(const LayerLaunch &L);
 int layer_routed_blocks(const LayerLaunch &L);
+int layer_router_blocks(const LayerLaunch &L);
 int layer_grid(const LayerLaunch &L);
 size_t layer_smem(const LayerLaunch &L);
 size_t layer_table_off(const LayerLaunch &L);
 hipError_t layer_capacity(const LayerLaunch &L, int *cap);
 int layer_shared_blocks(const LayerLaunch &L);
 hipError_t launch_layer(const LayerLaunch &L, hipStream_t s);
+// blocks [first, first + n) of the dispatch order L.order (0 or 1), two-launch variant
+hipError_t launch_layer_ordered(LayerLaunch L, int first, int n, hipStream_t s);
 // blocks [blk0, blk0 + n) of the grid only (streamed experts: shared blocks
 // first, then the rest once the pool has the selected experts)
 hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s);

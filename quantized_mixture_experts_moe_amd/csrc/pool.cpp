@@ -85,8 +85,11 @@ struct moe_pool {
   uint32_t *h_flag = nullptr;                 // pinned [ids_cap]
   int32_t *d_ids_host = nullptr;              // device addresses of h_ids and h_flag
   uint32_t *d_flag_host = nullptr;
+  // or, from the one-launch layer's router blocks, (id, epoch) words
+  uint64_t *h_sel = nullptr;                  // pinned [ids_cap]
+  uint64_t *d_sel_host = nullptr;
   uint32_t epoch = 0;
-  bool ids_direct = false;                    // the current call's ids come that way
+  int ids_mode = 0;                           // this call's ids: 0 copied, 1 ids + flags, 2 words
   moe_pool_stats stats{};
 };
 
@@ -111,30 +114,43 @@ static moe_status ensure_ids(moe_pool *p, int n) {
     if (p->h_ids) (void)hipHostFree(p->h_ids);
     if (p->h_slot) (void)hipHostFree(p->h_slot);
     if (p->h_flag) (void)hipHostFree(p->h_flag);
+    if (p->h_sel) (void)hipHostFree(p->h_sel);
     p->h_ids = nullptr;
     p->h_slot = nullptr;
     p->h_flag = nullptr;
+    p->h_sel = nullptr;
     p->ids_cap = 0;
     // coherent (uncached on the device): the kernels read what the host
     // wrote before their launch, and the host polls what they write
     const unsigned fl = hipHostMallocCoherent;
     if (hipHostMalloc((void **)&p->h_ids, sizeof(int32_t) * n, fl) != hipSuccess ||
         hipHostMalloc((void **)&p->h_slot, sizeof(void *) * n, fl) != hipSuccess ||
-        hipHostMalloc((void **)&p->h_flag, sizeof(uint32_t) * n, fl) != hipSuccess)
+        hipHostMalloc((void **)&p->h_flag, sizeof(uint32_t) * n, fl) != hipSuccess ||
+        hipHostMalloc((void **)&p->h_sel, sizeof(uint64_t) * n, fl) != hipSuccess)
       return MOE_E_HIP;
-    for (int i = 0; i < n; ++i) p->h_flag[i] = 0u;
+    for (int i = 0; i < n; ++i) p->h_flag[i] = 0u, p->h_sel[i] = 0u;
     p->epoch = 0;
-    void *dv = nullptr, *di = nullptr, *df = nullptr;
+    void *dv = nullptr, *di = nullptr, *df = nullptr, *ds = nullptr;
     if (hipHostGetDevicePointer(&dv, p->h_slot, 0) != hipSuccess ||
         hipHostGetDevicePointer(&di, p->h_ids, 0) != hipSuccess ||
-        hipHostGetDevicePointer(&df, p->h_flag, 0) != hipSuccess)
+        hipHostGetDevicePointer(&df, p->h_flag, 0) != hipSuccess ||
+        hipHostGetDevicePointer(&ds, p->h_sel, 0) != hipSuccess)
       return MOE_E_HIP;
     p->d_slot = (const void *const *)dv;
     p->d_ids_host = (int32_t *)di;
     p->d_flag_host = (uint32_t *)df;
+    p->d_sel_host = (uint64_t *)ds;
     p->ids_cap = n;
   }
   return MOE_OK;
+}
+
+// The next call's epoch (flags and words of earlier calls hold older ones).
+static void next_epoch(moe_pool *p) {
+  if (++p->epoch == 0) {  // wrapped: no flag or word may hold the new epoch already
+    for (int i = 0; i < p->ids_cap; ++i) p->h_flag[i] = 0u, p->h_sel[i] = 0u;
+    p->epoch = 1;
+  }
 }
 
 moe_status pool_route_ids(moe_pool *p, int T, int k, int32_t **host_ids, uint32_t **host_flag,
@@ -142,24 +158,31 @@ moe_status pool_route_ids(moe_pool *p, int T, int k, int32_t **host_ids, uint32_
   *host_ids = nullptr;
   *host_flag = nullptr;
   *epoch = 0;
-  p->ids_direct = false;
+  p->ids_mode = 0;
   if (T >= 16) return MOE_OK;  // the matrix-core router: ids copied back
   const moe_status st = ensure_ids(p, T * k);
   if (st) return st;
-  if (++p->epoch == 0) {  // wrapped: no flag may hold the new epoch already
-    for (int i = 0; i < p->ids_cap; ++i) p->h_flag[i] = 0u;
-    p->epoch = 1;
-  }
+  next_epoch(p);
   *host_ids = p->d_ids_host;
   *host_flag = p->d_flag_host;
   *epoch = p->epoch;
-  p->ids_direct = true;
+  p->ids_mode = 1;
+  return MOE_OK;
+}
+
+moe_status pool_layer_sel(moe_pool *p, int T, int k, uint64_t **host_sel, uint32_t *epoch) {
+  const moe_status st = ensure_ids(p, T * k);
+  if (st) return st;
+  next_epoch(p);
+  *host_sel = p->d_sel_host;
+  *epoch = p->epoch;
+  p->ids_mode = 2;
   return MOE_OK;
 }
 
 moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s) {
-  if (p->ids_direct) {
-    // the router kernel writes them; the event is the fallback wait
+  if (p->ids_mode) {
+    // a kernel writes them into host memory; the event is the fallback wait
     return hipEventRecord(p->ev_ids, s) == hipSuccess ? MOE_OK : MOE_E_HIP;
   }
   const moe_status st = ensure_ids(p, n);
@@ -174,10 +197,18 @@ moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t 
 // Waits until the router kernel's per-token flags carry the call's epoch:
 // a short spin (the ids arrive a few microseconds after the kernel ends),
 // then a blocking wait for the kernel, after which they must be there.
-static moe_status wait_direct_ids(moe_pool *p, int T) {
+static moe_status wait_direct_ids(moe_pool *p, int T, int k) {
   auto ready = [&]() {
-    for (int t = 0; t < T; ++t)
-      if (__atomic_load_n(p->h_flag + t, __ATOMIC_ACQUIRE) != p->epoch) return false;
+    if (p->ids_mode == 1) {
+      for (int t = 0; t < T; ++t)
+        if (__atomic_load_n(p->h_flag + t, __ATOMIC_ACQUIRE) != p->epoch) return false;
+      return true;
+    }
+    for (int i = 0; i < T * k; ++i) {
+      const uint64_t v = __atomic_load_n(p->h_sel + i, __ATOMIC_ACQUIRE);
+      if ((uint32_t)(v >> 32) != p->epoch) return false;
+      p->h_ids[i] = (int32_t)(uint32_t)v;
+    }
     return true;
   };
   const auto t0 = std::chrono::steady_clock::now();
@@ -192,7 +223,7 @@ static moe_status wait_direct_ids(moe_pool *p, int T) {
 
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
                               const void *const **table, const void *const **slot_blob) {
-  const moe_status ws = p->ids_direct ? wait_direct_ids(p, T)
+  const moe_status ws = p->ids_mode ? wait_direct_ids(p, T, k)
                                       : (hipEventSynchronize(p->ev_ids) == hipSuccess ? MOE_OK
                                                                                        : MOE_E_HIP);
   if (ws) return ws;
@@ -336,6 +367,7 @@ moe_status moe_pool_destroy(moe_pool *p) {
   if (p->h_ids) (void)hipHostFree(p->h_ids);
   if (p->h_slot) (void)hipHostFree(p->h_slot);
   if (p->h_flag) (void)hipHostFree(p->h_flag);
+  if (p->h_sel) (void)hipHostFree(p->h_sel);
   if (p->ev_ids) (void)hipEventDestroy(p->ev_ids);
   if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
   if (p->ev_slot) (void)hipEventDestroy(p->ev_slot);

@@ -35,6 +35,10 @@ int pool_F(const moe_pool *p);
 // ids in host memory and the epoch of this call's flags (null otherwise).
 moe_status pool_route_ids(moe_pool *p, int T, int k, int32_t **host_ids, uint32_t **host_flag,
                           uint32_t *epoch);
+// Before the first of two launches of the one-launch decode layer (router
+// and shared blocks): where its router blocks store the (id, epoch) words
+// of the selection, and this call's epoch.
+moe_status pool_layer_sel(moe_pool *p, int T, int k, uint64_t **host_sel, uint32_t *epoch);
 // After it: the ids back to the host (a copy, unless the kernel writes them).
 moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t s);
 // Plans the call's experts, copies the misses into HBM slots on the side
