@@ -160,8 +160,11 @@ moe_status moe_permute(const int32_t *ids, int32_t T, int32_t k, int32_t E, int3
  * `routed` may be NULL; the experts of layer `layer` are served from the
  * pool's HBM slots, missing ones copied from pinned host memory on the
  * pool's side stream while the shared expert runs; this call then blocks the
- * host once to read the selected ids back (the pages' CPU fetch plan:
- * es.news.hada.io, "Proceso de generacion de tokens"). */
+ * host once, until the selected ids have arrived in the pool's pinned host
+ * memory (written there by the routing kernels; the pages' CPU fetch plan:
+ * es.news.hada.io, "Proceso de generacion de tokens").  Consecutive calls
+ * with one pool go on one stream (the pool's host-side buffers are reused
+ * once the previous call's kernels are done, which it checks). */
 moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *router,
                              const float *logit_bias, int32_t k, const moe_bank *routed,
                              const moe_bank *shared, moe_pool *pool, int32_t layer, void *out,
