@@ -123,6 +123,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
     q[i] = as_global((const u32x4 *)a.codes)[(size_t)c * E + e];
     mw[i] = as_global(a.meta)[(size_t)(c >> 2) * E + e];
   }
+  // the logit bias of the row that wave 0's lane finishes (lane % ROWS)
+  const float lbias =
+      a.logit_bias ? a.logit_bias[min((int)blockIdx.x * ROWS + lane % ROWS, E - 1)] : 0.0f;
   stage_x<F16X, (TT * 8192 / 8 + kThreads - 1) / kThreads>(x, nt * D, sx);
   for (int i = nt * D + tid; i < TT * D; i += kThreads) sx[i] = 0.0f;
   __syncthreads();
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
       float s = 0.0f;
       for (int jj = 0; jj < KL; ++jj) s += red[jj * (ROWS * TT) + lane];
       if (ee < E && tt < nt) {
-        if (a.logit_bias) s += a.logit_bias[ee];
+        if (a.logit_bias) s += lbias;
         st_dev(a.logits + (size_t)(t0 + tt) * E + ee, s);
       }
     }
@@ -444,6 +447,11 @@ __global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp
     const int row = part * per + j;
     if (row >= nt) break;  // uniform over the wave
     const int t = t0 + row;
+    // the logit bias before the wait (no load after it but the polls)
+    float bias[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      bias[q] = a.logit_bias ? a.logit_bias[min(lane + 64 * q, E - 1)] : 0.0f;
     // every part's words of the token in one round trip per try
     uint64_t w[kRouteParts][NV];
     for (long sp = 0;; ++sp) {
@@ -472,7 +480,7 @@ __global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp
     for (int q = 0; q < NV; ++q) {
       const int e = lane + 64 * q;
       if (e < E) {
-        if (a.logit_bias) v[q] += a.logit_bias[e];
+        if (a.logit_bias) v[q] += bias[q];
         a.logits[(size_t)t * E + e] = v[q];
       } else {
         v[q] = -INFINITY;
