@@ -468,25 +468,47 @@ __global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
 }
 
 // four consecutive outputs per thread (16-byte loads of y), the k routed
-// rows in fixed j order after the shared expert's partial sums
+// rows in fixed j order after the shared expert's partial sums.  The rows'
+// positions and gates are read first and every row's load is issued before
+// the sums (KB rows per batch), so a thread waits for two round trips per
+// batch instead of two per row.
+template <int KB>
 __global__ void combine_prefill_kernel(PrefillLaunch p) {
   const size_t total = (size_t)p.T * p.D, total4 = total / 4;
-  const int D4 = p.D / 4;
+  const int D4 = p.D / 4, k = p.k;
   const bool aligned = ((uintptr_t)p.out & 15) == 0;  // else element by element
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total4;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t t = i / D4, d = (i - t * D4) * 4;
     float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (p.sblobs)
-      for (int ks = 0; ks < p.sks; ++ks) {
-        const float4 v = *(const float4 *)(p.ys + (size_t)ks * total + t * p.D + d);
-        s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+    if (p.sblobs) {
+      float4 v[kMaxSharedSplits];
+#pragma unroll
+      for (int ks = 0; ks < kMaxSharedSplits; ++ks)
+        if (ks < p.sks) v[ks] = *(const float4 *)(p.ys + (size_t)ks * total + t * p.D + d);
+#pragma unroll
+      for (int ks = 0; ks < kMaxSharedSplits; ++ks)
+        if (ks < p.sks) s.x += v[ks].x, s.y += v[ks].y, s.z += v[ks].z, s.w += v[ks].w;
+    }
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      int row[KB];
+      float gt[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int jj = min(j0 + j, k - 1);
+        row[j] = p.inv[t * k + jj];
+        gt[j] = p.gates[t * k + jj];
       }
-    for (int j = 0; j < p.k; ++j) {
-      const float gt = p.gates[t * p.k + j];
-      const float4 v = *(const float4 *)(p.y + (size_t)p.inv[t * p.k + j] * p.D + d);
-      s.x = fmaf(gt, v.x, s.x), s.y = fmaf(gt, v.y, s.y);
-      s.z = fmaf(gt, v.z, s.z), s.w = fmaf(gt, v.w, s.w);
+      float4 v[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) v[j] = *(const float4 *)(p.y + (size_t)row[j] * p.D + d);
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (j0 + j < k) {
+          s.x = fmaf(gt[j], v[j].x, s.x), s.y = fmaf(gt[j], v[j].y, s.y);
+          s.z = fmaf(gt[j], v[j].z, s.z), s.w = fmaf(gt[j], v[j].w, s.w);
+        }
+      }
     }
     const size_t o = t * p.D + d;
     if (!aligned) {
@@ -538,7 +560,7 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   const size_t total = (size_t)p.T * p.D / 4;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(combine_prefill_kernel, dim3(blocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(combine_prefill_kernel<8>, dim3(blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
