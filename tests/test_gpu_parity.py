@@ -530,6 +530,49 @@ def test_layer_forward_prefill_out_dtypes(out_dtype):
         assert torch.equal(out.view(torch.int16), want.view(torch.int16)), off
 
 
+@pytest.mark.parametrize("path,T", [("layer", 3), ("fused", 2), ("three", 5), ("three", 20)])
+def test_pool_paths_streamed_equals_resident(path, T):
+    """Several tokens per call on every pooled shape: the layer kernel in two
+    launches (selection words into host memory), the fused expert phase and
+    the three-kernel shape after the row router (ids and flags into host
+    memory), and 20 tokens (ids copied back).  Streamed output and ids are
+    bitwise the resident ones; every (token, slot) is one lookup."""
+    _case(f"pool paths: {path} T={T}")
+    _tune(**_PATHS[path])
+    # resident calls of 16 or more tokens would take the grouped prefill
+    # kernels, pooled ones the three-kernel shape: compare like with like
+    moe.moe_set_tuning("prefill_min_t", T + 1)
+    try:
+        cfg = gen.CONFIGS["tiny"]
+        L = dev_layer("tiny", seed=5, layer=0)
+        host = [torch.from_numpy(L.lw.experts.copy()).pin_memory()]
+        pool = moe.Pool(host, 1, cfg.E, cfg.E, cfg.D, cfg.F)
+        ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+        bias = torch.from_numpy(gen.zipf_bias(5, 0, cfg.E, 2.0)).cuda()
+        for call in range(4):
+            xb = gen.activations(5, 0, call * T, T, cfg.D, cfg.x_dtype)
+            x = x_dev(xb, cfg.x_dtype)
+            o_s = torch.empty(T, cfg.D, dtype=torch.float32, device="cuda")
+            o_r = torch.empty_like(o_s)
+            i_s = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+            i_r = torch.empty_like(i_s)
+            moe.moe_layer_forward(x, L.router, cfg.k, None, L.shared, o_s, ws, logit_bias=bias,
+                                  pool=pool, layer=0, ids_out=i_s)
+            moe.moe_layer_forward(x, L.router, cfg.k, L.routed, L.shared, o_r, ws,
+                                  logit_bias=bias, ids_out=i_r)
+            torch.cuda.synchronize()
+            assert torch.equal(i_s, i_r), call
+            assert torch.equal(o_s, o_r), call
+        _check_layer(L, xb, o_s.cpu().numpy(), i_s.cpu().numpy(), cfg.k, bias.cpu().numpy())
+        assert ws.timeouts() == 0
+        st = pool.stats()
+        assert st["lookups"] == 4 * T * cfg.k and st["hits"] + st["misses"] == st["lookups"]
+        pool.close()
+    finally:
+        _tune(**_DEFAULTS)
+        moe.moe_set_tuning("prefill_min_t", 16)
+
+
 @pytest.mark.parametrize("variant", [1, 2])
 def test_pool_decode_shapes_streamed_equals_resident(variant):
     """Decode-shaped layers, 16 HBM slots each: streamed output is bitwise the
