@@ -18,8 +18,12 @@
  * passed in; the library keeps no pointer past the call except inside a pool
  * (moe_pool_create).  Calls are asynchronous on `stream` (a hipStream_t; NULL
  * is the default stream) unless stated otherwise.  Arguments are validated
- * before anything is launched: a negative status means nothing was enqueued.
- * MOE_E_HIP reports a HIP runtime error from a launch or copy; device faults
+ * before anything is launched: a negative status means nothing was enqueued,
+ * except for a moe_layer_forward with a pool, which plans its slots after
+ * routing: there MOE_E_POOL (more distinct experts in the call than slots)
+ * or MOE_E_HIP can come after work was enqueued, and the call's outputs are
+ * undefined.  MOE_E_HIP reports a HIP runtime error from a launch or copy;
+ * after one, zero-fill the workspace again before reusing it.  Device faults
  * surface at the caller's next synchronisation.  No call aborts and no C++
  * exception crosses this boundary.  Results are bitwise reproducible: every
  * reduction has a fixed order and no floating-point atomics are used (where

@@ -466,7 +466,11 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   L.sblobs = shared ? shared->blobs : nullptr;
   L.ids_out = ids_out; L.gates_out = gates_out; L.out = out; L.out_dtype = out_dtype;
   L.two = pool != nullptr;  // streamed experts: the two-launch variant (its occupancy)
-  const bool use_layer = plan_layer(w, &L);
+  // Streamed experts run the layer kernel in two launches with the slot plan
+  // between them; only when every expert of the call is sure to fit the
+  // slots, so that the plan cannot fail once the first launch has left its
+  // blocks' epochs and partial sums waiting for the second.
+  const bool use_layer = (!pool || T * k <= pool_slots(pool)) && plan_layer(w, &L);
   if (use_layer && !pool) {
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_layer(L, s)));

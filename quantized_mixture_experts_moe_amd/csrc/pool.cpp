@@ -103,6 +103,7 @@ moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k) {
 }
 
 int pool_F(const moe_pool *p) { return p->F; }
+int pool_slots(const moe_pool *p) { return p->slots; }
 
 static moe_status ensure_ids(moe_pool *p, int n) {
   if (n > p->ids_cap) {

@@ -31,6 +31,7 @@ class LfuPlanner {
 
 moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k);
 int pool_F(const moe_pool *p);
+int pool_slots(const moe_pool *p);
 // Before the router kernel: with fewer than 16 tokens, where it writes the
 // ids in host memory and the epoch of this call's flags (null otherwise).
 moe_status pool_route_ids(moe_pool *p, int T, int k, int32_t **host_ids, uint32_t **host_flag,
