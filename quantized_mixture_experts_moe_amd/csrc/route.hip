@@ -324,21 +324,33 @@ __device__ __forceinline__ void group_fold(u32x4 q, uint32_t mw, const uint16_t 
 // g0 + j, g0 + j + R, ... and is refilled right after its use, so every wait
 // covers exactly the group it needs (ng is a multiple of R).  A group's
 // address is a scalar base plus the lane's 32-bit offset.
-template <bool F16X, int R>
-__device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng, int e, int g4,
-                                            const uint16_t *xa, const float *sX,
-                                            float (&acc)[4]) {
-  const int E = a.E, gl = g0 + ng - 1;
+template <int R>
+__device__ __forceinline__ void tile_issue(const RouteLaunch &a, int g0, int e, int g4,
+                                           u32x4 (&q)[R], uint32_t (&mw)[R]) {
+  const int E = a.E;
   const uint8_t *cb = (const uint8_t *)a.codes, *mb = (const uint8_t *)a.meta;
   const uint32_t vq = (uint32_t)(g4 * E + e) * 16u, vm = (uint32_t)e * 4u;
   const size_t cs = (size_t)E * 64, ms = (size_t)E * 4;  // bytes per group
-  u32x4 q[R];
-  uint32_t mw[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     q[j] = *(const u32x4 *)(cb + (g0 + j) * cs + vq);
     mw[j] = *(const uint32_t *)(mb + (g0 + j) * ms + vm);
     __builtin_amdgcn_sched_barrier(0);  // issued in slot order
+  }
+}
+// The ring's first R groups already issued (tile_issue); ng a multiple of R.
+template <bool F16X, int R>
+__device__ __forceinline__ void tile_run(const RouteLaunch &a, int g0, int ng, int e, int g4,
+                                         const uint16_t *xa, const float *sX, float (&acc)[4],
+                                         u32x4 (&q)[R], uint32_t (&mw)[R]) {
+  const int E = a.E, gl = g0 + ng - 1;
+  const uint8_t *cb = (const uint8_t *)a.codes, *mb = (const uint8_t *)a.meta;
+  const uint32_t vq = (uint32_t)(g4 * E + e) * 16u, vm = (uint32_t)e * 4u;
+  const size_t cs = (size_t)E * 64, ms = (size_t)E * 4;  // bytes per group
+  if (ng == R) {  // the whole part in the ring: no refill
+#pragma unroll
+    for (int j = 0; j < R; ++j) group_fold<F16X>(q[j], mw[j], xa, sX, j, g4, acc);
+    return;
   }
   for (int gb = g0; gb <= gl; gb += R) {
 #pragma unroll
@@ -350,6 +362,15 @@ __device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng
       __builtin_amdgcn_sched_barrier(0);  // the refill stays right after its use
     }
   }
+}
+template <bool F16X, int R>
+__device__ __forceinline__ void tile_logits(const RouteLaunch &a, int g0, int ng, int e, int g4,
+                                            const uint16_t *xa, const float *sX,
+                                            float (&acc)[4]) {
+  u32x4 q[R];
+  uint32_t mw[R];
+  tile_issue<R>(a, g0, e, g4, q, mw);
+  tile_run<F16X, R>(a, g0, ng, e, g4, xa, sX, acc, q, mw);
 }
 
 size_t route_mfma_smem(int D, int kp) {
@@ -393,6 +414,12 @@ __global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp
     const int tk = min(i / PW, nt - 1), w = i % PW;
     xv[r] = *(const u32x4 *)(x + (size_t)(t0 + tk) * D + 64 * g0 + 8 * w);
   }
+  // the router codes of this wave's first expert tile, in flight while the
+  // activations are staged (lane l: expert 16 tile + l % 16, chunk l / 16)
+  const int NT = (E + 15) / 16, g4 = lane >> 4, col = lane & 15;
+  u32x4 q0[R];
+  uint32_t m0[R];
+  tile_issue<R>(a, g0, min(wave * 16 + col, E - 1), g4, q0, m0);
 #pragma unroll
   for (int r = 0; r < kRMaxWords; ++r) {
     const int i = tid + r * kRThr;
@@ -409,28 +436,17 @@ __global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp
     if (in && (w & 7) == 0) sX[(w >> 3) * kRTok + tk] = tok ? gs : 0.0f;
   }
   __syncthreads();
-  // the pairs and sums the 4-bit expert kernels read, for this part's groups
-  for (int i = tid; i < nt * PW; i += kRThr) {
-    const int tk = i / PW, w = i - tk * PW;
-    const u32x4 v = *(const u32x4 *)(sx + (size_t)tk * ldx + 8 * w);
-    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      o[m] = ((wd[m / 2] >> (16 * (m % 2))) & 0xFFFFu) |
-             (((wd[2 + m / 2] >> (16 * (m % 2))) & 0xFFFFu) << 16);
-    *(u32x4 *)(a.xp + (size_t)(t0 + tk) * (D / 2) + 32 * g0 + 4 * w) = u32x4{o[0], o[1], o[2], o[3]};
-    if ((w & 7) == 0) a.xs[(size_t)(t0 + tk) * G + g0 + (w >> 3)] = sX[(w >> 3) * kRTok + tk];
-  }
 
   // this part's sums of the logits: wave w takes expert tiles w, w + 8, ...;
   // lane l supplies expert 16 tile + l % 16 and the 16-column chunk l / 16
-  const int NT = (E + 15) / 16, g4 = lane >> 4, col = lane & 15;
   uint64_t *mine = a.rtag + (size_t)part * a.T * E;
   for (int et = wave; et < NT; et += kRWaves) {
     const int e = min(et * 16 + col, E - 1);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    tile_logits<F16X, R>(a, g0, P, e, g4, sx + (size_t)col * ldx + 16 * g4, sX, acc);
+    if (et == wave)  // the first tile: its codes were issued above
+      tile_run<F16X, R>(a, g0, P, e, g4, sx + (size_t)col * ldx + 16 * g4, sX, acc, q0, m0);
+    else
+      tile_logits<F16X, R>(a, g0, P, e, g4, sx + (size_t)col * ldx + 16 * g4, sX, acc);
     const int ee = et * 16 + col;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -495,6 +511,20 @@ __global__ __launch_bounds__(kRThr) void route_mfma_kernel(RouteLaunch a, int kp
       a.gates[o] = gate;
       if (a.slot_blob) a.slot_blob[o] = a.table[id];
     }
+  }
+  // the pairs and sums the 4-bit expert kernels read, for this part's groups
+  // (after the waits: a store ahead of a load would make its wait longer)
+  for (int i = tid; i < nt * PW; i += kRThr) {
+    const int tk = i / PW, w = i - tk * PW;
+    const u32x4 v = *(const u32x4 *)(sx + (size_t)tk * ldx + 8 * w);
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[m] = ((wd[m / 2] >> (16 * (m % 2))) & 0xFFFFu) |
+             (((wd[2 + m / 2] >> (16 * (m % 2))) & 0xFFFFu) << 16);
+    *(u32x4 *)(a.xp + (size_t)(t0 + tk) * (D / 2) + 32 * g0 + 4 * w) = u32x4{o[0], o[1], o[2], o[3]};
+    if ((w & 7) == 0) a.xs[(size_t)(t0 + tk) * G + g0 + (w >> 3)] = sX[(w >> 3) * kRTok + tk];
   }
   // every block of the tile has read its epoch (their logits are in), so
   // part 0 can advance it, and the copies tt + j ntt with it, once its own
