@@ -333,6 +333,36 @@ def test_layer_forward_bitwise_repeatable():
     assert np.array_equal(ia, ib) and torch.equal(a, b)
 
 
+@pytest.mark.parametrize("path", ["layer", "fused", "three"])
+def test_layer_forward_k_equals_E_is_dense(path):
+    """k = E (every expert selected): the gates are a plain softmax over all
+    logits and the layer is the dense mixture of all experts, which the
+    oracle's brute-force path (every expert on every token, decoded on its
+    own) computes in float64."""
+    _case(f"layer_forward k=E ({path})")
+    _tune(**_PATHS[path])
+    try:
+        L = dev_layer("tiny")
+        cfg = L.cfg
+        k = cfg.E
+        xb = gen.activations(8, 0, 0, 3, cfg.D, cfg.x_dtype)
+        bias = gen.zipf_bias(0, 0, cfg.E, 1.0)
+        out, ids, gates = _layer_gpu(L, xb, k, bias)
+        xf = x_float(xb, cfg.x_dtype)
+        ref = O.dense_bruteforce(xf, L.lw, k, bias)
+        w = np.zeros((xb.shape[0], cfg.E))
+        for t in range(xb.shape[0]):
+            assert sorted(ids[t].tolist()) == list(range(cfg.E))  # every expert once
+            w[t, ids[t]] = gates[t]
+        assert np.abs(w - ref["weights"]).max() < 1e-5
+        got = out.cpu().numpy()
+        r, m = rel_l2(got, ref["out"]), max_abs(got, ref["out"])
+        print(f"    rel_l2={r:.2e} max_abs={m:.2e}", flush=True)
+        assert r < REL_L2 and m < MAX_ABS
+    finally:
+        _tune(**_DEFAULTS)
+
+
 def test_layer_forward_x_zero():
     _case("layer_forward x=0")
     L = dev_layer("tiny")
