@@ -80,6 +80,9 @@ Workspace carve(void *base, const Dims &d) {
   // at most one partial chunk per expert: sum ceil(c / R) <= E + T k / R
   w.perm_items = c.take<int32_t>((size_t)d.E + (T * k + kPrefillRows - 1) / kPrefillRows, 4);
   w.perm_n_items = c.take<int32_t>(1, 4);
+  w.perm_info = c.take<int2>((size_t)d.E + (T * k + kPrefillRows - 1) / kPrefillRows, 8);
+  w.perm_iblob =
+      c.take<const void *>((size_t)d.E + (T * k + kPrefillRows - 1) / kPrefillRows, 8);
   w.perm = c.take<int32_t>(T * k, 4);
   w.perm_inv = c.take<int32_t>(T * k, 4);
   w.hplanes = c.take<uint16_t>(3 * units, 2);
@@ -586,13 +589,15 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   if (!pool && T >= tuning().prefill_min_t && T * k <= 65536 && D / 64 <= kMaxDGroups &&
       F / 64 <= kMaxHGroups && Fs / 64 <= kMaxHGroups) {
     if (launch_permute(r.ids, T, k, E, w.perm_counts, w.perm_offsets, w.perm, w.perm_inv,
-                       w.perm_items, w.perm_n_items, kPrefillRows, s) !=
+                       w.perm_items, w.perm_n_items, kPrefillRows, s, w.perm_info,
+                       w.perm_iblob, routed->blobs) !=
         hipSuccess)
       return MOE_E_HIP;
     PrefillLaunch pl;
     pl.f16x = r.f16x; pl.T = T; pl.k = k; pl.E = E; pl.D = D; pl.F = F; pl.Fs = Fs;
     pl.counts = w.perm_counts; pl.offsets = w.perm_offsets; pl.perm = w.perm; pl.inv = w.perm_inv;
     pl.items = w.perm_items; pl.n_items = w.perm_n_items;
+    pl.item_info = w.perm_info; pl.item_blob = w.perm_iblob;
     pl.gates = r.gates; pl.rblobs = routed->blobs; pl.sblobs = shared ? shared->blobs : nullptr;
     pl.xp = w.xp; pl.xs = w.xs;
     pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;

@@ -121,6 +121,8 @@ struct Workspace {
   uint32_t *fcounters; // its counters (zero between calls)
   uint32_t *err;       // sticky count of timed-out waits
   int32_t *perm_counts, *perm_offsets, *perm, *perm_inv, *perm_items, *perm_n_items;
+  int2 *perm_info;               // per work-list item: its expert's (count, offset)
+  const void **perm_iblob;       // per work-list item: its expert's blob
   uint16_t *hplanes;   // prefill: hidden activations as three bf16 planes
   float *hsum;         // prefill: 64-unit sums of the hidden activations
   float *y, *ys;       // prefill: routed outputs per pair, shared outputs per token
@@ -207,6 +209,8 @@ struct PrefillLaunch {
   int f16x, T, k, E, D, F, Fs;
   const int32_t *counts, *offsets, *perm, *inv;
   const int32_t *items, *n_items;    // work list: expert | row chunk << 16, longest first
+  const int2 *item_info;              // per item: its expert's (count, offset)
+  const void *const *item_blob;       // per item: its expert's blob
   const float *gates;
   const void *const *rblobs, *const *sblobs;
   const uint32_t *xp; const float *xs;
@@ -276,9 +280,12 @@ hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s);
 
 // items (optional, [E * ceil(T k / chunk_rows)]): the grouped kernels' work
 // list, expert | chunk << 16, experts by count (most first, ties by index);
-// n_items: its length
+// n_items: its length; info, iblob (optional, with blobs: the bank's blob
+// table): each item's expert's (count, offset) and blob, so that a block
+// reads everything about its item at once
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *items,
-                          int32_t *n_items, int chunk_rows, hipStream_t s);
+                          int32_t *n_items, int chunk_rows, hipStream_t s, int2 *info = nullptr,
+                          const void **iblob = nullptr, const void *const *blobs = nullptr);
 
 }  // namespace moe

@@ -27,7 +27,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
                                                        int32_t *__restrict__ inv,
                                                        int32_t *__restrict__ items,
                                                        int32_t *__restrict__ n_items,
-                                                       int chunk_rows) {
+                                                       int chunk_rows, int2 *__restrict__ info,
+                                                       const void **__restrict__ iblob,
+                                                       const void *const *__restrict__ blobs) {
   extern __shared__ int sm[];
   __shared__ int s_bkt[kMaxE], s_bst[kMaxE];
   int *cnt = sm, *fill = sm + E, *sid = sm + 2 * E;
@@ -106,7 +108,11 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
         const int b = (cnt[e] + half - 1) / half, nc = chunks(b);
         if (nc == 0) continue;
         const int at = s_bst[b] + atomicAdd(&s_bkt[b], 1) * nc;
-        for (int yc = 0; yc < nc; ++yc) items[at + yc] = e | (yc << 16);
+        const void *bl = info ? blobs[e] : nullptr;
+        for (int yc = 0; yc < nc; ++yc) {
+          items[at + yc] = e | (yc << 16);
+          if (info) info[at + yc] = make_int2(cnt[e], fill[e]), iblob[at + yc] = bl;
+        }
       }
     } else if (tid < 64) {  // too many buckets: experts in index order
       const int per = (E + 63) / 64, base = lane * per;
@@ -121,8 +127,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
       int at = incl - sum;
       for (int j = 0; j < per; ++j) {
         if (base + j < E) {
-          const int nc = (cnt[base + j] + chunk_rows - 1) / chunk_rows;
-          for (int yc = 0; yc < nc; ++yc) items[at + yc] = (base + j) | (yc << 16);
+          const int e = base + j, nc = (cnt[e] + chunk_rows - 1) / chunk_rows;
+          const void *bl = info && nc ? blobs[e] : nullptr;
+          for (int yc = 0; yc < nc; ++yc) {
+            items[at + yc] = e | (yc << 16);
+            if (info) info[at + yc] = make_int2(cnt[e], fill[e]), iblob[at + yc] = bl;
+          }
           at += nc;
         }
       }
@@ -208,8 +218,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t *__restrict
 
 hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *items,
-                          int32_t *n_items, int chunk_rows, hipStream_t s) {
+                          int32_t *n_items, int chunk_rows, hipStream_t s, int2 *info,
+                          const void **iblob, const void *const *blobs) {
   if (E > kMaxE || (items && (!n_items || chunk_rows < 1))) return hipErrorInvalidValue;
+  if (info && (!items || !iblob || !blobs)) return hipErrorInvalidValue;
   const int n = T * k;
   const int nch = (n + 63) / 64;
   const bool par = n <= kStageIds && nch <= 16 && nch * E <= kChunkHist;  // as the kernel decides
@@ -217,7 +229,7 @@ hipError_t launch_permute(const int32_t *ids, int T, int k, int E, int32_t *coun
       sizeof(int) * (2 * (size_t)E + (n <= kStageIds ? n : 0) + (par ? (size_t)nch * E : 0));
   if (smem > 64 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), smem, s, ids, n, E, counts, offsets,
-                     perm, inv, items, n_items, chunk_rows);
+                     perm, inv, items, n_items, chunk_rows, info, iblob, blobs);
   return hipGetLastError();
 }
 

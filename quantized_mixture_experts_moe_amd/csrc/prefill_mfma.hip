@@ -278,19 +278,25 @@ __global__ __launch_bounds__(256, 4) void glu_mfma_kernel(PrefillLaunch p) {
   const int mch = (p.T + kRows - 1) / kRows;
   const int bid = blockIdx.x;
   int g_idx, nt, yc;
+  Group rg{};
   if (bid < NTs * mch) {
     g_idx = p.E;
     yc = bid / NTs;
     nt = bid - yc * NTs;
   } else {
+    g_idx = -1;
     const int r = bid - NTs * mch, item = r / NT;
-    if (item >= *p.n_items) return;
-    const int it = p.items[item];
-    g_idx = it & 0xFFFF;
-    yc = it >> 16;
     nt = r - item * NT;
+    // the item, its expert's count, offset and blob, and the list's length
+    // in one round trip (every index here is inside the arrays)
+    const int n_it = *p.n_items, it = p.items[item];
+    const int2 inf = p.item_info[item];
+    const void *bl = p.item_blob[item];
+    if (item >= n_it) return;
+    yc = it >> 16;
+    rg.count = inf.x, rg.off = inf.y, rg.F = p.F, rg.blob = (const uint8_t *)bl, rg.shared = false;
   }
-  const Group g = group_of(p, g_idx);
+  const Group g = g_idx < 0 ? rg : group_of(p, g_idx);
   const int m0 = yc * kRows;
   if (g.count <= m0) return;
   const int nrow = min(kRows, g.count - m0);
@@ -433,6 +439,7 @@ __global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
   const int mch = (p.T + kDRows - 1) / kDRows, nsh = p.sblobs ? p.sks * mch * NB : 0;
   const int bid = blockIdx.x;
   int g_idx, nb, yc, ks = 0;
+  Group rg{};
   if (bid < nsh) {
     g_idx = p.E;
     ks = bid / (mch * NB);
@@ -440,15 +447,20 @@ __global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
     yc = r / NB;
     nb = r - yc * NB;
   } else {
+    g_idx = -1;
     const int r = bid - nsh, item = r / (2 * NB);
-    if (item >= *p.n_items) return;
-    const int it = p.items[item];
     const int rr = r - item * 2 * NB, half = rr / NB;
-    g_idx = it & 0xFFFF;
-    yc = 2 * (it >> 16) + half;
     nb = rr - half * NB;
+    // the item, its expert's count, offset and blob, and the list's length
+    // in one round trip (every index here is inside the arrays)
+    const int n_it = *p.n_items, it = p.items[item];
+    const int2 inf = p.item_info[item];
+    const void *bl = p.item_blob[item];
+    if (item >= n_it) return;
+    yc = 2 * (it >> 16) + half;
+    rg.count = inf.x, rg.off = inf.y, rg.F = p.F, rg.blob = (const uint8_t *)bl, rg.shared = false;
   }
-  const Group g = group_of(p, g_idx);
+  const Group g = g_idx < 0 ? rg : group_of(p, g_idx);
   const int m0 = yc * kDRows;
   if (g.count <= m0) return;
   const int nrow = min(kDRows, g.count - m0);
