@@ -203,8 +203,29 @@ moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
  * Process-wide, single host thread. */
 moe_status moe_set_profile_events(void *const *events, int32_t n_pairs);
 
-/* Tuning knobs of the launch shapes ("glu_ks", "down_ks", ...); returns
- * MOE_E_INVALID for an unknown key or value.  Process-wide. */
+/* Tuning knobs of the launch shapes; returns MOE_E_INVALID for an unknown
+ * key or value.  Process-wide.  Every setting gives results within the same
+ * parity bounds; the defaults are the measured fastest.  Keys (default):
+ *   layer (1)            decode of up to 4 tokens in one launch of the layer
+ *                        kernel; 2: its whole-tile variant; 0: off
+ *   layer_ksg, layer_ksd (0)  its gate/up and down splits; 0: the widest
+ *                        whose grid stays resident
+ *   layer_order (1)      dispatch the shared expert's blocks before the routed
+ *   layer_select (0)     1: the routed blocks rank the logits themselves
+ *   layer_direct_h (0)   down waves poll the hidden values (1), two rounds
+ *                        in flight (2), or a hint word first (0)
+ *   layer_down_late (1)  down weights requested after the gate/up reduction
+ *                        (1), with the gate/up weights (0), after its
+ *                        arithmetic (2)
+ *   layer_shared_wait (0)  shared blocks wait for the router's logits
+ *   layer_sel_copies (16), layer_log_copies (16), layer_sel_stride (0)
+ *                        copies and spacing of the published selection
+ *   fused (1)            the one-launch expert phase when the layer kernel
+ *                        is off; fused_ksg, fused_ksd (0) its splits
+ *   glu_ks, down_ks (0)  reduction splits of the few-token kernels
+ *   prefill_min_t (16)   tokens per call from which the grouped matrix-core
+ *                        kernels run
+ *   route_mfma (1)       router of 16 or more tokens on the matrix cores */
 moe_status moe_set_tuning(const char *key, int32_t value);
 
 /* Static text for a status code. */
