@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill", "stack30", "streamed"])
     ap.add_argument("--stream-tokens", type=int, default=64)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per step for decode / prefill (default: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -248,7 +250,7 @@ def main():
         print(json.dumps({"config": a.config, **res}), flush=True)
         return
     n_layers = cfg.layers
-    T = cfg.T
+    T = a.tokens if a.tokens > 0 else cfg.T
     log(f"config {cfg.name}: generating {n_layers} layer(s)")
     t0 = time.perf_counter()
     layers = build_layers(cfg, n_layers, a.seed, moe, torch)
@@ -306,7 +308,11 @@ def main():
     # step on the router + expert-phase path) the library records events
     # around that phase's launches on the same stream, in eager steps.
     layer_path = T == 1 and "layer=0" not in a.tune
-    if layer_path:
+    tune = dict(kv.split("=") for kv in a.tune)
+    grouped = T >= int(tune.get("prefill_min_t", 8))  # the library's default crossover
+    if layer_path or (T > 1 and not grouped):
+        # one launch per step, or (2 to 7 tokens) the router kernel and the
+        # few-token expert kernels, timed as the whole step
         k_us = ms_step * 1e3
     else:
         n_prof = min(512, steps)
@@ -341,8 +347,13 @@ def main():
         k_bytes = (float(np.mean(uniq)) * gen.blob_bytes(cfg.D, cfg.F)
                    + (gen.blob_bytes(cfg.D, cfg.F_shared) if cfg.F_shared else 0)
                    + T * cfg.D * 2 + T * cfg.D * 4)
-        k_name = (f"grouped prefill expert kernels (gate/up, down, combine; "
-                  f"{np.mean(uniq):.1f} distinct experts per chunk)")
+        if not grouped:
+            k_bytes += gen.codes_bytes(cfg.E, cfg.D, 8) + gen.meta_bytes(cfg.E, cfg.D)
+            k_name = (f"whole step of {T} tokens: router kernel and the few-token expert "
+                      f"kernels ({np.mean(uniq):.1f} distinct experts)")
+        else:
+            k_name = (f"grouped prefill expert kernels (gate/up, down, combine; "
+                      f"{np.mean(uniq):.1f} distinct experts per chunk)")
         traffic = None
     k_gbps = k_bytes / (k_us * 1e-6) / 1e9 if k_bytes else None
     log(f"timed kernel: {k_us:.2f} us per launch" + (f", {k_gbps:,.0f} GB/s" if k_gbps else ""))

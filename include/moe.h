@@ -223,7 +223,7 @@ moe_status moe_set_profile_events(void *const *events, int32_t n_pairs);
  *   fused (1)            the one-launch expert phase when the layer kernel
  *                        is off; fused_ksg, fused_ksd (0) its splits
  *   glu_ks, down_ks (0)  reduction splits of the few-token kernels
- *   prefill_min_t (16)   tokens per call from which the grouped matrix-core
+ *   prefill_min_t (8)    tokens per call from which the grouped matrix-core
  *                        kernels run
  *   route_mfma (1)       router of 16 or more tokens on the matrix cores */
 moe_status moe_set_tuning(const char *key, int32_t value);

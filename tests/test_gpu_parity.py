@@ -600,7 +600,7 @@ def test_pool_paths_streamed_equals_resident(path, T):
         pool.close()
     finally:
         _tune(**_DEFAULTS)
-        moe.moe_set_tuning("prefill_min_t", 16)
+        moe.moe_set_tuning("prefill_min_t", 8)
 
 
 @pytest.mark.parametrize("variant", [1, 2])
