@@ -171,7 +171,8 @@ def run_streamed(cfg, a, moe, torch):
                      moe.DeviceBank.from_numpy(lw.shared[None, :], cfg.D, cfg.F_shared),
                      torch.from_numpy(gen.zipf_bias(a.seed, l, cfg.E, cfg.beta)).cuda()))
     log(f"host experts ready ({time.perf_counter() - t0:.1f} s)")
-    pool = moe.Pool(host, n_layers, cfg.slots, cfg.E, cfg.D, cfg.F)
+    slots = a.slots if a.slots > 0 else cfg.slots
+    pool = moe.Pool(host, n_layers, slots, cfg.E, cfg.D, cfg.F)
     xb = np.stack([gen.activations(a.seed, 2000 + l, 0, n_tok + 16, cfg.D, cfg.x_dtype)
                    for l in range(n_layers)])
     x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16)
@@ -204,7 +205,7 @@ def run_streamed(cfg, a, moe, torch):
         dst.copy_(src, non_blocking=True)
     torch.cuda.synchronize()
     peak = 4 * src.numel() / (time.perf_counter() - t1) / 1e9
-    res = {"tokens": n_tok, "layers": n_layers, "slots": cfg.slots, "s": el,
+    res = {"tokens": n_tok, "layers": n_layers, "slots": slots, "s": el,
            "tokens_per_s": n_tok / el, "hit_rate": st["hits"] / max(1, st["lookups"]),
            "miss_MB_per_token": st["bytes_h2d"] / n_tok / 1e6,
            "h2d_GBps": st["bytes_h2d"] / el / 1e9, "pinned_copy_peak_GBps": peak, "beta": cfg.beta}
@@ -221,6 +222,8 @@ def main():
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill", "stack30", "streamed"])
     ap.add_argument("--stream-tokens", type=int, default=64)
+    ap.add_argument("--slots", type=int, default=0,
+                    help="HBM expert slots per layer for the streamed workload (default 16)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="tokens per step for decode / prefill (default: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
