@@ -173,6 +173,7 @@ def run_streamed(cfg, a, moe, torch):
     log(f"host experts ready ({time.perf_counter() - t0:.1f} s)")
     slots = a.slots if a.slots > 0 else cfg.slots
     pool = moe.Pool(host, n_layers, slots, cfg.E, cfg.D, cfg.F)
+    pool.set_policy(1 if a.pool_policy == "lru" else 0)
     xb = np.stack([gen.activations(a.seed, 2000 + l, 0, n_tok + 16, cfg.D, cfg.x_dtype)
                    for l in range(n_layers)])
     x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16)
@@ -205,7 +206,7 @@ def run_streamed(cfg, a, moe, torch):
         dst.copy_(src, non_blocking=True)
     torch.cuda.synchronize()
     peak = 4 * src.numel() / (time.perf_counter() - t1) / 1e9
-    res = {"tokens": n_tok, "layers": n_layers, "slots": slots, "s": el,
+    res = {"tokens": n_tok, "layers": n_layers, "slots": slots, "policy": a.pool_policy, "s": el,
            "tokens_per_s": n_tok / el, "hit_rate": st["hits"] / max(1, st["lookups"]),
            "miss_MB_per_token": st["bytes_h2d"] / n_tok / 1e6,
            "h2d_GBps": st["bytes_h2d"] / el / 1e9, "pinned_copy_peak_GBps": peak, "beta": cfg.beta}
@@ -222,6 +223,8 @@ def main():
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill", "stack30", "streamed"])
     ap.add_argument("--stream-tokens", type=int, default=64)
+    ap.add_argument("--pool-policy", choices=["lfu", "lru"], default="lfu",
+                    help="slot replacement of the streamed workload (lfu: the pages')")
     ap.add_argument("--slots", type=int, default=0,
                     help="HBM expert slots per layer for the streamed workload (default 16)")
     ap.add_argument("--tokens", type=int, default=0,

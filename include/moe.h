@@ -194,6 +194,18 @@ moe_status moe_pool_reset_stats(moe_pool *pool);
 moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
                           const int32_t *ids, int32_t *events);
 
+/* Replacement policy of a pool's slots: 0 least frequently used (the pages'
+ * choice: stork.ai blog, "Mas inteligente que tu RAM"; the default), 1 least
+ * recently used (victim: the resident expert the call does not need that was
+ * used longest ago, ties to the lowest slot), for comparison (the pages weigh
+ * other cache policies against LFU: hndistilled.com, "Enfoque tecnico").
+ * Applies to the pool's later calls.  MOE_E_INVALID for another value. */
+moe_status moe_pool_set_policy(moe_pool *pool, int32_t policy);
+
+/* moe_lfu_replay for either policy (0 LFU, 1 LRU). */
+moe_status moe_cache_replay(int32_t policy, int32_t slots, int32_t E, int32_t k,
+                            int32_t n_tokens, const int32_t *ids, int32_t *events);
+
 /* Timing probe for measurement tools: while set, every moe_layer_forward
  * records events[2i] (a hipEvent_t) on its stream just before its expert
  * phase -- all work after routing: the one-launch expert kernel for decode,

@@ -402,3 +402,44 @@ class LFUCache:
             events.append((e, s, False, victim))
         self.now += 1
         return events
+
+
+class LRUCache:
+    """Slot cache of one layer, least-recently-used replacement: a policy to
+    compare with the pages' LFU (they report other cache policies losing to
+    it: hndistilled.com, "Enfoque tecnico").  The victim is the resident
+    expert that the current token does not need and whose last use is the
+    oldest, ties to the lowest slot; empty slots fill in slot order.
+    """
+
+    def __init__(self, slots: int, E: int):
+        self.slots = slots
+        self.last_use = [-1] * E
+        self.where = [-1] * E          # slot of each resident expert
+        self.holder = [-1] * slots     # expert in each slot
+        self.t = 0
+
+    def access(self, ids: Sequence[int]) -> List[Tuple[int, int, bool, int]]:
+        """Serve one token's experts; returns (expert, slot, hit, evicted)."""
+        ids = [int(e) for e in ids]
+        if len(set(ids)) != len(ids) or len(ids) > self.slots:
+            raise ValueError("ids must be distinct and fit the slots")
+        for e in ids:
+            self.last_use[e] = self.t
+        out = []
+        for e in ids:
+            if self.where[e] >= 0:
+                out.append((e, self.where[e], True, -1))
+                continue
+            if -1 in self.holder:
+                slot, evicted = self.holder.index(-1), -1
+            else:
+                slot = min((s for s in range(self.slots) if self.holder[s] not in ids),
+                           key=lambda s: (self.last_use[self.holder[s]], s))
+                evicted = self.holder[slot]
+                self.where[evicted] = -1
+            self.holder[slot] = e
+            self.where[e] = slot
+            out.append((e, slot, False, evicted))
+        self.t += 1
+        return out

@@ -45,8 +45,10 @@ bool LfuPlanner::access(const int *experts, int n, std::vector<Event> *events) {
         bool needed = false;
         for (int j = 0; j < n; ++j) needed |= experts[j] == v;
         if (needed) continue;
-        if (victim < 0 || count_[v] < count_[victim] ||
-            (count_[v] == count_[victim] && last_[v] < last_[victim])) {
+        const bool older = lru_ ? last_[v] < last_[victim]
+                                : count_[v] < count_[victim] ||
+                                      (count_[v] == count_[victim] && last_[v] < last_[victim]);
+        if (victim < 0 || older) {
           victim = v;
           slot = s;
         }
@@ -297,9 +299,22 @@ extern "C" {
 
 moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
                           const int32_t *ids, int32_t *events) {
-  if (slots < 1 || E < 1 || k < 1 || k > slots || n_tokens < 0 || !ids || !events)
+  return moe_cache_replay(0, slots, E, k, n_tokens, ids, events);
+}
+
+moe_status moe_pool_set_policy(moe_pool *p, int32_t policy) {
+  if (!p || policy < 0 || policy > 1) return MOE_E_INVALID;
+  for (auto &pl : p->planners) pl.set_policy(policy);
+  return MOE_OK;
+}
+
+moe_status moe_cache_replay(int32_t policy, int32_t slots, int32_t E, int32_t k,
+                            int32_t n_tokens, const int32_t *ids, int32_t *events) {
+  if (slots < 1 || E < 1 || k < 1 || k > slots || n_tokens < 0 || !ids || !events ||
+      policy < 0 || policy > 1)
     return MOE_E_INVALID;
   LfuPlanner pl(slots, E);
+  pl.set_policy(policy);
   std::vector<LfuPlanner::Event> ev;
   for (int t = 0; t < n_tokens; ++t) {
     const int32_t *row = ids + (size_t)t * k;

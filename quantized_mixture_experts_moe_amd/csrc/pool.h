@@ -17,6 +17,10 @@ class LfuPlanner {
     int expert, slot, hit, evicted;
   };
   LfuPlanner(int slots, int E);
+  // 0: least frequently used (the pages' policy); 1: least recently used
+  // (victim: the resident expert not needed now that was used longest ago,
+  // ties to the lowest slot), for comparison
+  void set_policy(int policy) { lru_ = policy == 1; }
   // Serve the experts of one call (distinct, in first-use order).  Returns
   // false if they do not fit the slots.
   bool access(const int *experts, int n, std::vector<Event> *events);
@@ -24,6 +28,7 @@ class LfuPlanner {
 
  private:
   int slots_;
+  bool lru_ = false;
   long now_ = 0;
   std::vector<long> count_, last_;
   std::vector<int> slot_of_, expert_in_;

@@ -35,6 +35,7 @@ EXPORTS = (
     "moe_blob_bytes", "moe_workspace_bytes", "moe_route", "moe_expert_ffn", "moe_combine",
     "moe_permute", "moe_layer_forward", "moe_pool_create", "moe_pool_destroy",
     "moe_pool_get_stats", "moe_pool_reset_stats", "moe_lfu_replay", "moe_set_tuning",
+    "moe_pool_set_policy", "moe_cache_replay",
     "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
 )
 
@@ -82,6 +83,8 @@ def _load() -> ctypes.CDLL:
         "moe_pool_get_stats": (i32, [vp, P(moe_pool_stats)]),
         "moe_pool_reset_stats": (i32, [vp]),
         "moe_lfu_replay": (i32, [i32, i32, i32, i32, vp, vp]),
+        "moe_pool_set_policy": (i32, [vp, i32]),
+        "moe_cache_replay": (i32, [i32, i32, i32, i32, i32, vp, vp]),
         "moe_set_tuning": (i32, [ctypes.c_char_p, i32]),
         "moe_set_profile_events": (i32, [vp, i32]),
         "moe_workspace_timeouts": (i32, [vp, sz, P(ctypes.c_uint32), vp]),
@@ -262,6 +265,15 @@ def moe_layer_forward(x: torch.Tensor, router: DeviceQMat, k: int, routed: Optio
         "moe_layer_forward")
 
 
+def moe_cache_replay(policy: int, slots: int, E: int, ids: np.ndarray) -> np.ndarray:
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n, k = ids.shape
+    ev = np.zeros((n, k, 4), dtype=np.int32)
+    _check(lib.moe_cache_replay(policy, slots, E, k, n, ids.ctypes.data_as(ctypes.c_void_p),
+                                ev.ctypes.data_as(ctypes.c_void_p)), "moe_cache_replay")
+    return ev
+
+
 def moe_lfu_replay(slots: int, E: int, ids: np.ndarray) -> np.ndarray:
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     n, k = ids.shape
@@ -290,6 +302,10 @@ class Pool:
                                    ctypes.cast(arr, ctypes.c_void_p)),
                "moe_pool_create")
         self.handle = h
+
+    def set_policy(self, policy: int) -> None:
+        """0: least frequently used (default), 1: least recently used."""
+        _check(lib.moe_pool_set_policy(self.handle, policy), "moe_pool_set_policy")
 
     def stats(self) -> dict:
         st = moe_pool_stats()

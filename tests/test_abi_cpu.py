@@ -136,6 +136,23 @@ def test_lfu_planner_matches_oracle_model(beta):
         assert [tuple(r) for r in got[t]] == ref, t
 
 
+@pytest.mark.parametrize("beta", [0.0, 4.0, 6.5])
+def test_lru_planner_matches_oracle_model(beta):
+    rng = np.random.default_rng(7 + int(beta * 10))
+    E, k, slots, n = 128, 8, 16, 400
+    w = np.exp(-beta * 1.1 * np.log(1 + rng.permutation(E)) / 4)
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=w / w.sum()) for _ in range(n)])
+    got = moe.moe_cache_replay(1, slots, E, ids)
+    model = O.LRUCache(slots, E)
+    for t in range(n):
+        ref = [(e, s, 1 if h else 0, v) for (e, s, h, v) in model.access(ids[t])]
+        assert [tuple(r) for r in got[t]] == ref, t
+    # policy 0 is the LFU replay
+    assert np.array_equal(moe.moe_cache_replay(0, slots, E, ids), moe.moe_lfu_replay(slots, E, ids))
+    with pytest.raises(moe.MoEError):
+        moe.moe_cache_replay(2, slots, E, ids)
+
+
 def test_lfu_planner_rejects_bad_traces():
     with pytest.raises(moe.MoEError):
         moe.moe_lfu_replay(4, 16, np.array([[1, 1]]))   # repeated expert

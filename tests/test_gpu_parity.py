@@ -375,14 +375,18 @@ def test_layer_forward_x_zero():
 
 
 # ---------------------------------------------------------------- streamed experts (pool)
-def test_pool_streamed_equals_resident_and_trace():
-    _case("pool streamed vs resident (tiny, 2 layers, 4 slots)")
+@pytest.mark.parametrize("policy", [0, 1])
+def test_pool_streamed_equals_resident_and_trace(policy):
+    """Streamed output bitwise the resident one, and the pool's hits and
+    misses those of the oracle's cache model: LFU (0) or LRU (1)."""
+    _case(f"pool streamed vs resident (tiny, 2 layers, 4 slots, policy {policy})")
     cfg = gen.CONFIGS["tiny"]
     layers = [dev_layer("tiny", seed=3, layer=l) for l in range(2)]
     host = [torch.from_numpy(L.lw.experts.copy()).pin_memory() for L in layers]
     pool = moe.Pool(host, 2, 4, cfg.E, cfg.D, cfg.F)
+    pool.set_policy(policy)
     ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
-    models = [O.LFUCache(4, cfg.E) for _ in range(2)]
+    models = [(O.LRUCache if policy else O.LFUCache)(4, cfg.E) for _ in range(2)]
     misses = 0
     for tok in range(24):
         for l, L in enumerate(layers):

@@ -267,6 +267,20 @@ def test_lfu_handworked_trace():
         assert c.access(ids) == evs
 
 
+def test_lru_handworked_trace():
+    """Two slots, one expert per token: 0, 0, 1, 2, 0.  At the fourth token
+    LRU evicts expert 0 (last used at token 1; expert 1 at token 2), where
+    LFU would evict expert 1 (used once against twice); at the fifth, expert
+    0 misses and expert 1 (token 2, older than expert 2 at token 3) goes."""
+    c = O.LRUCache(2, 4)
+    got = [c.access([e]) for e in (0, 0, 1, 2, 0)]
+    assert got == [[(0, 0, False, -1)], [(0, 0, True, -1)], [(1, 1, False, -1)],
+                   [(2, 0, False, 0)], [(0, 1, False, 1)]]
+    f = O.LFUCache(2, 4)
+    lfu = [f.access([e]) for e in (0, 0, 1, 2)]
+    assert lfu[3] == [(2, 1, False, 1)]  # the policies part here
+
+
 def test_lfu_never_evicts_needed_and_bounds():
     rng = np.random.default_rng(11)
     c = O.LFUCache(16, 128)
