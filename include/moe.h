@@ -202,6 +202,14 @@ moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
  * Applies to the pool's later calls.  MOE_E_INVALID for another value. */
 moe_status moe_pool_set_policy(moe_pool *pool, int32_t policy);
 
+/* Test hook for the failure path of a pool's fetches: the pool lets `after`
+ * more host -> HBM copies through and then reports the next one as failed
+ * (once; -1 clears the hook).  The call that meets the failure returns
+ * MOE_E_HIP after invalidating every slot it may have written, so that the
+ * next call needing any of those experts fetches it again; as after any
+ * MOE_E_HIP, zero-fill the workspace again before reusing it. */
+moe_status moe_pool_fail_copy(moe_pool *pool, int32_t after);
+
 /* moe_lfu_replay for either policy (0 LFU, 1 LRU). */
 moe_status moe_cache_replay(int32_t policy, int32_t slots, int32_t E, int32_t k,
                             int32_t n_tokens, const int32_t *ids, int32_t *events);

@@ -39,8 +39,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
+def _newest_header() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    hs += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    if incremental and os.path.exists(obj):
+        t = os.path.getmtime(obj)
+        if t > os.path.getmtime(os.path.join(CSRC, src)) and t > _newest_header():
+            return obj
     cmd = [hipcc()] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -48,11 +58,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
+def build(jobs: int = 8, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (or, with incremental, those changed since their
+    object was built) and link libmoe.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, incremental), srcs))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,9 +79,11 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=8)
+    ap.add_argument("--incremental", action="store_true",
+                    help="recompile only sources changed since their object file")
     a = ap.parse_args()
     try:
-        build(a.jobs, verbose=True)
+        build(a.jobs, verbose=True, incremental=a.incremental)
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

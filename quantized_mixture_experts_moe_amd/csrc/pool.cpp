@@ -15,57 +15,6 @@
 #include <chrono>
 #include <new>
 
-namespace moe {
-
-LfuPlanner::LfuPlanner(int slots, int E)
-    : slots_(slots), count_(E, 0), last_(E, -1), slot_of_(E, -1), expert_in_(slots, -1) {}
-
-bool LfuPlanner::access(const int *experts, int n, std::vector<Event> *events) {
-  if (n > slots_) return false;
-  for (int i = 0; i < n; ++i) {
-    count_[experts[i]] += 1;
-    last_[experts[i]] = now_;
-  }
-  for (int i = 0; i < n; ++i) {
-    const int e = experts[i];
-    if (slot_of_[e] >= 0) {
-      if (events) events->push_back({e, slot_of_[e], 1, -1});
-      continue;
-    }
-    int slot = -1, victim = -1;
-    for (int s = 0; s < slots_; ++s) {
-      if (expert_in_[s] < 0) {
-        slot = s;
-        break;
-      }
-    }
-    if (slot < 0) {
-      for (int s = 0; s < slots_; ++s) {
-        const int v = expert_in_[s];
-        bool needed = false;
-        for (int j = 0; j < n; ++j) needed |= experts[j] == v;
-        if (needed) continue;
-        const bool older = lru_ ? last_[v] < last_[victim]
-                                : count_[v] < count_[victim] ||
-                                      (count_[v] == count_[victim] && last_[v] < last_[victim]);
-        if (victim < 0 || older) {
-          victim = v;
-          slot = s;
-        }
-      }
-      if (slot < 0) return false;
-      slot_of_[victim] = -1;
-    }
-    expert_in_[slot] = e;
-    slot_of_[e] = slot;
-    if (events) events->push_back({e, slot, 0, victim});
-  }
-  ++now_;
-  return true;
-}
-
-}  // namespace moe
-
 struct moe_pool {
   int n_layers = 0, slots = 0, E = 0, D = 0, F = 0;
   size_t blob_bytes = 0;
@@ -93,6 +42,12 @@ struct moe_pool {
   uint32_t epoch = 0;
   int ids_mode = 0;                           // this call's ids: 0 copied, 1 ids + flags, 2 words
   moe_pool_stats stats{};
+  // the device table of a layer is uploaded by the next call that reads it
+  // whenever the host table has changed since its last upload
+  std::vector<char> table_dirty;
+  hipEvent_t ev_table = nullptr;              // after the last upload (its source is h_tables)
+  bool table_pending = false;
+  int fail_copy_at = -1;                      // test hook: copies to let through before one fails
 };
 
 namespace moe {
@@ -224,49 +179,55 @@ static moe_status wait_direct_ids(moe_pool *p, int T, int k) {
   return MOE_OK;
 }
 
+namespace {
+// Misses go host -> HBM by hipMemcpyAsync on the pool's side stream.
+struct HipCopyEngine final : CopyEngine {
+  hipStream_t side;
+  explicit HipCopyEngine(hipStream_t s) : side(s) {}
+  int copy(void *dst, const void *src, size_t bytes) override {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, side) == hipSuccess ? 0 : 1;
+  }
+};
+}  // namespace
+
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
                               const void *const **table, const void *const **slot_blob) {
   const moe_status ws = p->ids_mode ? wait_direct_ids(p, T, k)
                                       : (hipEventSynchronize(p->ev_ids) == hipSuccess ? MOE_OK
                                                                                        : MOE_E_HIP);
   if (ws) return ws;
-  // distinct experts of the call in first-use order
-  std::vector<int> need;
-  need.reserve(T * k);
-  for (int i = 0; i < T * k; ++i) {
-    const int e = p->h_ids[i];
-    if (e < 0 || e >= p->E) return MOE_E_POOL;
-    if (std::find(need.begin(), need.end(), e) == need.end()) need.push_back(e);
+  // the host table may still be the source of an earlier upload
+  if (p->table_pending) {
+    if (hipEventSynchronize(p->ev_table) != hipSuccess) return MOE_E_HIP;
+    p->table_pending = false;
   }
-  std::vector<LfuPlanner::Event> ev;
-  if (!p->planners[layer].access(need.data(), (int)need.size(), &ev)) return MOE_E_POOL;
-  // counts: one lookup per (token, slot) use; the call's first use of a
-  // missing expert is its miss, repeated uses inside the call are hits
-  p->stats.lookups += (uint64_t)T * k;
   const void **tab = p->h_tables + (size_t)layer * p->E;
   uint8_t *base = p->slot_mem + (size_t)layer * p->slots * p->blob_bytes;
-  int copies = 0;
-  for (const auto &e : ev) {
-    if (e.hit) continue;
-    uint8_t *dst = base + (size_t)e.slot * p->blob_bytes;
-    const void *src = p->host_blobs[(size_t)layer * p->E + e.expert];
-    if (hipMemcpyAsync(dst, src, p->blob_bytes, hipMemcpyHostToDevice, p->side) != hipSuccess)
-      return MOE_E_HIP;
-    if (e.evicted >= 0) {
-      tab[e.evicted] = base;  // not resident; never read for a call that does not select it
-      p->stats.evictions += 1;
-    }
-    tab[e.expert] = dst;
-    p->stats.misses += 1;
-    p->stats.bytes_h2d += p->blob_bytes;
-    ++copies;
-  }
-  p->stats.hits += (uint64_t)T * k - copies;
-  bool queued = copies > 0;
-  if (copies && table) {
+  LayerPlanArgs a;
+  a.ids = p->h_ids; a.n = T * k; a.E = p->E;
+  a.slot_base = base; a.blob_bytes = p->blob_bytes;
+  a.host_blobs = p->host_blobs.data() + (size_t)layer * p->E;
+  a.table = tab;
+  HipCopyEngine eng(p->side);
+  CopyEngine *ce = &eng;
+  FailingCopyEngine fail(ce, p->fail_copy_at);
+  if (p->fail_copy_at >= 0) ce = &fail;
+  const PlanResult r = plan_layer_call(p->planners[layer], a, *ce, &p->stats);
+  if (p->fail_copy_at >= 0) p->fail_copy_at = fail.remaining();
+  // a failed copy may have changed the table too (invalidated slots)
+  p->table_dirty[layer] = true;
+  if (r.status) return r.status;
+  bool queued = r.copies > 0;
+  if (table && p->table_dirty[layer]) {
+    // every change of the host table since the last upload (this call's and
+    // those of calls that only read the per-pair slot addresses)
     if (hipMemcpyAsync(p->d_tables + (size_t)layer * p->E, tab, sizeof(void *) * p->E,
                        hipMemcpyHostToDevice, p->side) != hipSuccess)
       return MOE_E_HIP;
+    if (hipEventRecord(p->ev_table, p->side) != hipSuccess) return MOE_E_HIP;
+    p->table_pending = true;
+    p->table_dirty[layer] = false;
+    queued = true;
   }
   if (slot_blob) {
     // the kernels read the addresses from pinned host memory: no copy, and
@@ -300,6 +261,12 @@ extern "C" {
 moe_status moe_lfu_replay(int32_t slots, int32_t E, int32_t k, int32_t n_tokens,
                           const int32_t *ids, int32_t *events) {
   return moe_cache_replay(0, slots, E, k, n_tokens, ids, events);
+}
+
+moe_status moe_pool_fail_copy(moe_pool *p, int32_t after) {
+  if (!p || after < -1) return MOE_E_INVALID;
+  p->fail_copy_at = after;
+  return MOE_OK;
 }
 
 moe_status moe_pool_set_policy(moe_pool *p, int32_t policy) {
@@ -348,6 +315,7 @@ moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int3
   p->blob_bytes = blob_layout(D, F).total;
   p->host_blobs.assign(host_blobs, host_blobs + (size_t)n_layers * E);
   for (int l = 0; l < n_layers; ++l) p->planners.emplace_back(slots, E);
+  p->table_dirty.assign(n_layers, 0);
   bool ok = hipMalloc((void **)&p->slot_mem, (size_t)n_layers * slots * p->blob_bytes) ==
             hipSuccess;
   ok = ok && hipMalloc((void **)&p->d_tables, sizeof(void *) * n_layers * E) == hipSuccess;
@@ -357,6 +325,7 @@ moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int3
   ok = ok && hipEventCreateWithFlags(&p->ev_ids, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_copies, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_slot, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->ev_table, hipEventDisableTiming) == hipSuccess;
   if (ok) {
     // every table entry starts at the layer's first slot (nothing resident yet)
     for (int l = 0; l < n_layers; ++l)
@@ -387,6 +356,7 @@ moe_status moe_pool_destroy(moe_pool *p) {
   if (p->ev_ids) (void)hipEventDestroy(p->ev_ids);
   if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
   if (p->ev_slot) (void)hipEventDestroy(p->ev_slot);
+  if (p->ev_table) (void)hipEventDestroy(p->ev_table);
   if (p->side) (void)hipStreamDestroy(p->side);
   delete p;
   return MOE_OK;

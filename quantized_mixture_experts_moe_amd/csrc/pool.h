@@ -4,35 +4,9 @@
 #include <vector>
 
 #include "moe_internal.h"
+#include "pool_plan.h"
 
 namespace moe {
-
-// Least-frequently-used slot planner of one layer.  Use counts are per
-// expert, cumulative, and kept after eviction; the victim is a resident
-// expert the current call does not need with the smallest count, ties to the
-// least recently used, then the lowest slot; empty slots fill in slot order.
-class LfuPlanner {
- public:
-  struct Event {
-    int expert, slot, hit, evicted;
-  };
-  LfuPlanner(int slots, int E);
-  // 0: least frequently used (the pages' policy); 1: least recently used
-  // (victim: the resident expert not needed now that was used longest ago,
-  // ties to the lowest slot), for comparison
-  void set_policy(int policy) { lru_ = policy == 1; }
-  // Serve the experts of one call (distinct, in first-use order).  Returns
-  // false if they do not fit the slots.
-  bool access(const int *experts, int n, std::vector<Event> *events);
-  int slot_of(int e) const { return slot_of_[e]; }
-
- private:
-  int slots_;
-  bool lru_ = false;
-  long now_ = 0;
-  std::vector<long> count_, last_;
-  std::vector<int> slot_of_, expert_in_;
-};
 
 moe_status pool_check(const moe_pool *p, int layer, int E, int D, int k);
 int pool_F(const moe_pool *p);

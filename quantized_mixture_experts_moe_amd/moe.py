@@ -35,7 +35,7 @@ EXPORTS = (
     "moe_blob_bytes", "moe_workspace_bytes", "moe_route", "moe_expert_ffn", "moe_combine",
     "moe_permute", "moe_layer_forward", "moe_pool_create", "moe_pool_destroy",
     "moe_pool_get_stats", "moe_pool_reset_stats", "moe_lfu_replay", "moe_set_tuning",
-    "moe_pool_set_policy", "moe_cache_replay",
+    "moe_pool_set_policy", "moe_cache_replay", "moe_pool_fail_copy",
     "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
 )
 
@@ -84,6 +84,7 @@ def _load() -> ctypes.CDLL:
         "moe_pool_reset_stats": (i32, [vp]),
         "moe_lfu_replay": (i32, [i32, i32, i32, i32, vp, vp]),
         "moe_pool_set_policy": (i32, [vp, i32]),
+        "moe_pool_fail_copy": (i32, [vp, i32]),
         "moe_cache_replay": (i32, [i32, i32, i32, i32, i32, vp, vp]),
         "moe_set_tuning": (i32, [ctypes.c_char_p, i32]),
         "moe_set_profile_events": (i32, [vp, i32]),
@@ -306,6 +307,10 @@ class Pool:
     def set_policy(self, policy: int) -> None:
         """0: least frequently used (default), 1: least recently used."""
         _check(lib.moe_pool_set_policy(self.handle, policy), "moe_pool_set_policy")
+
+    def fail_copy(self, after: int) -> None:
+        """Test hook: let `after` copies through, then fail one (-1 clears)."""
+        _check(lib.moe_pool_fail_copy(self.handle, after), "moe_pool_fail_copy")
 
     def stats(self) -> dict:
         st = moe_pool_stats()

@@ -207,15 +207,108 @@ def test_oracle_matches_dense_bruteforce(seed, E, k, T, D, F, Fs):
     assert rel32 <= 1e-6
 
 
-def test_combine_definition():
-    rng = np.random.default_rng(2)
-    y = rng.standard_normal((3, 4, 16))
-    g = rng.random((3, 4))
-    ys = rng.standard_normal((3, 16))
-    out = O.combine(y, g, ys)
-    for t in range(3):
-        ref = ys[t] + sum(g[t, j] * y[t, j] for j in range(4))
-        np.testing.assert_allclose(out[t], ref, rtol=1e-14)
+def test_combine_handworked():
+    """One token, two routed outputs and a shared one, worked by hand:
+    out = ys + 0.25 y0 + 0.75 y1 = [10 + 0.25 + 3, 20 + 0.5 + 3.75, 30 + 0.75 + 4.5]."""
+    y = np.array([[[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]]])
+    g = np.array([[0.25, 0.75]])
+    ys = np.array([[10.0, 20.0, 30.0]])
+    assert O.combine(y, g, ys).tolist() == [[13.25, 24.25, 35.25]]
+    # without a shared expert the routed part alone
+    assert O.combine(y, g, None).tolist() == [[3.25, 4.25, 5.25]]
+    # a one-hot gate picks that output
+    assert O.combine(y, np.array([[0.0, 1.0]]), None).tolist() == [[4.0, 5.0, 6.0]]
+
+
+@pytest.mark.parametrize("seed,E,k", [(0, 16, 4), (3, 8, 8)])
+def test_combine_equals_dense_bruteforce(seed, E, k):
+    """combine of the oracle's per-slot outputs, gates and shared output is
+    the dense evaluation of every expert weighted by the masked,
+    renormalised softmax (an independent decoder and evaluation)."""
+    lw = _tiny_layer(seed, E=E)
+    x = O.activations_to_float(gen.activations(seed, 0, 0, 3, 256, "fp16"), "fp16")
+    r = O.layer_forward(x, lw, k)
+    ref = O.dense_bruteforce(x, lw, k)
+    out = O.combine(r["y"], r["gates"], r["y_shared"])
+    assert np.linalg.norm(out - ref["out"]) / np.linalg.norm(ref["out"]) < 1e-10
+
+
+# ---------------------------------------------------------------- activation decoding
+_ACT_EDGES = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x4000,
+              0xC000, 0x7F7F, 0xFF7F, 0x3C00, 0x7BFF, 0x0400, 0x03FF, 0x3555]
+
+
+def test_activations_to_float_literals():
+    """Bit patterns decoded by hand from the IEEE layouts."""
+    bf = O.activations_to_float(np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x8000, 0x4049],
+                                         np.uint16), "bf16")
+    assert bf[0] == 1.0 and bf[1] == -2.0
+    assert bf[2] == 2.0 ** -133                      # smallest bf16 subnormal
+    assert bf[3] == (2 - 2.0 ** -7) * 2.0 ** 127     # largest finite bf16
+    assert bf[4] == 0.0 and math.copysign(1.0, bf[4]) == -1.0
+    assert bf[5] == 3.140625                         # 0x4049: 1.5703125 * 2
+    hf = O.activations_to_float(np.array([0x3C00, 0x0001, 0x7BFF, 0xC000, 0x0400, 0x3555],
+                                         np.uint16), "fp16")
+    assert hf[0] == 1.0 and hf[1] == 2.0 ** -24 and hf[2] == 65504.0 and hf[3] == -2.0
+    assert hf[4] == 2.0 ** -14                       # smallest normal fp16
+    assert hf[5] == 0.333251953125                   # 0x3555: (1 + 341/1024) / 4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_activations_to_float_matches_torch(dtype):
+    """Every finite bit pattern (all 65,536 minus NaN/inf) against torch's own
+    bfloat16 / float16 types widened to float64."""
+    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    ref = torch.from_numpy(u.view(np.int16)).view(tdt).double().numpy()
+    fin = np.isfinite(ref)
+    got = O.activations_to_float(u, dtype)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    edges = np.array(_ACT_EDGES, np.uint16)
+    assert np.array_equal(O.activations_to_float(edges, dtype),
+                          torch.from_numpy(edges.view(np.int16)).view(tdt).double().numpy(),
+                          equal_nan=True)
+
+
+# ---------------------------------------------------------------- blob sections
+def test_blob_layout_offsets_handworked():
+    """Section offsets worked by hand.  D = 2816, F = 704: codes [704, 2816]
+    at 4 bits are 991,232 B, metas 44 x 704 x 4 = 123,904 B and
+    11 x 2816 x 4 = 123,904 B, all multiples of 256.  D = 256, F = 128 (the
+    tiny config): codes 16,384 B, metas 2,048 B."""
+    lay = O.blob_layout(2816, 704)
+    assert [lay[n][0] for n in ("gate.codes", "up.codes", "down.codes", "gate.meta", "up.meta",
+                                "down.meta")] == [0, 991_232, 1_982_464, 2_973_696, 3_097_600,
+                                                  3_221_504]
+    assert lay["total"][1] == 3_345_408
+    tiny = O.blob_layout(256, 128)
+    assert [tiny[n] for n in ("gate.codes", "up.codes", "down.codes", "gate.meta", "up.meta",
+                              "down.meta")] == [(0, 16384), (16384, 16384), (32768, 16384),
+                                                (49152, 2048), (51200, 2048), (53248, 2048)]
+    assert tiny["total"][1] == 55_296
+    # a width whose sections need padding: D = 64, F = 64 -> 2,048 B codes,
+    # 256 B metas: no padding either; D = 64, F = 192 -> meta 192 x 4 = 768 B
+    odd = O.blob_layout(64, 192)
+    assert odd["gate.meta"] == (18432, 768) and odd["up.meta"] == (19200, 768)
+    assert odd["down.meta"] == (19968, 3 * 64 * 4) and odd["total"][1] == 20736
+
+
+def test_blob_layout_matches_generator_and_header():
+    """The oracle's sections equal the generator's and follow the order the
+    C header documents."""
+    for D, F in [(2816, 704), (2816, 2112), (256, 128), (64, 192)]:
+        assert O.blob_layout(D, F) == gen.blob_sections(D, F)
+    hdr = open(os.path.join(os.path.dirname(GOLDEN), "..", "include", "moe.h")).read()
+    i = hdr.index("Expert blob")
+    order = []
+    for name in ("gate.codes", "up.codes", "down.codes", "gate.meta", "up.meta", "down.meta"):
+        order.append(hdr.index(name, i))
+    assert order == sorted(order)
+    lay = O.blob_layout(2816, 704)
+    offs = [lay[n][0] for n in ("gate.codes", "up.codes", "down.codes", "gate.meta", "up.meta",
+                                "down.meta")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
 
 
 # ---------------------------------------------------------------- permutation
@@ -352,3 +445,35 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(O, "gelu_tanh", lambda x: 0.5 * np.asarray(x) * (1 + scipy.special.erf(np.asarray(x) / math.sqrt(2))))
     with pytest.raises(AssertionError):
         test_gelu_tanh_golden_points()
+
+    # (5) combine that drops the shared output -> hand-worked combine fails
+    orig_c = O.combine
+    monkeypatch.setattr(O, "combine", lambda y, g, ys: orig_c(y, g, None))
+    with pytest.raises(AssertionError):
+        test_combine_handworked()
+    monkeypatch.setattr(O, "combine", orig_c)
+
+    # (6) bf16 widened by a shift of 8 instead of 16 -> literal decoding fails
+    orig_a = O.activations_to_float
+
+    def shifted(x_bits, x_dtype):
+        if x_dtype == "bf16":
+            u = np.asarray(x_bits, dtype=np.uint16)
+            return (u.astype(np.uint32) << 8).view(np.float32).astype(np.float64)
+        return orig_a(x_bits, x_dtype)
+    monkeypatch.setattr(O, "activations_to_float", shifted)
+    with pytest.raises(AssertionError):
+        test_activations_to_float_literals()
+    monkeypatch.setattr(O, "activations_to_float", orig_a)
+
+    # (7) blob sections with gate and up codes exchanged -> offsets fail
+    orig_b = O.blob_layout
+
+    def exchanged_sections(D, F):
+        lay = dict(orig_b(D, F))
+        lay["gate.codes"], lay["up.codes"] = lay["up.codes"], lay["gate.codes"]
+        return lay
+    monkeypatch.setattr(O, "blob_layout", exchanged_sections)
+    with pytest.raises(AssertionError):
+        test_blob_layout_offsets_handworked()
+    monkeypatch.setattr(O, "blob_layout", orig_b)
