@@ -175,6 +175,27 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
                              int32_t out_dtype, int32_t *ids_out, float *gates_out, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* moe_layer_forward with every expert resident (no pool), for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The caller passes inputs
+ * and outputs as for moe_layer_forward; the workspace is a fixed 48 MiB
+ * device array inside the library (one per GPU, held until the process
+ * ends), so nothing is allocated, by the library or by the caller.
+ *   Calls whose moe_workspace_bytes(T, k, E, D, F, F_shared) exceeds 48 MiB
+ *   return MOE_E_WORKSPACE and enqueue nothing (the Gemma-4-26B-A4B-shaped
+ *   layer fits up to 128 tokens per call: 40.1 MiB).
+ *   The first call on a device enqueues a zero-fill of the array on `stream`
+ *   before its own kernels; every call leaves the array ready for the next.
+ *   All calls on one GPU share the array: calls that overlap in time on one
+ *   GPU (different streams or host threads without ordering) race and their
+ *   outputs are undefined.  Errors as for moe_layer_forward; after MOE_E_HIP
+ *   the next call on the device clears the array again. */
+moe_status moe_layer_forward_noalloc(const void *x, int32_t x_dtype, int32_t T,
+                                     const moe_qmat *router, const float *logit_bias, int32_t k,
+                                     const moe_bank *routed, const moe_bank *shared, void *out,
+                                     int32_t out_dtype, int32_t *ids_out, float *gates_out,
+                                     void *stream);
+
 /* HBM expert slot pool (per layer `slots` blobs in HBM; least-frequently-used
  * replacement: stork.ai blog, "Mas inteligente que tu RAM"; 16 slots per
  * layer: hndistilled.com, "Enfoque tecnico").  host_blobs is a HOST array of

@@ -264,6 +264,34 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
 
 }  // namespace
 
+moe_status layer_forward_args(const void *x, int x_dtype, int T, const moe_qmat *router, int k,
+                              const moe_bank *routed, const moe_bank *shared, moe_pool *pool,
+                              int layer, const void *out, int out_dtype, Dims *d) {
+  if (!x || !aligned16(x) || !dtype_x_ok(x_dtype) || T < 1 || !out || !dtype_out_ok(out_dtype))
+    return MOE_E_INVALID;
+  moe_status st = check_router(router);
+  if (st) return st;
+  const int E = router->rows, D = router->cols;
+  if (k < 1 || k > E || k > kMaxK) return MOE_E_INVALID;
+  int F = 0;
+  if (pool) {
+    st = pool_check(pool, layer, E, D, k);
+    if (st) return st;
+    F = pool_F(pool);
+  } else {
+    st = check_bank(routed, D);
+    if (st) return st;
+    if (routed->E != E) return MOE_E_INVALID;
+    F = routed->F;
+  }
+  if (shared) {
+    st = check_bank(shared, D);
+    if (st) return st;
+  }
+  *d = Dims{T, k, E, D, F, shared ? shared->F : 0};
+  return MOE_OK;
+}
+
 Workspace carve_workspace(void *base, const Dims &d) { return carve(base, d); }
 size_t workspace_bytes(const Dims &d) { return carve(nullptr, d).total; }
 
@@ -433,30 +461,12 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
                              const moe_bank *shared, moe_pool *pool, int32_t layer, void *out,
                              int32_t out_dtype, int32_t *ids_out, float *gates_out, void *ws,
                              size_t ws_bytes, void *stream) {
-  if (!x || !aligned16(x) || !dtype_x_ok(x_dtype) || T < 1 || !out || !dtype_out_ok(out_dtype) ||
-      !ws)
-    return MOE_E_INVALID;
-  moe_status st = check_router(router);
+  if (!ws) return MOE_E_INVALID;
+  Dims d;
+  moe_status st = layer_forward_args(x, x_dtype, T, router, k, routed, shared, pool, layer, out,
+                                     out_dtype, &d);
   if (st) return st;
-  const int E = router->rows, D = router->cols;
-  if (k < 1 || k > E || k > kMaxK) return MOE_E_INVALID;
-  int F = 0;
-  if (pool) {
-    st = pool_check(pool, layer, E, D, k);
-    if (st) return st;
-    F = pool_F(pool);
-  } else {
-    st = check_bank(routed, D);
-    if (st) return st;
-    if (routed->E != E) return MOE_E_INVALID;
-    F = routed->F;
-  }
-  if (shared) {
-    st = check_bank(shared, D);
-    if (st) return st;
-  }
-  const int Fs = shared ? shared->F : 0;
-  const Dims d{T, k, E, D, F, Fs};
+  const int E = d.E, D = d.D, F = d.F, Fs = d.Fs;
   if (ws_bytes < workspace_bytes(d)) return MOE_E_WORKSPACE;
   Workspace w = carve(ws, d);
   hipStream_t s = (hipStream_t)stream;

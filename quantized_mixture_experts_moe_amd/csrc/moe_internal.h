@@ -135,6 +135,11 @@ struct Dims {
 };
 
 Workspace carve_workspace(void *base, const Dims &d);
+// Argument checks of moe_layer_forward (everything but the workspace); on
+// success *d holds the call's sizes.
+moe_status layer_forward_args(const void *x, int x_dtype, int T, const moe_qmat *router, int k,
+                              const moe_bank *routed, const moe_bank *shared, moe_pool *pool,
+                              int layer, const void *out, int out_dtype, Dims *d);
 size_t workspace_bytes(const Dims &d);
 
 // Host-side launchers (return hipError_t of the launch).

@@ -37,6 +37,7 @@ EXPORTS = (
     "moe_pool_get_stats", "moe_pool_reset_stats", "moe_lfu_replay", "moe_set_tuning",
     "moe_pool_set_policy", "moe_cache_replay", "moe_pool_fail_copy",
     "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
+    "moe_layer_forward_noalloc",
 )
 
 
@@ -78,6 +79,8 @@ def _load() -> ctypes.CDLL:
         "moe_permute": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
         "moe_layer_forward": (i32, [vp, i32, i32, P(moe_qmat), vp, i32, P(moe_bank),
                                     P(moe_bank), vp, i32, vp, i32, vp, vp, vp, sz, vp]),
+        "moe_layer_forward_noalloc": (i32, [vp, i32, i32, P(moe_qmat), vp, i32, P(moe_bank),
+                                            P(moe_bank), vp, i32, vp, vp, vp]),
         "moe_pool_create": (i32, [P(vp), i32, i32, i32, i32, i32, vp]),
         "moe_pool_destroy": (i32, [vp]),
         "moe_pool_get_stats": (i32, [vp, P(moe_pool_stats)]),
@@ -264,6 +267,21 @@ def moe_layer_forward(x: torch.Tensor, router: DeviceQMat, k: int, routed: Optio
         pool.handle if pool is not None else None, layer, _ptr(out), _DTYPES[out.dtype],
         _ptr(ids_out), _ptr(gates_out), _ptr(ws.buf), ws.nbytes, _stream(stream)),
         "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(x: torch.Tensor, router: DeviceQMat, k: int, routed: DeviceBank,
+                              shared: Optional[DeviceBank], out: torch.Tensor,
+                              logit_bias: Optional[torch.Tensor] = None,
+                              ids_out: Optional[torch.Tensor] = None,
+                              gates_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """moe_layer_forward (resident experts) on the library's own fixed
+    scratch array: nothing is allocated."""
+    T = x.shape[0]
+    _check(lib.moe_layer_forward_noalloc(
+        _ptr(x), _x_dtype(x), T, ctypes.byref(router.struct), _ptr(logit_bias), k,
+        ctypes.byref(routed.struct), ctypes.byref(shared.struct) if shared is not None else None,
+        _ptr(out), _DTYPES[out.dtype], _ptr(ids_out), _ptr(gates_out), _stream(stream)),
+        "moe_layer_forward_noalloc")
 
 
 def moe_cache_replay(policy: int, slots: int, E: int, ids: np.ndarray) -> np.ndarray:
