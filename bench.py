@@ -215,13 +215,127 @@ def run_streamed(cfg, a, moe, torch):
     return res
 
 
+def run_store(cfg, a, moe, torch):
+    """The NVMe -> pinned-host tier: cold reads of expert blobs from a file on
+    local storage by bounded-parallel pread (direct I/O) against mmap, then
+    streamed decode with the pool's misses read from the file."""
+    import tempfile
+    n_layers = a.store_layers
+    path = a.store_path or os.path.join(tempfile.gettempdir(), f"moe_experts_{os.getpid()}.bin")
+    stride = gen.store_stride(cfg.D, cfg.F)
+    nb = gen.blob_bytes(cfg.D, cfg.F)
+    t0 = time.perf_counter()
+    size = gen.write_expert_file(path, a.seed, n_layers, cfg)
+    log(f"store: wrote {size / 1e9:.2f} GB ({n_layers} layers) to {path} in "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    def drop_cache():
+        fd = os.open(path, os.O_RDONLY)
+        try:
+            os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+        finally:
+            os.close(fd)
+
+    raw = torch.empty(16 * stride + 4096, dtype=torch.uint8, pin_memory=True)
+    base = raw.data_ptr() + (-raw.data_ptr()) % 4096
+    bufs = [base + i * stride for i in range(16)]
+    rng = np.random.default_rng(a.seed + 1)
+    res = {"config": "store", "layers": n_layers, "file_GB": size / 1e9,
+           "expert_bytes": nb, "chunk_bytes": a.store_chunk}
+
+    def cold(flags, threads, per_call, n_calls, chunk):
+        drop_cache()
+        st = moe.Store(path, n_layers, cfg.E, cfg.D, cfg.F, flags=flags, threads=threads)
+        ms = []
+        for _ in range(n_calls):
+            layer = int(rng.integers(n_layers))
+            ids = rng.choice(cfg.E, size=per_call, replace=False)
+            t = time.perf_counter()
+            st.read(layer, ids, bufs[:per_call], chunk)
+            ms.append((time.perf_counter() - t) * 1e3)
+        st.close()
+        med = float(np.median(ms))
+        return {"ms_per_call": med, "ms_per_expert": med / per_call,
+                "GBps": per_call * nb / (med * 1e-3) / 1e9}
+
+    qd = {}
+    for threads in (1, 2, 4, 8, 16, 32):
+        qd[str(threads)] = cold(moe.MOE_STORE_DIRECT, threads, 1, 24, a.store_chunk)
+        log(f"store: pread direct, queue depth {threads}: {qd[str(threads)]}")
+    res["pread_direct_one_expert_by_queue_depth"] = qd
+    res["pread_direct_token_8_experts_qd32"] = cold(moe.MOE_STORE_DIRECT, 32, 8, 16, a.store_chunk)
+    res["pread_buffered_one_expert_qd16"] = cold(0, 16, 1, 24, a.store_chunk)
+    res["mmap_one_expert_1_thread"] = cold(moe.MOE_STORE_MMAP, 1, 1, 24, 0)
+    res["mmap_one_expert_16_threads"] = cold(moe.MOE_STORE_MMAP, 16, 1, 24, a.store_chunk)
+    log(f"store: {res}")
+
+    # streamed decode, misses read from the file (pool staging -> HBM slots)
+    slots = a.slots if a.slots > 0 else 16
+    devs = []
+    for l in range(n_layers):
+        lw = gen.layer_weights(a.seed, l, cfg)
+        devs.append((moe.DeviceQMat(lw.router.codes, lw.router.meta, cfg.E, cfg.D, 8),
+                     moe.DeviceBank.from_numpy(lw.shared[None, :], cfg.D, cfg.F_shared),
+                     torch.from_numpy(gen.zipf_bias(a.seed, l, cfg.E, gen.BETA_STACK)).cuda()))
+    n_tok = a.stream_tokens
+    xb = np.stack([gen.activations(a.seed, 2000 + l, 0, n_tok + 16, cfg.D, cfg.x_dtype)
+                   for l in range(n_layers)])
+    x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    drop_cache()
+    store = moe.Store(path, n_layers, cfg.E, cfg.D, cfg.F, flags=moe.MOE_STORE_DIRECT,
+                      threads=a.store_threads)
+    pool = moe.Pool.from_store(store, slots, chunk=a.store_chunk)
+
+    def token(t):
+        for l in range(n_layers):
+            router, shared, bias = devs[l]
+            moe.moe_layer_forward(x_all[l, t:t + 1], router, cfg.k, None, shared, out, ws,
+                                  logit_bias=bias, pool=pool, layer=l)
+
+    for t in range(16):
+        token(n_tok + t)
+    torch.cuda.synchronize()
+    pool.reset_stats()
+    s0 = store.stats()
+    t0 = time.perf_counter()
+    for t in range(n_tok):
+        token(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    pst, s1 = pool.stats(), store.stats()
+    read_s = (s1["ns"] - s0["ns"]) * 1e-9
+    res["streamed_from_file"] = {
+        "tokens": n_tok, "layers": n_layers, "slots": slots, "beta": gen.BETA_STACK,
+        "layer_tokens_per_s": n_tok * n_layers / el, "us_per_layer_token": el * 1e6 / n_tok / n_layers,
+        "hit_rate": pst["hits"] / max(1, pst["lookups"]),
+        "miss_MB_per_layer_token": pst["bytes_h2d"] / (n_tok * n_layers) / 1e6,
+        "store_read_GBps": (s1["bytes"] - s0["bytes"]) / max(read_s, 1e-9) / 1e9,
+        "store_read_share_of_time": read_s / el, "store_threads": a.store_threads}
+    log(f"store: streamed from file {res['streamed_from_file']}")
+    pool.close()
+    store.close()
+    if not a.store_path:
+        os.remove(path)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--config", default="decode",
-                    choices=["decode", "prefill", "stack30", "streamed"])
+                    choices=["decode", "prefill", "stack30", "streamed", "store"])
+    ap.add_argument("--store-layers", type=int, default=4,
+                    help="layers written to the expert file of the store workload")
+    ap.add_argument("--store-path", default="",
+                    help="expert file of the store workload (default: a temporary file)")
+    ap.add_argument("--store-threads", type=int, default=32,
+                    help="reads in flight of the store (queue depth)")
+    ap.add_argument("--store-chunk", type=int, default=256 << 10,
+                    help="bytes per pread piece of the store")
     ap.add_argument("--stream-tokens", type=int, default=64)
     ap.add_argument("--pool-policy", choices=["lfu", "lru"], default="lfu",
                     help="slot replacement of the streamed workload (lfu: the pages')")
@@ -250,6 +364,10 @@ def main():
     for kv in a.tune:
         key, val = kv.split("=")
         moe.moe_set_tuning(key, int(val))
+    if a.config == "store":
+        res = run_store(gen.CONFIGS["streamed"], a, moe, torch)
+        print(json.dumps(res), flush=True)
+        return
     cfg = gen.CONFIGS[a.config]
     if a.config in ("stack30", "streamed"):
         res = (run_stack if a.config == "stack30" else run_streamed)(cfg, a, moe, torch)

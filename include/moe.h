@@ -175,6 +175,57 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
                              int32_t out_dtype, int32_t *ids_out, float *gates_out, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* Expert store: every layer's expert blobs in one file on local storage,
+ * blob (layer l, expert e) at byte offset (l * E + e) * moe_store_stride(D, F)
+ * (the blob's size rounded up to 4096 bytes, zero padded), read on demand
+ * with bounded-parallel pread rather than mmap: the pages' SSD tier
+ * (hndistilled.com, "Enfoque tecnico (MoE + transmision desde SSD)";
+ * yodev.dev, "Por que pread y no mmap"). */
+typedef struct moe_store moe_store;
+
+typedef struct moe_store_stats {
+  uint64_t blobs;      /* expert blobs read                                  */
+  uint64_t bytes;      /* blob bytes read (without the padding)              */
+  uint64_t ns;         /* wall time spent in reads                           */
+  uint64_t errors;     /* reads that failed                                  */
+  uint64_t last_errno; /* errno of the last failure (0: none)                */
+  uint64_t bounced;    /* 1: direct reads go through bounce buffers (the
+                          destinations refused direct I/O)                   */
+} moe_store_stats;
+
+#define MOE_STORE_DIRECT 1 /* O_DIRECT: bypass the page cache (buffered if refused) */
+#define MOE_STORE_MMAP 2   /* for comparison: map the file and copy out of it      */
+
+size_t moe_store_stride(int32_t D, int32_t F);
+
+/* Opens the file at `path` (host path) holding n_layers * E blobs of shape
+ * (D, F).  flags: 0 (buffered pread), MOE_STORE_DIRECT or MOE_STORE_MMAP.
+ * threads (1..64): reads in flight at once (the queue depth).  The store owns
+ * its file descriptor and reader threads.  MOE_E_INVALID for bad arguments,
+ * a missing file or one shorter than the blobs need. */
+moe_status moe_store_open(moe_store **store, const char *path, int32_t n_layers, int32_t E,
+                          int32_t D, int32_t F, int32_t flags, int32_t threads);
+
+/* Reads blobs (layer, experts[i]), i < n, into host buffers dst[i] (HOST array
+ * of n pointers; each buffer at least moe_store_stride bytes and, with direct
+ * I/O, 4096-byte aligned: page-locked memory from hipHostMalloc is), split
+ * into pieces of chunk_bytes (rounded up to 4096; 0: whole blobs) that the
+ * reader threads fetch in parallel.  Blocks until done.  MOE_E_POOL if a read
+ * fails. */
+moe_status moe_store_read(moe_store *store, int32_t layer, const int32_t *experts, int32_t n,
+                          void *const *dst, size_t chunk_bytes);
+moe_status moe_store_get_stats(const moe_store *store, moe_store_stats *stats);
+moe_status moe_store_close(moe_store *store);
+
+/* HBM expert slot pool whose misses come from a store instead of pinned host
+ * blobs: a call's missing experts are read by the store's threads into the
+ * pool's page-locked staging buffers (one per slot) and copied into the HBM
+ * slots on the side stream, while the shared expert runs.  Everything else
+ * as moe_pool_create (layers and shapes from the store; the store must
+ * outlive the pool).  chunk_bytes as in moe_store_read. */
+moe_status moe_pool_create_store(moe_pool **pool, int32_t slots, moe_store *store,
+                                 size_t chunk_bytes);
+
 /* moe_layer_forward with every expert resident (no pool), for callers that
  * cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc.  The caller passes inputs

@@ -328,6 +328,58 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+__device__ __forceinline__ int u_max(int a, int b) {
+  return (int)((uint32_t)a > (uint32_t)b ? (uint32_t)a : (uint32_t)b);
+}
+// wave-wide maximum of unsigned values (every lane receives it)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  int v = (int)x;
+  MOE_DPP_REDUCE(int, v, u_max, 0, dpp_i32)
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k of one token's logits held by one wave, by k rounds of a wave-wide
+// maximum: v[j] is the logit of expert lane + 64 j (-inf or skipped beyond
+// E).  Round r takes the largest remaining order-preserving key, the lowest
+// expert index among equal keys, so the result is the descending order with
+// ties to the lower index.  Lane r < k receives the r-th expert's id and
+// logit; no LDS and no barrier.
+template <int NV>
+__device__ __forceinline__ void topk_rounds(const float (&v)[NV], int E, int k, int32_t *id_out,
+                                            float *val_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) key[j] = lane + 64 * j < E ? order_key(v[j]) : 0u;  // 0: below all
+  int32_t my_id = 0;
+  uint32_t my_key = 0u;
+  for (int r = 0; r < k; ++r) {
+    uint32_t m = key[0];
+#pragma unroll
+    for (int j = 1; j < NV; ++j) m = m > key[j] ? m : key[j];
+    m = wave_max_u32(m);
+    int win = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const uint64_t b = __ballot(key[j] == m);
+      if (!found && b) {
+        win = 64 * j + (int)__builtin_ctzll(b);
+        found = true;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (win == lane + 64 * j) key[j] = 0u;
+    if (lane == r) {
+      my_id = win;
+      my_key = m;
+    }
+  }
+  *id_out = my_id;
+  *val_out = key_value(my_key);
+}
+
 // Top-k of one token's logits held by one wave, v[j] = logit of expert
 // lane + 64 j (-inf beyond E): larger first, equal logits to the lower index.
 // Lane r < k receives the r-th id and its softmax gate over the k selected

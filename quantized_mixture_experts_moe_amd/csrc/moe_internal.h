@@ -102,6 +102,8 @@ struct Tuning {
   int layer_log_copies = 16;
   int layer_sel_copies = 16;
   int layer_sel_stride = 0;  // words between selection lines; 0: packed
+  int layer_one_down_delay = 0;  // single-token layer: routed down weights this many
+                                 // 10 ns ticks after the selection
 };
 Tuning &tuning();
 
@@ -268,6 +270,8 @@ struct LayerLaunch {
   // selection lines as usual and the blob of rank r from given_blob[t][r]
   uint64_t *host_sel; uint32_t host_epoch;
   int two;                            // that variant of the kernel (set before planning)
+  int down_delay;                     // single-token layer: routed down weights requested this
+                                      // many 10 ns ticks after the selection
 };
 int layer_m(const LayerLaunch &L);
 int layer_routed_blocks(const LayerLaunch &L);
@@ -278,6 +282,15 @@ size_t layer_table_off(const LayerLaunch &L);
 hipError_t layer_capacity(const LayerLaunch &L, int *cap);
 int layer_shared_blocks(const LayerLaunch &L);
 hipError_t launch_layer(const LayerLaunch &L, hipStream_t s);
+// The single-token layer with one routing hop and full-width gate/up tiles
+// (decode_one_kernel): its shape, resources and launch.
+bool layer_one_fits(const LayerLaunch &L);
+int layer_one_grid(const LayerLaunch &L);
+int layer_one_shared_splits(const LayerLaunch &L);
+size_t layer_one_table_off(const LayerLaunch &L);
+size_t layer_one_smem(const LayerLaunch &L);
+hipError_t layer_one_capacity(const LayerLaunch &L, int *cap);
+hipError_t launch_layer_one(LayerLaunch L, hipStream_t s);
 // blocks [first, first + n) of the dispatch order L.order (0 or 1), two-launch variant
 hipError_t launch_layer_ordered(LayerLaunch L, int first, int n, hipStream_t s);
 // blocks [blk0, blk0 + n) of the grid only (streamed experts: shared blocks

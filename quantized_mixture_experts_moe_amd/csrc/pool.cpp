@@ -9,6 +9,8 @@
 // stream; the main stream waits on an event before the routed experts run.
 #include "pool.h"
 
+#include "store.h"
+
 #include <string.h>
 
 #include <algorithm>
@@ -48,6 +50,13 @@ struct moe_pool {
   hipEvent_t ev_table = nullptr;              // after the last upload (its source is h_tables)
   bool table_pending = false;
   int fail_copy_at = -1;                      // test hook: copies to let through before one fails
+  // misses read from a store: page-locked staging buffers, one per slot
+  // index (shared by the layers), each reusable once its copy is done
+  moe_store *store = nullptr;
+  size_t store_chunk = 0;
+  uint8_t *staging = nullptr;
+  std::vector<hipEvent_t> stg_ev;
+  std::vector<char> stg_pending;
 };
 
 namespace moe {
@@ -184,8 +193,52 @@ namespace {
 struct HipCopyEngine final : CopyEngine {
   hipStream_t side;
   explicit HipCopyEngine(hipStream_t s) : side(s) {}
-  int copy(void *dst, const void *src, size_t bytes) override {
+  int copy(int, int, void *dst, const void *src, size_t bytes) override {
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, side) == hipSuccess ? 0 : 1;
+  }
+};
+
+// Misses read from the store: copy() records them; flush() reads all of the
+// call's missing blobs at once (every piece of every blob spread over the
+// store's threads) into the staging buffers of their slots, then enqueues the
+// host -> HBM copies on the side stream.
+struct StoreCopyEngine final : CopyEngine {
+  moe_pool *p;
+  int layer;
+  std::vector<int32_t> experts;
+  std::vector<int> slots;
+  std::vector<void *> dsts;
+  StoreCopyEngine(moe_pool *pool, int l) : p(pool), layer(l) {}
+  int copy(int expert, int slot, void *dst, const void *, size_t) override {
+    experts.push_back(expert);
+    slots.push_back(slot);
+    dsts.push_back(dst);
+    return 0;
+  }
+  int flush() override {
+    if (experts.empty()) return 0;
+    const size_t stride = store_stride_of(p->store);
+    std::vector<void *> stg(experts.size());
+    for (size_t i = 0; i < experts.size(); ++i) {
+      const int s = slots[i];
+      // the staging buffer's previous copy (any layer) has left it
+      if (p->stg_pending[s]) {
+        if (hipEventSynchronize(p->stg_ev[s]) != hipSuccess) return 1;
+        p->stg_pending[s] = 0;
+      }
+      stg[i] = p->staging + (size_t)s * stride;
+    }
+    if (store_read(p->store, layer, experts.data(), (int)experts.size(), stg.data(),
+                   p->store_chunk) != MOE_OK)
+      return 1;
+    for (size_t i = 0; i < experts.size(); ++i) {
+      if (hipMemcpyAsync(dsts[i], stg[i], p->blob_bytes, hipMemcpyHostToDevice, p->side) !=
+              hipSuccess ||
+          hipEventRecord(p->stg_ev[slots[i]], p->side) != hipSuccess)
+        return 1;
+      p->stg_pending[slots[i]] = 1;
+    }
+    return 0;
   }
 };
 }  // namespace
@@ -206,10 +259,11 @@ moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t 
   LayerPlanArgs a;
   a.ids = p->h_ids; a.n = T * k; a.E = p->E;
   a.slot_base = base; a.blob_bytes = p->blob_bytes;
-  a.host_blobs = p->host_blobs.data() + (size_t)layer * p->E;
+  a.host_blobs = p->store ? nullptr : p->host_blobs.data() + (size_t)layer * p->E;
   a.table = tab;
-  HipCopyEngine eng(p->side);
-  CopyEngine *ce = &eng;
+  HipCopyEngine hip_eng(p->side);
+  StoreCopyEngine store_eng(p, layer);
+  CopyEngine *ce = p->store ? (CopyEngine *)&store_eng : (CopyEngine *)&hip_eng;
   FailingCopyEngine fail(ce, p->fail_copy_at);
   if (p->fail_copy_at >= 0) ce = &fail;
   const PlanResult r = plan_layer_call(p->planners[layer], a, *ce, &p->stats);
@@ -303,17 +357,16 @@ moe_status moe_cache_replay(int32_t policy, int32_t slots, int32_t E, int32_t k,
   return MOE_OK;
 }
 
-moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int32_t E, int32_t D,
-                           int32_t F, const void *const *host_blobs) {
-  if (!out || n_layers < 1 || slots < 1 || E < 1 || slots > E || !host_blobs) return MOE_E_INVALID;
-  if (D < 64 || F < 64 || D % 64 || F % 64) return MOE_E_INVALID;
-  for (size_t i = 0; i < (size_t)n_layers * E; ++i)
-    if (!host_blobs[i]) return MOE_E_INVALID;
+static moe_status pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int32_t E,
+                              int32_t D, int32_t F, const void *const *host_blobs,
+                              moe_store *store, size_t chunk) {
   moe_pool *p = new (std::nothrow) moe_pool;
   if (!p) return MOE_E_POOL;
   p->n_layers = n_layers; p->slots = slots; p->E = E; p->D = D; p->F = F;
   p->blob_bytes = blob_layout(D, F).total;
-  p->host_blobs.assign(host_blobs, host_blobs + (size_t)n_layers * E);
+  if (host_blobs) p->host_blobs.assign(host_blobs, host_blobs + (size_t)n_layers * E);
+  p->store = store;
+  p->store_chunk = chunk;
   for (int l = 0; l < n_layers; ++l) p->planners.emplace_back(slots, E);
   p->table_dirty.assign(n_layers, 0);
   bool ok = hipMalloc((void **)&p->slot_mem, (size_t)n_layers * slots * p->blob_bytes) ==
@@ -334,12 +387,38 @@ moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int3
     ok = hipMemcpy(p->d_tables, p->h_tables, sizeof(void *) * n_layers * E,
                    hipMemcpyHostToDevice) == hipSuccess;
   }
+  if (ok && store) {
+    ok = hipHostMalloc((void **)&p->staging, (size_t)slots * store_stride_of(store),
+                       hipHostMallocDefault) == hipSuccess;
+    p->stg_ev.assign(slots, nullptr);
+    p->stg_pending.assign(slots, 0);
+    for (int s = 0; ok && s < slots; ++s)
+      ok = hipEventCreateWithFlags(&p->stg_ev[s], hipEventDisableTiming) == hipSuccess;
+  }
   if (!ok) {
     moe_pool_destroy(p);
     return MOE_E_HIP;
   }
   *out = p;
   return MOE_OK;
+}
+
+moe_status moe_pool_create(moe_pool **out, int32_t n_layers, int32_t slots, int32_t E, int32_t D,
+                           int32_t F, const void *const *host_blobs) {
+  if (!out || n_layers < 1 || slots < 1 || E < 1 || slots > E || !host_blobs) return MOE_E_INVALID;
+  if (D < 64 || F < 64 || D % 64 || F % 64) return MOE_E_INVALID;
+  for (size_t i = 0; i < (size_t)n_layers * E; ++i)
+    if (!host_blobs[i]) return MOE_E_INVALID;
+  return pool_create(out, n_layers, slots, E, D, F, host_blobs, nullptr, 0);
+}
+
+moe_status moe_pool_create_store(moe_pool **out, int32_t slots, moe_store *store,
+                                 size_t chunk_bytes) {
+  if (!out || !store) return MOE_E_INVALID;
+  const int E = store_E(store);
+  if (slots < 1 || slots > E) return MOE_E_INVALID;
+  return pool_create(out, store_layers(store), slots, E, store_D(store), store_F(store), nullptr,
+                     store, chunk_bytes);
 }
 
 moe_status moe_pool_destroy(moe_pool *p) {
@@ -357,6 +436,9 @@ moe_status moe_pool_destroy(moe_pool *p) {
   if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
   if (p->ev_slot) (void)hipEventDestroy(p->ev_slot);
   if (p->ev_table) (void)hipEventDestroy(p->ev_table);
+  for (auto e : p->stg_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (p->staging) (void)hipHostFree(p->staging);
   if (p->side) (void)hipStreamDestroy(p->side);
   delete p;
   return MOE_OK;

@@ -103,9 +103,13 @@ class LfuPlanner {
 // Where the bytes of one miss go.  Returns 0 once the copy is enqueued
 // (or done), nonzero if it could not be; after a failure the destination may
 // hold any bytes.
+// copy() may also only record the copy and flush() carry out all of the
+// call's copies at once (0: all enqueued; nonzero: the slots of every copy
+// recorded since the last flush may hold any bytes).
 struct CopyEngine {
   virtual ~CopyEngine() = default;
-  virtual int copy(void *dst, const void *src, size_t bytes) = 0;
+  virtual int copy(int expert, int slot, void *dst, const void *src, size_t bytes) = 0;
+  virtual int flush() { return 0; }
 };
 
 // Test hook: passes `pass` copies through to `inner`, then fails the next one
@@ -114,14 +118,15 @@ struct FailingCopyEngine final : CopyEngine {
   CopyEngine *inner;
   int left;  // copies still to pass before the failure; -1: already failed
   FailingCopyEngine(CopyEngine *e, int pass) : inner(e), left(pass) {}
-  int copy(void *dst, const void *src, size_t bytes) override {
+  int copy(int expert, int slot, void *dst, const void *src, size_t bytes) override {
     if (left == 0) {
       left = -1;
       return 1;
     }
     if (left > 0) --left;
-    return inner->copy(dst, src, bytes);
+    return inner->copy(expert, slot, dst, src, bytes);
   }
+  int flush() override { return inner->flush(); }
   int remaining() const { return left; }
 };
 
@@ -131,7 +136,8 @@ struct LayerPlanArgs {
   int n, E;
   uint8_t *slot_base;                 // device address of the layer's first slot
   size_t blob_bytes;
-  const void *const *host_blobs;      // [E] the layer's blobs in host memory
+  const void *const *host_blobs;      // [E] the layer's blobs in host memory (null: the
+                                      // copy engine finds them itself)
   const void **table;                 // [E] host table: expert -> blob address (slot or placeholder)
 };
 
@@ -149,6 +155,18 @@ struct PlanResult {
 // needs any of them fetches it again.  A call whose distinct experts do not
 // fit the slots, or with an id outside [0, E), changes nothing and returns
 // MOE_E_POOL.
+// After a failed copy: the slots of the first n events' misses may hold any
+// bytes; their old experts are no longer resident (and nothing new is).
+inline void invalidate_misses(LfuPlanner &planner, const LayerPlanArgs &a,
+                              const std::vector<LfuPlanner::Event> &ev, size_t n) {
+  for (size_t j = 0; j < n; ++j) {
+    if (ev[j].hit) continue;
+    const int old = planner.expert_in(ev[j].slot);
+    if (old >= 0) a.table[old] = a.slot_base;
+    planner.invalidate_slot(ev[j].slot);
+  }
+}
+
 inline PlanResult plan_layer_call(LfuPlanner &planner, const LayerPlanArgs &a, CopyEngine &eng,
                                   moe_pool_stats *stats) {
   PlanResult r;
@@ -171,18 +189,20 @@ inline PlanResult plan_layer_call(LfuPlanner &planner, const LayerPlanArgs &a, C
   for (size_t i = 0; i < ev.size(); ++i) {
     if (ev[i].hit) continue;
     uint8_t *dst = a.slot_base + (size_t)ev[i].slot * a.blob_bytes;
-    if (eng.copy(dst, a.host_blobs[ev[i].expert], a.blob_bytes) != 0) {
+    const void *src = a.host_blobs ? a.host_blobs[ev[i].expert] : nullptr;
+    if (eng.copy(ev[i].expert, ev[i].slot, dst, src, a.blob_bytes) != 0) {
       // slots of this and the earlier misses may hold new or partial bytes
-      for (size_t j = 0; j <= i; ++j) {
-        if (ev[j].hit) continue;
-        const int old = planner.expert_in(ev[j].slot);
-        if (old >= 0) a.table[old] = a.slot_base;
-        planner.invalidate_slot(ev[j].slot);
-      }
+      invalidate_misses(planner, a, ev, i + 1);
       r.status = MOE_E_HIP;
       return r;
     }
     ++r.copies;
+  }
+  if (eng.flush() != 0) {
+    invalidate_misses(planner, a, ev, ev.size());
+    r.status = MOE_E_HIP;
+    r.copies = 0;
+    return r;
   }
   planner = trial;
   for (const auto &e : ev) {

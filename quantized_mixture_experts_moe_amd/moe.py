@@ -37,8 +37,12 @@ EXPORTS = (
     "moe_pool_get_stats", "moe_pool_reset_stats", "moe_lfu_replay", "moe_set_tuning",
     "moe_pool_set_policy", "moe_cache_replay", "moe_pool_fail_copy",
     "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
-    "moe_layer_forward_noalloc",
+    "moe_layer_forward_noalloc", "moe_store_stride", "moe_store_open", "moe_store_read",
+    "moe_store_get_stats", "moe_store_close", "moe_pool_create_store",
 )
+
+MOE_STORE_DIRECT = 1
+MOE_STORE_MMAP = 2
 
 
 class MoEError(RuntimeError):
@@ -63,6 +67,12 @@ class moe_pool_stats(ctypes.Structure):
                 ("bytes_h2d", ctypes.c_uint64)]
 
 
+class moe_store_stats(ctypes.Structure):
+    _fields_ = [("blobs", ctypes.c_uint64), ("bytes", ctypes.c_uint64), ("ns", ctypes.c_uint64),
+                ("errors", ctypes.c_uint64), ("last_errno", ctypes.c_uint64),
+                ("bounced", ctypes.c_uint64)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -82,6 +92,12 @@ def _load() -> ctypes.CDLL:
         "moe_layer_forward_noalloc": (i32, [vp, i32, i32, P(moe_qmat), vp, i32, P(moe_bank),
                                             P(moe_bank), vp, i32, vp, vp, vp]),
         "moe_pool_create": (i32, [P(vp), i32, i32, i32, i32, i32, vp]),
+        "moe_store_stride": (sz, [i32, i32]),
+        "moe_store_open": (i32, [P(vp), ctypes.c_char_p, i32, i32, i32, i32, i32, i32]),
+        "moe_store_read": (i32, [vp, i32, vp, i32, vp, sz]),
+        "moe_store_get_stats": (i32, [vp, P(moe_store_stats)]),
+        "moe_store_close": (i32, [vp]),
+        "moe_pool_create_store": (i32, [P(vp), i32, vp, sz]),
         "moe_pool_destroy": (i32, [vp]),
         "moe_pool_get_stats": (i32, [vp, P(moe_pool_stats)]),
         "moe_pool_reset_stats": (i32, [vp]),
@@ -302,6 +318,48 @@ def moe_lfu_replay(slots: int, E: int, ids: np.ndarray) -> np.ndarray:
     return ev
 
 
+def moe_store_stride(D: int, F: int) -> int:
+    return int(lib.moe_store_stride(D, F))
+
+
+class Store:
+    """Expert blobs of every layer in one file, read by bounded-parallel pread
+    (moe_store_open).  flags: 0 buffered, MOE_STORE_DIRECT, MOE_STORE_MMAP."""
+
+    def __init__(self, path: str, n_layers: int, E: int, D: int, F: int, flags: int = 1,
+                 threads: int = 16):
+        h = ctypes.c_void_p()
+        _check(lib.moe_store_open(ctypes.byref(h), path.encode(), n_layers, E, D, F, flags,
+                                  threads), "moe_store_open")
+        self.handle = h
+        self.n_layers, self.E, self.D, self.F = n_layers, E, D, F
+        self.stride = moe_store_stride(D, F)
+
+    def read(self, layer: int, experts: Sequence[int], dst: Sequence[int], chunk: int = 0) -> None:
+        """Read blobs into host buffers at the given addresses (each >= stride)."""
+        ids = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
+        ptrs = (ctypes.c_void_p * len(dst))(*[int(d) for d in dst])
+        _check(lib.moe_store_read(self.handle, layer, ctypes.cast(ids, ctypes.c_void_p),
+                                  len(experts), ctypes.cast(ptrs, ctypes.c_void_p), chunk),
+               "moe_store_read")
+
+    def stats(self) -> dict:
+        st = moe_store_stats()
+        _check(lib.moe_store_get_stats(self.handle, ctypes.byref(st)), "moe_store_get_stats")
+        return {f: int(getattr(st, f)) for f, _ in moe_store_stats._fields_}
+
+    def close(self) -> None:
+        if self.handle:
+            lib.moe_store_close(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class Pool:
     """HBM expert slot pool over pinned host blobs (moe_pool_create)."""
 
@@ -321,6 +379,17 @@ class Pool:
                                    ctypes.cast(arr, ctypes.c_void_p)),
                "moe_pool_create")
         self.handle = h
+
+    @classmethod
+    def from_store(cls, store: "Store", slots: int, chunk: int = 0) -> "Pool":
+        """A pool whose misses are read from the store (moe_pool_create_store)."""
+        self = cls.__new__(cls)
+        self._keep = [store]
+        h = ctypes.c_void_p()
+        _check(lib.moe_pool_create_store(ctypes.byref(h), slots, store.handle, chunk),
+               "moe_pool_create_store")
+        self.handle = h
+        return self
 
     def set_policy(self, policy: int) -> None:
         """0: least frequently used (default), 1: least recently used."""

@@ -32,6 +32,7 @@ expert: hndistilled.com, "Enfoque tecnico"; es.news.hada.io, HN thread).
 from __future__ import annotations
 
 import dataclasses
+import os
 import math
 from typing import Dict, Tuple
 
@@ -294,3 +295,25 @@ def algorithmic_decode_bytes(cfg: MoEConfig) -> int:
     s = blob_bytes(cfg.D, cfg.F_shared) if cfg.F_shared else 0
     act = cfg.D * 2 + cfg.D * 4
     return r + e + s + act
+
+
+def store_stride(D: int, F: int) -> int:
+    """Bytes per blob in an expert file: the blob rounded up to 4096."""
+    return (blob_bytes(D, F) + 4095) // 4096 * 4096
+
+
+def write_expert_file(path: str, seed: int, n_layers: int, cfg: MoEConfig) -> int:
+    """Every routed expert blob of layers 0..n_layers-1 into one file, blob
+    (l, e) at (l * E + e) * store_stride, zero padded; returns the file size.
+    The same seeded bytes as layer_weights()."""
+    stride = store_stride(cfg.D, cfg.F)
+    nb = blob_bytes(cfg.D, cfg.F)
+    buf = np.zeros((cfg.E, stride), dtype=np.uint8)
+    with open(path, "wb") as f:
+        for l in range(n_layers):
+            for e in range(cfg.E):
+                expert_blob(seed, l, e, cfg.D, cfg.F, out=buf[e, :nb])
+            f.write(buf.tobytes())
+        f.flush()
+        os.fsync(f.fileno())
+    return n_layers * cfg.E * stride

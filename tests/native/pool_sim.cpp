@@ -30,7 +30,7 @@ struct RecordingEngine final : moe::CopyEngine {
   uint8_t *slot_base = nullptr;
   const std::vector<std::vector<uint8_t>> *host = nullptr;
   std::vector<std::pair<int, int>> log;  // (expert, slot) of each copy
-  int copy(void *dst, const void *src, size_t bytes) override {
+  int copy(int, int, void *dst, const void *src, size_t bytes) override {
     const size_t off = (uint8_t *)dst - slot_base;
     if (off % kBlob != 0 || bytes != kBlob) {
       fprintf(stderr, "bad copy: offset %zu bytes %zu\n", off, bytes);
