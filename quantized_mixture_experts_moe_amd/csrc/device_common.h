@@ -381,74 +381,26 @@ __device__ __forceinline__ void topk_rounds(const float (&v)[NV], int E, int k, 
 }
 
 // Top-k of one token's logits held by one wave, v[j] = logit of expert
-// lane + 64 j (-inf beyond E): larger first, equal logits to the lower index.
+// lane + 64 j (-inf beyond E): larger first, equal logits to the lower index
+// (topk_rounds; the -inf entries rank last and k <= E never reaches them).
 // Lane r < k receives the r-th id and its softmax gate over the k selected
-// logits.  The k-th largest key is found bit by bit from the top (32 rounds
-// of compare + ballot + popcount), the selected entries are compacted in
-// index order through xch (LDS, 128 entries for this wave) and ranked among
-// themselves.  NV is a compile-time bound so that v[] stays in registers.
+// logits: max = the rank-0 logit, exp of the differences, a DPP wave sum, a
+// division -- every selection in the library uses this arithmetic, so they
+// all give the same bits.  xch is unused (kept for the callers' layout).
 template <int NV>
 __device__ __forceinline__ void topk_regs(float (&v)[NV], int k, uint2 *xch, int32_t *id_out,
                                           float *gate_out) {
+  (void)xch;
   const int lane = threadIdx.x & 63;
-  uint32_t key[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) key[j] = order_key(v[j]);
-  // tau: the largest key with at least k keys >= tau, i.e. the k-th largest
-  uint32_t tau = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-    if (cnt >= k) tau = cand;
-  }
-  // selected: keys above tau, then keys equal to tau in index order
-  int quota = k;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) quota -= __popcll(__ballot(key[j] > tau));
-  int before = 0;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    uint64_t eq = __ballot(key[j] == tau);
-    uint64_t take = 0;
-    while (quota > 0 && eq) {
-      const uint64_t low = eq & (~eq + 1);
-      take |= low;
-      eq ^= low;
-      --quota;
-    }
-    const uint64_t sel = __ballot(key[j] > tau) | take;
-    if ((sel >> lane) & 1u) xch[before + (int)lanes_below(sel)] = make_uint2(key[j], lane + 64 * j);
-    before += __popcll(sel);
-  }
-  __builtin_amdgcn_wave_barrier();
-  // rank among the selected (entries are in index order): larger keys first,
-  // equal keys by position
-  uint2 mine = make_uint2(0u, 0u);
-  int rank = 0;
-  if (lane < k) {
-    mine = xch[lane];
-    for (int s2 = 0; s2 < k; ++s2) {
-      const uint2 o = xch[s2];
-      rank += (o.x > mine.x || (o.x == mine.x && s2 < lane)) ? 1 : 0;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (lane < k) xch[64 + rank] = mine;
-  __builtin_amdgcn_wave_barrier();
-  float myv = 0.0f;
-  int myi = 0;
-  if (lane < k) {
-    const uint2 r = xch[64 + lane];
-    myv = key_value(r.x);
-    myi = (int)r.y;
-  }
+  int32_t myi;
+  float myv;
+  topk_rounds(v, 64 * NV, k, &myi, &myv);
+  if (lane >= k) myv = 0.0f;
   const float m0 =
       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
   const float z = lane < k ? expf(myv - m0) : 0.0f;
   const float sum = wave_sum(z);
-  *id_out = myi;
+  *id_out = lane < k ? myi : 0;
   *gate_out = z / sum;
 }
 

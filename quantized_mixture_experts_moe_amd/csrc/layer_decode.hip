@@ -314,9 +314,22 @@ __device__ void select_from_logits(const LayerLaunch &L, int t, int copy, uint32
 #pragma unroll
   for (int j = 0; j < NV; ++j)
     v[j] = lane + 64 * j < E ? __uint_as_float((uint32_t)w[j]) : -INFINITY;
+  // k rounds of a wave maximum (two registers per lane up to 128 experts),
+  // then the router kernel's gate arithmetic: same ids and gates, bit for bit
   int32_t id;
-  float gate;
-  topk_regs(v, k, xch, &id, &gate);
+  float myv;
+  if (E <= 128) {
+    const float v2[2] = {v[0], v[1]};
+    topk_rounds(v2, E, k, &id, &myv);
+  } else {
+    topk_rounds(v, E, k, &id, &myv);
+  }
+  if (lane >= k) myv = 0.0f;
+  const float m0 =
+      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
+  const float z = lane < k ? expf(myv - m0) : 0.0f;
+  const float gate = z / wave_sum(z);
+  (void)xch;
   const uint32_t ids = min((uint32_t)id, (uint32_t)E - 1);
   if (lane < k) {
     blob_out[lane] = (const uint8_t *)table[ids];
@@ -492,9 +505,7 @@ struct NoHook {
 // With L.hu null the hidden activations are single tagged words h in L.hg
 // (gelu(gate) * up, finished by one block); otherwise gelu(gate) in L.hg and
 // up in L.hu.  on_hint runs once the units' first words are seen.
-// NP: bf16 planes of h (3: hi + mid + lo, the fp32 value; 2: hi + lo, 16
-// significant bits)
-template <int M, class OnHint = NoHook, int NP = 3>
+template <int M, class OnHint = NoHook>
 __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const DownRegs<M> &R,
                                                  const size_t (&hp)[M], const float (&gate)[M],
                                                  const bool (&use)[M], uint32_t (&hpl)[kNW][M][3][32],
@@ -573,13 +584,11 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
     const uint32_t p0 = f32_to_bf16(hv);
     const float r1 = hv - __uint_as_float(p0 << 16);
     const uint32_t p1 = f32_to_bf16(r1);
+    const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
     uint16_t *hp16 = (uint16_t *)&hpl[wave][i][0][0];
     hp16[pos] = (uint16_t)p0;
     hp16[64 + pos] = (uint16_t)p1;
-    if constexpr (NP == 3) {
-      const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
-      hp16[128 + pos] = (uint16_t)p2;
-    }
+    hp16[128 + pos] = (uint16_t)p2;
     hsum[i] = wave_sum(hv);
   }
   __builtin_amdgcn_wave_barrier();
@@ -588,7 +597,7 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
   // hold plane p of h as A row 4 (l / 16) + p, so registers 0..2 of lane l
   // accumulate the three planes' dot products of output row l.
   const int plane = (lane & 15) - 4 * (lane >> 4);
-  const bool ha_lane = plane >= 0 && plane < NP;
+  const bool ha_lane = plane >= 0 && plane < 3;
   const uint32_t umagic = opaque_vgpr(0x3F803F80u);
   float acc = 0.0f;
 #pragma unroll
@@ -611,8 +620,7 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
       d1 = mma16<false>(a[w + 1], code_pairs_unit(wd[w + 1], umagic), d1);
     }
     // sum (1 + q/16) h = sum h + sum q h / 16, three planes
-    const float dsum = NP == 3 ? ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2])
-                               : (d0[0] + d1[0]) + (d0[1] + d1[1]);
+    const float dsum = ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2]);
     const float sc = f16_to_f32(R.dmw[i]), bi = f16_to_f32(R.dmw[i] >> 16);
     const float v = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum[i]);
     acc = fmaf(gate[i], v, acc);
@@ -1219,393 +1227,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_stream_kernel(LayerLaunch 
     for (int j = b; j < kMaxLayerGrid; j += L.grid_full) st_dev(L.bep + j, tag);
 }
 
-// ---------------------------------------------------------------- one token, one routing hop
-//
-// The single-token layer with four hand-offs on its critical path instead of
-// six.  The router blocks only publish their logits; every block that needs
-// the selection ranks the 128 logits itself (the same top-k arithmetic as
-// the router kernel, so all of them agree bit for bit), which saves the
-// second routing hop.  A gate/up block owns 32 hidden rows of one expert
-// over the whole model width, so it finishes h = gelu(gate) * up itself: no
-// split reduction, no atomic round trip before h is published.  A down block
-// owns 64 output rows of one selected expert (or a third of the shared
-// expert's hidden units) and requests its weights as soon as it knows the
-// expert, long before h arrives; it adds its gated partial to the output
-// with one counted fixed-point atomic.
-//   blocks: [router | shared gate/up | shared down | routed gate/up | routed down]
-constexpr int kT1Rows = 32;    // hidden rows of a gate/up block
-constexpr int kT1Ring = 6;     // column groups in flight per wave
-constexpr int kT1Copies = 16;  // copies of the published logits
-constexpr int kT1M = 3;        // down units (64 hidden rows) per wave
-
-struct T1Roles {
-  int nR, nSG, nSD, nRG, nRD;
-  int b_sg, b_sd, b_rg, b_rd, total;
-  int KSds, UPs;  // shared down splits and units per split
-};
-__host__ __device__ inline T1Roles t1_roles(int E, int k, int D, int F, int Fs) {
-  T1Roles r;
-  const int NB = D / 64, Us = Fs / 64;
-  r.nR = (E + kRows - 1) / kRows;
-  r.nSG = Fs / kT1Rows;
-  r.KSds = Us > 0 ? (Us + kNW * kT1M - 1) / (kNW * kT1M) : 0;
-  r.UPs = r.KSds > 0 ? (Us + r.KSds - 1) / r.KSds : 0;
-  r.nSD = NB * r.KSds;
-  r.nRG = k * (F / kT1Rows);
-  r.nRD = k * NB;
-  r.b_sg = r.nR;
-  r.b_sd = r.b_sg + r.nSG;
-  r.b_rg = r.b_sd + r.nSD;
-  r.b_rd = r.b_rg + r.nRG;
-  r.total = r.b_rd + r.nRD;
-  return r;
-}
-
-struct T1Stage {
-  u32x4 g, u;
-  uint32_t mg, mu;
-};
-
-// activation pairs (x[8w + m], x[8w + m + 4]) of every column group into
-// s_xp [G][32] and 32-column sums into s_xh [2G] (token 0)
-constexpr int kT1XV = 8192 / 8 / kThreads;  // 16-byte pieces of x per thread
-__device__ __forceinline__ void t1_issue_x(const LayerLaunch &L, u32x4 (&xq)[kT1XV]) {
-  const gptr<u32x4> xr = as_global((const u32x4 *)L.x);
-#pragma unroll
-  for (int i = 0; i < kT1XV; ++i) xq[i] = xr[min((int)threadIdx.x + i * kThreads, L.D / 8 - 1)];
-}
-template <bool F16X>
-__device__ __forceinline__ void t1_stage_x(const LayerLaunch &L, const u32x4 (&xq)[kT1XV],
-                                           uint32_t *s_xp, float *s_xh) {
-  const int tid = threadIdx.x, D = L.D;
-  constexpr int kMaxXV = kT1XV;
-#pragma unroll
-  for (int i = 0; i < kMaxXV; ++i) {
-    const int c8 = tid + i * kThreads;  // 8-column block
-    if (i * kThreads >= D / 8) break;
-    const uint32_t a0 = xq[i].x, a1 = xq[i].y, a2 = xq[i].z, a3 = xq[i].w;
-    u32x4 pq;
-    pq.x = (a0 & 0xFFFFu) | (a2 << 16);
-    pq.y = (a0 >> 16) | (a2 & 0xFFFF0000u);
-    pq.z = (a1 & 0xFFFFu) | (a3 << 16);
-    pq.w = (a1 >> 16) | (a3 & 0xFFFF0000u);
-    const uint32_t w[4] = {a0, a1, a2, a3};
-    float s8 = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      s8 += x_to_f32<F16X>(w[m] & 0xFFFFu);
-      s8 += x_to_f32<F16X>(w[m] >> 16);
-    }
-    // 4 lanes of 8 columns: ((s0 + s1) + (s2 + s3))
-    s8 = s8 + dpp_f32<0xB1>(s8, 0.0f);
-    s8 = s8 + dpp_f32<0x4E>(s8, 0.0f);
-    if (c8 < D / 8) {
-      *(u32x4 *)&s_xp[4 * c8] = pq;
-      if ((c8 & 3) == 0) s_xh[c8 / 4] = s8;
-    }
-  }
-}
-
-// The selection of token 0 from the E logits in copy `copy`: wave 0 polls
-// the logits (bounded wait, two polls in flight), takes the top k by k
-// rounds of a wave-wide maximum (descending, ties to the lower index) and
-// computes the softmax gates with the router kernel's arithmetic (max = the
-// rank-0 logit, exp, a DPP wave sum, a division), so every block gets the
-// router kernel's ids and gates bit for bit.  s_blob, s_gate, s_id, s_lv
-// receive, at place r < k, the r-th expert's blob, gate, id and logit.
-// report: also write ids_out / gates_out.  Called by every thread of the
-// block (it ends with a barrier).
-// nx: the caller's registers for the polls; the last poll is still in
-// flight when the selection is done, and the caller keeps them allocated
-// (t1_keep) until its weight loads are issued, so that no wait for that poll
-// is placed before them (reusing a register that an outstanding load will
-// write needs the load to complete first).
-template <int NV>
-__device__ __forceinline__ void t1_keep(const uint64_t (&nx)[NV]) {
-#pragma unroll
-  for (int j = 0; j < NV; ++j) asm volatile("" ::"v"(nx[j]));
-}
-template <int NV>
-__device__ void t1_select(const LayerLaunch &L, int copy, uint32_t tag, const void *const *table,
-                          const uint8_t **s_blob, float *s_gate, int32_t *s_id, float *s_lv,
-                          bool report, uint64_t (&nx)[NV]) {
-  const int tid = threadIdx.x, lane = tid & 63, E = L.E, k = L.k;
-  if (tid < 64) {
-    // the selection heads the chain of dependent steps: its wave issues ahead
-    // of the waves that stream weights on the same SIMD
-    __builtin_amdgcn_s_setprio(3);
-    const uint64_t *lg = L.rlog + (size_t)copy * E;
-    uint64_t w[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) w[j] = ld_dev64(lg + min(lane + 64 * j, E - 1));
-    for (long s = 0;; ++s) {
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int j = 0; j < NV; ++j) nx[j] = ld_dev64(lg + min(lane + 64 * j, E - 1));
-      bool ok = true;
-#pragma unroll
-      for (int j = 0; j < NV; ++j) ok = ok && (lane + 64 * j >= E || has_tag(w[j], tag));
-      if (__all(ok)) break;
-      if (s > kSpin) {
-        if (lane == 0) add_dev(L.err, 1u);
-        break;
-      }
-#pragma unroll
-      for (int j = 0; j < NV; ++j) w[j] = nx[j];
-    }
-    float v[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = __uint_as_float((uint32_t)w[j]);
-    int32_t myi;
-    float myv;
-    topk_rounds(v, E, k, &myi, &myv);
-    if (lane >= k) myv = 0.0f;
-    const float m0 =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myv), 0));
-    const float z = lane < k ? expf(myv - m0) : 0.0f;
-    const float sum = wave_sum(z);
-    const float gate = z / sum;
-    const int32_t id = min(max(myi, 0), E - 1);
-    if (lane < k) {
-      s_blob[lane] = (const uint8_t *)table[id];
-      s_gate[lane] = gate;
-      s_id[lane] = id;
-      s_lv[lane] = myv;
-      if (report) {
-        if (L.ids_out) L.ids_out[lane] = id;
-        if (L.gates_out) L.gates_out[lane] = gate;
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  }
-  __syncthreads();
-}
-
-// Full-K gate/up of hidden rows tile * 32 + (lane & 31) of `blob` (hidden
-// width F).  Lane l reads chunk 2g + (l >> 5) of its row for each group g of
-// its wave (g = wave, wave + 4, ...): the matrix-core B operand as loaded
-// (16 rows by 4 words of one 32-column chunk per 16 lanes), with the
-// activation pairs in the lanes 0, 20, 40, 60 as A rows 0, 4, 8, 12, so that
-// register 0 of lane l accumulates row l's dot product over its half of each
-// group.  kT1Ring groups are in flight per wave.  h is published as tagged
-// words hg[hrow + r], r < 32.
-template <bool F16X, int NG>
-__device__ __forceinline__ void t1_glu(const LayerLaunch &L, const uint8_t *blob, int F, int tile,
-                                       size_t hrow, const uint32_t *s_xp, const float *s_xh,
-                                       float (&red)[kNW][2][64], int wave, int lane,
-                                       uint32_t tag) {
-  const int D = L.D, G = D / 64;
-  const int hs = lane >> 5;
-  const int row = tile * kT1Rows + (lane & 31);
-  const BlobLayout BL = blob_layout(D, F);
-  const gptr<u32x4> gc = as_global((const u32x4 *)(blob + BL.gate_codes) + row);
-  const gptr<u32x4> uc = as_global((const u32x4 *)(blob + BL.up_codes) + row);
-  const gptr<uint32_t> gm = as_global((const uint32_t *)(blob + BL.gate_meta) + row);
-  const gptr<uint32_t> um = as_global((const uint32_t *)(blob + BL.up_meta) + row);
-  const int ng = NG > 0 ? NG : (G - wave + kNW - 1) / kNW;
-  auto issue = [&](T1Stage &S, int i) {
-    const int g = wave + kNW * min(i, ng - 1);  // past the end: repeated, weight 0
-    const size_t cc = (size_t)(2 * g + hs) * F;
-    S.g = gc[cc];
-    S.u = uc[cc];
-    S.mg = gm[(size_t)g * F];
-    S.mu = um[(size_t)g * F];
-  };
-  const bool xa_lane = (lane & 15) == 4 * (lane >> 4);
-  const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
-  float accg = 0.0f, accu = 0.0f;
-  T1Stage ring[kT1Ring];
-#pragma unroll
-  for (int s = 0; s < kT1Ring - 1; ++s) issue(ring[s], s);
-  constexpr int kRounds = NG > 0 ? (NG + kT1Ring - 1) / kT1Ring : 1;
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-    for (int i0 = r * kT1Ring; i0 < (NG > 0 ? (r + 1) * kT1Ring : ng); i0 += kT1Ring) {
-#pragma unroll
-      for (int s = 0; s < kT1Ring; ++s) {
-        const int i = i0 + s;
-        if (NG > 0 && i >= NG) break;
-        if (NG == 0 || i + kT1Ring - 1 < NG) issue(ring[(s + kT1Ring - 1) % kT1Ring], i + kT1Ring - 1);
-        const T1Stage &S = ring[s];
-        const bool live = i < ng;
-        const int g = wave + kNW * min(i, ng - 1);
-        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
-        const uint32_t wg[4] = {S.g.x, S.g.y, S.g.z, S.g.w};
-        const uint32_t wu[4] = {S.u.x, S.u.y, S.u.z, S.u.w};
-        u32x4 a[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
-        if (xa_lane) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) a[w] = *(const u32x4 *)&s_xp[32 * g + 4 * (4 * hs + w)];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          dg = mma16<F16X>(a[w], code_pairs(wg[w], magic), dg);
-          du = mma16<F16X>(a[w], code_pairs(wu[w], magic), du);
-        }
-        const float xsh = s_xh[2 * g + hs];
-        const float sg = live ? f16_to_f32(S.mg) : 0.0f, bg = live ? f16_to_f32(S.mg >> 16) : 0.0f;
-        const float su = live ? f16_to_f32(S.mu) : 0.0f, bu = live ? f16_to_f32(S.mu >> 16) : 0.0f;
-        accg = fmaf(sg, dg[0], accg);
-        accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsh, accg);
-        accu = fmaf(su, du[0], accu);
-        accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsh, accu);
-      }
-    }
-  red[wave][0][lane] = accg;
-  red[wave][1][lane] = accu;
-  __syncthreads();
-  if (wave == 0 && lane < kT1Rows) {
-    float g = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      g += red[w][0][lane] + red[w][0][lane + 32];
-      u += red[w][1][lane] + red[w][1][lane + 32];
-    }
-    st_dev64(L.hg + hrow + lane, tagged(__float_as_uint(gelu_tanh(g) * u), tag));
-  }
-}
-
-// NV: 64-expert registers per lane of the selecting wave (E <= 64 NV)
-template <bool F16X, int MAXC, int NV>
-__global__ __launch_bounds__(kThreads, 3) void decode_one_kernel(LayerLaunch L) {
-  extern __shared__ __align__(16) uint8_t dsm[];
-  __shared__ float red[kNW][2][64];
-  __shared__ __align__(16) uint32_t hpl[kNW][kT1M][3][32];
-  __shared__ const uint8_t *s_blob[kMaxK];
-  __shared__ float s_gate[kMaxK];
-  __shared__ int32_t s_id[kMaxK];
-  __shared__ float s_lv[kMaxK];
-  __shared__ SelectLds s_select;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x;
-  const int D = L.D, E = L.E, k = L.k, G = D / 64, NB = D / 64;
-  const T1Roles R = t1_roles(E, k, D, L.F, L.sblobs ? L.Fs : 0);
-  uint32_t tag = 0;
-  auto load_tag = [&]() {
-    tag = __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
-  };
-  uint32_t *s_xp = (uint32_t *)dsm;                  // gate/up blocks: [G][32]
-  float *s_xh = (float *)(dsm + 128 * (size_t)G);    // [2G]
-  const void **s_table = (const void **)(dsm + L.table_off);
-
-  if (b < R.b_sg) {
-    // ---------------- router rows: publish the logits (every copy)
-    __builtin_amdgcn_s_setprio(3);
-    router_role<F16X, MAXC, false, 3>(L, b, tag, dsm, s_select);
-  } else if (b < R.b_sd || (b >= R.b_rg && b < R.b_rd)) {
-    // ---------------- gate/up: 32 hidden rows over the whole model width
-    const bool routed = b >= R.b_rg;
-    const int gb = routed ? b - R.b_rg : b - R.b_sg;
-    const int tpe = (routed ? L.F : L.Fs) / kT1Rows;  // tiles per expert
-    const int j = routed ? gb / tpe : 0, tile = gb - j * tpe;
-    const uint8_t *blob;
-    uint64_t held[NV];
-    if (routed) {
-      constexpr int kTab = kMaxLayerE / kThreads;
-      const void *tb[kTab];
-      u32x4 xq[kT1XV];
-      t1_issue_x(L, xq);
-#pragma unroll
-      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
-      load_tag();
-      t1_stage_x<F16X>(L, xq, s_xp, s_xh);
-#pragma unroll
-      for (int i = 0; i < kTab; ++i)
-        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
-      __syncthreads();
-      t1_select<NV>(L, gb % kT1Copies, tag, s_table, s_blob, s_gate, s_id, s_lv,
-                    /*report=*/gb == 0, held);
-      blob = s_blob[j];
-    } else {
-      // a scalar load (the bank was written before the launch): no vector
-      // load is pending where the routed and shared paths meet
-      blob = (const uint8_t *)as_const(L.sblobs)[0];
-      u32x4 xq[kT1XV];
-      t1_issue_x(L, xq);
-      load_tag();
-      t1_stage_x<F16X>(L, xq, s_xp, s_xh);
-      __syncthreads();
-    }
-    const int F = routed ? L.F : L.Fs;
-    const size_t hrow = routed ? (size_t)j * L.F + (size_t)tile * kT1Rows
-                               : (size_t)k * L.F + (size_t)tile * kT1Rows;
-    if (G % kNW == 0 && G / kNW == 11)
-      t1_glu<F16X, 11>(L, blob, F, tile, hrow, s_xp, s_xh, red, wave, lane, tag);
-    else
-      t1_glu<F16X, 0>(L, blob, F, tile, hrow, s_xp, s_xh, red, wave, lane, tag);
-    t1_keep(held);
-  } else {
-    // ---------------- down: 64 output rows of one slot (or a split of the
-    // shared expert's units), added to the output with a counted atomic
-    const bool routed = b >= R.b_rd;
-    const int db = routed ? b - R.b_rd : b - R.b_sd;
-    int j, ot, u0, u1;
-    if (routed) {
-      j = db / NB;
-      ot = db - j * NB;
-      u0 = 0;
-      u1 = L.F / 64;
-    } else {
-      j = -1;
-      ot = db / R.KSds;
-      const int ks = db - ot * R.KSds;
-      u0 = ks * R.UPs;
-      u1 = min(u0 + R.UPs, L.Fs / 64);
-    }
-    const int n = ot * 64 + lane;
-    const uint8_t *blob;
-    float gj = 1.0f;
-    uint64_t held[NV];
-    if (routed) {
-      constexpr int kTab = kMaxLayerE / kThreads;
-      const void *tb[kTab];
-#pragma unroll
-      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
-      load_tag();
-#pragma unroll
-      for (int i = 0; i < kTab; ++i)
-        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
-      __syncthreads();
-      t1_select<NV>(L, db % kT1Copies, tag, s_table, s_blob, s_gate, s_id, s_lv, false, held);
-      blob = s_blob[j];
-      gj = s_gate[j];
-      if (L.down_delay > 0) {
-        // pace: the gate/up weights, needed first, go ahead of these
-        const uint64_t t_go = __builtin_amdgcn_s_memrealtime() + (uint64_t)L.down_delay;
-        while (__builtin_amdgcn_s_memrealtime() < t_go) __builtin_amdgcn_s_sleep(8);
-      }
-    } else {
-      blob = (const uint8_t *)as_const(L.sblobs)[0];
-      load_tag();
-    }
-    const int Fx = routed ? L.F : L.Fs;
-    DownRegs<kT1M> dr;
-    size_t hp[kT1M];
-    float gate[kT1M];
-    bool use[kT1M];
-#pragma unroll
-    for (int i = 0; i < kT1M; ++i) {
-      const int uu = u0 + wave + i * kNW;
-      const int u = min(uu, u1 - 1);
-      use[i] = uu < u1;
-      gate[i] = gj;
-      hp[i] = (routed ? (size_t)j * L.F : (size_t)k * L.F) + (size_t)u * 64;
-      issue_down(dr, i, blob, D, Fx, u, n);
-    }
-    down_and_combine<kT1M, NoHook, 2>(L, dr, hp, gate, use, hpl, red, ot, (size_t)n, wave, lane,
-                                      tag);
-    t1_keep(held);
-  }
-
-  // ---------------- advance every copy of the epoch (block b: b, b + grid, ...)
-  if (tid == 0)
-    for (int jj = b; jj < kMaxLayerGrid; jj += L.grid_full) st_dev(L.bep + jj, tag);
-}
-
 using KernelFn = void (*)(LayerLaunch);
 template <bool F16X, int MAXC>
 KernelFn pick(int m, bool stream, bool two) {
@@ -1632,17 +1253,6 @@ KernelFn pick_layer(const LayerLaunch &L, int m) {
   if (L.f16x) return small_d ? pick<true, 3>(m, st, two) : pick<true, 8>(m, st, two);
   return small_d ? pick<false, 3>(m, st, two) : pick<false, 8>(m, st, two);
 }
-
-template <int NV>
-KernelFn pick_one_nv(const LayerLaunch &L) {
-  const bool small_d = L.D <= 3072;
-  if (L.f16x) return small_d ? decode_one_kernel<true, 3, NV> : decode_one_kernel<true, 8, NV>;
-  return small_d ? decode_one_kernel<false, 3, NV> : decode_one_kernel<false, 8, NV>;
-}
-KernelFn pick_one(const LayerLaunch &L) {
-  return L.E <= 128 ? pick_one_nv<2>(L) : pick_one_nv<kMaxLayerE / 64>(L);
-}
-int g_one_capacity[2][2][2][64];  // [f16x][MAXC 3/8][E <= 128][device]
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -1733,56 +1343,6 @@ hipError_t launch_layer_ordered(LayerLaunch L, int first, int n, hipStream_t s) 
   if (n == 0) return hipSuccess;
   L.blk0 = first;
   hipLaunchKernelGGL(k, dim3(n), dim3(kThreads), layer_smem(L), s, L);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- one-token launch (host)
-bool layer_one_fits(const LayerLaunch &L) {
-  return L.T == 1 && L.E <= kMaxLayerE && L.k <= kMaxK && L.F % kT1Rows == 0 &&
-         L.F / 64 <= kNW * kT1M && (!L.sblobs || L.Fs % kT1Rows == 0) && L.D <= 8192 &&
-         L.D % 64 == 0;
-}
-int layer_one_grid(const LayerLaunch &L) {
-  return t1_roles(L.E, L.k, L.D, L.F, L.sblobs ? L.Fs : 0).total;
-}
-int layer_one_shared_splits(const LayerLaunch &L) {
-  return t1_roles(L.E, L.k, L.D, L.F, L.sblobs ? L.Fs : 0).KSds;
-}
-size_t layer_one_table_off(const LayerLaunch &L) {
-  // router staging (x as fp32, 16-column sums, partial logits) or the
-  // gate/up blocks' activation pairs and 32-column sums
-  const size_t router = sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads);
-  const size_t glu = (size_t)136 * (L.D / 64);
-  return align_up(max(router, glu));
-}
-size_t layer_one_smem(const LayerLaunch &L) {
-  return layer_one_table_off(L) + sizeof(void *) * (size_t)L.E;
-}
-hipError_t layer_one_capacity(const LayerLaunch &L, int *cap) {
-  *cap = 0;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int &slot = g_one_capacity[L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1][L.E <= 128 ? 1 : 0][dev];
-  const size_t smem = layer_one_smem(L);
-  if (smem > 64 * 1024) return hipSuccess;
-  if (!slot) {
-    int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)pick_one(L),
-                                                     kThreads, smem);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    slot = per_cu * cus;
-  }
-  *cap = slot;
-  return hipSuccess;
-}
-hipError_t launch_layer_one(LayerLaunch L, hipStream_t s) {
-  L.grid_full = layer_one_grid(L);
-  L.blk0 = 0;
-  hipLaunchKernelGGL(pick_one(L), dim3(L.grid_full), dim3(kThreads), layer_one_smem(L), s, L);
   return hipGetLastError();
 }
 

@@ -262,39 +262,6 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   return true;
 }
 
-// The single-token layer with one routing hop (decode_one_kernel): its
-// tagged words in the workspace's fixed region; false if it does not apply.
-bool plan_layer_one(const Workspace &w, LayerLaunch *L) {
-  if (tuning().layer != 3 || !layer_one_fits(*L)) return false;
-  const int k = L->k, E = L->E, F = L->F, Fs = L->sblobs ? L->Fs : 0;
-  L->n_gtiles = 0;
-  L->KSg = 1;
-  L->KSdr = k;
-  L->KSds = layer_one_shared_splits(*L);
-  if (L->KSdr + L->KSds > 255 || L->D / 64 > kMaxOutTiles) return false;
-  L->select = 1;
-  L->log_copies = 16;
-  L->direct_h = 0;
-  L->order = 0;
-  L->stream = 0;
-  L->down_late = 0;
-  L->down_delay = tuning().layer_one_down_delay;
-  int cap = 0;
-  if (layer_one_capacity(*L, &cap) != hipSuccess) return false;
-  if (layer_one_grid(*L) > cap || layer_one_grid(*L) > kMaxLayerGrid) return false;
-  L->bep = (uint32_t *)w.layer;
-  set_split_accumulators(w, &L->gacc, &L->dacc, &L->gcnt, &L->dcnt);
-  Carver c{w.layer + kTaggedOff};
-  L->rlog = c.take<uint64_t>((size_t)L->log_copies * E, 8);
-  L->sel = nullptr;  // every block that needs the selection ranks the logits itself
-  L->hg = c.take<uint64_t>((size_t)k * F + (size_t)Fs, 8);
-  L->hu = nullptr;
-  if (kTaggedOff + c.off > kRouteTagOff) return false;
-  L->table_off = layer_one_table_off(*L);
-  L->err = w.err;
-  return true;
-}
-
 }  // namespace
 
 moe_status layer_forward_args(const void *x, int x_dtype, int T, const moe_qmat *router, int k,
@@ -413,8 +380,6 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_sel_stride = value;
   } else if (!strcmp(key, "layer_shared_wait")) {
     tuning().layer_shared_wait = value;
-  } else if (!strcmp(key, "layer_one_down_delay")) {
-    tuning().layer_one_down_delay = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
   } else if (!strcmp(key, "route_mfma")) {
@@ -518,10 +483,6 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   // between them; only when every expert of the call is sure to fit the
   // slots, so that the plan cannot fail once the first launch has left its
   // blocks' epochs and partial sums waiting for the second.
-  if (!pool && plan_layer_one(w, &L)) {
-    const int pi = prof_begin(s);
-    return hip_status(prof_end(pi, s, launch_layer_one(L, s)));
-  }
   const bool use_layer = (!pool || T * k <= pool_slots(pool)) && plan_layer(w, &L);
   if (use_layer && !pool) {
     const int pi = prof_begin(s);

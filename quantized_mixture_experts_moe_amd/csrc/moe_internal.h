@@ -98,12 +98,10 @@ struct Tuning {
   int layer_down_late = 1;
   int layer_order = 1;
   int layer_direct_h = 0;
-  int layer_select = 0;
+  int layer_select = 1;  // measured: 17.0 against 17.5 us per decode step
   int layer_log_copies = 16;
   int layer_sel_copies = 16;
   int layer_sel_stride = 0;  // words between selection lines; 0: packed
-  int layer_one_down_delay = 0;  // single-token layer: routed down weights this many
-                                 // 10 ns ticks after the selection
 };
 Tuning &tuning();
 
@@ -270,8 +268,6 @@ struct LayerLaunch {
   // selection lines as usual and the blob of rank r from given_blob[t][r]
   uint64_t *host_sel; uint32_t host_epoch;
   int two;                            // that variant of the kernel (set before planning)
-  int down_delay;                     // single-token layer: routed down weights requested this
-                                      // many 10 ns ticks after the selection
 };
 int layer_m(const LayerLaunch &L);
 int layer_routed_blocks(const LayerLaunch &L);
@@ -282,15 +278,6 @@ size_t layer_table_off(const LayerLaunch &L);
 hipError_t layer_capacity(const LayerLaunch &L, int *cap);
 int layer_shared_blocks(const LayerLaunch &L);
 hipError_t launch_layer(const LayerLaunch &L, hipStream_t s);
-// The single-token layer with one routing hop and full-width gate/up tiles
-// (decode_one_kernel): its shape, resources and launch.
-bool layer_one_fits(const LayerLaunch &L);
-int layer_one_grid(const LayerLaunch &L);
-int layer_one_shared_splits(const LayerLaunch &L);
-size_t layer_one_table_off(const LayerLaunch &L);
-size_t layer_one_smem(const LayerLaunch &L);
-hipError_t layer_one_capacity(const LayerLaunch &L, int *cap);
-hipError_t launch_layer_one(LayerLaunch L, hipStream_t s);
 // blocks [first, first + n) of the dispatch order L.order (0 or 1), two-launch variant
 hipError_t launch_layer_ordered(LayerLaunch L, int first, int n, hipStream_t s);
 // blocks [blk0, blk0 + n) of the grid only (streamed experts: shared blocks

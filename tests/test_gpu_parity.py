@@ -208,9 +208,8 @@ def test_selection_exact_ties(name, T):
     # one token per call: the one-launch layer, with the selection ranked by
     # the router blocks (0) or by every routed block from the logits (1)
     try:
-        for sel in (0, 1, 3):
-            # 3: the single-token layer with every block ranking the logits
-            _tune(layer_select=min(sel, 1), layer=3 if sel == 3 else 1)
+        for sel in (0, 1):
+            _tune(layer_select=sel)
             for t in range(T):
                 out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
                 ids1 = torch.empty(1, cfg.k, dtype=torch.int32, device="cuda")
@@ -515,14 +514,14 @@ def test_pool_streamed_equals_resident_and_trace(policy):
     pool.close()
 
 
-_PATHS = {"one": {"layer": 3}, "layer": {"layer": 1}, "order0": {"layer": 1, "layer_order": 0},
+_PATHS = {"layer": {"layer": 1}, "order0": {"layer": 1, "layer_order": 0},
           "order1": {"layer": 1, "layer_order": 1}, "hint0": {"layer": 1, "layer_direct_h": 0},
           "hint1": {"layer": 1, "layer_direct_h": 1}, "hint2": {"layer": 1, "layer_direct_h": 2},
           "select0": {"layer": 1, "layer_select": 0}, "select1": {"layer": 1, "layer_select": 1},
           "stream": {"layer": 2}, "fused": {"layer": 0, "fused": 1},
           "three": {"layer": 0, "fused": 0}}
 _DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_shared_wait": 0, "layer_down_late": 1,
-             "layer_order": 1, "layer_direct_h": 0, "layer_select": 0}
+             "layer_order": 1, "layer_direct_h": 0, "layer_select": 1}
 
 
 def _tune(**kv):
@@ -530,7 +529,7 @@ def _tune(**kv):
         moe.moe_set_tuning(key, v)
 
 
-@pytest.mark.parametrize("path", ["one", "layer", "order0", "order1", "hint0", "hint1", "hint2",
+@pytest.mark.parametrize("path", ["layer", "order0", "order1", "hint0", "hint1", "hint2",
                                   "select0", "select1", "stream", "fused", "three"])
 def test_layer_forward_decode_all_paths(path):
     """The one-launch layer (split or whole gate/up tiles), the router +
