@@ -175,6 +175,33 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
                              int32_t out_dtype, int32_t *ids_out, float *gates_out, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* The residual block around the layer (the pages list the normalisation and
+ * residual work of a block among what a production engine fuses around the
+ * experts, without defining it: es.news.hada.io, "Alcance de implementacion y
+ * registro experimental"; the reading taken is a Gemma-style RMSNorm on both
+ * sides of the layer):
+ *   u   = x / sqrt(mean_d(x^2) + eps) * (1 + w_pre), rounded to x_dtype
+ *         (round to nearest even): the layer's input
+ *   y   = moe_layer_forward(u) in fp32
+ *   out = x + y / sqrt(mean_d(y^2) + eps) * (1 + w_post), in out_dtype
+ * Arguments as moe_layer_forward, and:
+ *   w_pre, w_post  device [D] fp32;  eps >= 0;  D <= 8192
+ *   out       device [T, D]; may be x itself when out_dtype == x_dtype (the
+ *             residual stream updated in place); no other overlap with x
+ *   u_out     device [T, D] of x_dtype, 16-byte aligned, or NULL: receives u
+ *   ws        device scratch of moe_block_workspace_bytes(T, k, E, D, F,
+ *             F_shared) bytes (the layer's workspace, then u and y)
+ * Errors: MOE_E_INVALID for a bad argument or overlap, MOE_E_WORKSPACE for a
+ * short workspace, else as moe_layer_forward. */
+moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const float *w_pre,
+                             const float *w_post, float eps, const moe_qmat *router,
+                             const float *logit_bias, int32_t k, const moe_bank *routed,
+                             const moe_bank *shared, moe_pool *pool, int32_t layer, void *out,
+                             int32_t out_dtype, void *u_out, int32_t *ids_out, float *gates_out,
+                             void *ws, size_t ws_bytes, void *stream);
+size_t moe_block_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t D, int32_t F,
+                                 int32_t F_shared);
+
 /* Expert store: every layer's expert blobs in one file on local storage,
  * blob (layer l, expert e) at byte offset (l * E + e) * moe_store_stride(D, F)
  * (the blob's size rounded up to 4096 bytes, zero padded), read on demand

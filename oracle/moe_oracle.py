@@ -34,6 +34,10 @@ design notes):
 Arithmetic is float64 by default (dequantised weights are exact in float64);
 ``dtype=np.float32`` gives the fp32 dequantise-and-matmul variant.
 
+The block around the layer (a reading: the pages define no norm): a
+Gemma-style pre-norm RMSNorm of the residual stream, rounded to bf16, feeds
+the layer, and out = x + RMSNorm(layer output) with its own weights.
+
 Parity pins (tests/test_oracle_pins.py): hand-built code words, one-hot and
 constant-code closed forms, GELU values at fixed points, x = 0, k = E softmax,
 a single-expert dense GeGLU MLP, an independently decoded brute-force dense
@@ -139,7 +143,8 @@ def activations_to_float(x_bits: np.ndarray, x_dtype: str) -> np.ndarray:
     if x_dtype == "fp16":
         return u.view(np.float16).astype(np.float64)
     if x_dtype == "bf16":
-        return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # signalling NaN patterns stay NaN
+            return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     raise ValueError(x_dtype)
 
 
@@ -240,6 +245,54 @@ def combine(y: np.ndarray, gates: np.ndarray, y_shared: Optional[np.ndarray]) ->
     for j in range(k):
         out = out + np.asarray(gates[:, j:j + 1], np.float64) * np.asarray(y[:, j, :], np.float64)
     return out
+
+
+# --------------------------------------------------------------------------
+# the transformer block around the layer (synthetic: the pages name the
+# normalisation and residual work of a block but do not define it)
+# --------------------------------------------------------------------------
+NORM_EPS = 1e-6
+
+
+def rms_norm(v: np.ndarray, w: np.ndarray, eps: float = NORM_EPS) -> np.ndarray:
+    """Gemma-style RMSNorm of each row: v / sqrt(mean(v^2) + eps) * (1 + w)."""
+    v = np.asarray(v, dtype=np.float64)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * (1.0 + np.asarray(w, dtype=np.float64))
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Float values rounded to fp32, then to the nearest bf16 (ties to even),
+    as uint16 bits: the rounding decision taken in fp32, as the kernels take
+    it."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def block_forward(x: np.ndarray, layer, k: int, w_pre: np.ndarray, w_post: np.ndarray,
+                  eps: float = NORM_EPS, logit_bias=None, ids=None,
+                  u: Optional[np.ndarray] = None, x_dtype: str = "bf16") -> Dict[str, np.ndarray]:
+    """A pre/post-normed residual block around the MoE layer:
+    out = x + rms_norm(MoE(u), w_post) with u = rms_norm(x, w_pre) rounded to
+    the layer's 16-bit activations (x_dtype, round to nearest even).  ``u``
+    (float values) replaces the rounded pre-norm when given: the rounding is
+    a decision the GPU takes in its own fp32 arithmetic, and the layer is then
+    compared on the same inputs."""
+    x = np.asarray(x, dtype=np.float64)
+    if u is None:
+        v = rms_norm(x, w_pre, eps)
+        if x_dtype == "bf16":
+            u = activations_to_float(round_to_bf16(v), "bf16")
+        elif x_dtype == "fp16":
+            u = v.astype(np.float16).astype(np.float64)
+        else:
+            raise ValueError(x_dtype)
+    r = layer_forward(u, layer, k, logit_bias, ids=ids)
+    out = x + rms_norm(r["out"], w_post, eps)
+    return {"out": out, "u": u, "moe": r["out"], "ids": r["ids"], "gates": r["gates"],
+            "logits": r["logits"]}
 
 
 # --------------------------------------------------------------------------

@@ -23,7 +23,8 @@ OUT = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "libmoe")
 
 SOURCES = ["moe_api.cpp", "pool.cpp", "route.hip", "expert_gemv.hip", "expert_fused.hip",
-           "permute.hip", "prefill_mfma.hip", "layer_decode.hip", "noalloc.cpp", "store.cpp"]
+           "permute.hip", "prefill_mfma.hip", "layer_decode.hip", "block_norm.hip", "noalloc.cpp",
+           "store.cpp"]
 
 
 def hipcc() -> str:

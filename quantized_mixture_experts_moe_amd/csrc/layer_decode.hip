@@ -790,7 +790,12 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   // lines still give the ids and gates)
   const bool given = !TWO && L.given_blob != nullptr;
   const int n_rt = T * k * Gf;                 // routed gate/up tiles, then the shared ones
-  const int dw = max(wave - 1, 0);             // down units: waves 1..3 (wave 0 mirrors 1)
+  // down units: waves 1..3 (wave 0 mirrors wave 1 and does the gate/up
+  // reduction's atomics), or all four waves (dw4: more units per block, for
+  // grids that would not be resident otherwise)
+  const int dwc = L.dw4 ? kNW : kDW;
+  const int dw = L.dw4 ? wave : max(wave - 1, 0);
+  const bool dwave = L.dw4 || wave > 0;
 
   if (b < T * nrb) {
     // ---------------- router rows and the selection of the token.  They
@@ -837,7 +842,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     auto load_down = [&]() {
 #pragma unroll
       for (int i = 0; i < M; ++i)
-        issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * kDW, u1 - 1), n);
+        issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * dwc, u1 - 1), n);
     };
     if (L.down_late == 0) load_down();
     stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
@@ -850,17 +855,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     }
     // down weights of waves 1..3 once their gate/up data is in (2) or after
     // the split reduction (1); wave 0 does the reduction's atomics
-    if (L.down_late == 2 && wave > 0) load_down();
+    if (L.down_late == 2 && dwave) load_down();
     if (has_g) glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, wave, lane, tag);
-    if (L.down_late == 1 && wave > 0) load_down();
+    if (L.down_late == 1 && dwave) load_down();
     if (has_d) {
       size_t hp[M];
       float gate[M];
       bool use[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) {
-        const int u = min(u0 + dw + i * kDW, u1 - 1);
-        use[i] = wave > 0 && u0 + dw + i * kDW < u1;
+        const int u = min(u0 + dw + i * dwc, u1 - 1);
+        use[i] = dwave && u0 + dw + i * dwc < u1;
         gate[i] = 1.0f;
         hp[i] = (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
       }
@@ -938,7 +943,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     auto load_down = [&]() {
 #pragma unroll
       for (int i = 0; i < M; ++i) {
-        const int u = min(u0 + dw + i * kDW, u1 - 1);
+        const int u = min(u0 + dw + i * dwc, u1 - 1);
         const int jj = u / Gf;
         issue_down(dr, i, s_blob[ds][jj], D, L.F, u - jj * Gf, n);
       }
@@ -952,18 +957,18 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     }
     // down weights of waves 1..3 once their gate/up data is in (2) or after
     // the split reduction (1); wave 0 does the reduction's atomics
-    if (L.down_late == 2 && wave > 0) load_down();
+    if (L.down_late == 2 && dwave) load_down();
     if (has_g) glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, wave, lane, tag);
-    if (L.down_late == 1 && wave > 0) load_down();
+    if (L.down_late == 1 && dwave) load_down();
     if (has_d) {
       size_t hp[M];
       float gate[M];
       bool use[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) {
-        const int u = min(u0 + dw + i * kDW, u1 - 1);
+        const int u = min(u0 + dw + i * dwc, u1 - 1);
         const int jj = u / Gf;
-        use[i] = wave > 0 && u0 + dw + i * kDW < u1;
+        use[i] = dwave && u0 + dw + i * dwc < u1;
         gate[i] = s_gate[ds][jj];
         hp[i] = (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
       }
@@ -1262,9 +1267,10 @@ int g_layer_capacity[3][2][2][3][64];  // [resident, stream, two][f16x][MAXC 3/8
 
 int layer_m(const LayerLaunch &L) {
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
+  const int dwc = L.dw4 && !L.stream ? kNW : kNW - 1;  // waves with down units
   int m = L.stream ? 2 : ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
-  m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), kNW - 1));  // down units: 3 waves
-  if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), kNW - 1));
+  m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), dwc));
+  if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), dwc));
   return m < 2 ? 2 : m;
 }
 

@@ -1,4 +1,5 @@
 // C ABI of libmoe: argument checks, workspace carve-up and kernel dispatch.
+#include <cmath>
 #include <string.h>
 
 #include <new>
@@ -132,7 +133,8 @@ void set_split_accumulators(const Workspace &w, uint64_t **gacc, uint64_t **dacc
 struct Splits {
   int ksg, ksdr, ksds;
 };
-Splits plan_splits(int T, int k, int D, int F, int Fs, int ksg_override, int ksd_override) {
+Splits plan_splits(int T, int k, int D, int F, int Fs, int ksg_override, int ksd_override,
+                   int units_per_block = 12) {
   const int G = D / 64, NB = D / 64;
   const int n_rt = T * k * (F / 64), n_st = T * (Fs / 64);
   const int Ur = k * (F / 64), Us = Fs / 64;
@@ -142,11 +144,12 @@ Splits plan_splits(int T, int k, int D, int F, int Fs, int ksg_override, int ksd
   sp.ksg = clampi(sp.ksg, (G + 15) / 16, G < kMaxKS ? G : kMaxKS);
   // about one down item per gate/up item in each group of blocks
   int ksdr = ksd_override > 0 ? ksd_override : (n_rt * sp.ksg + T * NB - 1) / (T * NB);
-  sp.ksdr = clampi(ksdr, (Ur + 11) / 12, Ur < kMaxFusedKSd ? Ur : kMaxFusedKSd);
+  const int upb = units_per_block;
+  sp.ksdr = clampi(ksdr, (Ur + upb - 1) / upb, Ur < kMaxFusedKSd ? Ur : kMaxFusedKSd);
   sp.ksds = 0;
   if (Us > 0) {
     int ksds = ksd_override > 0 ? ksd_override : (n_st * sp.ksg + T * NB - 1) / (T * NB);
-    sp.ksds = clampi(ksds, (Us + 11) / 12, Us < kMaxFusedKSd ? Us : kMaxFusedKSd);
+    sp.ksds = clampi(ksds, (Us + upb - 1) / upb, Us < kMaxFusedKSd ? Us : kMaxFusedKSd);
   }
   return sp;
 }
@@ -222,20 +225,25 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
     if (!found) L->stream = 0;
   }
   // the most gate/up splits (and with them down splits) whose grid is still
-  // resident all at once: more, smaller blocks overlap more of the transfer
+  // resident all at once: more, smaller blocks overlap more of the transfer.
+  // Several tokens: if no grid fits with three waves of down units per
+  // block, every wave takes down units (16 per block instead of 12)
   const int ksg_hi = tuning().layer_ksg > 0 ? tuning().layer_ksg : (G < kMaxKS ? G : kMaxKS);
   const int ksg_lo = tuning().layer_ksg > 0 ? tuning().layer_ksg : 1;
-  for (int ksg = ksg_hi; ksg >= ksg_lo && !found; --ksg) {
-    const Splits sp = plan_splits(T, k, D, F, Fs, ksg, tuning().layer_ksd);
-    L->KSg = sp.ksg;
-    L->KSdr = sp.ksdr;
-    L->KSds = sp.ksds;
-    L->NR = layer_routed_blocks(*L);
-    if (layer_m(*L) > 4) continue;
-    const int grid = layer_grid(*L);
-    int cap = 0;
-    if (layer_capacity(*L, &cap) != hipSuccess) return false;
-    found = grid <= cap && grid <= kMaxLayerGrid;
+  for (int dw4 = 0; dw4 <= (T > 1 && !L->stream && !L->two ? 1 : 0) && !found; ++dw4) {
+    L->dw4 = dw4;
+    for (int ksg = ksg_hi; ksg >= ksg_lo && !found; --ksg) {
+      const Splits sp = plan_splits(T, k, D, F, Fs, ksg, tuning().layer_ksd, dw4 ? 16 : 12);
+      L->KSg = sp.ksg;
+      L->KSdr = sp.ksdr;
+      L->KSds = sp.ksds;
+      L->NR = layer_routed_blocks(*L);
+      if (layer_m(*L) > 4) continue;
+      const int grid = layer_grid(*L);
+      int cap = 0;
+      if (layer_capacity(*L, &cap) != hipSuccess) return false;
+      found = grid <= cap && grid <= kMaxLayerGrid;
+    }
   }
   if (!found) return false;
   if (L->stream) {  // the whole-tile variant reads the published selection
@@ -294,6 +302,16 @@ moe_status layer_forward_args(const void *x, int x_dtype, int T, const moe_qmat 
 
 Workspace carve_workspace(void *base, const Dims &d) { return carve(base, d); }
 size_t workspace_bytes(const Dims &d) { return carve(nullptr, d).total; }
+
+// The residual block's buffers after the layer's workspace: the normalised
+// input u [T, D] 16-bit and the layer's output y [T, D] fp32.
+BlockTail block_tail(size_t layer_bytes, int T, int D) {
+  BlockTail b;
+  b.u_off = align_up(layer_bytes);
+  b.y_off = align_up(b.u_off + (size_t)T * D * 2);
+  b.total = align_up(b.y_off + (size_t)T * D * 4);
+  return b;
+}
 
 }  // namespace moe
 
@@ -646,6 +664,51 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   a.glu_first = 0; a.glu_count = routed_blocks;
   if (launch_glu(a, s) != hipSuccess) return MOE_E_HIP;
   return hip_status(launch_down(a, true, s));
+}
+
+
+size_t moe_block_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t D, int32_t F,
+                                 int32_t F_shared) {
+  const size_t layer = moe_workspace_bytes(T, k, E, D, F, F_shared);
+  if (!layer) return 0;
+  return block_tail(layer, T, D).total;
+}
+
+moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const float *w_pre,
+                             const float *w_post, float eps, const moe_qmat *router,
+                             const float *logit_bias, int32_t k, const moe_bank *routed,
+                             const moe_bank *shared, moe_pool *pool, int32_t layer, void *out,
+                             int32_t out_dtype, void *u_out, int32_t *ids_out, float *gates_out,
+                             void *ws, size_t ws_bytes, void *stream) {
+  if (!ws || !w_pre || !w_post || !(eps >= 0.0f) || !std::isfinite(eps)) return MOE_E_INVALID;
+  Dims d;
+  moe_status st = layer_forward_args(x, x_dtype, T, router, k, routed, shared, pool, layer, out,
+                                     out_dtype, &d);
+  if (st) return st;
+  if (d.D > kBlockMaxD) return MOE_E_INVALID;
+  if (u_out && ((uintptr_t)u_out % 16)) return MOE_E_INVALID;
+  // out may be x itself (the residual stream updated in place: each element
+  // is read, then written, by one thread) but no other overlap
+  const size_t xb = (size_t)T * d.D * 2;
+  const size_t ob = (size_t)T * d.D * (out_dtype == MOE_F32 ? 4 : 2);
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  if (oa < xa + xb && xa < oa + ob && !(oa == xa && ob == xb)) return MOE_E_INVALID;
+  if (u_out) {
+    const uintptr_t ua = (uintptr_t)u_out;
+    if ((ua < xa + xb && xa < ua + xb) || (ua < oa + ob && oa < ua + xb)) return MOE_E_INVALID;
+  }
+  const size_t lb = workspace_bytes(d);
+  const BlockTail bt = block_tail(lb, T, d.D);
+  if (ws_bytes < bt.total) return MOE_E_WORKSPACE;
+  uint16_t *u = u_out ? (uint16_t *)u_out : (uint16_t *)((uint8_t *)ws + bt.u_off);
+  float *y = (float *)((uint8_t *)ws + bt.y_off);
+  hipStream_t s = (hipStream_t)stream;
+  const int f16x = x_dtype == MOE_F16;
+  if (launch_block_pre(x, f16x, T, d.D, w_pre, eps, u, s) != hipSuccess) return MOE_E_HIP;
+  st = moe_layer_forward(u, x_dtype, T, router, logit_bias, k, routed, shared, pool, layer, y,
+                         MOE_F32, ids_out, gates_out, ws, lb, stream);
+  if (st) return st;
+  return hip_status(launch_block_post(y, x, f16x, T, d.D, w_post, eps, out, out_dtype, s));
 }
 
 }  // extern "C"

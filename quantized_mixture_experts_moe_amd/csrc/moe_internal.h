@@ -166,6 +166,19 @@ struct RouteLaunch {
 };
 hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 // x pairs and 64-column sums for the expert kernels without routing
+// Residual block around the layer (block_norm.hip): pre-norm RMSNorm of x
+// into the layer's 16-bit input u, post-norm RMSNorm of the layer's fp32
+// output y added to x.  D <= kBlockMaxD.
+constexpr int kBlockMaxD = 8192;
+struct BlockTail {
+  size_t u_off, y_off, total;
+};
+BlockTail block_tail(size_t layer_bytes, int T, int D);
+hipError_t launch_block_pre(const void *x, int f16x, int T, int D, const float *w, float eps,
+                            uint16_t *u, hipStream_t s);
+hipError_t launch_block_post(const float *y, const void *x, int f16x, int T, int D,
+                             const float *w, float eps, void *out, int out_dtype, hipStream_t s);
+
 hipError_t launch_prep_x(const void *x, int f16x, int T, int D, uint32_t *xp, float *xs,
                          hipStream_t s);
 
@@ -268,6 +281,7 @@ struct LayerLaunch {
   // selection lines as usual and the blob of rank r from given_blob[t][r]
   uint64_t *host_sel; uint32_t host_epoch;
   int two;                            // that variant of the kernel (set before planning)
+  int dw4;                            // every wave of a block takes down units (16 per block)
 };
 int layer_m(const LayerLaunch &L);
 int layer_routed_blocks(const LayerLaunch &L);

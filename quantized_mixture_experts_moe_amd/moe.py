@@ -38,7 +38,8 @@ EXPORTS = (
     "moe_pool_set_policy", "moe_cache_replay", "moe_pool_fail_copy",
     "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
     "moe_layer_forward_noalloc", "moe_store_stride", "moe_store_open", "moe_store_read",
-    "moe_store_get_stats", "moe_store_close", "moe_pool_create_store",
+    "moe_store_get_stats", "moe_store_close", "moe_pool_create_store", "moe_block_forward",
+    "moe_block_workspace_bytes",
 )
 
 MOE_STORE_DIRECT = 1
@@ -91,6 +92,10 @@ def _load() -> ctypes.CDLL:
                                     P(moe_bank), vp, i32, vp, i32, vp, vp, vp, sz, vp]),
         "moe_layer_forward_noalloc": (i32, [vp, i32, i32, P(moe_qmat), vp, i32, P(moe_bank),
                                             P(moe_bank), vp, i32, vp, vp, vp]),
+        "moe_block_forward": (i32, [vp, i32, i32, vp, vp, ctypes.c_float, P(moe_qmat), vp, i32,
+                                    P(moe_bank), P(moe_bank), vp, i32, vp, i32, vp, vp, vp, vp,
+                                    sz, vp]),
+        "moe_block_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
         "moe_pool_create": (i32, [P(vp), i32, i32, i32, i32, i32, vp]),
         "moe_store_stride": (sz, [i32, i32]),
         "moe_store_open": (i32, [P(vp), ctypes.c_char_p, i32, i32, i32, i32, i32, i32]),
@@ -145,6 +150,10 @@ def moe_blob_bytes(D: int, F: int) -> int:
 
 def moe_workspace_bytes(T: int, k: int, E: int, D: int, F: int, F_shared: int) -> int:
     return int(lib.moe_workspace_bytes(T, k, E, D, F, F_shared))
+
+
+def moe_block_workspace_bytes(T: int, k: int, E: int, D: int, F: int, F_shared: int) -> int:
+    return int(lib.moe_block_workspace_bytes(T, k, E, D, F, F_shared))
 
 
 def moe_set_tuning(key: str, value: int) -> None:
@@ -211,10 +220,11 @@ class DeviceBank:
 
 
 class Workspace:
-    """Zero-filled device scratch for calls up to the given sizes."""
+    """Zero-filled device scratch for calls up to the given sizes (block:
+    sized for moe_block_forward)."""
 
-    def __init__(self, T, k, E, D, F, F_shared, device="cuda"):
-        n = moe_workspace_bytes(T, k, E, D, F, F_shared)
+    def __init__(self, T, k, E, D, F, F_shared, device="cuda", block=False):
+        n = (moe_block_workspace_bytes if block else moe_workspace_bytes)(T, k, E, D, F, F_shared)
         if n == 0:
             raise ValueError("invalid workspace sizes")
         self.buf = torch.zeros(n, dtype=torch.uint8, device=device)
@@ -283,6 +293,24 @@ def moe_layer_forward(x: torch.Tensor, router: DeviceQMat, k: int, routed: Optio
         pool.handle if pool is not None else None, layer, _ptr(out), _DTYPES[out.dtype],
         _ptr(ids_out), _ptr(gates_out), _ptr(ws.buf), ws.nbytes, _stream(stream)),
         "moe_layer_forward")
+
+
+def moe_block_forward(x: torch.Tensor, w_pre: torch.Tensor, w_post: torch.Tensor, eps: float,
+                      router: DeviceQMat, k: int, routed: Optional[DeviceBank],
+                      shared: Optional[DeviceBank], out: torch.Tensor, ws: Workspace,
+                      logit_bias: Optional[torch.Tensor] = None, pool: Optional["Pool"] = None,
+                      layer: int = 0, u_out: Optional[torch.Tensor] = None,
+                      ids_out: Optional[torch.Tensor] = None,
+                      gates_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    T = x.shape[0]
+    _check(lib.moe_block_forward(
+        _ptr(x), _x_dtype(x), T, _ptr(w_pre), _ptr(w_post), float(eps),
+        ctypes.byref(router.struct), _ptr(logit_bias), k,
+        ctypes.byref(routed.struct) if routed is not None else None,
+        ctypes.byref(shared.struct) if shared is not None else None,
+        pool.handle if pool is not None else None, layer, _ptr(out), _DTYPES[out.dtype],
+        _ptr(u_out), _ptr(ids_out), _ptr(gates_out), _ptr(ws.buf), ws.nbytes, _stream(stream)),
+        "moe_block_forward")
 
 
 def moe_layer_forward_noalloc(x: torch.Tensor, router: DeviceQMat, k: int, routed: DeviceBank,

@@ -43,7 +43,7 @@ ALIGN = 256
 
 # spawn-key kinds: every tensor has its own child seed so that any single
 # expert, router or activation block can be regenerated on its own.
-KIND_EXPERT, KIND_SHARED, KIND_ROUTER, KIND_X, KIND_ZIPF = 0, 1, 2, 3, 4
+KIND_EXPERT, KIND_SHARED, KIND_ROUTER, KIND_X, KIND_ZIPF, KIND_NORM = 0, 1, 2, 3, 4, 5
 PART_GATE, PART_UP, PART_DOWN = 0, 1, 2
 
 
@@ -239,6 +239,29 @@ def activations(seed: int, layer: int, stream: int, T: int, D: int,
     """x ~ N(0, 1) rounded to fp16 or bf16; returned as uint16 bit patterns."""
     rng = _rng(seed, KIND_X, layer, stream)
     x = rng.standard_normal((T, D)).astype(np.float32)
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        return _round_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def norm_weights(seed: int, layer: int, D: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The residual block's two RMSNorm weight vectors (pre, post), fp32,
+    w ~ N(0, 0.25^2): effective scales 1 + w scattered around 1."""
+    rng = _rng(seed, KIND_NORM, layer)
+    w = (0.25 * rng.standard_normal((2, D))).astype(np.float32)
+    return w[0].copy(), w[1].copy()
+
+
+def residual_stream(seed: int, layer: int, stream: int, T: int, D: int,
+                    dtype: str) -> np.ndarray:
+    """The residual stream entering a block: N(0, 1) rows with a per-row scale
+    drawn log-uniformly in [1/4, 16] (the stream's norm grows along the layer
+    stack), rounded to fp16 or bf16; uint16 bit patterns."""
+    rng = _rng(seed, KIND_X, layer, stream, 1)
+    scale = np.exp(rng.uniform(np.log(0.25), np.log(16.0), size=(T, 1)))
+    x = (rng.standard_normal((T, D)) * scale).astype(np.float32)
     if dtype == "fp16":
         return x.astype(np.float16).view(np.uint16)
     if dtype == "bf16":

@@ -160,3 +160,33 @@ def test_lfu_planner_rejects_bad_traces():
         moe.moe_lfu_replay(4, 16, np.array([[1, 16]]))  # out of range
     with pytest.raises(moe.MoEError):
         moe.moe_lfu_replay(2, 16, np.array([[1, 2, 3]]))  # k > slots
+
+
+def test_block_argument_checks_launch_nothing():
+    lib = moe.lib
+    q = moe.moe_qmat(1, 1, 128, 256, 8)
+    bank = moe.moe_bank(1, 128, 256, 128)
+    p = ctypes.c_void_p(4096)  # never dereferenced: every call fails its checks first
+    o = ctypes.c_void_p(4096 + 256 * 2 + 64)
+
+    def call(x=p, out=o, w=p, eps=1e-6, u=None, ws_bytes=1 << 30, out_dtype=moe.MOE_F32):
+        return lib.moe_block_forward(x, moe.MOE_BF16, 1, w, w, eps, ctypes.byref(q), None, 8,
+                                     ctypes.byref(bank), None, None, 0, out, out_dtype, u, None,
+                                     None, p, ws_bytes, None)
+
+    assert call(w=None) == moe.MOE_E_INVALID
+    assert call(eps=-1.0) == moe.MOE_E_INVALID
+    assert call(eps=float("nan")) == moe.MOE_E_INVALID
+    assert call(eps=float("inf")) == moe.MOE_E_INVALID
+    # out overlapping x other than exactly (same dtype)
+    assert call(out=ctypes.c_void_p(4096 + 16)) == moe.MOE_E_INVALID
+    assert call(out=p, out_dtype=moe.MOE_F32) == moe.MOE_E_INVALID
+    # u_out misaligned, or overlapping x
+    assert call(u=ctypes.c_void_p(1 << 20 | 8)) == moe.MOE_E_INVALID
+    assert call(u=ctypes.c_void_p(4096 + 256)) == moe.MOE_E_INVALID
+    # workspace: the layer's is not enough
+    layer_ws = moe.moe_workspace_bytes(1, 8, 128, 256, 128, 0)
+    block_ws = moe.moe_block_workspace_bytes(1, 8, 128, 256, 128, 0)
+    assert block_ws >= layer_ws + 256 * 2 + 256 * 4
+    assert call(ws_bytes=layer_ws) == moe.MOE_E_WORKSPACE
+    assert moe.moe_block_workspace_bytes(0, 8, 128, 256, 128, 0) == 0

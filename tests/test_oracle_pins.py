@@ -311,6 +311,50 @@ def test_blob_layout_matches_generator_and_header():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
 
 
+# ---------------------------------------------------------------- block norms and residual
+def test_rms_norm_handworked_and_torch():
+    """x = [3, 4]: mean square 12.5, rms 3.5355...; with w = 0 and eps = 0 the
+    output is [3, 4] / 3.5355 = [0.8485, 1.1314]; and random rows against
+    torch.nn.functional.rms_norm with weight (1 + w)."""
+    got = O.rms_norm(np.array([[3.0, 4.0]]), np.zeros(2), eps=0.0)
+    np.testing.assert_allclose(got, [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=1e-15)
+    assert abs(got[0, 0] - 0.848528137423857) < 1e-12
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 2816)) * 3
+    w = rng.standard_normal(2816) * 0.1
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (2816,),
+                                       weight=torch.from_numpy(1.0 + w), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(x, w, 1e-6), ref, rtol=1e-12, atol=1e-14)
+    # w = 0: every row has unit root mean square (up to eps)
+    u = O.rms_norm(x, np.zeros(2816), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(u * u, axis=1)), 1.0, rtol=1e-12)
+
+
+def test_round_to_bf16_ties_and_torch():
+    """1 + 2^-8 is halfway between bf16 1 and 1 + 2^-7: ties to even gives 1;
+    1 + 3 * 2^-8 rounds up to 1 + 2^-6.  Random values against torch."""
+    assert O.round_to_bf16(np.array([1.0 + 2 ** -8]))[0] == 0x3F80
+    assert O.round_to_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 0x3F82
+    v = np.random.default_rng(3).standard_normal(10000) * 10
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(O.round_to_bf16(v), ref.view(np.uint16))
+
+
+def test_block_forward_structure():
+    """out - x has the root mean square of (1 + w_post) per row, and the
+    block's layer input is the rounded pre-norm of x."""
+    lw = _tiny_layer(0)
+    x = O.activations_to_float(gen.activations(5, 0, 0, 3, 256, "fp16"), "fp16") * 4
+    rng = np.random.default_rng(8)
+    w_pre, w_post = rng.standard_normal(256) * 0.1, np.zeros(256)
+    r = O.block_forward(x, lw, 4, w_pre, w_post, eps=0.0)
+    d = r["out"] - x
+    np.testing.assert_allclose(np.sqrt(np.mean(d * d, axis=1)), 1.0, rtol=1e-12)
+    u = O.activations_to_float(O.round_to_bf16(O.rms_norm(x, w_pre, 0.0)), "bf16")
+    assert np.array_equal(r["u"], u)
+    np.testing.assert_allclose(r["moe"], O.layer_forward(u, lw, 4)["out"], rtol=1e-13)
+
+
 # ---------------------------------------------------------------- permutation
 def test_permutation_handworked():
     ids = np.array([[2, 0], [0, 1], [2, 1]])
@@ -477,3 +521,13 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_blob_layout_offsets_handworked()
     monkeypatch.setattr(O, "blob_layout", orig_b)
+
+    # (8) RMSNorm without the (1 + w) offset -> the torch comparison fails
+    orig_n = O.rms_norm
+
+    def no_offset(v, w, eps=O.NORM_EPS):
+        return orig_n(v, np.asarray(w) - 1.0, eps)
+    monkeypatch.setattr(O, "rms_norm", no_offset)
+    with pytest.raises(AssertionError):
+        test_rms_norm_handworked_and_torch()
+    monkeypatch.setattr(O, "rms_norm", orig_n)
