@@ -7,10 +7,14 @@ token through one layer: router GEMV + top-8 + gates, fused-dequant GLU of the
 8 routed experts and the shared expert, down projection and combine.  Sixteen
 seeded replicas of the layer are rotated (6.9 GB of experts resident in HBM,
 595 MB touched per rotation) so the 256 MB Infinity Cache cannot hold the
-weights; each step takes a fresh seeded token.  Steps are replayed from a HIP
-graph.  Prints one JSON line.
+weights; each step takes a fresh seeded token.  Steps are replayed from HIP
+graphs of --graph-steps steps (plus one graph of the remainder, so exactly W
+warmup and K timed steps run); the median of --regions timed regions of K
+steps each is reported.  --block times the residual block around the layer.
+Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config decode|prefill|stack30]
+    python bench.py [--steps K] [--warmup W] [--config decode|prefill|stack30|streamed|store]
+                    [--block]
 """
 from __future__ import annotations
 
@@ -51,27 +55,52 @@ def build_layers(cfg, n_layers, seed, moe, torch):
 
 
 def cpu_baseline(cfg, seed, budget_s):
-    """The oracle as it stands, on the host cores, for a bounded sample."""
+    """The oracle as it stands, on the host cores, for a bounded sample: the
+    workload's own calls with every BLAS thread, one call on one thread, and
+    (decode) one 128-token chunk of the prefill workload."""
     from oracle import moe_oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     lw = gen.layer_weights(seed, 0, cfg)
     bias = gen.zipf_bias(seed, 0, cfg.E, cfg.beta) if cfg.beta else None
-    n, t0 = 0, time.perf_counter()
-    while True:
-        xb = gen.activations(seed, 0, 10_000 + n, cfg.T, cfg.D, cfg.x_dtype)
-        O.layer_forward(O.activations_to_float(xb, cfg.x_dtype), lw, cfg.k, bias)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} calls of {cfg.T} token(s) through layer 0 of the '{cfg.name}' "
-                      f"workload in {el:.1f} s (float64 numpy oracle, BLAS threads {threads}, "
-                      f"host cpu_count {os.cpu_count()})"}
+
+    def calls(budget, stream0):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            xb = gen.activations(seed, 0, stream0 + n, cfg.T, cfg.D, cfg.x_dtype)
+            O.layer_forward(O.activations_to_float(xb, cfg.x_dtype), lw, cfg.k, bias)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+
+    n, el = calls(budget_s * 0.4, 10_000)
+    res = {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} calls of {cfg.T} token(s) through layer 0 of the '{cfg.name}' "
+                     f"workload in {el:.1f} s (float64 numpy oracle, BLAS threads {threads}, "
+                     f"host cpu_count {os.cpu_count()})"}
+    if threadpool_limits is not None:
+        with threadpool_limits(1):
+            n1, el1 = calls(budget_s * 0.2, 20_000)
+        res["single_thread"] = {"value": n1 * cfg.T / el1, "unit": "tokens/s", "cores": 1,
+                                "sample": f"{n1} calls in {el1:.1f} s"}
+    if cfg.name == "decode":
+        pc = gen.CONFIGS["prefill"]
+        xb = gen.activations(seed, 0, 0, pc.T, pc.D, pc.x_dtype)
+        t0 = time.perf_counter()
+        O.layer_forward(O.activations_to_float(xb, pc.x_dtype), lw, pc.k,
+                        gen.zipf_bias(seed, 0, pc.E, pc.beta))
+        elp = time.perf_counter() - t0
+        res["prefill_chunk"] = {"value": pc.T / elp, "unit": "tokens/s", "cores": int(threads),
+                                "sample": f"one {pc.T}-token chunk (Zipf beta {pc.beta}) in "
+                                          f"{elp:.1f} s"}
+        res["stack30"] = {"value": res["value"] / 30, "unit": "tokens/s", "cores": int(threads),
+                          "sample": "derived: the decode rate over 30 layers of the same shape"}
+    return res
 
 
 # sources that build (and launch) the decode layer kernel: its counters are
@@ -343,8 +372,13 @@ def main():
                     help="HBM expert slots per layer for the streamed workload (default 16)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="tokens per step for decode / prefill (default: the workload's)")
+    ap.add_argument("--block", action="store_true",
+                    help="time the residual block (pre-norm, layer, post-norm and residual) "
+                         "instead of the layer alone")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=64)
+    ap.add_argument("--regions", type=int, default=5,
+                    help="timed regions of --steps steps each; the median is reported")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -385,10 +419,22 @@ def main():
                          for i in range(n_x)])
     x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16).reshape(n_x, T, cfg.D)
     out = torch.empty(n_x, T, cfg.D, dtype=torch.float32, device="cuda")
-    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared, block=a.block)
+    if a.block:
+        xb = np.concatenate([gen.residual_stream(a.seed, 1000 + i, 0, T, cfg.D, cfg.x_dtype)
+                             for i in range(n_x)])
+        x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16).reshape(
+            n_x, T, cfg.D)
+        norms = [tuple(torch.from_numpy(w).cuda() for w in gen.norm_weights(a.seed, l, cfg.D))
+                 for l in range(n_layers)]
 
     def step(i):
         router, routed, shared, bias = layers[i % n_layers]
+        if a.block:
+            w_pre, w_post = norms[i % n_layers]
+            moe.moe_block_forward(x_all[i % n_x], w_pre, w_post, 1e-6, router, cfg.k, routed,
+                                  shared, out[i % n_x], ws, logit_bias=bias)
+            return
         moe.moe_layer_forward(x_all[i % n_x], router, cfg.k, routed, shared, out[i % n_x], ws,
                               logit_bias=bias)
 
@@ -397,27 +443,48 @@ def main():
         for i in range(G):  # eager pass (also loads the kernels)
             step(i)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(G):
-            step(i)
+    graphs = {}
+
+    def graph_of(n):
+        # one graph of n consecutive steps, captured once
+        if n not in graphs:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for i in range(n):
+                    step(i)
+            torch.cuda.synchronize()
+            graphs[n] = gr
+        return graphs[n]
+
+    def run(n):
+        # exactly n steps: full graphs of G steps, then one of the remainder
+        full, rem = divmod(n, G)
+        gf = graph_of(G) if full else None
+        gr = graph_of(rem) if rem else None
+        with torch.cuda.stream(stream):
+            for _ in range(full):
+                gf.replay()
+            if gr is not None:
+                gr.replay()
+
+    steps = max(1, a.steps)
+    graph_of(G)
+    graph_of(steps % G) if steps % G else None
+    graph_of(a.warmup % G) if a.warmup % G else None
+    run(a.warmup)
     torch.cuda.synchronize()
-    reps_w = max(1, a.warmup // G)
-    reps = max(1, a.steps // G)
-    steps = reps * G
-    with torch.cuda.stream(stream):
-        for _ in range(reps_w):
-            graph.replay()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
+    # the median of several timed regions of exactly `steps` steps each
+    region_ms = []
+    for _ in range(max(1, a.regions)):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         ev0.record(stream)
-        for _ in range(reps):
-            graph.replay()
+        run(steps)
         ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
+        torch.cuda.synchronize()
+        region_ms.append(ev0.elapsed_time(ev1))
+    ms = float(np.median(region_ms))
     ms_step = ms / steps
     tokens_per_s = steps * T / (ms / 1e3)
     step_bytes = gen.algorithmic_decode_bytes(cfg) * T if T == 1 else None
@@ -431,10 +498,10 @@ def main():
     # step.  Otherwise (the expert phase of a prefill chunk, or of a decode
     # step on the router + expert-phase path) the library records events
     # around that phase's launches on the same stream, in eager steps.
-    layer_path = T == 1 and "layer=0" not in a.tune
+    layer_path = T == 1 and "layer=0" not in a.tune and not a.block
     tune = dict(kv.split("=") for kv in a.tune)
     grouped = T >= int(tune.get("prefill_min_t", 8))  # the library's default crossover
-    if layer_path or (T > 1 and not grouped):
+    if layer_path or (T > 1 and not grouped) or a.block:
         # one launch per step, or (2 to 7 tokens) the router kernel and the
         # few-token expert kernels, timed as the whole step
         k_us = ms_step * 1e3
@@ -446,7 +513,14 @@ def main():
             torch.cuda.synchronize()
             kms = pe.elapsed_ms(n_prof)
         k_us = 1e3 * float(np.mean(kms))
-    if layer_path:
+    if a.block:
+        # the layer's bytes plus the block's own: x read by both norms, the
+        # two weight vectors
+        k_bytes = (gen.algorithmic_decode_bytes(cfg) + cfg.D * 2 + 2 * cfg.D * 4
+                   if T == 1 else None)
+        k_name = "whole residual block step (pre-norm, layer, post-norm and residual)"
+        traffic = None
+    elif layer_path:
         k_bytes = gen.algorithmic_decode_bytes(cfg)
         k_name = ("decode_layer_kernel (router, top-8, gate/up, down and combine of the 8 "
                   "routed and the shared expert in one launch)")
@@ -501,14 +575,18 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": reps_w * G,
+        "warmup": a.warmup,
         "ms_per_step": ms_step,
+        "timed_regions_ms": [round(v, 4) for v in region_ms],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 activations, int4/int8 weights, fp32 accumulate",
         "data": "synthetic (seeded weights and activations)",
-        "config": {"workload": f"{cfg.name}: one Gemma-4-26B-A4B-shaped MoE layer, "
+        "config": {"workload": f"{cfg.name}: "
+                               + ("residual block (RMSNorm, layer, RMSNorm, residual) around "
+                                  if a.block else "")
+                               + "one Gemma-4-26B-A4B-shaped MoE layer, "
                                f"{T} token(s) per step, d_model {cfg.D}, {cfg.E} experts of "
                                f"GLU width {cfg.F} (4-bit, group 64), top-{cfg.k}, shared expert "
                                f"{cfg.F_shared}, 8-bit router; {n_layers} seeded layer replicas "

@@ -185,12 +185,14 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
  *   y   = moe_layer_forward(u) in fp32
  *   out = x + y / sqrt(mean_d(y^2) + eps) * (1 + w_post), in out_dtype
  * Arguments as moe_layer_forward, and:
- *   w_pre, w_post  device [D] fp32;  eps >= 0;  D <= 8192
- *   out       device [T, D]; may be x itself when out_dtype == x_dtype (the
- *             residual stream updated in place); no other overlap with x
+ *   w_pre, w_post  device [D] fp32, 16-byte aligned;  eps >= 0;  D <= 8192
+ *   out       device [T, D], 16-byte aligned; may be x itself when
+ *             out_dtype == x_dtype (the residual stream updated in place); no
+ *             other overlap with x
  *   u_out     device [T, D] of x_dtype, 16-byte aligned, or NULL: receives u
  *   ws        device scratch of moe_block_workspace_bytes(T, k, E, D, F,
- *             F_shared) bytes (the layer's workspace, then u and y)
+ *             F_shared) bytes, zero-filled before its first use (the
+ *             layer's workspace, then u, y and per-token counters)
  * Errors: MOE_E_INVALID for a bad argument or overlap, MOE_E_WORKSPACE for a
  * short workspace, else as moe_layer_forward. */
 moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const float *w_pre,

@@ -292,6 +292,87 @@ __device__ __forceinline__ float wave_sum(float v) {
   MOE_DPP_REDUCE(float, v, f_add, 0.0f, dpp_f32)
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// ---------------------------------------------------------------- RMSNorm of the residual block
+// Every kernel that normalises a row sums its squares in one fixed order, so
+// fused and separate paths give the same bits: the row is read as chunks of
+// 8 columns; thread t of 256 squares and adds chunks t, t + 256, ... in
+// column order (fmaf from 0); each wave of 64 threads sums its lanes with
+// wave_sum; the four wave sums are added in wave order.  The normalised
+// value is (v * inv) * (1 + w) with inv = 1 / sqrt(sum / D + eps).
+constexpr int kNormThreads = 256;
+__device__ __forceinline__ float sumsq8(const float (&v)[8], float acc) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc = fmaf(v[m], v[m], acc);
+  return acc;
+}
+__device__ __forceinline__ float norm_inv(float sumsq, int D, float eps) {
+  return 1.0f / sqrtf(sumsq / (float)D + eps);
+}
+__device__ __forceinline__ float norm_scale(float v, float inv, float w) {
+  return v * inv * (1.0f + w);
+}
+// The sum by one wave standing in for the 256 threads: lane l plays threads
+// l, l + 64, l + 128, l + 192.  load(c, v) reads chunk c into v[8].
+template <class Load>
+__device__ __forceinline__ float row_sumsq_wave(int nch, Load load) {
+  const int lane = threadIdx.x & 63;
+  float tot = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kNormThreads / 64; ++s) {
+    float p = 0.0f;
+    for (int c = s * 64 + lane; c < nch; c += kNormThreads) {
+      float v[8];
+      load(c, v);
+      p = sumsq8(v, p);
+    }
+    tot += wave_sum(p);
+  }
+  return tot;
+}
+// The sum by a block of 256 threads, from each thread's own partial (chunks
+// t, t + 256, ...).  red4: 4 floats of LDS, read back after a barrier.
+__device__ __forceinline__ float row_sumsq_block(float p, float *red4) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float w = wave_sum(p);
+  if (lane == 0) red4[wave] = w;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kNormThreads / 64; ++s) tot += red4[s];
+  return tot;
+}
+template <bool F16X>
+__device__ __forceinline__ float act_to_f32(uint32_t bits) {
+  return F16X ? f16_to_f32(bits) : bf16_to_f32(bits);
+}
+template <bool F16X>
+__device__ __forceinline__ uint32_t f32_to_act(float v) {
+  return F16X ? f32_to_f16(v) : f32_to_bf16(v);
+}
+// the 8 values of a chunk of 16-bit activations (column order)
+template <bool F16X>
+__device__ __forceinline__ void unpack8(const u32x4 q, float (&v)[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    v[2 * m] = act_to_f32<F16X>(w[m] & 0xFFFFu);
+    v[2 * m + 1] = act_to_f32<F16X>(w[m] >> 16);
+  }
+}
+// u of a chunk: the normalised values rounded to the activation type
+template <bool F16X>
+__device__ __forceinline__ u32x4 norm_chunk(const u32x4 q, float inv, const float4 w0,
+                                            const float4 w1) {
+  float v[8];
+  unpack8<F16X>(q, v);
+  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m] = f32_to_act<F16X>(norm_scale(v[m], inv, w[m]));
+  return u32x4{o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
+               o[6] | (o[7] << 16)};
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   MOE_DPP_REDUCE(float, v, fmaxf, -INFINITY, dpp_f32)
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));

@@ -505,7 +505,79 @@ struct NoHook {
 // With L.hu null the hidden activations are single tagged words h in L.hg
 // (gelu(gate) * up, finished by one block); otherwise gelu(gate) in L.hg and
 // up in L.hu.  on_hint runs once the units' first words are seen.
-template <int M, class OnHint = NoHook>
+// The residual block's post-norm of token t, by the token's first router
+// block once its routing is done: it polls the layer's output row y (tagged
+// words, stored by the lanes that complete each element) until every element
+// carries the launch's epoch, then normalises it (w_post) and adds the
+// residual row x into out.  Thread tid takes chunks tid, tid + 256, ..., the
+// fixed summation order of the separate post-norm kernel (same bits).  The
+// last element is seen one poll after its store: no counter, no store fence.
+template <bool F16X, int NX>
+__device__ __forceinline__ void post_norm_poll(const LayerLaunch &L, int t, uint32_t tag,
+                                               float *red4) {
+  const int tid = threadIdx.x, D = L.D, nch = D / 8;
+  const uint64_t *yr = L.ybuf + (size_t)t * D;
+  const gptr<u32x4> xr = as_global((const u32x4 *)((const uint16_t *)L.x + (size_t)t * D));
+  const float4 *w4 = (const float4 *)L.w_post;
+  u32x4 xq[NX];
+  float4 wa[NX], wb[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int c = min(tid + i * kThreads, nch - 1);
+    xq[i] = xr[c];
+    wa[i] = w4[2 * c];
+    wb[i] = w4[2 * c + 1];
+  }
+  float yv[NX][8];
+  for (long s = 0;; ++s) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int c = min(tid + i * kThreads, nch - 1);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const uint64_t v = ld_dev64(yr + 8 * c + m);
+        ok = ok && has_tag(v, tag);
+        yv[i][m] = __uint_as_float((uint32_t)v);
+      }
+    }
+    if (__syncthreads_and(ok)) break;
+    if (s > kSpin) {
+      if (tid == 0) add_dev(L.err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  float p = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NX; ++i)
+    if (tid + i * kThreads < nch) p = sumsq8(yv[i], p);
+  const float inv = norm_inv(row_sumsq_block(p, red4), D, L.eps);
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int c = tid + i * kThreads;
+    if (c >= nch) continue;
+    float xv[8], r[8];
+    unpack8<F16X>(xq[i], xv);
+    const float wv[8] = {wa[i].x, wa[i].y, wa[i].z, wa[i].w, wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) r[m] = xv[m] + norm_scale(yv[i][m], inv, wv[m]);
+    const size_t o = (size_t)t * D + 8 * c;
+    if (L.out_dtype == MOE_F32) {
+      ((float4 *)((float *)L.out + o))[0] = float4{r[0], r[1], r[2], r[3]};
+      ((float4 *)((float *)L.out + o))[1] = float4{r[4], r[5], r[6], r[7]};
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        h[m] = L.out_dtype == MOE_BF16 ? f32_to_bf16(r[m]) : f32_to_f16(r[m]);
+      *(u32x4 *)((uint16_t *)L.out + o) = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                               h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
+  }
+}
+
+template <int M, bool NORM = false, class OnHint = NoHook>
 __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const DownRegs<M> &R,
                                                  const size_t (&hp)[M], const float (&gate)[M],
                                                  const bool (&use)[M], uint32_t (&hpl)[kNW][M][3][32],
@@ -633,13 +705,19 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
 #pragma unroll
     for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
     const int nsp = L.KSdr + L.KSds;
-    if (nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s)) {
-      if (L.out_dtype == MOE_F32)
-        ((float *)L.out)[out_idx] = s;
-      else if (L.out_dtype == MOE_BF16)
-        ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_bf16(s);
-      else
-        ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_f16(s);
+    const bool done = nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s);
+    if constexpr (!NORM) {
+      if (done) {
+        if (L.out_dtype == MOE_F32)
+          ((float *)L.out)[out_idx] = s;
+        else if (L.out_dtype == MOE_BF16)
+          ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_bf16(s);
+        else
+          ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_f16(s);
+      }
+    } else {
+      // the output element goes to ybuf as a tagged word for the post-norm
+      if (done) st_dev64(L.ybuf + out_idx, tagged(__float_as_uint(s), tag));
     }
   }
 }
@@ -647,9 +725,9 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
 // Router rows e0 .. e0 + kRows - 1 of token r_t and the selection of the
 // token (every router block publishes its winners).  They head the chain of
 // dependent steps, so these blocks do nothing else.
-template <bool F16X, int MAXC, bool HS = false, int PRIO = 1>
+template <bool F16X, int MAXC, bool HS = false, int PRIO = 1, bool NORM = false>
 __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_t &tag, uint8_t *dsm,
-                                            SelectLds &s_select) {
+                                            SelectLds &s_select, float *red4 = nullptr) {
   constexpr int MAXX = MAXC == 3 ? 2 : 4;  // 16-byte pieces of x per thread
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -668,6 +746,16 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
   const gptr<u32x4> xt = as_global((const u32x4 *)(x + (size_t)r_t * D));
 #pragma unroll
   for (int i = 0; i < MAXX; ++i) xr[i] = xt[min(tid + i * kThreads, D / 8 - 1)];
+  float4 wn[NORM ? MAXX : 1][2];
+  if constexpr (NORM) {
+    const float4 *w4 = (const float4 *)L.w_pre;
+#pragma unroll
+    for (int i = 0; i < MAXX; ++i) {
+      const int c = min(tid + i * kThreads, D / 8 - 1);
+      wn[i][0] = w4[2 * c];
+      wn[i][1] = w4[2 * c + 1];
+    }
+  }
   const int e = min(r_e0 + rr, E - 1);
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
@@ -679,6 +767,28 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
   tag = __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
   float lbias = 0.0f;
   if (L.logit_bias && wave == 0 && lane < kRows) lbias = L.logit_bias[min(r_e0 + lane, E - 1)];
+  if constexpr (NORM) {
+    // the layer's input u: this thread's chunks are those of the fixed
+    // summation order (chunks tid, tid + 256, ...)
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXX; ++i) {
+      if (tid + i * kThreads < D / 8) {
+        float v[8];
+        unpack8<F16X>(xr[i], v);
+        p = sumsq8(v, p);
+      }
+    }
+    const float inv = norm_inv(row_sumsq_block(p, red4), D, L.eps);
+#pragma unroll
+    for (int i = 0; i < MAXX; ++i) xr[i] = norm_chunk<F16X>(xr[i], inv, wn[i][0], wn[i][1]);
+    if (L.u_out && r_e0 == 0) {
+#pragma unroll
+      for (int i = 0; i < MAXX; ++i)
+        if (tid + i * kThreads < D / 8)
+          ((u32x4 *)(L.u_out + (size_t)r_t * D))[tid + i * kThreads] = xr[i];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MAXX; ++i) {
     const int c = tid + i * kThreads;
@@ -751,10 +861,52 @@ __device__ __forceinline__ void router_role(const LayerLaunch &L, int b, uint32_
   __builtin_amdgcn_s_setprio(0);
 }
 
+// The pre-norm in a gate/up block: the row's chunks of the fixed summation
+// order (tid, tid + 256, ...) and the norm weights of the thread's own chunk
+// (the one issue_x loads) are requested with x; finish_norm sums, and turns
+// the thread's chunk into the layer's input u.  Every thread of the block
+// takes part (a barrier).
+template <int NX>
+struct NormIn {
+  u32x4 q[NX];
+  float4 w0, w1;
+};
+template <int NX>
+__device__ __forceinline__ void issue_norm(const LayerLaunch &L, int t, int g0, int g1, int tid,
+                                           NormIn<NX> &n) {
+  const int nch = L.D / 8;
+  const gptr<u32x4> xr = as_global((const u32x4 *)((const uint16_t *)L.x + (size_t)t * L.D));
+#pragma unroll
+  for (int i = 0; i < NX; ++i) n.q[i] = xr[min(tid + i * kThreads, nch - 1)];
+  const int c = 8 * g0 + min(tid, (g1 - g0) * 8 - 1);
+  const float4 *w4 = (const float4 *)L.w_pre;
+  n.w0 = w4[2 * c];
+  n.w1 = w4[2 * c + 1];
+}
+template <bool F16X, int NX>
+__device__ __forceinline__ u32x4 finish_norm(const LayerLaunch &L, const NormIn<NX> &n, u32x4 xq,
+                                             float *red4) {
+  const int tid = threadIdx.x, nch = L.D / 8;
+  float p = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    if (tid + i * kThreads < nch) {
+      float v[8];
+      unpack8<F16X>(n.q[i], v);
+      p = sumsq8(v, p);
+    }
+  }
+  const float inv = norm_inv(row_sumsq_block(p, red4), L.D, L.eps);
+  return norm_chunk<F16X>(xq, inv, n.w0, n.w1);
+}
+
 // TWO: the streamed variant in two launches (router and shared blocks, then
 // the routed blocks); its router blocks also store the selection into host
-// memory and its routed blocks take each rank's blob from given_blob
-template <bool F16X, int M, int MAXC, bool TWO>
+// memory and its routed blocks take each rank's blob from given_blob.
+// NORM: the residual block fused around the layer (resident experts, one
+// launch): x is the residual stream, every role normalises it into the
+// layer's input, and the output rows get the post-norm and the residual.
+template <bool F16X, int M, int MAXC, bool TWO, bool NORM = false>
 __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L) {
   extern __shared__ __align__(16) uint8_t dsm[];
   __shared__ float red[kNW][2][64];
@@ -765,6 +917,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   __shared__ float s_gate[2][kMaxK];
   __shared__ SelectLds s_select;
   __shared__ uint2 s_xch[2][128];  // top-k exchange of the selecting waves
+  __shared__ float s_red4[kNW];    // the pre-norm's wave sums
+  constexpr int NX = MAXC == 3 ? 2 : 4;  // chunks of x per thread in the pre-norm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -801,9 +955,12 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     // ---------------- router rows and the selection of the token.  They
     // head the chain of dependent steps, so these blocks do nothing else.
     if (!given)
-      router_role<F16X, MAXC, TWO>(L, b, tag, dsm, s_select);
+      router_role<F16X, MAXC, TWO, 1, NORM>(L, b, tag, dsm, s_select, s_red4);
     else
       load_tag();
+    // the first router block of each token then does its post-norm
+    if constexpr (NORM)
+      if (b % nrb == 0) post_norm_poll<F16X, NX>(L, b / nrb, tag, s_red4);
   } else if (b >= L.NR) {
     // ---------------- shared expert: its gate/up tiles and its part of the
     // down projection; nothing waits on the routing
@@ -821,7 +978,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     const int u0 = ksd * Gs / L.KSds, u1 = (ksd + 1) * Gs / L.KSds;
 
     const uint8_t *sblob = (const uint8_t *)as_global(L.sblobs)[0];
-    const u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    NormIn<NX> nx;
+    if constexpr (NORM) issue_norm(L, gt.t, g0, g1, tid, nx);
     load_tag();
     if (L.shared_wait && !given) {
       // hold the weight loads until the router logits are out: the router's
@@ -845,6 +1004,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
         issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * dwc, u1 - 1), n);
     };
     if (L.down_late == 0) load_down();
+    if constexpr (NORM) xq = finish_norm<F16X>(L, nx, xq, s_red4);
     stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
     __syncthreads();
     if (has_g) {
@@ -869,8 +1029,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
         gate[i] = 1.0f;
         hp[i] = (size_t)T * k * L.F + (size_t)t_out * L.Fs + (size_t)u * 64;
       }
-      down_and_combine<M>(L, dr, hp, gate, use, hpl, red, ot, (size_t)t_out * D + n, wave, lane,
-                          tag);
+      down_and_combine<M, NORM>(L, dr, hp, gate, use, hpl, red, ot, (size_t)t_out * D + n, wave,
+                                lane, tag);
     }
   } else {
     // ---------------- routed blocks: gate/up tiles and the routed part of
@@ -889,8 +1049,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     const int Ur = k * Gf;
     const int u0 = ksd * Ur / L.KSdr, u1 = (ksd + 1) * Ur / L.KSdr;
 
-    const u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    u32x4 xq = issue_x(L, gt.t, g0, g1, tid);
+    NormIn<NX> nx;
+    if constexpr (NORM) issue_norm(L, gt.t, g0, g1, tid, nx);
     load_tag();
+    if constexpr (NORM) xq = finish_norm<F16X>(L, nx, xq, s_red4);
     const void **s_table = (const void **)(dsm + L.table_off);
     if (!given) {
       if constexpr (!TWO) {
@@ -972,8 +1135,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
         gate[i] = s_gate[ds][jj];
         hp[i] = (size_t)(t_out * k + jj) * L.F + (size_t)(u - jj * Gf) * 64;
       }
-      down_and_combine<M>(L, dr, hp, gate, use, hpl, red, ot, (size_t)t_out * D + n, wave, lane,
-                          tag);
+      down_and_combine<M, NORM>(L, dr, hp, gate, use, hpl, red, ot, (size_t)t_out * D + n, wave,
+                                lane, tag);
     }
   }
 
@@ -1234,7 +1397,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_stream_kernel(LayerLaunch 
 
 using KernelFn = void (*)(LayerLaunch);
 template <bool F16X, int MAXC>
-KernelFn pick(int m, bool stream, bool two) {
+KernelFn pick(int m, bool stream, bool two, bool norm) {
+  if (norm) {
+    if (stream || two) return nullptr;
+    if (m == 2) return decode_layer_kernel<F16X, 2, MAXC, false, true>;
+    if (m == 3) return decode_layer_kernel<F16X, 3, MAXC, false, true>;
+    if (m == 4) return decode_layer_kernel<F16X, 4, MAXC, false, true>;
+    return nullptr;
+  }
   if (stream) {
     if (m == 2) return decode_stream_kernel<F16X, 2, MAXC>;
     if (m == 3) return decode_stream_kernel<F16X, 3, MAXC>;
@@ -1254,14 +1424,14 @@ KernelFn pick(int m, bool stream, bool two) {
 }
 KernelFn pick_layer(const LayerLaunch &L, int m) {
   const bool small_d = L.D <= 3072;  // router chunks per thread: 3 (D <= 3072) or 8
-  const bool st = L.stream != 0, two = L.two != 0;
-  if (L.f16x) return small_d ? pick<true, 3>(m, st, two) : pick<true, 8>(m, st, two);
-  return small_d ? pick<false, 3>(m, st, two) : pick<false, 8>(m, st, two);
+  const bool st = L.stream != 0, two = L.two != 0, nm = L.w_pre != nullptr;
+  if (L.f16x) return small_d ? pick<true, 3>(m, st, two, nm) : pick<true, 8>(m, st, two, nm);
+  return small_d ? pick<false, 3>(m, st, two, nm) : pick<false, 8>(m, st, two, nm);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int g_layer_capacity[3][2][2][3][64];  // [resident, stream, two][f16x][MAXC 3/8][m - 2][device]
+int g_layer_capacity[4][2][2][3][64];  // [resident, stream, two, norm][f16x][MAXC 3/8][m - 2][device]
 
 }  // namespace
 
@@ -1309,7 +1479,8 @@ hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int &slot = g_layer_capacity[L.stream ? 1 : L.two ? 2 : 0][L.f16x ? 1 : 0][L.D <= 3072 ? 0 : 1]
+  int &slot = g_layer_capacity[L.stream ? 1 : L.two ? 2 : L.w_pre ? 3 : 0][L.f16x ? 1 : 0]
+                              [L.D <= 3072 ? 0 : 1]
                               [m - 2][dev];
   const size_t smem = layer_smem(L);
   if (smem > 64 * 1024) return hipSuccess;

@@ -301,15 +301,30 @@ moe_status layer_forward_args(const void *x, int x_dtype, int T, const moe_qmat 
 }
 
 Workspace carve_workspace(void *base, const Dims &d) { return carve(base, d); }
+
+void init_layer_launch(LayerLaunch *L, const void *x, int x_dtype, const Dims &d,
+                       const moe_qmat *router, const float *logit_bias, int k,
+                       const moe_bank *routed, const moe_bank *shared, moe_pool *pool, void *out,
+                       int out_dtype, int32_t *ids_out, float *gates_out) {
+  L->f16x = x_dtype == MOE_F16; L->T = d.T; L->k = k; L->E = d.E; L->D = d.D; L->F = d.F;
+  L->Fs = d.Fs;
+  L->x = x; L->rcodes = (const uint8_t *)router->codes; L->rmeta = (const uint32_t *)router->meta;
+  L->logit_bias = logit_bias; L->rblobs = pool ? nullptr : routed->blobs;
+  L->sblobs = shared ? shared->blobs : nullptr;
+  L->ids_out = ids_out; L->gates_out = gates_out; L->out = out; L->out_dtype = out_dtype;
+  L->two = pool != nullptr;  // streamed experts: the two-launch variant (its occupancy)
+}
 size_t workspace_bytes(const Dims &d) { return carve(nullptr, d).total; }
 
 // The residual block's buffers after the layer's workspace: the normalised
-// input u [T, D] 16-bit and the layer's output y [T, D] fp32.
+// input u [T, D] 16-bit, the layer's output y [T, D] fp32 (separate
+// kernels) and the one-launch path's tagged output words [min(T, 4), D].
 BlockTail block_tail(size_t layer_bytes, int T, int D) {
   BlockTail b;
   b.u_off = align_up(layer_bytes);
   b.y_off = align_up(b.u_off + (size_t)T * D * 2);
-  b.total = align_up(b.y_off + (size_t)T * D * 4);
+  b.yt_off = align_up(b.y_off + (size_t)T * D * 4);
+  b.total = align_up(b.yt_off + (size_t)min(T, kMaxLayerT) * D * 8);
   return b;
 }
 
@@ -398,6 +413,8 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_sel_stride = value;
   } else if (!strcmp(key, "layer_shared_wait")) {
     tuning().layer_shared_wait = value;
+  } else if (!strcmp(key, "block_fused")) {
+    tuning().block_fused = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
   } else if (!strcmp(key, "route_mfma")) {
@@ -491,12 +508,8 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
 
   // decode: router, selection, experts and combine in one launch
   LayerLaunch L{};
-  L.f16x = x_dtype == MOE_F16; L.T = T; L.k = k; L.E = E; L.D = D; L.F = F; L.Fs = Fs;
-  L.x = x; L.rcodes = (const uint8_t *)router->codes; L.rmeta = (const uint32_t *)router->meta;
-  L.logit_bias = logit_bias; L.rblobs = pool ? nullptr : routed->blobs;
-  L.sblobs = shared ? shared->blobs : nullptr;
-  L.ids_out = ids_out; L.gates_out = gates_out; L.out = out; L.out_dtype = out_dtype;
-  L.two = pool != nullptr;  // streamed experts: the two-launch variant (its occupancy)
+  init_layer_launch(&L, x, x_dtype, d, router, logit_bias, k, routed, shared, pool, out,
+                    out_dtype, ids_out, gates_out);
   // Streamed experts run the layer kernel in two launches with the slot plan
   // between them; only when every expert of the call is sure to fit the
   // slots, so that the plan cannot fail once the first launch has left its
@@ -686,7 +699,9 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const fl
                                      out_dtype, &d);
   if (st) return st;
   if (d.D > kBlockMaxD) return MOE_E_INVALID;
-  if (u_out && ((uintptr_t)u_out % 16)) return MOE_E_INVALID;
+  if ((u_out && ((uintptr_t)u_out % 16)) || (uintptr_t)out % 16 || (uintptr_t)w_pre % 16 ||
+      (uintptr_t)w_post % 16)
+    return MOE_E_INVALID;
   // out may be x itself (the residual stream updated in place: each element
   // is read, then written, by one thread) but no other overlap
   const size_t xb = (size_t)T * d.D * 2;
@@ -704,6 +719,20 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const fl
   float *y = (float *)((uint8_t *)ws + bt.y_off);
   hipStream_t s = (hipStream_t)stream;
   const int f16x = x_dtype == MOE_F16;
+  if (!pool && tuning().block_fused && tuning().layer) {
+    // one launch: the decode layer kernel normalises x in every role and
+    // adds the post-norm and the residual to each completed output row
+    LayerLaunch L{};
+    init_layer_launch(&L, x, x_dtype, d, router, logit_bias, k, routed, shared, nullptr, out,
+                      out_dtype, ids_out, gates_out);
+    L.w_pre = w_pre; L.w_post = w_post; L.eps = eps;
+    L.ybuf = (uint64_t *)((uint8_t *)ws + bt.yt_off); L.u_out = (uint16_t *)u_out;
+    Workspace w = carve(ws, d);
+    if (plan_layer(w, &L) && !L.stream) {
+      const int pi = prof_begin(s);
+      return hip_status(prof_end(pi, s, launch_layer(L, s)));
+    }
+  }
   if (launch_block_pre(x, f16x, T, d.D, w_pre, eps, u, s) != hipSuccess) return MOE_E_HIP;
   st = moe_layer_forward(u, x_dtype, T, router, logit_bias, k, routed, shared, pool, layer, y,
                          MOE_F32, ids_out, gates_out, ws, lb, stream);

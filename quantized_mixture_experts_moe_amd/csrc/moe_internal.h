@@ -102,6 +102,7 @@ struct Tuning {
   int layer_log_copies = 16;
   int layer_sel_copies = 16;
   int layer_sel_stride = 0;  // words between selection lines; 0: packed
+  int block_fused = 1;       // residual block: norms inside the one-launch decode layer
 };
 Tuning &tuning();
 
@@ -171,7 +172,7 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 // output y added to x.  D <= kBlockMaxD.
 constexpr int kBlockMaxD = 8192;
 struct BlockTail {
-  size_t u_off, y_off, total;
+  size_t u_off, y_off, yt_off, total;
 };
 BlockTail block_tail(size_t layer_bytes, int T, int D);
 hipError_t launch_block_pre(const void *x, int f16x, int T, int D, const float *w, float eps,
@@ -282,6 +283,16 @@ struct LayerLaunch {
   uint64_t *host_sel; uint32_t host_epoch;
   int two;                            // that variant of the kernel (set before planning)
   int dw4;                            // every wave of a block takes down units (16 per block)
+  // the residual block fused around the layer (w_pre non-null; one launch,
+  // resident experts): x is the residual stream, normalised (w_pre) by every
+  // role into the layer's input (also stored to u_out [T][D] if non-null);
+  // each output element goes to ybuf [T][D] as a tagged word, and each
+  // token's first router block polls its row and writes out = x + the
+  // post-norm (w_post) of it
+  const float *w_pre, *w_post;
+  float eps;
+  uint64_t *ybuf;
+  uint16_t *u_out;
 };
 int layer_m(const LayerLaunch &L);
 int layer_routed_blocks(const LayerLaunch &L);

@@ -82,7 +82,7 @@ CONFIGS: Dict[str, MoEConfig] = {
                          T=1, x_dtype="bf16", layers=30, tokens=256,
                          beta=BETA_STACK),
     "prefill": MoEConfig("prefill", D=2816, E=128, F=704, F_shared=2112, k=8,
-                         T=128, x_dtype="bf16", layers=1, chunks=8,
+                         T=128, x_dtype="bf16", layers=2, chunks=8,
                          beta=BETA_PREFILL),
     "streamed": MoEConfig("streamed", D=2816, E=128, F=704, F_shared=2112,
                           k=8, T=1, x_dtype="bf16", layers=30, tokens=256,

@@ -165,3 +165,37 @@ def test_block_forward_repeatable():
     a, _, _ = _block_gpu(L, xb, w_pre, w_post)
     b, _, _ = _block_gpu(L, xb, w_pre, w_post)
     assert torch.equal(a, b)
+
+
+def _set_fused(v):
+    moe.moe_set_tuning("block_fused", v)
+
+
+@pytest.mark.parametrize("name,T,in_place", [("decode", 1, False), ("decode", 1, True),
+                                             ("decode", 2, False), ("decode", 4, True),
+                                             ("tiny", 3, False), ("tiny", 4, True)])
+def test_block_fused_launch_equals_separate_kernels(name, T, in_place):
+    """The one-launch decode layer with both norms inside gives the same bits
+    as the three-step path (pre-norm kernel, layer, post-norm kernel): the
+    layer's input u, the ids and the block output, over repeated calls (the
+    per-token counters return to zero)."""
+    _case(f"block fused vs separate {name} T={T} in_place={in_place}")
+    L = dev_layer(name)
+    cfg = L.cfg
+    xb = gen.residual_stream(11, 0, T, T, cfg.D, cfg.x_dtype)
+    w_pre, w_post = gen.norm_weights(2, 0, cfg.D)
+    odt = TORCH_X[cfg.x_dtype] if in_place else torch.float32
+    try:
+        _set_fused(0)
+        ref, ref_u, ref_ids = _block_gpu(L, xb, w_pre, w_post, out_dtype=odt, in_place=in_place)
+        _set_fused(1)
+        for _ in range(3):
+            got, got_u, got_ids = _block_gpu(L, xb, w_pre, w_post, out_dtype=odt,
+                                             in_place=in_place)
+            assert np.array_equal(got_ids, ref_ids)
+            if not in_place:
+                assert np.array_equal(got_u, ref_u)
+            assert torch.equal(got.view(torch.int16) if odt != torch.float32 else got,
+                               ref.view(torch.int16) if odt != torch.float32 else ref)
+    finally:
+        _set_fused(1)
