@@ -238,6 +238,7 @@ struct PrefillLaunch {
   float *hsum, *y, *ys;                // ys: sks partial sums of the shared expert, [sks][T][D]
   int sks;                            // splits of the shared down projection over its hidden groups
   void *out; int out_dtype;
+  int max_items;                      // work-list entries the grids cover (set by the launcher)
 };
 constexpr int kMaxSharedSplits = 4;
 hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s);

@@ -50,6 +50,27 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRows = kPrefillRows;  // group rows per block (one or two 16-row tiles)
 static_assert(kRows == 32, "one or two 16-row tiles");
 
+// XCD-grouped block order.  Workgroups go to the 8 XCDs round robin (block b
+// to XCD b % 8), and each XCD has its own L2.  Blocks that read the same
+// weights (the row chunks of one weight slice) or the same activations (the
+// tiles of one work-list item) are given indices that are equal mod 8 and
+// close together, so the second reader finds the bytes in its XCD's L2
+// instead of fetching them again.  A part of the grid covers n_slices
+// slices of `per` blocks each: slice i lives on one XCD, slices alternate
+// over the XCDs in a serpentine (0..7, 7..0, ...) so that a list sorted
+// longest first spreads evenly.  Its block count is a multiple of 8, so the
+// next part keeps the same XCD for the same index mod 8.
+constexpr int kXcd = 8;
+__host__ __device__ inline int grouped_blocks(int n_slices, int per) {
+  return (n_slices + kXcd - 1) / kXcd * kXcd * per;
+}
+// block r of the part -> (slice, sub-block); slice may be >= n_slices (padding)
+__device__ __forceinline__ void grouped_index(int r, int per, int *slice, int *sub) {
+  const int x = r % kXcd, q = r / kXcd, i = q / per;
+  *sub = q - i * per;
+  *slice = i * kXcd + ((i & 1) ? kXcd - 1 - x : x);
+}
+
 template <bool F16>
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   if constexpr (F16)
@@ -276,17 +297,20 @@ __global__ __launch_bounds__(256, 4) void glu_mfma_kernel(PrefillLaunch p) {
   // past the list's end return at once
   const int NT = p.F / 64, NTs = p.sblobs ? p.Fs / 64 : 0;
   const int mch = (p.T + kRows - 1) / kRows;
-  const int bid = blockIdx.x;
+  const int bid = blockIdx.x, nsh = NTs ? grouped_blocks(NTs, mch) : 0;
   int g_idx, nt, yc;
   Group rg{};
-  if (bid < NTs * mch) {
+  if (bid < nsh) {
+    // the shared expert: hidden tile nt's row chunks on one XCD
     g_idx = p.E;
-    yc = bid / NTs;
-    nt = bid - yc * NTs;
+    grouped_index(bid, mch, &nt, &yc);
+    if (nt >= NTs) return;
   } else {
     g_idx = -1;
-    const int r = bid - NTs * mch, item = r / NT;
-    nt = r - item * NT;
+    // a work-list item's hidden tiles on one XCD
+    int item;
+    grouped_index(bid - nsh, NT, &item, &nt);
+    if (item >= p.max_items) return;
     // the item, its expert's count, offset and blob, and the list's length
     // in one round trip (every index here is inside the arrays)
     const int n_it = *p.n_items, it = p.items[item];
@@ -436,20 +460,27 @@ __global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
   // items x their two 16-row halves x 256 output rows (the second half of
   // an item with 16 rows or fewer returns at once)
   const int D = p.D, NB = (D + 255) / 256;
-  const int mch = (p.T + kDRows - 1) / kDRows, nsh = p.sblobs ? p.sks * mch * NB : 0;
+  const int mch = (p.T + kDRows - 1) / kDRows;
+  const int nsh = p.sblobs ? grouped_blocks(p.sks * NB, mch) : 0;
   const int bid = blockIdx.x;
   int g_idx, nb, yc, ks = 0;
   Group rg{};
   if (bid < nsh) {
+    // the shared expert: the row chunks of weight slice (ks, nb) on one XCD
     g_idx = p.E;
-    ks = bid / (mch * NB);
-    const int r = bid - ks * (mch * NB);
-    yc = r / NB;
-    nb = r - yc * NB;
+    int w;
+    grouped_index(bid, mch, &w, &yc);
+    if (w >= p.sks * NB) return;
+    ks = w / NB;
+    nb = w - ks * NB;
   } else {
     g_idx = -1;
-    const int r = bid - nsh, item = r / (2 * NB);
-    const int rr = r - item * 2 * NB, half = rr / NB;
+    // a work-list item's halves and output tiles on one XCD (the halves
+    // read the same weights, the tiles the same hidden values)
+    int item, rr;
+    grouped_index(bid - nsh, 2 * NB, &item, &rr);
+    if (item >= p.max_items) return;
+    const int half = rr / NB;
     nb = rr - half * NB;
     // the item, its expert's count, offset and blob, and the list's length
     // in one round trip (every index here is inside the arrays)
@@ -555,24 +586,27 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   const int mchunks = (p.T + kRows - 1) / kRows;
   // routed blocks: the work list has at most one partial chunk per expert
   const int max_items = std::min(p.E * mchunks, p.E + (p.T * p.k + kRows - 1) / kRows);
-  dim3 g1(max_items * (p.F / 64) + (p.sblobs ? (p.Fs / 64) * mchunks : 0));
+  PrefillLaunch q = p;
+  q.max_items = max_items;
+  dim3 g1(grouped_blocks(max_items, p.F / 64) +
+          (p.sblobs ? grouped_blocks(p.Fs / 64, mchunks) : 0));
   const size_t smem = sizeof(float) * kRows * (p.D / 64);
   if (p.f16x)
-    hipLaunchKernelGGL(glu_mfma_kernel<true>, g1, dim3(256), smem, s, p);
+    hipLaunchKernelGGL(glu_mfma_kernel<true>, g1, dim3(256), smem, s, q);
   else
-    hipLaunchKernelGGL(glu_mfma_kernel<false>, g1, dim3(256), smem, s, p);
+    hipLaunchKernelGGL(glu_mfma_kernel<false>, g1, dim3(256), smem, s, q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb4 = (p.D + 255) / 256;  // 256 output rows per down block
   const int mch16 = (p.T + 15) / 16;  // 16-row chunks of the shared expert
-  dim3 g2(2 * max_items * nb4 + (p.sblobs ? p.sks * nb4 * mch16 : 0));
-  hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, p);
+  dim3 g2(grouped_blocks(max_items, 2 * nb4) + (p.sblobs ? grouped_blocks(p.sks * nb4, mch16) : 0));
+  hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t total = (size_t)p.T * p.D / 4;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(combine_prefill_kernel<8>, dim3(blocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(combine_prefill_kernel<8>, dim3(blocks), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 
