@@ -102,12 +102,17 @@ size_t moe_blob_bytes(int32_t D, int32_t F);
 size_t moe_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t D, int32_t F,
                            int32_t F_shared);
 
-/* Number of bounded device-side waits that timed out in calls on `ws` since
- * it was last zero-filled.  The one-launch kernels hand data between blocks
- * that must all be resident; a wait that gives up (after about a second)
- * counts here and lets the kernel finish with undefined results instead of
- * hanging.  A nonzero count means the outputs of those calls are undefined
- * and the workspace must be zero-filled again before further use.
+/* Number of device-side errors in calls on `ws` since it was last
+ * zero-filled: bounded waits that timed out, and partial sums outside the
+ * range of the fixed-point split reductions.  The one-launch kernels hand
+ * data between blocks that must all be resident; a wait that gives up (after
+ * about a second) counts here and lets the kernel finish with undefined
+ * results instead of hanging.  The split reductions add partials as 64-bit
+ * fixed-point integers (sums below 2^27 in magnitude in the decode layer
+ * kernel, 2^31 in the expert phase); a partial that could take a sum out of
+ * that range, or is not finite, counts here too.  A nonzero count means the
+ * outputs of those calls are undefined and the workspace must be zero-filled
+ * again before further use.
  *   ws      device workspace (as passed to the other calls), ws_bytes its size
  *   count   host; receives the count
  * Blocks the host: the word is copied after the work queued on `stream`. */
@@ -130,7 +135,11 @@ moe_status moe_route(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *
                      const float *logit_bias, int32_t k, int32_t *ids, float *gates,
                      float *logits, void *ws, size_t ws_bytes, void *stream);
 
-/* Expert FFN of every (token, slot) pair: y[t, j, :] = FFN_{ids[t,j]}(x[t]).
+/* Expert FFN of every (token, slot) pair: y[t, j, :] = FFN_{ids[t,j]}(x[t]),
+ * the selected experts' FFNs of the pages (es.news.hada.io, "Proceso de
+ * generacion de tokens"), stored as MLX-style 4-bit affine weights in groups
+ * of 64 (es.news.hada.io, "Estructura de ejecucion para reducir memoria"):
+ * gate and up dequantised and applied to x, gelu_tanh(gate) * up, then down.
  *   bank      experts of shape (D, F); D, F multiples of 64
  *   ids       device [T, k] int32 in [0, E), or NULL: every row uses expert 0
  *             and k must be 1 (the shared expert)
@@ -328,17 +337,14 @@ moe_status moe_set_profile_events(void *const *events, int32_t n_pairs);
  * key or value.  Process-wide.  Every setting gives results within the same
  * parity bounds; the defaults are the measured fastest.  Keys (default):
  *   layer (1)            decode of up to 4 tokens in one launch of the layer
- *                        kernel; 2: its whole-tile variant; 0: off
+ *                        kernel; 0: off
  *   layer_ksg, layer_ksd (0)  its gate/up and down splits; 0: the widest
  *                        whose grid stays resident
  *   layer_order (1)      dispatch the shared expert's blocks before the routed
- *   layer_select (0)     1: the routed blocks rank the logits themselves
- *   layer_direct_h (0)   down waves poll the hidden values (1), two rounds
- *                        in flight (2), or a hint word first (0)
- *   layer_down_late (1)  down weights requested after the gate/up reduction
- *                        (1), with the gate/up weights (0), after its
- *                        arithmetic (2)
- *   layer_shared_wait (0)  shared blocks wait for the router's logits
+ *   layer_select (1)     the routed blocks rank the logits themselves; 0: the
+ *                        router blocks rank and publish the selection
+ *   block_fused (1)      moe_block_forward: both norms inside the one-launch
+ *                        layer kernel; 0: separate row kernels
  *   layer_sel_copies (16), layer_log_copies (16), layer_sel_stride (0)
  *                        copies and spacing of the published selection
  *   fused (1)            the one-launch expert phase when the layer kernel

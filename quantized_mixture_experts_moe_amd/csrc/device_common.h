@@ -227,7 +227,7 @@ __device__ __forceinline__ float dot_group_f32(const u32x4 q0, const u32x4 q1, c
 // counter; the split that arrives last reads the sums into out[] (returns
 // true) and puts the accumulators and the counter back to zero, so they are
 // zero between calls.  The rounding is 2^-33 per partial; sums must stay
-// below 2^31 in magnitude.
+// below 2^31 in magnitude, and a partial that could break that bumps *err.
 __device__ __forceinline__ long long to_fixed32(float v) {
   return __double2ll_rn((double)v * 4294967296.0);
 }
@@ -236,8 +236,15 @@ __device__ __forceinline__ float from_fixed32(long long a) {
 }
 template <int R>
 __device__ __forceinline__ bool split_reduce_fixed(uint64_t *acc, uint32_t *counter, int nsplits,
-                                                   const float (&v)[R], float (&out)[R]) {
+                                                   const float (&v)[R], float (&out)[R],
+                                                   uint32_t *err) {
   const int lane = threadIdx.x & 63;
+  // a partial outside |v| < 2^31 / nsplits (or not finite) could wrap the
+  // sum: counted as an error of the call
+  bool range_ok = true;
+#pragma unroll
+  for (int r = 0; r < R; ++r) range_ok = range_ok && fabsf(v[r]) * (float)nsplits < 2147483648.0f;
+  if (!range_ok) add_dev(err, 1u);
 #pragma unroll
   for (int r = 0; r < R; ++r)
     __hip_atomic_fetch_add(acc + r * 64 + lane, (uint64_t)to_fixed32(v[r]), __ATOMIC_RELAXED,

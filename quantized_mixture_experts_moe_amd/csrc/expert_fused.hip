@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
         const float pv[2] = {v0, v1};
         float sv[2];
         last = split_reduce_fixed<2>(f.gacc + (size_t)tile * 128, f.gcnt + (size_t)tile * kCntStride,
-                                     f.KSg, pv, sv);
+                                     f.KSg, pv, sv, f.err);
         v0 = sv[0];
         v1 = sv[1];
       }
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kNW * 64) void experts_fused_kernel(FusedLaunch f) 
         const float pv[1] = {s};
         float sv[1];
         last = split_reduce_fixed<1>(f.dacc + (size_t)ot * 64, f.dcnt + (size_t)ot * kCntStride,
-                                     f.KSd, pv, sv);
+                                     f.KSd, pv, sv, f.err);
         s = sv[0];
       }
       if (last) {

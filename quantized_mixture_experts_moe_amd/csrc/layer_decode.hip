@@ -7,17 +7,18 @@
 // and add the two outputs (es.news.hada.io, "Proceso de generacion de
 // tokens"; yodev.dev, "Por que funciona: el A4B del nombre").  Routing is a
 // short chain of dependent steps; the shared expert does not depend on it.
-// So the grid has two groups of blocks:
-//   router blocks: the router rows (8 experts per block) and the selection;
+// So the grid has three groups of blocks:
+//   router blocks: the router rows (4 experts per block).  They publish their
+//     logits; by default every routed block then ranks all of a token's
+//     logits itself (layer_select 1), else wave 0 of every router block
+//     ranks its own candidates against all logits and publishes the
+//     selection lines (layer_select 0, and the streamed two-launch variant);
 //   routed blocks: the routed gate/up tiles and the routed part of the down
 //     projection.  They issue no weight loads before the selection arrives,
 //     so their polls are not queued behind outstanding loads (a wave's loads
-//     complete in order).
+//     complete in order);
 //   shared blocks: the shared expert's gate/up tiles and its part of the down
 //     projection; they stream from the first cycle, while routing runs.
-// Every router block of a token, once all logits of the token are published,
-// selects the experts (block-wide rank) and publishes ids and gates in its
-// own copy; each routed block polls one copy.
 //
 // Handoffs between blocks are tagged words: a 64-bit store of (value, tag)
 // with device scope, where the tag is the call's epoch.  A reader loads until
@@ -31,7 +32,7 @@
 // every wait is bounded and a timeout bumps an error counter.
 //
 // Work split (one token, k = 8, D = 2816, F = 704, F_s = 2112):
-//   router:  16 blocks of 8 experts (they do nothing else);
+//   router:  32 blocks of 4 experts;
 //   gate/up: 88 routed + 33 shared tiles of 64 hidden rows x KSg reduction
 //            splits over the 44 column groups;
 //   down:    44 tiles of 64 output rows x (KSdr splits of the 88 routed units
@@ -120,8 +121,12 @@ __device__ __forceinline__ int wait_hint(const uint64_t *p, bool active, uint32_
 // returned word tells each lane whether its add completed the n partials;
 // that lane alone gets the sum (integer addition: the same for any arrival
 // order) and puts the word back to zero for the next call.  Sums must stay
-// below 2^27 in magnitude.
-__device__ __forceinline__ bool counted_add(uint64_t *word, float v, int n, float *sum) {
+// below 2^27 in magnitude; a partial that could break that counts in *err.
+__device__ __forceinline__ bool counted_add(uint64_t *word, float v, int n, float *sum,
+                                            uint32_t *err) {
+  // a partial outside |v| < 2^27 / n (or not finite) could wrap the sum:
+  // counted as an error of the call
+  if (!(fabsf(v) * (float)n < 134217728.0f)) add_dev(err, 1u);
   const uint64_t add = ((uint64_t)__double2ll_rn((double)v * 268435456.0) << 8) + 1u;
   const uint64_t old =
       __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -487,24 +492,14 @@ __device__ __forceinline__ void glu_publish(const LayerLaunch &L, float (&red)[k
     }
     float g = v0, u = v1;
     const bool last_g =
-        L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + lane, v0, L.KSg, &g);
+        L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + lane, v0, L.KSg, &g, L.err);
     const bool last_u =
-        L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + 64 + lane, v1, L.KSg, &u);
+        L.KSg == 1 || counted_add(L.gacc + (size_t)tile * 128 + 64 + lane, v1, L.KSg, &u, L.err);
     if (last_g) st_dev64(L.hg + ho + lane, tagged(__float_as_uint(gelu_tanh(g)), tag));
     if (last_u) st_dev64(L.hu + ho + lane, tagged(__float_as_uint(u), tag));
   }
 }
 
-// Down projection of output row n over this wave's units, then the split
-// reduction over the blocks of the output tile, which writes the output.
-// unit i: hidden rows hp[i] .. hp[i] + 63 (tagged words), weight gate[i].
-struct NoHook {
-  __device__ void operator()() const {}
-};
-
-// With L.hu null the hidden activations are single tagged words h in L.hg
-// (gelu(gate) * up, finished by one block); otherwise gelu(gate) in L.hg and
-// up in L.hu.  on_hint runs once the units' first words are seen.
 // The residual block's post-norm of token t, by the token's first router
 // block once its routing is done: it polls the layer's output row y (tagged
 // words, stored by the lanes that complete each element) until every element
@@ -577,46 +572,35 @@ __device__ __forceinline__ void post_norm_poll(const LayerLaunch &L, int t, uint
   }
 }
 
-template <int M, bool NORM = false, class OnHint = NoHook>
+// Down projection of output row n over this wave's units, then the split
+// reduction over the blocks of the output tile, which writes the output (or,
+// NORM, the tagged word the post-norm polls).  Unit i: hidden rows hp[i] ..
+// hp[i] + 63, gelu(gate) in L.hg and up in L.hu (tagged words), weight
+// gate[i].
+template <int M, bool NORM = false>
 __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const DownRegs<M> &R,
                                                  const size_t (&hp)[M], const float (&gate)[M],
                                                  const bool (&use)[M], uint32_t (&hpl)[kNW][M][3][32],
                                                  float (&red)[kNW][2][64], int ot, size_t out_idx,
-                                                 int wave, int lane, uint32_t tag,
-                                                 OnHint on_hint = OnHint()) {
-  // lanes 2i, 2i + 1 poll one word of unit i's rows, then the values are
-  // read (checked)
-  const bool single = L.hu == nullptr;
+                                                 int wave, int lane, uint32_t tag) {
+  // lanes 2i, 2i + 1 poll one word of unit i's rows (the hint), then the
+  // values are read (and checked).  Units a wave does not use are loaded too
+  // (valid rows) and not checked.
   const uint64_t *hint = L.hg + hp[0];
   bool active = false;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     if (use[i] && lane == 2 * i) hint = L.hg + hp[i], active = true;
-    if (use[i] && lane == 2 * i + 1 && !single) hint = L.hu + hp[i], active = true;
+    if (use[i] && lane == 2 * i + 1) hint = L.hu + hp[i], active = true;
   }
-  if (L.direct_h != 1) wait_hint(hint, active, tag, L.err);
-  on_hint();
-  // the values: with a hint first (direct_h 0, 2) or polled directly
-  // (direct_h 1); direct_h 2 keeps two rounds of loads in flight (see
-  // wait_hint).  Units a wave does not use are loaded too (valid rows) and
-  // not checked.
-  const uint64_t *hu = single ? L.hg : L.hu;
+  wait_hint(hint, active, tag, L.err);
   uint64_t wg[M], wu[M];
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     wg[i] = ld_dev64(L.hg + hp[i] + lane);
-    wu[i] = ld_dev64(hu + hp[i] + lane);
+    wu[i] = ld_dev64(L.hu + hp[i] + lane);
   }
   for (long s = 0;; ++s) {
-    uint64_t ng[M], nu[M];
-    if (L.direct_h == 2) {
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int i = 0; i < M; ++i) {
-        ng[i] = ld_dev64(L.hg + hp[i] + lane);
-        nu[i] = ld_dev64(hu + hp[i] + lane);
-      }
-    }
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < M; ++i) ok = ok && (!use[i] || (has_tag(wg[i], tag) && has_tag(wu[i], tag)));
@@ -625,27 +609,17 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
       if (lane == 0) add_dev(L.err, 1u);
       break;
     }
-    if (L.direct_h == 2) {
+    __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-      for (int i = 0; i < M; ++i) {
-        wg[i] = ng[i];
-        wu[i] = nu[i];
-      }
-    } else {
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int i = 0; i < M; ++i) {
-        wg[i] = ld_dev64(L.hg + hp[i] + lane);
-        wu[i] = ld_dev64(hu + hp[i] + lane);
-      }
+    for (int i = 0; i < M; ++i) {
+      wg[i] = ld_dev64(L.hg + hp[i] + lane);
+      wu[i] = ld_dev64(L.hu + hp[i] + lane);
     }
   }
   float hv0[M];
 #pragma unroll
   for (int i = 0; i < M; ++i)
-    hv0[i] = use[i] ? __uint_as_float((uint32_t)wg[i]) *
-                          (single ? 1.0f : __uint_as_float((uint32_t)wu[i]))
-                    : 0.0f;
+    hv0[i] = use[i] ? __uint_as_float((uint32_t)wg[i]) * __uint_as_float((uint32_t)wu[i]) : 0.0f;
   // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
   // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
   float hsum[M];
@@ -705,7 +679,7 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
 #pragma unroll
     for (int w = 0; w < kNW; ++w) s += red[w][0][lane];
     const int nsp = L.KSdr + L.KSds;
-    const bool done = nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s);
+    const bool done = nsp == 1 || counted_add(L.dacc + (size_t)ot * 64 + lane, s, nsp, &s, L.err);
     if constexpr (!NORM) {
       if (done) {
         if (L.out_dtype == MOE_F32)
@@ -940,9 +914,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   auto load_tag = [&]() {
     tag = __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
   };
-  // selection from the caller (blob addresses by rank alone: the selection
-  // lines still give the ids and gates)
-  const bool given = !TWO && L.given_blob != nullptr;
   const int n_rt = T * k * Gf;                 // routed gate/up tiles, then the shared ones
   // down units: waves 1..3 (wave 0 mirrors wave 1 and does the gate/up
   // reduction's atomics), or all four waves (dw4: more units per block, for
@@ -954,10 +925,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
   if (b < T * nrb) {
     // ---------------- router rows and the selection of the token.  They
     // head the chain of dependent steps, so these blocks do nothing else.
-    if (!given)
-      router_role<F16X, MAXC, TWO, 1, NORM>(L, b, tag, dsm, s_select, s_red4);
-    else
-      load_tag();
+    router_role<F16X, MAXC, TWO, 1, NORM>(L, b, tag, dsm, s_select, s_red4);
     // the first router block of each token then does its post-norm
     if constexpr (NORM)
       if (b % nrb == 0) post_norm_poll<F16X, NX>(L, b / nrb, tag, s_red4);
@@ -982,19 +950,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     NormIn<NX> nx;
     if constexpr (NORM) issue_norm(L, gt.t, g0, g1, tid, nx);
     load_tag();
-    if (L.shared_wait && !given) {
-      // hold the weight loads until the router logits are out: the router's
-      // loads head the chain of dependent steps
-      if (wave == 0) {
-        for (int base = 0; base < T * nrb; base += 64) {
-          const int q = base + lane;
-          const int qq = min(q, T * nrb - 1);
-          wait_hint(L.rlog + (size_t)(qq / nrb) * E + (size_t)(qq % nrb) * kRows, q < T * nrb, tag,
-                    L.err);
-        }
-      }
-      __syncthreads();
-    }
     GluRegs<M> gr;
     issue_glu(gr, sblob, D, L.Fs, gt.rb, g0, g1, wave, lane);
     DownRegs<M> dr;
@@ -1003,7 +958,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       for (int i = 0; i < M; ++i)
         issue_down(dr, i, sblob, D, L.Fs, min(u0 + dw + i * dwc, u1 - 1), n);
     };
-    if (L.down_late == 0) load_down();
     if constexpr (NORM) xq = finish_norm<F16X>(L, nx, xq, s_red4);
     stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
     __syncthreads();
@@ -1013,11 +967,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
       red[wave][0][lane] = accg;
       red[wave][1][lane] = accu;
     }
-    // down weights of waves 1..3 once their gate/up data is in (2) or after
-    // the split reduction (1); wave 0 does the reduction's atomics
-    if (L.down_late == 2 && dwave) load_down();
+    // down weights of waves 1..3 after the split reduction (requested with
+    // the gate/up weights they would queue in front of them); wave 0 does
+    // the reduction's atomics
     if (has_g) glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, wave, lane, tag);
-    if (L.down_late == 1 && dwave) load_down();
+    if (dwave) load_down();
     if (has_d) {
       size_t hp[M];
       float gate[M];
@@ -1055,46 +1009,36 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     load_tag();
     if constexpr (NORM) xq = finish_norm<F16X>(L, nx, xq, s_red4);
     const void **s_table = (const void **)(dsm + L.table_off);
-    if (!given) {
-      if constexpr (!TWO) {
-        constexpr int kTab = kMaxLayerE / kThreads;
-        const void *tb[kTab];
+    if constexpr (!TWO) {
+      constexpr int kTab = kMaxLayerE / kThreads;
+      const void *tb[kTab];
 #pragma unroll
-        for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
-        stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
+      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
+      stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
 #pragma unroll
-        for (int i = 0; i < kTab; ++i)
-          if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
-      } else {
-        stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
-      }
-      __syncthreads();
-      const int copy = sb % L.sel_copies;
-      // the first block of each token's first gate/up tile reports the selection
-      const bool report = has_g && gt.j == 0 && gt.rb == 0 && ks == 0;
-      if (!TWO && L.select == 1) {
-        const int lc = sb % L.log_copies;
-        if (wave == 0)
-          select_from_logits(L, gt.t, lc, tag, s_table, s_blob[0], s_gate[0], report, s_xch[0]);
-        if (wave == 1 && t_out != gt.t)
-          select_from_logits(L, t_out, lc, tag, s_table, s_blob[1], s_gate[1], false, s_xch[1]);
-      } else {
-        // the blob table: by expert id, or (two launches) by rank per token
-        const void *const *t0 = TWO ? L.given_blob + (size_t)gt.t * k : s_table;
-        const void *const *t1 = TWO ? L.given_blob + (size_t)t_out * k : s_table;
-        if (wave == 0)
-          wait_selection<TWO>(L, gt.t, copy, tag, t0, s_blob[0], s_gate[0], report);
-        if (wave == 1 && t_out != gt.t)
-          wait_selection<TWO>(L, t_out, copy, tag, t1, s_blob[1], s_gate[1], false);
-      }
+      for (int i = 0; i < kTab; ++i)
+        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
     } else {
       stage_x<F16X>(xq, (g1 - g0) * 8, tid, s_xp, s_xs);
-      if (tid < k) {  // written by earlier work on the stream: plain loads
-        s_blob[0][tid] = (const uint8_t *)L.given_blob[(size_t)gt.t * k + tid];
-        s_gate[0][tid] = L.given_gates[(size_t)gt.t * k + tid];
-        s_blob[1][tid] = (const uint8_t *)L.given_blob[(size_t)t_out * k + tid];
-        s_gate[1][tid] = L.given_gates[(size_t)t_out * k + tid];
-      }
+    }
+    __syncthreads();
+    const int copy = sb % L.sel_copies;
+    // the first block of each token's first gate/up tile reports the selection
+    const bool report = has_g && gt.j == 0 && gt.rb == 0 && ks == 0;
+    if (!TWO && L.select == 1) {
+      const int lc = sb % L.log_copies;
+      if (wave == 0)
+        select_from_logits(L, gt.t, lc, tag, s_table, s_blob[0], s_gate[0], report, s_xch[0]);
+      if (wave == 1 && t_out != gt.t)
+        select_from_logits(L, t_out, lc, tag, s_table, s_blob[1], s_gate[1], false, s_xch[1]);
+    } else {
+      // the blob table: by expert id, or (two launches) by rank per token
+      const void *const *t0 = TWO ? L.given_blob + (size_t)gt.t * k : s_table;
+      const void *const *t1 = TWO ? L.given_blob + (size_t)t_out * k : s_table;
+      if (wave == 0)
+        wait_selection<TWO>(L, gt.t, copy, tag, t0, s_blob[0], s_gate[0], report);
+      if (wave == 1 && t_out != gt.t)
+        wait_selection<TWO>(L, t_out, copy, tag, t1, s_blob[1], s_gate[1], false);
     }
     __syncthreads();
     const int ds = t_out == gt.t ? 0 : 1;  // selection of the down token
@@ -1111,18 +1055,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
         issue_down(dr, i, s_blob[ds][jj], D, L.F, u - jj * Gf, n);
       }
     };
-    if (L.down_late == 0) load_down();
     if (has_g) {
       float accg, accu;
       glu_dots<F16X, M>(gr, s_xp, s_xs, g0, g1, wave, lane, accg, accu);
       red[wave][0][lane] = accg;
       red[wave][1][lane] = accu;
     }
-    // down weights of waves 1..3 once their gate/up data is in (2) or after
-    // the split reduction (1); wave 0 does the reduction's atomics
-    if (L.down_late == 2 && dwave) load_down();
+    // down weights of waves 1..3 after the split reduction (requested with
+    // the gate/up weights they would queue in front of them); wave 0 does
+    // the reduction's atomics
     if (has_g) glu_publish(L, red, tile, gt.hoff + (size_t)gt.rb * 64, wave, lane, tag);
-    if (L.down_late == 1 && dwave) load_down();
+    if (dwave) load_down();
     if (has_d) {
       size_t hp[M];
       float gate[M];
@@ -1145,270 +1088,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     for (int j = b; j < kMaxLayerGrid; j += L.grid_full) st_dev(L.bep + j, tag);
 }
 
-// ---------------------------------------------------------------- one token, full-K gate/up blocks
-//
-// The variant for one token.  Each gate/up block owns a whole hidden tile
-// (64 rows of one selected expert or of the shared expert, all column
-// groups), so it finishes h = gelu(gate) * up itself: no split reduction
-// and no hand-off of partial sums.  Its waves stream groups wave, wave + 4,
-// ... through a register ring (kRs groups per wave, the next kRs - 1 in
-// flight), which bounds the bytes in flight per block instead of requesting
-// everything at once: a queue of tens of megabytes in front of the memory
-// controllers would delay every hand-off behind it.
-//   router blocks [0, nR);  routed gate/up [nR, nR + n_rt);  routed down
-//   splits [.., NR);  shared gate/up [NR, NR + n_st);  shared down splits.
-constexpr int kRs = 4;
-
-struct GluStage {
-  u32x4 g0, g1, u0, u1;
-  uint32_t mg, mu;
-};
-
-// full-K gate/up of hidden rows rb * 64 + lane of `blob` (hidden width F);
-// the activation pairs and 64-column sums of all groups are in s_xp, s_xs.
-// NG > 0: exactly NG groups per wave, straight-line code (the waits then
-// cover exactly the group each step needs); NG = 0: any count, a loop.
-template <bool F16X, int NG>
-__device__ __forceinline__ void glu_full(const LayerLaunch &L, const uint8_t *blob, int F, int rb,
-                                         size_t hrow, const uint32_t *s_xp, const float *s_xs,
-                                         float (&red)[kNW][2][64], int wave, int lane,
-                                         uint32_t tag) {
-  const int D = L.D, G = D / 64;
-  const int j = rb * 64 + lane;
-  const BlobLayout BL = blob_layout(D, F);
-  const gptr<u32x4> gc = as_global((const u32x4 *)(blob + BL.gate_codes) + j);
-  const gptr<u32x4> uc = as_global((const u32x4 *)(blob + BL.up_codes) + j);
-  const gptr<uint32_t> gm = as_global((const uint32_t *)(blob + BL.gate_meta) + j);
-  const gptr<uint32_t> um = as_global((const uint32_t *)(blob + BL.up_meta) + j);
-  const int ng = NG > 0 ? NG : (G - wave + kNW - 1) / kNW;  // groups wave, wave + 4, ...
-  auto issue = [&](GluStage &S, int i) {
-    const int g = wave + kNW * min(i, ng - 1);  // past the end: repeat, weight 0
-    const size_t c0 = (size_t)(2 * g) * F;
-    S.g0 = gc[c0];
-    S.g1 = gc[c0 + F];
-    S.u0 = uc[c0];
-    S.u1 = uc[c0 + F];
-    S.mg = gm[(size_t)g * F];
-    S.mu = um[(size_t)g * F];
-  };
-  const bool xa_lane = (lane & 15) == 4 * (lane >> 4);
-  const uint32_t magic = opaque_vgpr(Magic<F16X>::bits);
-  float accg = 0.0f, accu = 0.0f;
-  GluStage ring[kRs];
-#pragma unroll
-  for (int s = 0; s < kRs - 1; ++s) issue(ring[s], s);
-  constexpr int kRounds = NG > 0 ? (NG + kRs - 1) / kRs : 1;
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-  for (int i0 = r * kRs; i0 < (NG > 0 ? (r + 1) * kRs : ng); i0 += kRs) {
-#pragma unroll
-    for (int s = 0; s < kRs; ++s) {
-      const int i = i0 + s;
-      if (NG > 0 && i >= NG) break;  // straight-line form: no steps past the last group
-      if (NG == 0 || i + kRs - 1 < NG) issue(ring[(s + kRs - 1) % kRs], i + kRs - 1);
-      const GluStage &S = ring[s];
-      const bool live = i < ng;
-      const int g = wave + kNW * min(i, ng - 1);
-      f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f}, du = {0.0f, 0.0f, 0.0f, 0.0f};
-      const uint32_t wg[8] = {S.g0.x, S.g0.y, S.g0.z, S.g0.w, S.g1.x, S.g1.y, S.g1.z, S.g1.w};
-      const uint32_t wu[8] = {S.u0.x, S.u0.y, S.u0.z, S.u0.w, S.u1.x, S.u1.y, S.u1.z, S.u1.w};
-      u32x4 a[8];
-#pragma unroll
-      for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
-      if (xa_lane) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&s_xp[32 * g + 4 * w];
-      }
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        dg = mma16<F16X>(a[w], code_pairs(wg[w], magic), dg);
-        du = mma16<F16X>(a[w], code_pairs(wu[w], magic), du);
-      }
-      const float xsg = s_xs[g];
-      const float sg = live ? f16_to_f32(S.mg) : 0.0f, bg = live ? f16_to_f32(S.mg >> 16) : 0.0f;
-      const float su = live ? f16_to_f32(S.mu) : 0.0f, bu = live ? f16_to_f32(S.mu >> 16) : 0.0f;
-      accg = fmaf(sg, dg[0], accg);
-      accg = fmaf(fmaf(-Magic<F16X>::offset, sg, bg), xsg, accg);
-      accu = fmaf(su, du[0], accu);
-      accu = fmaf(fmaf(-Magic<F16X>::offset, su, bu), xsg, accu);
-    }
-  }
-  red[wave][0][lane] = accg;
-  red[wave][1][lane] = accu;
-  __syncthreads();
-  if (wave == 0) {
-    float g = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      g += red[w][0][lane];
-      u += red[w][1][lane];
-    }
-    st_dev64(L.hg + hrow + lane, tagged(__float_as_uint(gelu_tanh(g) * u), tag));
-  }
-}
-
-// activation pairs (x[8w + m], x[8w + m + 4]) and 64-column sums of all
-// column groups of token t into s_xp [G][32], s_xs [G]
-template <bool F16X>
-__device__ __forceinline__ void stage_x_all(const LayerLaunch &L, int t, uint32_t *s_xp,
-                                            float *s_xs) {
-  const int tid = threadIdx.x, D = L.D;
-  constexpr int kMaxXV = 8192 / 8 / kThreads;  // 16-byte pieces of x per thread
-  const gptr<u32x4> xr = as_global((const u32x4 *)((const uint16_t *)L.x + (size_t)t * D));
-  u32x4 xq[kMaxXV];
-#pragma unroll
-  for (int i = 0; i < kMaxXV; ++i) xq[i] = xr[min(tid + i * kThreads, D / 8 - 1)];
-  // piece i: 8-column blocks i * kThreads + tid (8 threads per group)
-#pragma unroll
-  for (int i = 0; i < kMaxXV; ++i)
-    if (i * kThreads < D / 8)
-      stage_x<F16X>(xq[i], D / 8 - i * kThreads, tid, s_xp + 4 * i * kThreads, s_xs + i * kThreads / 8);
-}
-
-template <bool F16X, int M, int MAXC>
-__global__ __launch_bounds__(kThreads, 3) void decode_stream_kernel(LayerLaunch L) {
-  extern __shared__ __align__(16) uint8_t dsm[];
-  __shared__ float red[kNW][2][64];
-  __shared__ __align__(16) uint32_t hpl[kNW][M][3][32];
-  __shared__ const uint8_t *s_blob[kMaxK];
-  __shared__ float s_gate[kMaxK];
-  __shared__ SelectLds s_select;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = L.blk0 + blockIdx.x;
-  const int D = L.D, E = L.E, k = L.k;
-  const int NB = D / 64, G = D / 64;
-  const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
-  uint32_t tag =
-      __hip_atomic_load(L.bep + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1u;
-  const bool given = L.given_blob != nullptr;
-  const int nR = (E + kRows - 1) / kRows;
-  const int n_rt = k * Gf;
-  const int r_down0 = nR + n_rt;
-  const int dw = max(wave - 1, 0);  // down units: waves 1..3
-
-  uint32_t *s_xp = (uint32_t *)dsm;           // gate/up blocks: [G][32]
-  float *s_xs = (float *)(dsm + 128 * G);     // [G]
-  const void **s_table = (const void **)(dsm + L.table_off);
-
-  if (b < nR) {
-    if (!given) router_role<F16X, MAXC>(L, b, tag, dsm, s_select);
-  } else if (b < r_down0 || (b >= L.NR && b < L.NR + Gs)) {
-    // ---------------- a whole gate/up tile
-    const bool routed = b < r_down0;
-    const int tile = routed ? b - nR : n_rt + (b - L.NR);
-    const Tile gt = glu_tile(L, tile);
-    const uint8_t *blob = nullptr;
-    if (routed && !given) {
-      constexpr int kTab = kMaxLayerE / kThreads;
-      const void *tb[kTab];
-#pragma unroll
-      for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
-      stage_x_all<F16X>(L, 0, s_xp, s_xs);
-#pragma unroll
-      for (int i = 0; i < kTab; ++i)
-        if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
-      __syncthreads();
-      const bool report = gt.j == 0 && gt.rb == 0;
-      if (wave == 0) wait_selection(L, 0, tile % L.sel_copies, tag, s_table, s_blob, s_gate, report);
-      __syncthreads();
-      blob = s_blob[gt.j];
-    } else {
-      stage_x_all<F16X>(L, 0, s_xp, s_xs);
-      blob = routed ? (const uint8_t *)L.given_blob[gt.j] : (const uint8_t *)as_global(L.sblobs)[0];
-      __syncthreads();
-    }
-    if (G == 44)
-      glu_full<F16X, 11>(L, blob, gt.F, gt.rb, gt.hoff + (size_t)gt.rb * 64, s_xp, s_xs, red, wave,
-                         lane, tag);
-    else
-      glu_full<F16X, 0>(L, blob, gt.F, gt.rb, gt.hoff + (size_t)gt.rb * 64, s_xp, s_xs, red, wave,
-                        lane, tag);
-  } else {
-    // ---------------- a split of the down projection (routed or shared)
-    const bool routed = b < L.NR;
-    const int sb = routed ? b - r_down0 : b - L.NR - Gs;
-    const int KSx = routed ? L.KSdr : L.KSds;
-    const int Ux = routed ? k * Gf : Gs;
-    const int ot = sb / KSx, ksd = sb % KSx;
-    const int n = ot * 64 + lane;
-    const int u0 = ksd * Ux / KSx, u1 = (ksd + 1) * Ux / KSx;
-    const uint8_t *sblob = routed ? nullptr : (const uint8_t *)as_global(L.sblobs)[0];
-    if (routed) {
-      if (!given) {
-        constexpr int kTab = kMaxLayerE / kThreads;
-        const void *tb[kTab];
-#pragma unroll
-        for (int i = 0; i < kTab; ++i) tb[i] = as_global(L.rblobs)[min(tid + i * kThreads, E - 1)];
-#pragma unroll
-        for (int i = 0; i < kTab; ++i)
-          if (tid + i * kThreads < E) s_table[tid + i * kThreads] = tb[i];
-        __syncthreads();
-        if (wave == 0) wait_selection(L, 0, sb % L.sel_copies, tag, s_table, s_blob, s_gate, false);
-      } else if (tid < k) {
-        s_blob[tid] = (const uint8_t *)L.given_blob[tid];
-        s_gate[tid] = L.given_gates[tid];
-      }
-      __syncthreads();
-    }
-    DownRegs<M> dr;
-    auto load_down = [&]() {
-      if (wave > 0) {
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-          const int u = min(u0 + dw + i * kDW, u1 - 1);
-          if (routed) {
-            const int jj = u / Gf;
-            issue_down(dr, i, s_blob[jj], D, L.F, u - jj * Gf, n);
-          } else {
-            issue_down(dr, i, sblob, D, L.Fs, u, n);
-          }
-        }
-      }
-    };
-    size_t hp[M];
-    float gate[M];
-    bool use[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const int u = min(u0 + dw + i * kDW, u1 - 1);
-      use[i] = wave > 0 && u0 + dw + i * kDW < u1;
-      if (routed) {
-        const int jj = u / Gf;
-        gate[i] = s_gate[jj];
-        hp[i] = (size_t)jj * L.F + (size_t)(u - jj * Gf) * 64;
-      } else {
-        gate[i] = 1.0f;
-        hp[i] = (size_t)k * L.F + (size_t)u * 64;
-      }
-    }
-    if (!L.down_late) load_down();
-    auto late = [&]() {
-      if (L.down_late) load_down();
-    };
-    down_and_combine<M>(L, dr, hp, gate, use, hpl, red, ot, (size_t)n, wave, lane, tag, late);
-  }
-
-  // ---------------- advance every copy of the epoch (block b: b, b + grid, ...)
-  if (tid == 0)
-    for (int j = b; j < kMaxLayerGrid; j += L.grid_full) st_dev(L.bep + j, tag);
-}
-
 using KernelFn = void (*)(LayerLaunch);
 template <bool F16X, int MAXC>
-KernelFn pick(int m, bool stream, bool two, bool norm) {
+KernelFn pick(int m, bool two, bool norm) {
   if (norm) {
-    if (stream || two) return nullptr;
+    if (two) return nullptr;
     if (m == 2) return decode_layer_kernel<F16X, 2, MAXC, false, true>;
     if (m == 3) return decode_layer_kernel<F16X, 3, MAXC, false, true>;
     if (m == 4) return decode_layer_kernel<F16X, 4, MAXC, false, true>;
-    return nullptr;
-  }
-  if (stream) {
-    if (m == 2) return decode_stream_kernel<F16X, 2, MAXC>;
-    if (m == 3) return decode_stream_kernel<F16X, 3, MAXC>;
-    if (m == 4) return decode_stream_kernel<F16X, 4, MAXC>;
     return nullptr;
   }
   if (two) {
@@ -1424,21 +1111,21 @@ KernelFn pick(int m, bool stream, bool two, bool norm) {
 }
 KernelFn pick_layer(const LayerLaunch &L, int m) {
   const bool small_d = L.D <= 3072;  // router chunks per thread: 3 (D <= 3072) or 8
-  const bool st = L.stream != 0, two = L.two != 0, nm = L.w_pre != nullptr;
-  if (L.f16x) return small_d ? pick<true, 3>(m, st, two, nm) : pick<true, 8>(m, st, two, nm);
-  return small_d ? pick<false, 3>(m, st, two, nm) : pick<false, 8>(m, st, two, nm);
+  const bool two = L.two != 0, nm = L.w_pre != nullptr;
+  if (L.f16x) return small_d ? pick<true, 3>(m, two, nm) : pick<true, 8>(m, two, nm);
+  return small_d ? pick<false, 3>(m, two, nm) : pick<false, 8>(m, two, nm);
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int g_layer_capacity[4][2][2][3][64];  // [resident, stream, two, norm][f16x][MAXC 3/8][m - 2][device]
+int g_layer_capacity[3][2][2][3][64];  // [resident, two, norm][f16x][MAXC 3/8][m - 2][device]
 
 }  // namespace
 
 int layer_m(const LayerLaunch &L) {
   const int Gf = L.F / 64, Gs = L.sblobs ? L.Fs / 64 : 0;
-  const int dwc = L.dw4 && !L.stream ? kNW : kNW - 1;  // waves with down units
-  int m = L.stream ? 2 : ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
+  const int dwc = L.dw4 ? kNW : kNW - 1;  // waves with down units
+  int m = ceil_div(ceil_div(L.D / 64, L.KSg), kNW);
   m = max(m, ceil_div(ceil_div(L.k * Gf, L.KSdr), dwc));
   if (L.KSds > 0) m = max(m, ceil_div(ceil_div(Gs, L.KSds), dwc));
   return m < 2 ? 2 : m;
@@ -1451,12 +1138,10 @@ int layer_router_blocks(const LayerLaunch &L) { return L.T * ((L.E + kRows - 1) 
 int layer_routed_blocks(const LayerLaunch &L) {
   const int n_rt = L.T * L.k * (L.F / 64);
   const int r = L.T * ((L.E + kRows - 1) / kRows);  // router blocks come first
-  if (L.stream) return r + n_rt + L.T * (L.D / 64) * L.KSdr;
   return r + max(n_rt * L.KSg, L.T * (L.D / 64) * L.KSdr);
 }
 int layer_shared_blocks(const LayerLaunch &L) {
   const int n_st = L.n_gtiles - L.T * L.k * (L.F / 64);
-  if (L.stream) return n_st + L.T * (L.D / 64) * L.KSds;
   return max(n_st * L.KSg, L.T * (L.D / 64) * L.KSds);
 }
 int layer_grid(const LayerLaunch &L) { return layer_routed_blocks(L) + layer_shared_blocks(L); }
@@ -1465,7 +1150,6 @@ size_t layer_table_off(const LayerLaunch &L) {
   // router staging: x as fp32, 16-column sums, partial logits; full-K gate/up
   // blocks: activation pairs and 64-column sums of every group
   size_t stage = sizeof(float) * ((size_t)L.D + L.D / 16 + kThreads);
-  if (L.stream) stage = max(stage, (size_t)132 * (L.D / 64));
   return align_up(stage);
 }
 size_t layer_smem(const LayerLaunch &L) { return layer_table_off(L) + sizeof(void *) * (size_t)L.E; }
@@ -1479,7 +1163,7 @@ hipError_t layer_capacity(const LayerLaunch &L, int *cap) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int &slot = g_layer_capacity[L.stream ? 1 : L.two ? 2 : L.w_pre ? 3 : 0][L.f16x ? 1 : 0]
+  int &slot = g_layer_capacity[L.two ? 1 : L.w_pre ? 2 : 0][L.f16x ? 1 : 0]
                               [L.D <= 3072 ? 0 : 1]
                               [m - 2][dev];
   const size_t smem = layer_smem(L);
@@ -1503,7 +1187,7 @@ hipError_t launch_layer_range(LayerLaunch L, int blk0, int n, hipStream_t s) {
   L.blk0 = blk0;
   L.grid_full = layer_grid(L);
   // the block order applies to whole-grid launches only (ranges are logical)
-  if (blk0 != 0 || n != L.grid_full || L.stream) L.order = 0;
+  if (blk0 != 0 || n != L.grid_full) L.order = 0;
   hipLaunchKernelGGL(k, dim3(n), dim3(kThreads), layer_smem(L), s, L);
   return hipGetLastError();
 }
@@ -1514,7 +1198,7 @@ hipError_t launch_layer(const LayerLaunch &L, hipStream_t s) {
 
 hipError_t launch_layer_ordered(LayerLaunch L, int first, int n, hipStream_t s) {
   KernelFn k = pick_layer(L, layer_m(L));
-  if (!k || L.stream || !L.two) return hipErrorInvalidValue;
+  if (!k || !L.two) return hipErrorInvalidValue;
   L.grid_full = layer_grid(L);
   if (first < 0 || n < 0 || first + n > L.grid_full) return hipErrorInvalidValue;
   if (n == 0) return hipSuccess;

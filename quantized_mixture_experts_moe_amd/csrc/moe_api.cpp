@@ -197,40 +197,17 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   const int NB = D / 64, G = D / 64;
   const int n_gtiles = T * k * (F / 64) + T * (Fs / 64);
   L->n_gtiles = n_gtiles;
-  L->shared_wait = tuning().layer_shared_wait;
-  L->down_late = tuning().layer_down_late;
   L->order = tuning().layer_order;
-  L->direct_h = tuning().layer_direct_h;
   L->select = tuning().layer_select == 1 ? 1 : 0;
   L->log_copies = L->select ? min(max(tuning().layer_log_copies, 1), 64) : 1;
   bool found = false;
-  L->stream = tuning().layer == 2 && T == 1;
-  if (L->stream) {
-    // one token: whole gate/up tiles per block; the most down splits whose
-    // grid is still resident
-    const int U = k * (F / 64), Us = Fs / 64;
-    const int hi = tuning().layer_ksd > 0 ? tuning().layer_ksd : (U < 16 ? U : 16);
-    const int lo = tuning().layer_ksd > 0 ? tuning().layer_ksd : 1;
-    for (int ksdr = hi; ksdr >= lo && !found; --ksdr) {
-      L->KSg = 1;
-      L->KSdr = ksdr;
-      L->KSds = Us ? (ksdr * Us + U - 1) / U : 0;
-      L->NR = layer_routed_blocks(*L);
-      if (layer_m(*L) > 4) break;  // fewer splits only make it larger
-      const int grid = layer_grid(*L);
-      int cap = 0;
-      if (layer_capacity(*L, &cap) != hipSuccess) return false;
-      found = grid <= cap && grid <= kMaxLayerGrid;
-    }
-    if (!found) L->stream = 0;
-  }
   // the most gate/up splits (and with them down splits) whose grid is still
   // resident all at once: more, smaller blocks overlap more of the transfer.
   // Several tokens: if no grid fits with three waves of down units per
   // block, every wave takes down units (16 per block instead of 12)
   const int ksg_hi = tuning().layer_ksg > 0 ? tuning().layer_ksg : (G < kMaxKS ? G : kMaxKS);
   const int ksg_lo = tuning().layer_ksg > 0 ? tuning().layer_ksg : 1;
-  for (int dw4 = 0; dw4 <= (T > 1 && !L->stream && !L->two ? 1 : 0) && !found; ++dw4) {
+  for (int dw4 = 0; dw4 <= (T > 1 && !L->two ? 1 : 0) && !found; ++dw4) {
     L->dw4 = dw4;
     for (int ksg = ksg_hi; ksg >= ksg_lo && !found; --ksg) {
       const Splits sp = plan_splits(T, k, D, F, Fs, ksg, tuning().layer_ksd, dw4 ? 16 : 12);
@@ -246,10 +223,6 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
     }
   }
   if (!found) return false;
-  if (L->stream) {  // the whole-tile variant reads the published selection
-    L->select = 0;
-    L->log_copies = 1;
-  }
   if (n_gtiles > kMaxAccTiles || T * NB > kMaxOutTiles) return false;
   L->bep = (uint32_t *)w.layer;
   set_split_accumulators(w, &L->gacc, &L->dacc, &L->gcnt, &L->dcnt);
@@ -263,7 +236,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   if (L->sel_stride > 4096) L->sel_stride = 4096;
   L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * L->sel_stride, 8);
   L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
-  L->hu = L->stream ? nullptr : c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
+  L->hu = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   if (kTaggedOff + c.off > kRouteTagOff) return false;
   L->table_off = layer_table_off(*L);
   L->err = w.err;
@@ -392,17 +365,14 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
   } else if (!strcmp(key, "fused_ksd")) {
     tuning().fused_ksd = value;
   } else if (!strcmp(key, "layer")) {
+    if (value > 1) return MOE_E_INVALID;
     tuning().layer = value;
   } else if (!strcmp(key, "layer_ksg")) {
     tuning().layer_ksg = value;
   } else if (!strcmp(key, "layer_ksd")) {
     tuning().layer_ksd = value;
-  } else if (!strcmp(key, "layer_down_late")) {
-    tuning().layer_down_late = value;
   } else if (!strcmp(key, "layer_order")) {
     tuning().layer_order = value;
-  } else if (!strcmp(key, "layer_direct_h")) {
-    tuning().layer_direct_h = value;
   } else if (!strcmp(key, "layer_select")) {
     tuning().layer_select = value;
   } else if (!strcmp(key, "layer_log_copies")) {
@@ -411,8 +381,6 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_sel_copies = value;
   } else if (!strcmp(key, "layer_sel_stride")) {
     tuning().layer_sel_stride = value;
-  } else if (!strcmp(key, "layer_shared_wait")) {
-    tuning().layer_shared_wait = value;
   } else if (!strcmp(key, "block_fused")) {
     tuning().block_fused = value;
   } else if (!strcmp(key, "prefill_min_t")) {
@@ -520,7 +488,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     return hip_status(prof_end(pi, s, launch_layer(L, s)));
   }
 
-  if (use_layer && pool && !L.stream) {
+  if (use_layer && pool) {
     // Streamed experts, two launches of the layer kernel.  First its router
     // blocks and the shared expert's blocks (dispatch order 1: router,
     // shared, routed); the ranking waves also store the selection into host
@@ -581,25 +549,6 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     r.zero2_stride = 32;
   }
   if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
-  if (use_layer && pool) {
-    // Streamed experts: ids back to the host; the shared expert's blocks run
-    // while the host plans and the side stream copies the missing experts
-    // into HBM slots; then the routed blocks with that selection.  The
-    // splits are those of the resident launch, so results are bitwise equal.
-    st = pool_fetch_ids(pool, r.ids, T * k, s);
-    if (st) return st;
-    const int NR = L.NR, NS = layer_shared_blocks(L);
-    if (launch_layer_range(L, NR, NS, s) != hipSuccess) return MOE_E_HIP;
-    const void *const *slots = nullptr;
-    st = pool_plan_and_copy(pool, layer, T, k, s, nullptr, &slots);
-    if (st) return st;
-    L.given_blob = slots;
-    L.given_gates = r.gates;
-    L.ids_out = nullptr;  // already written by the router kernel
-    L.gates_out = nullptr;
-    if (launch_layer_range(L, 0, NR, s) != hipSuccess) return MOE_E_HIP;
-    return pool_slots_read(pool, s);
-  }
   if (fused && !pool) {
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_fused(f, s)));
@@ -728,7 +677,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const fl
     L.w_pre = w_pre; L.w_post = w_post; L.eps = eps;
     L.ybuf = (uint64_t *)((uint8_t *)ws + bt.yt_off); L.u_out = (uint16_t *)u_out;
     Workspace w = carve(ws, d);
-    if (plan_layer(w, &L) && !L.stream) {
+    if (plan_layer(w, &L)) {
       const int pi = prof_begin(s);
       return hip_status(prof_end(pi, s, launch_layer(L, s)));
     }

@@ -91,13 +91,10 @@ struct Tuning {
   int prefill_min_t = 8;   // tokens per call from which the grouped matrix-core path runs
                            // (measured: equal at 8, 8 % faster at 12 than the few-token path)
   int route_mfma = 1;      // router of 16 or more tokens on the matrix cores
-  int layer = 1;       // one launch for the whole decode layer when it fits
+  int layer = 1;       // one launch for the whole decode layer when it fits (0: off)
   int layer_ksg = 0;   // its gate/up and down splits (0: chosen)
   int layer_ksd = 0;
-  int layer_shared_wait = 0;
-  int layer_down_late = 1;
   int layer_order = 1;
-  int layer_direct_h = 0;
   int layer_select = 1;  // measured: 17.0 against 17.5 us per decode step
   int layer_log_copies = 16;
   int layer_sel_copies = 16;
@@ -254,17 +251,12 @@ struct LayerLaunch {
   int KSdr, KSds;                     // down splits of the routed / shared units
   int NR;                             // router + routed blocks (the shared blocks follow)
   int blk0, grid_full;                // this launch covers blocks [blk0, blk0 + grid)
-  int shared_wait;                    // shared blocks load after the router logits are out
-  int down_late;                      // down weights: 0 with gate/up, 1 after its reduction, 2 after its arithmetic
-  int stream;                         // one token, whole gate/up tiles per block (hu unused)
   int order;                          // dispatch order: 0 router, routed, shared; 1 router, shared, routed
-  int direct_h;                       // down waves poll the hidden values, not a hint word first
   int select;                         // 0: router blocks rank and publish the selection; 1: routed blocks rank the logits
   int log_copies;                     // copies of the logits (select 1)
-  // selection given by the caller (streamed experts: ids from an earlier
-  // routing, blobs from the pool): [T][k] blob addresses and gates, or null
+  // streamed experts (two launches): the blob of rank r of token t in the
+  // pool's slots, given_blob[t][r]; null otherwise
   const void *const *given_blob;
-  const float *given_gates;
   size_t table_off;                   // LDS byte offset of the blob table
   uint32_t *bep;                      // per-block epochs [kMaxLayerGrid]
   uint64_t *rlog;                     // [log_copies][T][E] tagged logits
