@@ -501,13 +501,16 @@ __device__ __forceinline__ void glu_publish(const LayerLaunch &L, float (&red)[k
   }
 }
 
-// The residual block's post-norm of token t, by the token's first router
-// block once its routing is done: it polls the layer's output row y (tagged
-// words, stored by the lanes that complete each element) until every element
-// carries the launch's epoch, then normalises it (w_post) and adds the
-// residual row x into out.  Thread tid takes chunks tid, tid + 256, ..., the
-// fixed summation order of the separate post-norm kernel (same bits).  The
-// last element is seen one poll after its store: no counter, no store fence.
+// The residual block's post-norm of token t, by a router block once its
+// routing is done.  The lanes that complete output elements store them as
+// tagged words and add their number to the token's counter; one wave polls
+// that single word until it reaches D (polling the whole row instead put
+// kilobytes of device-scope loads per round on a few memory channels and
+// slowed the layer), then the block reads the row, checking every word's
+// epoch (a count may land before its stores), normalises it (w_post) and
+// adds the residual row x into out.  Thread tid takes chunks tid, tid + 256,
+// ..., the fixed summation order of the separate post-norm kernel (same
+// bits).  The counter goes back to zero for the next call.
 template <bool F16X, int NX>
 __device__ __forceinline__ void post_norm_poll(const LayerLaunch &L, int t, uint32_t tag,
                                                float *red4) {
@@ -524,6 +527,17 @@ __device__ __forceinline__ void post_norm_poll(const LayerLaunch &L, int t, uint
     wa[i] = w4[2 * c];
     wb[i] = w4[2 * c + 1];
   }
+  if (threadIdx.x < 64) {
+    for (long s = 0;; ++s) {
+      if (ld_dev(L.ocnt + t) >= (uint32_t)D) break;
+      if (s > kSpin) {
+        if (tid == 0) add_dev(L.err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
   float yv[NX][8];
   for (long s = 0;; ++s) {
     bool ok = true;
@@ -571,6 +585,7 @@ __device__ __forceinline__ void post_norm_poll(const LayerLaunch &L, int t, uint
                                                h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     }
   }
+  if (tid == 0) st_dev(L.ocnt + t, 0u);
 }
 
 // Down projection of output row n over this wave's units, then the split
@@ -691,8 +706,13 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
           ((uint16_t *)L.out)[out_idx] = (uint16_t)f32_to_f16(s);
       }
     } else {
-      // the output element goes to ybuf as a tagged word for the post-norm
+      // the output element goes to ybuf as a tagged word for the post-norm,
+      // and the wave's number of completed elements to the token's counter
       if (done) st_dev64(L.ybuf + out_idx, tagged(__float_as_uint(s), tag));
+      const uint32_t cnt = (uint32_t)__popcll(__ballot(done));
+      if (cnt && lane == 0)
+        __hip_atomic_fetch_add(L.ocnt + out_idx / (size_t)L.D, cnt, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -945,13 +965,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L
     // ---------------- router rows and the selection of the token.  They
     // head the chain of dependent steps, so these blocks do nothing else.
     router_role<F16X, MAXC, TWO, 1, NORM, RT>(L, b, tag, dsm, s_select, s_red4);
-    // the first router block of each token then does its post-norm
-    if constexpr (NORM)
-      if (b % nrb == 0) {
-        const int t0 = b / nrb * kRT;
-        post_norm_poll<F16X, NX>(L, t0, tag, s_red4);
-        if (RT > 1 && t0 + 1 < T) post_norm_poll<F16X, NX>(L, t0 + 1, tag, s_red4);
-      }
+    // router block i of a token group then does the post-norm of the
+    // group's token i (the tokens' polls run side by side; with fewer router
+    // blocks than tokens in a group, block i takes tokens i, i + nrb, ...)
+    if constexpr (NORM) {
+      const int t0 = b / nrb * kRT, i = b % nrb;
+      if (i < RT && t0 + i < T) post_norm_poll<F16X, NX>(L, t0 + i, tag, s_red4);
+      if (RT > 1 && nrb == 1 && t0 + 1 < T) post_norm_poll<F16X, NX>(L, t0 + 1, tag, s_red4);
+    }
   } else if (b >= L.NR) {
     // ---------------- shared expert: its gate/up tiles and its part of the
     // down projection; nothing waits on the routing

@@ -291,13 +291,15 @@ size_t workspace_bytes(const Dims &d) { return carve(nullptr, d).total; }
 
 // The residual block's buffers after the layer's workspace: the normalised
 // input u [T, D] 16-bit, the layer's output y [T, D] fp32 (separate
-// kernels) and the one-launch path's tagged output words [min(T, 4), D].
+// kernels), the one-launch path's tagged output words [min(T, 4), D] and its
+// per-token counters [4] (zero between calls).
 BlockTail block_tail(size_t layer_bytes, int T, int D) {
   BlockTail b;
   b.u_off = align_up(layer_bytes);
   b.y_off = align_up(b.u_off + (size_t)T * D * 2);
   b.yt_off = align_up(b.y_off + (size_t)T * D * 4);
-  b.total = align_up(b.yt_off + (size_t)min(T, kMaxLayerT) * D * 8);
+  b.cnt_off = align_up(b.yt_off + (size_t)min(T, kMaxLayerT) * D * 8);
+  b.total = align_up(b.cnt_off + (size_t)kMaxLayerT * 4);
   return b;
 }
 
@@ -676,6 +678,7 @@ moe_status moe_block_forward(const void *x, int32_t x_dtype, int32_t T, const fl
                       out_dtype, ids_out, gates_out);
     L.w_pre = w_pre; L.w_post = w_post; L.eps = eps;
     L.ybuf = (uint64_t *)((uint8_t *)ws + bt.yt_off); L.u_out = (uint16_t *)u_out;
+    L.ocnt = (uint32_t *)((uint8_t *)ws + bt.cnt_off);
     Workspace w = carve(ws, d);
     if (plan_layer(w, &L)) {
       const int pi = prof_begin(s);

@@ -169,7 +169,7 @@ hipError_t launch_route(const RouteLaunch &a, hipStream_t s);
 // output y added to x.  D <= kBlockMaxD.
 constexpr int kBlockMaxD = 8192;
 struct BlockTail {
-  size_t u_off, y_off, yt_off, total;
+  size_t u_off, y_off, yt_off, cnt_off, total;
 };
 BlockTail block_tail(size_t layer_bytes, int T, int D);
 hipError_t launch_block_pre(const void *x, int f16x, int T, int D, const float *w, float eps,
@@ -279,12 +279,13 @@ struct LayerLaunch {
   // the residual block fused around the layer (w_pre non-null; one launch,
   // resident experts): x is the residual stream, normalised (w_pre) by every
   // role into the layer's input (also stored to u_out [T][D] if non-null);
-  // each output element goes to ybuf [T][D] as a tagged word, and each
-  // token's first router block polls its row and writes out = x + the
-  // post-norm (w_post) of it
+  // each output element goes to ybuf [T][D] as a tagged word and is
+  // counted in ocnt [T] (zero between calls); a router block per token
+  // polls the count, then writes out = x + the post-norm (w_post) of the row
   const float *w_pre, *w_post;
   float eps;
   uint64_t *ybuf;
+  uint32_t *ocnt;
   uint16_t *u_out;
 };
 int layer_m(const LayerLaunch &L);

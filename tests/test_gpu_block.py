@@ -199,3 +199,29 @@ def test_block_fused_launch_equals_separate_kernels(name, T, in_place):
                                ref.view(torch.int16) if odt != torch.float32 else ref)
     finally:
         _set_fused(1)
+
+
+@pytest.mark.parametrize("T", [2, 3])
+def test_block_fused_with_one_router_block_per_group(T):
+    """Four experts: a token group has one router block, which then does the
+    post-norm of both its tokens; fused equals the separate kernels and the
+    oracle."""
+    _case(f"block fused, E=4 (one router block per token group), T={T}")
+    from tests.test_gpu_parity import DevLayer
+    cfg = gen.MoEConfig("e4", D=256, E=4, F=128, F_shared=256, k=2, T=T, x_dtype="fp16")
+    L = DevLayer(cfg, seed=3)
+    xb = gen.residual_stream(13, 0, T, T, cfg.D, cfg.x_dtype)
+    w_pre, w_post = gen.norm_weights(4, 0, cfg.D)
+    try:
+        _set_fused(0)
+        ref, ref_u, ref_ids = _block_gpu(L, xb, w_pre, w_post)
+        _set_fused(1)
+        got, got_u, got_ids = _block_gpu(L, xb, w_pre, w_post)
+    finally:
+        _set_fused(1)
+    assert np.array_equal(got_ids, ref_ids) and np.array_equal(got_u, ref_u)
+    assert torch.equal(got, ref)
+    xf = O.activations_to_float(xb, cfg.x_dtype)
+    out = O.block_forward(xf, L.lw, cfg.k, w_pre, w_post, EPS, x_dtype=cfg.x_dtype,
+                          u=O.activations_to_float(got_u, cfg.x_dtype), ids=got_ids)
+    _check_out(xf, out["moe"], w_post, got.cpu().numpy())
