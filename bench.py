@@ -54,10 +54,11 @@ def build_layers(cfg, n_layers, seed, moe, torch):
     return layers
 
 
-def cpu_baseline(cfg, seed, budget_s):
+def cpu_baseline(cfg, seed, budget_s, block=False):
     """The oracle as it stands, on the host cores, for a bounded sample: the
     workload's own calls with every BLAS thread, one call on one thread, and
-    (decode) one 128-token chunk of the prefill workload."""
+    (decode) one 128-token chunk of the prefill workload.  block: the
+    oracle's residual block around the layer instead of the layer."""
     from oracle import moe_oracle as O
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -68,11 +69,18 @@ def cpu_baseline(cfg, seed, budget_s):
     lw = gen.layer_weights(seed, 0, cfg)
     bias = gen.zipf_bias(seed, 0, cfg.E, cfg.beta) if cfg.beta else None
 
+    w_pre, w_post = gen.norm_weights(seed, 0, cfg.D)
+
     def calls(budget, stream0):
         n, t0 = 0, time.perf_counter()
         while True:
-            xb = gen.activations(seed, 0, stream0 + n, cfg.T, cfg.D, cfg.x_dtype)
-            O.layer_forward(O.activations_to_float(xb, cfg.x_dtype), lw, cfg.k, bias)
+            if block:
+                xb = gen.residual_stream(seed, 0, stream0 + n, cfg.T, cfg.D, cfg.x_dtype)
+                O.block_forward(O.activations_to_float(xb, cfg.x_dtype), lw, cfg.k, w_pre,
+                                w_post, logit_bias=bias, x_dtype=cfg.x_dtype)
+            else:
+                xb = gen.activations(seed, 0, stream0 + n, cfg.T, cfg.D, cfg.x_dtype)
+                O.layer_forward(O.activations_to_float(xb, cfg.x_dtype), lw, cfg.k, bias)
             n += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -80,7 +88,9 @@ def cpu_baseline(cfg, seed, budget_s):
 
     n, el = calls(budget_s * 0.4, 10_000)
     res = {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"{n} calls of {cfg.T} token(s) through layer 0 of the '{cfg.name}' "
+           "sample": f"{n} calls of {cfg.T} token(s) through "
+                     + ("the residual block around " if block else "")
+                     + f"layer 0 of the '{cfg.name}' "
                      f"workload in {el:.1f} s (float64 numpy oracle, BLAS threads {threads}, "
                      f"host cpu_count {os.cpu_count()})"}
     if threadpool_limits is not None:
@@ -88,7 +98,7 @@ def cpu_baseline(cfg, seed, budget_s):
             n1, el1 = calls(budget_s * 0.2, 20_000)
         res["single_thread"] = {"value": n1 * cfg.T / el1, "unit": "tokens/s", "cores": 1,
                                 "sample": f"{n1} calls in {el1:.1f} s"}
-    if cfg.name == "decode":
+    if cfg.name == "decode" and not block:
         pc = gen.CONFIGS["prefill"]
         xb = gen.activations(seed, 0, 0, pc.T, pc.D, pc.x_dtype)
         t0 = time.perf_counter()
@@ -567,7 +577,7 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
-        cpu = cpu_baseline(cfg, a.seed, a.cpu_seconds)
+        cpu = cpu_baseline(cfg, a.seed, a.cpu_seconds, block=a.block)
 
     line = {
         "metric": METRIC,
