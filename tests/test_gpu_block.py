@@ -172,8 +172,9 @@ def _set_fused(v):
 
 
 @pytest.mark.parametrize("name,T,in_place", [("decode", 1, False), ("decode", 1, True),
-                                             ("decode", 2, False), ("decode", 4, True),
-                                             ("tiny", 3, False), ("tiny", 4, True)])
+                                             ("decode", 2, False), ("decode", 2, True),
+                                             ("decode", 4, True), ("tiny", 3, False),
+                                             ("tiny", 4, True)])
 def test_block_fused_launch_equals_separate_kernels(name, T, in_place):
     """The one-launch decode layer with both norms inside gives the same bits
     as the three-step path (pre-norm kernel, layer, post-norm kernel): the
@@ -225,3 +226,34 @@ def test_block_fused_with_one_router_block_per_group(T):
     out = O.block_forward(xf, L.lw, cfg.k, w_pre, w_post, EPS, x_dtype=cfg.x_dtype,
                           u=O.activations_to_float(got_u, cfg.x_dtype), ids=got_ids)
     _check_out(xf, out["moe"], w_post, got.cpu().numpy())
+
+
+def test_block_forward_streamed_equals_resident():
+    """The block over a slot pool (pre-norm kernel, the layer in two launches
+    with the experts streamed into 4 HBM slots, post-norm kernel) gives the
+    bits of the resident block (both norms inside the one-launch layer)."""
+    _case("block_forward pooled vs resident (tiny, 4 slots, 12 tokens)")
+    L = dev_layer("tiny", seed=3)
+    cfg = L.cfg
+    host = [torch.from_numpy(L.lw.experts.copy()).pin_memory()]
+    pool = moe.Pool(host, 1, 4, cfg.E, cfg.D, cfg.F)
+    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared, block=True)
+    w_pre, w_post = gen.norm_weights(5, 0, cfg.D)
+    wp, wq = torch.from_numpy(w_pre).cuda(), torch.from_numpy(w_post).cuda()
+    bias = torch.from_numpy(gen.zipf_bias(3, 0, cfg.E, 4.0)).cuda()
+    try:
+        for tok in range(12):
+            xb = gen.residual_stream(17, 0, tok, 1, cfg.D, cfg.x_dtype)
+            x = _dev(xb, cfg.x_dtype)
+            o_s = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
+            o_r = torch.empty_like(o_s)
+            moe.moe_block_forward(x, wp, wq, EPS, L.router, cfg.k, None, L.shared, o_s, ws,
+                                  logit_bias=bias, pool=pool, layer=0)
+            moe.moe_block_forward(x, wp, wq, EPS, L.router, cfg.k, L.routed, L.shared, o_r, ws,
+                                  logit_bias=bias)
+            torch.cuda.synchronize()
+            assert torch.equal(o_s, o_r), tok
+        assert ws.timeouts() == 0
+        assert pool.stats()["misses"] > 0
+    finally:
+        pool.close()
