@@ -385,6 +385,8 @@ def main():
     ap.add_argument("--block", action="store_true",
                     help="time the residual block (pre-norm, layer, post-norm and residual) "
                          "instead of the layer alone")
+    ap.add_argument("--beta", type=float, default=None,
+                    help="Zipf skew of the router-logit bias (default: the workload's own)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--graph-steps", type=int, default=64)
     ap.add_argument("--regions", type=int, default=5,
@@ -413,6 +415,9 @@ def main():
         print(json.dumps(res), flush=True)
         return
     cfg = gen.CONFIGS[a.config]
+    if a.beta is not None:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, beta=a.beta)
     if a.config in ("stack30", "streamed"):
         res = (run_stack if a.config == "stack30" else run_streamed)(cfg, a, moe, torch)
         print(json.dumps({"config": a.config, **res}), flush=True)
@@ -557,8 +562,14 @@ def main():
                    + T * cfg.D * 2 + T * cfg.D * 4)
         if not grouped:
             k_bytes += gen.codes_bytes(cfg.E, cfg.D, 8) + gen.meta_bytes(cfg.E, cfg.D)
-            k_name = (f"whole step of {T} tokens: router kernel and the few-token expert "
-                      f"kernels ({np.mean(uniq):.1f} distinct experts)")
+            if T <= 2 and tune.get("layer", "1") != "0":
+                how = "one launch of the layer kernel"
+            elif tune.get("mid", "0") != "0" and T <= int(tune.get("mid_max_t", 7)):
+                how = ("router kernel and the batched-decode expert kernels (each distinct "
+                       "expert and the shared expert read once)")
+            else:
+                how = "router kernel and the few-token expert kernels"
+            k_name = f"whole step of {T} tokens: {how} ({np.mean(uniq):.1f} distinct experts)"
         else:
             k_name = (f"grouped prefill expert kernels (gate/up, down, combine; "
                       f"{np.mean(uniq):.1f} distinct experts per chunk)")
@@ -600,7 +611,9 @@ def main():
                                f"{T} token(s) per step, d_model {cfg.D}, {cfg.E} experts of "
                                f"GLU width {cfg.F} (4-bit, group 64), top-{cfg.k}, shared expert "
                                f"{cfg.F_shared}, 8-bit router; {n_layers} seeded layer replicas "
-                               f"rotated", "tokens_per_step": T, "layers_rotated": n_layers,
+                               f"rotated" + (f", Zipf-biased routing (beta {cfg.beta})"
+                                             if cfg.beta else ""),
+                   "tokens_per_step": T, "layers_rotated": n_layers,
                    "parallelism": "single GPU"},
         "hbm_GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -349,6 +349,13 @@ moe_status moe_set_profile_events(void *const *events, int32_t n_pairs);
  *                        copies and spacing of the published selection
  *   fused (1)            the one-launch expert phase when the layer kernel
  *                        is off; fused_ksg, fused_ksd (0) its splits
+ *   mid (0)              1: mid_min_t (2) to mid_max_t (7) tokens per
+ *                        call, resident experts, when the layer kernel does
+ *                        not take the call: kernels that read each distinct
+ *                        selected expert and the shared expert once for all
+ *                        tokens that use it (measured slower than the
+ *                        per-token kernels, so off); mid_ksg, mid_kss,
+ *                        mid_ksd (0) their routed, shared and down splits
  *   glu_ks, down_ks (0)  reduction splits of the few-token kernels
  *   prefill_min_t (8)    tokens per call from which the grouped matrix-core
  *                        kernels run

@@ -90,6 +90,10 @@ Workspace carve(void *base, const Dims &d) {
   w.hsum = c.take<float>(units / 64 + 1, 4);
   w.y = c.take<float>(T * k * (size_t)d.D, 4);
   w.ys = c.take<float>(kMaxSharedSplits * T * (size_t)d.D, 4);
+  // batched decode (T <= kMaxMidT): split sums of the two kernels
+  const bool mid = T <= (size_t)kMaxMidT && T * k <= 64;
+  w.mgacc = c.take<uint64_t>(mid ? 2 * units : 0, 8);
+  w.mdacc = c.take<uint64_t>(mid ? T * d.D : 0, 8);
   w.total = c.off;
   return w;
 }
@@ -385,6 +389,18 @@ moe_status moe_set_tuning(const char *key, int32_t value) {
     tuning().layer_sel_stride = value;
   } else if (!strcmp(key, "block_fused")) {
     tuning().block_fused = value;
+  } else if (!strcmp(key, "mid")) {
+    tuning().mid = value;
+  } else if (!strcmp(key, "mid_min_t")) {
+    tuning().mid_min_t = value;
+  } else if (!strcmp(key, "mid_max_t")) {
+    tuning().mid_max_t = value;
+  } else if (!strcmp(key, "mid_ksg")) {
+    tuning().mid_ksg = value;
+  } else if (!strcmp(key, "mid_ksd")) {
+    tuning().mid_ksd = value;
+  } else if (!strcmp(key, "mid_kss")) {
+    tuning().mid_kss = value;
   } else if (!strcmp(key, "prefill_min_t")) {
     tuning().prefill_min_t = value;
   } else if (!strcmp(key, "route_mfma")) {
@@ -541,6 +557,24 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   a.sblobs = shared ? shared->blobs : nullptr; a.Fs = Fs;
   a.h = w.h; a.hs = w.hs; a.part = w.part; a.counters = w.counters;
   a.y = nullptr; a.out = out; a.out_dtype = out_dtype;
+  // batched decode: each distinct expert and the shared expert read once for
+  // every token that uses it (router kernel, then the two kernels)
+  if (!pool && !use_layer && tuning().mid && T >= tuning().mid_min_t && T <= tuning().mid_max_t &&
+      T <= kMaxMidT && T * k <= 64 && T < tuning().prefill_min_t) {
+    MidLaunch m{};
+    m.a = a;
+    m.a.rblobs = routed->blobs;
+    m.gacc = w.mgacc;
+    m.dacc = w.mdacc;
+    m.err = w.err;
+    plan_mid(&m);
+    m.gcnt = w.counters;
+    m.dcnt = w.counters + m.n_tiles;
+    if (m.n_tiles + D / 64 > kMaxSplitBlocks) return MOE_E_UNSUPPORTED;
+    if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
+    const int pi = prof_begin(s);
+    return hip_status(prof_end(pi, s, launch_mid(m, s)));
+  }
   FusedLaunch f;
   const bool fused = !use_layer && tuning().fused && plan_fused(a, w, &f);
   if (fused) {

@@ -22,6 +22,10 @@ constexpr int kMaxHGroups = 64;        // hidden width / 64 handled by the prefi
 constexpr int kMaxLayerGrid = 4096;    // blocks of the one-launch decode layer
 constexpr int kMaxLayerT = 4;          // tokens of the one-launch decode layer
 constexpr int kMaxLayerE = 256;        // experts of the one-launch decode layer
+constexpr int kMaxMidT = 8;            // tokens of the batched-decode expert phase
+constexpr int kMaxMidKS = 16;          // its gate/up splits
+constexpr int kMaxMidGB = 16;          // column groups of one of its gate/up blocks
+constexpr int kMaxMidKSd = 64;         // its down splits
 // Region at the start of every workspace that holds the tagged words of the
 // one-launch decode layer: the per-block epochs, then 64-bit (value, tag)
 // words only.  Its place and size do not depend on the call, so no other
@@ -100,6 +104,13 @@ struct Tuning {
   int layer_sel_copies = 16;
   int layer_sel_stride = 0;  // words between selection lines; 0: packed
   int block_fused = 1;       // residual block: norms inside the one-launch decode layer
+  int mid = 0;               // batched decode: each distinct expert read once for its tokens
+                             // (measured slower than the per-token kernels: off)
+  int mid_min_t = 2;         // from this many tokens per call
+  int mid_max_t = 7;         // up to this many (and below prefill_min_t)
+  int mid_ksg = 0;           // its gate/up and down splits (0: chosen)
+  int mid_ksd = 0;
+  int mid_kss = 0;           // its shared-expert gate/up split (0: chosen)
 };
 Tuning &tuning();
 
@@ -125,6 +136,8 @@ struct Workspace {
   uint16_t *hplanes;   // prefill: hidden activations as three bf16 planes
   float *hsum;         // prefill: 64-unit sums of the hidden activations
   float *y, *ys;       // prefill: routed outputs per pair, shared outputs per token
+  uint64_t *mgacc;     // batched decode: gate/up split sums [units / 64][2][64]
+  uint64_t *mdacc;     // batched decode: output split sums [T][D]
   size_t total;
 };
 
@@ -194,6 +207,21 @@ struct ExpertLaunch {
   int glu_first, glu_count;           // GLU block range: routed tiles first, then shared
   int glu_ks;                         // reduction split of the GLU (0: from glu_count)
 };
+// Batched-decode expert phase (expert_mid.hip): gate/up and down kernels in
+// which every distinct selected expert, and the shared expert, is read once
+// for all tokens that use it.  T <= kMaxMidT and T k <= 64; ids, gates, xp, xs
+// from the router kernel; resident routed bank (rblobs).
+struct MidLaunch {
+  ExpertLaunch a;
+  uint64_t *gacc, *dacc;    // fixed-point split sums, zero between calls:
+                            // [units / 64][2][64] and [T][D] (workspace)
+  uint32_t *err;
+  uint32_t *gcnt, *dcnt;    // tile counters, zero between calls: [n_tiles], [D / 64]
+  int KSg, KSs, KSd;        // gate/up splits of the routed and the shared tiles; down splits
+  int n_tiles, n_blocks;    // gate/up tiles (routed, then shared) and blocks
+};
+void plan_mid(MidLaunch *m);
+hipError_t launch_mid(const MidLaunch &m, hipStream_t s);
 // One-launch expert phase (gate/up + down + combine) for a few tokens.
 constexpr int kFlagCopies = 16;  // replicas of each slot-ready flag (one 128-byte line each)
 struct FusedLaunch {

@@ -416,6 +416,44 @@ def test_layer_forward_decode_batches(T, beta):
     _check_rows(L, xb, out.cpu().numpy(), ids, cfg.k, bias, what=f"T={T}")
 
 
+@pytest.mark.parametrize("name,T,beta,ksg,ksd,kss", [
+    ("decode", 2, 6.5, 0, 0, 0), ("decode", 3, 0.0, 0, 0, 0), ("decode", 5, 6.5, 0, 0, 0),
+    ("decode", 7, 6.5, 0, 0, 0), ("decode", 4, 6.5, 3, 1, 3), ("decode", 6, 0.0, 16, 64, 16),
+    ("tiny", 7, 0.0, 0, 0, 0), ("tiny", 3, 2.0, 2, 3, 4)])
+def test_layer_forward_mid_batches(name, T, beta, ksg, ksd, kss):
+    """Batched decode through the kernels that read each distinct selected
+    expert, and the shared expert, once for all tokens that use it (the
+    one-launch layer switched off, so two tokens take them too), at default,
+    single and widest splits.  Every row element by element against the
+    oracle; repeated experts (Zipf-biased routing) are served by the blocks
+    of their first slot; bitwise repeatable; the per-token few-token kernels
+    agree far inside the bar."""
+    _case(f"layer_forward mid kernels {name} T={T} beta={beta} ksg={ksg} ksd={ksd} kss={kss}")
+    L = dev_layer(name)
+    cfg = L.cfg
+    xb = gen.activations(13, 0, T, T, cfg.D, cfg.x_dtype)
+    bias = gen.zipf_bias(0, 0, cfg.E, beta) if beta else None
+    _tune(layer=0, mid=1, mid_ksg=ksg, mid_ksd=ksd, mid_kss=kss)
+    try:
+        out, ids, _ = _layer_gpu(L, xb, cfg.k, bias)
+        n_rep = ids.size - len(np.unique(ids))
+        print(f"    repeated slots {n_rep}", flush=True)
+        if beta >= 6.5 or name == "tiny":
+            assert n_rep > 0
+        _check_rows(L, xb, out.cpu().numpy(), ids, cfg.k, bias, what=f"T={T}")
+        again, _, _ = _layer_gpu(L, xb, cfg.k, bias)
+        assert torch.equal(out, again)
+        o16, i16, _ = _layer_gpu(L, xb, cfg.k, bias, out_dtype=torch.bfloat16)
+        assert np.array_equal(i16, ids)
+        assert torch.equal(o16, out.to(torch.bfloat16))
+        _tune(mid=0)
+        o2, i2, _ = _layer_gpu(L, xb, cfg.k, bias)
+        assert np.array_equal(i2, ids)
+        assert rel_l2(o2.cpu().numpy(), out.cpu().numpy()) < 1e-5
+    finally:
+        _tune(**_DEFAULTS)
+
+
 def test_layer_forward_bf16_output_is_rounded_fp32():
     _case("layer_forward bf16 out")
     L = dev_layer("decode")
@@ -519,7 +557,7 @@ _PATHS = {"layer": {"layer": 1}, "order0": {"layer": 1, "layer_order": 0},
           "select0": {"layer": 1, "layer_select": 0}, "select1": {"layer": 1, "layer_select": 1},
           "fused": {"layer": 0, "fused": 1}, "three": {"layer": 0, "fused": 0}}
 _DEFAULTS = {"layer": 1, "fused": 1, "layer_ksg": 0, "layer_ksd": 0, "layer_order": 1,
-             "layer_select": 1}
+             "layer_select": 1, "mid": 0, "mid_ksg": 0, "mid_ksd": 0, "mid_kss": 0}
 
 
 def _tune(**kv):
