@@ -20,8 +20,8 @@
  * is the default stream) unless stated otherwise.  Arguments are validated
  * before anything is launched: a negative status means nothing was enqueued,
  * except for a moe_layer_forward with a pool, which plans its slots after
- * routing: there MOE_E_POOL (more distinct experts in the call than slots)
- * or MOE_E_HIP can come after work was enqueued, and the call's outputs are
+ * routing: there MOE_E_POOL (an expert id outside the pool's range) or
+ * MOE_E_HIP can come after work was enqueued, and the call's outputs are
  * undefined.  MOE_E_HIP reports a HIP runtime error from a launch or copy;
  * after one, zero-fill the workspace again before reusing it.  Device faults
  * surface at the caller's next synchronisation.  No call aborts and no C++
@@ -151,7 +151,8 @@ moe_status moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_b
 
 /* Combine (es.news.hada.io, "Proceso de generacion de tokens": the shared and
  * routed outputs are combined): out[t] = y_shared[t] + sum_j gates[t,j] y[t,j],
- * summed in j order.  y device [T,k,D] fp32; gates device [T,k] fp32;
+ * summed in j order in double precision and rounded once (to fp32, then to
+ * out_dtype).  y device [T,k,D] fp32; gates device [T,k] fp32;
  * y_shared device [T,D] fp32 or NULL; out device [T,D] of out_dtype
  * (MOE_F32, MOE_BF16 or MOE_F16, round to nearest even). */
 moe_status moe_combine(const float *y, const float *gates, const float *y_shared, int32_t T,
@@ -175,9 +176,17 @@ moe_status moe_permute(const int32_t *ids, int32_t T, int32_t k, int32_t E, int3
  * pool's side stream while the shared expert runs; this call then blocks the
  * host once, until the selected ids have arrived in the pool's pinned host
  * memory (written there by the routing kernels; the pages' CPU fetch plan:
- * es.news.hada.io, "Proceso de generacion de tokens").  Consecutive calls
- * with one pool go on one stream (the pool's host-side buffers are reused
- * once the previous call's kernels are done, which it checks). */
+ * es.news.hada.io, "Proceso de generacion de tokens").  A pooled call with
+ * more (token, slot) pairs than the pool has slots (a prefill chunk, a
+ * batch of tokens) runs its distinct experts in batches of at most `slots`,
+ * in first-use order: each batch's misses are fetched (after the previous
+ * batch's kernels, whose slots it may reuse) and the grouped kernels run
+ * that batch's experts; the shared expert runs with the first batch and the
+ * combine after the last, so one expert fetched once serves all of the
+ * call's rows that chose it (es.news.hada.io, same section).  The output is
+ * bitwise the resident grouped path's.  Consecutive calls with one pool go
+ * on one stream (the pool's host-side buffers are reused once the previous
+ * call's kernels are done, which it checks). */
 moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *router,
                              const float *logit_bias, int32_t k, const moe_bank *routed,
                              const moe_bank *shared, moe_pool *pool, int32_t layer, void *out,

@@ -271,8 +271,11 @@ __global__ void combine_kernel(const float *__restrict__ y, const float *__restr
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t t = i / D, n = i - t * D;
-    float s = ys ? ys[i] : 0.0f;
-    for (int j = 0; j < k; ++j) s = fmaf(gates[t * k + j], y[(t * k + j) * D + n], s);
+    // in double, rounded once (exact products; outputs of large magnitude)
+    double acc = ys ? (double)ys[i] : 0.0;
+    for (int j = 0; j < k; ++j)
+      acc = fma((double)gates[t * k + j], (double)y[(t * k + j) * D + n], acc);
+    const float s = (float)acc;
     if (out_dtype == MOE_F32)
       ((float *)out)[i] = s;
     else if (out_dtype == MOE_BF16)

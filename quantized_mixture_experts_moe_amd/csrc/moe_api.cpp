@@ -575,8 +575,14 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_mid(m, s)));
   }
+  // streamed experts whose call may need more experts than the slots hold:
+  // grouped kernels in slot-sized batches of experts
+  const bool batched = pool && T * k > pool_slots(pool);
+  if (batched && (T * k > 65536 || D / 64 > kMaxDGroups || F / 64 > kMaxHGroups ||
+                  Fs / 64 > kMaxHGroups))
+    return MOE_E_UNSUPPORTED;
   FusedLaunch f;
-  const bool fused = !use_layer && tuning().fused && plan_fused(a, w, &f);
+  const bool fused = !use_layer && !batched && tuning().fused && plan_fused(a, w, &f);
   if (fused) {
     r.zero = f.slot_cnt;
     r.zero_words = T * (k + 1);
@@ -585,6 +591,59 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
     r.zero2_stride = 32;
   }
   if (launch_route(r, s) != hipSuccess) return MOE_E_HIP;
+  // the grouped kernels' launch (prefill chunks, batched streamed calls)
+  auto prefill_launch = [&](const void *const *rblobs) {
+    PrefillLaunch pl{};
+    pl.f16x = r.f16x; pl.T = T; pl.k = k; pl.E = E; pl.D = D; pl.F = F; pl.Fs = Fs;
+    pl.counts = w.perm_counts; pl.offsets = w.perm_offsets; pl.perm = w.perm; pl.inv = w.perm_inv;
+    pl.items = w.perm_items; pl.n_items = w.perm_n_items;
+    pl.item_info = w.perm_info; pl.item_blob = w.perm_iblob;
+    pl.gates = r.gates; pl.rblobs = rblobs; pl.sblobs = shared ? shared->blobs : nullptr;
+    pl.xp = w.xp; pl.xs = w.xs;
+    pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;
+    pl.hsum = w.hsum; pl.y = w.y; pl.ys = w.ys; pl.out = out; pl.out_dtype = out_dtype;
+    // the shared down projection in as many splits as make its blocks no
+    // longer than a routed expert's
+    pl.sks = shared ? min(kMaxSharedSplits, max(1, (Fs / 64 + F / 64 - 1) / (F / 64))) : 1;
+    pl.batch_blob = nullptr;
+    pl.skip_combine = 0;
+    return pl;
+  };
+  if (batched) {
+    // Streamed call with more (token, slot) pairs than slots: the work list
+    // of the grouped kernels, the ids back to the host, then for each batch
+    // of at most `slots` distinct experts (first-use order) the pool fetches
+    // the batch's misses and the gate/up and down kernels run the batch's
+    // items only (the shared expert with the first batch); one combine at
+    // the end.  Each item computes as in the resident call: the output is
+    // bitwise the resident grouped path's.
+    const void *const *ltab = pool_table(pool, layer);
+    if (launch_permute(r.ids, T, k, E, w.perm_counts, w.perm_offsets, w.perm, w.perm_inv,
+                       w.perm_items, w.perm_n_items, kPrefillRows, s, w.perm_info,
+                       w.perm_iblob, ltab) != hipSuccess)
+      return MOE_E_HIP;
+    st = pool_fetch_ids(pool, r.ids, T * k, s);
+    if (st) return st;
+    std::vector<std::vector<int>> batches;
+    st = pool_batches(pool, T, k, &batches);
+    if (st) return st;
+    PrefillLaunch pl = prefill_launch(ltab);
+    pl.skip_combine = 1;
+    for (size_t b = 0; b < batches.size(); ++b) {
+      const void *const *bt = nullptr;
+      st = pool_plan_batch(pool, layer, (int)b, batches[b], T, k, s, &bt);
+      if (st) return st;
+      pl.batch_blob = bt;
+      pl.sblobs = b == 0 && shared ? shared->blobs : nullptr;
+      if (launch_prefill_experts(pl, s) != hipSuccess) return MOE_E_HIP;
+      st = pool_batch_done(pool, s);
+      if (st) return st;
+    }
+    pl.sblobs = shared ? shared->blobs : nullptr;
+    pl.batch_blob = nullptr;
+    if (launch_prefill_combine(pl, s) != hipSuccess) return MOE_E_HIP;
+    return pool_batches_read(pool, s);
+  }
   if (fused && !pool) {
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_fused(f, s)));
@@ -619,18 +678,7 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
                        w.perm_iblob, routed->blobs) !=
         hipSuccess)
       return MOE_E_HIP;
-    PrefillLaunch pl;
-    pl.f16x = r.f16x; pl.T = T; pl.k = k; pl.E = E; pl.D = D; pl.F = F; pl.Fs = Fs;
-    pl.counts = w.perm_counts; pl.offsets = w.perm_offsets; pl.perm = w.perm; pl.inv = w.perm_inv;
-    pl.items = w.perm_items; pl.n_items = w.perm_n_items;
-    pl.item_info = w.perm_info; pl.item_blob = w.perm_iblob;
-    pl.gates = r.gates; pl.rblobs = routed->blobs; pl.sblobs = shared ? shared->blobs : nullptr;
-    pl.xp = w.xp; pl.xs = w.xs;
-    pl.hp = w.hplanes; pl.plane = (size_t)T * k * F + (size_t)T * Fs;
-    pl.hsum = w.hsum; pl.y = w.y; pl.ys = w.ys; pl.out = out; pl.out_dtype = out_dtype;
-    // the shared down projection in as many splits as make its blocks no
-    // longer than a routed expert's
-    pl.sks = shared ? min(kMaxSharedSplits, max(1, (Fs / 64 + F / 64 - 1) / (F / 64))) : 1;
+    const PrefillLaunch pl = prefill_launch(routed->blobs);
     const int pi = prof_begin(s);
     return hip_status(prof_end(pi, s, launch_prefill_experts(pl, s)));
   }

@@ -264,9 +264,14 @@ struct PrefillLaunch {
   int sks;                            // splits of the shared down projection over its hidden groups
   void *out; int out_dtype;
   int max_items;                      // work-list entries the grids cover (set by the launcher)
+  // a batch of a streamed call (null otherwise): expert -> blob in its slot,
+  // null for the experts of other batches, whose items are skipped
+  const void *const *batch_blob;
+  int skip_combine;                   // gate/up and down only (the combine runs apart)
 };
 constexpr int kMaxSharedSplits = 4;
 hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s);
+hipError_t launch_prefill_combine(const PrefillLaunch &p, hipStream_t s);
 
 // The whole decode layer in one launch (router, top-k, experts, combine).
 struct LayerLaunch {

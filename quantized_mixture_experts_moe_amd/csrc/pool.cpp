@@ -57,6 +57,15 @@ struct moe_pool {
   uint8_t *staging = nullptr;
   std::vector<hipEvent_t> stg_ev;
   std::vector<char> stg_pending;
+  // calls with more distinct experts than slots run in batches of at most
+  // `slots` experts: one device-readable table per batch (pinned, coherent:
+  // expert -> slot address, null for experts of other batches)
+  const void **h_btab = nullptr;              // [max_batches][E]
+  const void *const *d_btab = nullptr;
+  int max_batches = 0;
+  hipEvent_t ev_btab = nullptr;               // after the last kernel that reads h_btab
+  bool btab_pending = false;
+  hipEvent_t ev_batch = nullptr;              // after a batch's kernels (the next batch's copies wait)
 };
 
 namespace moe {
@@ -188,6 +197,12 @@ static moe_status wait_direct_ids(moe_pool *p, int T, int k) {
   return MOE_OK;
 }
 
+// The call's ids are in h_ids (copied back, or written by the router kernel).
+static moe_status wait_ids(moe_pool *p, int T, int k) {
+  return p->ids_mode ? wait_direct_ids(p, T, k)
+                     : (hipEventSynchronize(p->ev_ids) == hipSuccess ? MOE_OK : MOE_E_HIP);
+}
+
 namespace {
 // Misses go host -> HBM by hipMemcpyAsync on the pool's side stream.
 struct HipCopyEngine final : CopyEngine {
@@ -245,9 +260,7 @@ struct StoreCopyEngine final : CopyEngine {
 
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
                               const void *const **table, const void *const **slot_blob) {
-  const moe_status ws = p->ids_mode ? wait_direct_ids(p, T, k)
-                                      : (hipEventSynchronize(p->ev_ids) == hipSuccess ? MOE_OK
-                                                                                       : MOE_E_HIP);
+  const moe_status ws = wait_ids(p, T, k);
   if (ws) return ws;
   // the host table may still be the source of an earlier upload
   if (p->table_pending) {
@@ -298,6 +311,87 @@ moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t 
   }
   if (table) *table = p->d_tables + (size_t)layer * p->E;
   return MOE_OK;
+}
+
+moe_status pool_batches(moe_pool *p, int T, int k, std::vector<std::vector<int>> *batches) {
+  const moe_status ws = wait_ids(p, T, k);
+  if (ws) return ws;
+  std::vector<char> seen(p->E, 0);
+  std::vector<int> order;
+  for (int i = 0; i < T * k; ++i) {
+    const int e = p->h_ids[i];
+    if (e < 0 || e >= p->E) return MOE_E_POOL;
+    if (!seen[e]) {
+      seen[e] = 1;
+      order.push_back(e);
+    }
+  }
+  batches->clear();
+  for (size_t i = 0; i < order.size(); i += p->slots)
+    batches->emplace_back(order.begin() + i,
+                          order.begin() + std::min(order.size(), i + (size_t)p->slots));
+  return (int)batches->size() <= p->max_batches ? MOE_OK : MOE_E_POOL;
+}
+
+moe_status pool_plan_batch(moe_pool *p, int layer, int b, const std::vector<int> &experts, int T,
+                           int k, hipStream_t s, const void *const **btab) {
+  if (b < 0 || b >= p->max_batches) return MOE_E_POOL;
+  // the previous batch's kernels read slots this batch may evict
+  if (b > 0 && hipStreamWaitEvent(p->side, p->ev_batch, 0) != hipSuccess) return MOE_E_HIP;
+  // the kernels of an earlier call may still read the batch tables
+  if (b == 0 && p->btab_pending) {
+    if (hipEventSynchronize(p->ev_btab) != hipSuccess) return MOE_E_HIP;
+    p->btab_pending = false;
+  }
+  if (p->table_pending) {
+    if (hipEventSynchronize(p->ev_table) != hipSuccess) return MOE_E_HIP;
+    p->table_pending = false;
+  }
+  // this batch's uses, in (token, slot) order: one lookup each
+  std::vector<char> in(p->E, 0);
+  for (int e : experts) in[e] = 1;
+  std::vector<int32_t> uses;
+  for (int i = 0; i < T * k; ++i)
+    if (in[p->h_ids[i]]) uses.push_back(p->h_ids[i]);
+  const void **tab = p->h_tables + (size_t)layer * p->E;
+  LayerPlanArgs a;
+  a.ids = uses.data(); a.n = (int)uses.size(); a.E = p->E;
+  a.slot_base = p->slot_mem + (size_t)layer * p->slots * p->blob_bytes;
+  a.blob_bytes = p->blob_bytes;
+  a.host_blobs = p->store ? nullptr : p->host_blobs.data() + (size_t)layer * p->E;
+  a.table = tab;
+  HipCopyEngine hip_eng(p->side);
+  StoreCopyEngine store_eng(p, layer);
+  CopyEngine *ce = p->store ? (CopyEngine *)&store_eng : (CopyEngine *)&hip_eng;
+  FailingCopyEngine fail(ce, p->fail_copy_at);
+  if (p->fail_copy_at >= 0) ce = &fail;
+  const PlanResult r = plan_layer_call(p->planners[layer], a, *ce, &p->stats);
+  if (p->fail_copy_at >= 0) p->fail_copy_at = fail.remaining();
+  p->table_dirty[layer] = true;
+  if (r.status) return r.status;
+  const void **bt = p->h_btab + (size_t)b * p->E;
+  for (int e = 0; e < p->E; ++e) bt[e] = nullptr;
+  for (int e : experts) bt[e] = tab[e];
+  if (r.copies > 0) {
+    if (hipEventRecord(p->ev_copies, p->side) != hipSuccess) return MOE_E_HIP;
+    if (hipStreamWaitEvent(s, p->ev_copies, 0) != hipSuccess) return MOE_E_HIP;
+  }
+  *btab = p->d_btab + (size_t)b * p->E;
+  return MOE_OK;
+}
+
+moe_status pool_batch_done(moe_pool *p, hipStream_t s) {
+  return hipEventRecord(p->ev_batch, s) == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+moe_status pool_batches_read(moe_pool *p, hipStream_t s) {
+  if (hipEventRecord(p->ev_btab, s) != hipSuccess) return MOE_E_HIP;
+  p->btab_pending = true;
+  return MOE_OK;
+}
+
+const void *const *pool_table(const moe_pool *p, int layer) {
+  return p->d_tables + (size_t)layer * p->E;
 }
 
 moe_status pool_slots_read(moe_pool *p, hipStream_t s) {
@@ -379,6 +473,16 @@ static moe_status pool_create(moe_pool **out, int32_t n_layers, int32_t slots, i
   ok = ok && hipEventCreateWithFlags(&p->ev_copies, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_slot, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&p->ev_table, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->ev_btab, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->ev_batch, hipEventDisableTiming) == hipSuccess;
+  p->max_batches = (E + slots - 1) / slots;
+  ok = ok && hipHostMalloc((void **)&p->h_btab, sizeof(void *) * p->max_batches * E,
+                           hipHostMallocCoherent) == hipSuccess;
+  if (ok) {
+    void *dv = nullptr;
+    ok = hipHostGetDevicePointer(&dv, p->h_btab, 0) == hipSuccess;
+    p->d_btab = (const void *const *)dv;
+  }
   if (ok) {
     // every table entry starts at the layer's first slot (nothing resident yet)
     for (int l = 0; l < n_layers; ++l)
@@ -425,6 +529,7 @@ moe_status moe_pool_destroy(moe_pool *p) {
   if (!p) return MOE_E_INVALID;
   if (p->side) (void)hipStreamSynchronize(p->side);
   if (p->slot_pending) (void)hipEventSynchronize(p->ev_slot);
+  if (p->btab_pending) (void)hipEventSynchronize(p->ev_btab);
   if (p->slot_mem) (void)hipFree(p->slot_mem);
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->h_tables) (void)hipHostFree(p->h_tables);
@@ -436,6 +541,9 @@ moe_status moe_pool_destroy(moe_pool *p) {
   if (p->ev_copies) (void)hipEventDestroy(p->ev_copies);
   if (p->ev_slot) (void)hipEventDestroy(p->ev_slot);
   if (p->ev_table) (void)hipEventDestroy(p->ev_table);
+  if (p->ev_btab) (void)hipEventDestroy(p->ev_btab);
+  if (p->ev_batch) (void)hipEventDestroy(p->ev_batch);
+  if (p->h_btab) (void)hipHostFree(p->h_btab);
   for (auto e : p->stg_ev)
     if (e) (void)hipEventDestroy(e);
   if (p->staging) (void)hipHostFree(p->staging);

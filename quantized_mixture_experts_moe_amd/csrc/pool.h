@@ -30,5 +30,21 @@ moe_status pool_fetch_ids(moe_pool *p, const int32_t *d_ids, int n, hipStream_t 
 moe_status pool_plan_and_copy(moe_pool *p, int layer, int T, int k, hipStream_t s,
                               const void *const **table, const void *const **slot_blob);
 moe_status pool_slots_read(moe_pool *p, hipStream_t s);
+// Calls with more distinct experts than slots run in batches of at most
+// `slots` experts.  pool_batches waits for the call's ids and splits its
+// distinct experts, in first-use order, into batches.  pool_plan_batch plans
+// batch b against the slots and copies its misses (the side stream first
+// waits for the previous batch's kernels, recorded by pool_batch_done, since
+// this batch may evict their experts), makes stream s wait for the copies and
+// publishes a device-readable table *btab [E]: the slot of each expert of the
+// batch, null for every other expert.  pool_batches_read: after the last
+// kernel that reads the tables.
+moe_status pool_batches(moe_pool *p, int T, int k, std::vector<std::vector<int>> *batches);
+moe_status pool_plan_batch(moe_pool *p, int layer, int b, const std::vector<int> &experts, int T,
+                           int k, hipStream_t s, const void *const **btab);
+moe_status pool_batch_done(moe_pool *p, hipStream_t s);
+moe_status pool_batches_read(moe_pool *p, hipStream_t s);
+// The layer's device table (expert -> slot address or a placeholder).
+const void *const *pool_table(const moe_pool *p, int layer);
 
 }  // namespace moe

@@ -317,6 +317,10 @@ __global__ __launch_bounds__(256, 4) void glu_mfma_kernel(PrefillLaunch p) {
     const int2 inf = p.item_info[item];
     const void *bl = p.item_blob[item];
     if (item >= n_it) return;
+    if (p.batch_blob) {  // a batch of a streamed call: only its experts, from their slots
+      bl = p.batch_blob[it & 0xFFFF];
+      if (!bl) return;
+    }
     yc = it >> 16;
     rg.count = inf.x, rg.off = inf.y, rg.F = p.F, rg.blob = (const uint8_t *)bl, rg.shared = false;
   }
@@ -390,9 +394,14 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   };
   const uint32_t umagic = opaque_vgpr(0x3F803F80u);  // bf16 1.0 pairs
 
-  f32x4_t t[kDT];
+  // each group's fold is added in double: the rows' sums reach about 5e4
+  // (the folds of a few groups already about 3e4), where adding the folds in
+  // fp32 rounds at several ulps of the result over the expert's groups
+  double t[kDT][4];
 #pragma unroll
-  for (int j = 0; j < kDT; ++j) t[j] = f32x4_t{0, 0, 0, 0};
+  for (int j = 0; j < kDT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[j][i] = 0.0;
 #pragma unroll
   for (int s = 0; s < kRd - 1; ++s) issue(buf(s), s);
   for (int g0 = 0; g0 < GH; g0 += kRd) {
@@ -432,7 +441,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
         const float sd = live ? f16_to_f32(mw) : 0.0f, bd = live ? f16_to_f32(mw >> 16) : 0.0f;
         const float s16 = 16.0f * sd, c16 = fmaf(-16.0f, sd, bd);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t[j][i] = fmaf(s16, a[i], fmaf(c16, hs[i], t[j][i]));
+        for (int i = 0; i < 4; ++i) t[j][i] += (double)fmaf(s16, a[i], c16 * hs[i]);
       }
     }
   }
@@ -444,7 +453,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = kb * 4 + i;
-      if (m < nrow && n < D) dst[(size_t)(row0 + m0 + m) * D + n] = t[j][i];
+      if (m < nrow && n < D) dst[(size_t)(row0 + m0 + m) * D + n] = (float)t[j][i];
     }
   }
 }
@@ -488,6 +497,10 @@ __global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
     const int2 inf = p.item_info[item];
     const void *bl = p.item_blob[item];
     if (item >= n_it) return;
+    if (p.batch_blob) {
+      bl = p.batch_blob[it & 0xFFFF];
+      if (!bl) return;
+    }
     yc = 2 * (it >> 16) + half;
     rg.count = inf.x, rg.off = inf.y, rg.F = p.F, rg.blob = (const uint8_t *)bl, rg.shared = false;
   }
@@ -523,7 +536,10 @@ __global__ void combine_prefill_kernel(PrefillLaunch p) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total4;
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t t = i / D4, d = (i - t * D4) * 4;
-    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    // summed in double and rounded once: the outputs reach about 1e5, where
+    // one fp32 rounding per added row would already cost several ulps (a
+    // product of two floats is exact in double)
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
     if (p.sblobs) {
       float4 v[kMaxSharedSplits];
 #pragma unroll
@@ -531,7 +547,7 @@ __global__ void combine_prefill_kernel(PrefillLaunch p) {
         if (ks < p.sks) v[ks] = *(const float4 *)(p.ys + (size_t)ks * total + t * p.D + d);
 #pragma unroll
       for (int ks = 0; ks < kMaxSharedSplits; ++ks)
-        if (ks < p.sks) s.x += v[ks].x, s.y += v[ks].y, s.z += v[ks].z, s.w += v[ks].w;
+        if (ks < p.sks) s[0] += v[ks].x, s[1] += v[ks].y, s[2] += v[ks].z, s[3] += v[ks].w;
     }
     for (int j0 = 0; j0 < k; j0 += KB) {
       int row[KB];
@@ -548,14 +564,16 @@ __global__ void combine_prefill_kernel(PrefillLaunch p) {
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         if (j0 + j < k) {
-          s.x = fmaf(gt[j], v[j].x, s.x), s.y = fmaf(gt[j], v[j].y, s.y);
-          s.z = fmaf(gt[j], v[j].z, s.z), s.w = fmaf(gt[j], v[j].w, s.w);
+          const double g = gt[j];
+          s[0] = fma(g, (double)v[j].x, s[0]), s[1] = fma(g, (double)v[j].y, s[1]);
+          s[2] = fma(g, (double)v[j].z, s[2]), s[3] = fma(g, (double)v[j].w, s[3]);
         }
       }
     }
+    const float4 sf = make_float4((float)s[0], (float)s[1], (float)s[2], (float)s[3]);
     const size_t o = t * p.D + d;
     if (!aligned) {
-      const float v[4] = {s.x, s.y, s.z, s.w};
+      const float v[4] = {sf.x, sf.y, sf.z, sf.w};
       for (int u = 0; u < 4; ++u) {
         if (p.out_dtype == MOE_F32)
           ((float *)p.out)[o + u] = v[u];
@@ -565,13 +583,13 @@ __global__ void combine_prefill_kernel(PrefillLaunch p) {
           ((uint16_t *)p.out)[o + u] = (uint16_t)f32_to_f16(v[u]);
       }
     } else if (p.out_dtype == MOE_F32) {
-      *(float4 *)((float *)p.out + o) = s;
+      *(float4 *)((float *)p.out + o) = sf;
     } else {
       const bool bf = p.out_dtype == MOE_BF16;
-      const uint32_t c0 = bf ? f32_to_bf16(s.x) : f32_to_f16(s.x);
-      const uint32_t c1 = bf ? f32_to_bf16(s.y) : f32_to_f16(s.y);
-      const uint32_t c2 = bf ? f32_to_bf16(s.z) : f32_to_f16(s.z);
-      const uint32_t c3 = bf ? f32_to_bf16(s.w) : f32_to_f16(s.w);
+      const uint32_t c0 = bf ? f32_to_bf16(sf.x) : f32_to_f16(sf.x);
+      const uint32_t c1 = bf ? f32_to_bf16(sf.y) : f32_to_f16(sf.y);
+      const uint32_t c2 = bf ? f32_to_bf16(sf.z) : f32_to_f16(sf.z);
+      const uint32_t c3 = bf ? f32_to_bf16(sf.w) : f32_to_f16(sf.w);
       *(uint2 *)((uint16_t *)p.out + o) = make_uint2(c0 | (c1 << 16), c2 | (c3 << 16));
     }
   }
@@ -602,7 +620,12 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   dim3 g2(grouped_blocks(max_items, 2 * nb4) + (p.sblobs ? grouped_blocks(p.sks * nb4, mch16) : 0));
   hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, q);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.skip_combine) return e;
+  return launch_prefill_combine(p, s);
+}
+
+hipError_t launch_prefill_combine(const PrefillLaunch &p, hipStream_t s) {
+  PrefillLaunch q = p;
   const size_t total = (size_t)p.T * p.D / 4;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
