@@ -599,6 +599,132 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
                                                  const bool (&use)[M], uint32_t (&hpl)[kNW][M][3][32],
                                                  float (&red)[kNW][2][64], int ot, size_t out_idx,
                                                  int wave, int lane, uint32_t tag) {
+  float acc = 0.0f;
+  if constexpr (M <= 3) {
+  // Each unit is taken as soon as its hidden values are published: lanes
+  // 2i, 2i + 1 poll one word of unit i's rows (the hint, two polls in
+  // flight); every round, the units whose hints have landed read their
+  // values (checked), go through LDS as three bf16 planes and meet their
+  // down codes on the matrix cores.  The units' contributions are added in
+  // unit order at the end, so the sum does not depend on the order in which
+  // the units arrived.
+  const uint64_t *hint = L.hg + hp[0];
+  uint32_t pending = 0;  // wave-uniform: units still to take
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    if (use[i]) pending |= 1u << i;
+    if (lane == 2 * i) hint = L.hg + hp[i];
+    if (lane == 2 * i + 1) hint = L.hu + hp[i];
+  }
+  // matrix cores: lane l holds word w (8 hidden rows) of output row l as
+  // B (codes as 1 + q / 16); lanes with l % 16 = 4 (l / 16) + p, p < 3,
+  // hold plane p of h as A row 4 (l / 16) + p, so registers 0..2 of lane l
+  // accumulate the three planes' dot products of output row l.
+  const int plane = (lane & 15) - 4 * (lane >> 4);
+  const bool ha_lane = plane >= 0 && plane < 3;
+  const uint32_t umagic = opaque_vgpr(0x3F803F80u);
+  const int pos = 2 * (4 * (lane >> 3) + (lane & 3)) + ((lane >> 2) & 1);
+  float vunit[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) vunit[i] = 0.0f;
+  uint64_t hw = ld_dev64(hint);
+  for (long s = 0; pending;) {
+    __builtin_amdgcn_s_sleep(1);
+    const uint64_t nx = ld_dev64(hint);
+    const uint64_t b = __ballot(has_tag(hw, tag));
+    uint32_t ready = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (((b >> (2 * i)) & 3u) == 3u) ready |= 1u << i;
+    ready &= pending;
+    hw = nx;
+    if (!ready) {
+      if (++s > kSpin) {
+        if (lane == 0) add_dev(L.err, 1u);
+        break;
+      }
+      continue;
+    }
+    pending &= ~ready;
+    // the ready units' values, read until every word carries the epoch (a
+    // hint may land before the other words of its unit)
+    uint64_t wg[M], wu[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      wg[i] = 0;
+      wu[i] = 0;
+      if (ready >> i & 1u) {
+        wg[i] = ld_dev64(L.hg + hp[i] + lane);
+        wu[i] = ld_dev64(L.hu + hp[i] + lane);
+      }
+    }
+    for (long r = 0;; ++r) {
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < M; ++i)
+        ok = ok && (!(ready >> i & 1u) || (has_tag(wg[i], tag) && has_tag(wu[i], tag)));
+      if (__all(ok)) break;
+      if (r > kSpin) {
+        if (lane == 0) add_dev(L.err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        if (ready >> i & 1u) {
+          wg[i] = ld_dev64(L.hg + hp[i] + lane);
+          wu[i] = ld_dev64(L.hu + hp[i] + lane);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (!(ready >> i & 1u)) continue;
+      const float hv = __uint_as_float((uint32_t)wg[i]) * __uint_as_float((uint32_t)wu[i]);
+      // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
+      // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
+      const uint32_t p0 = f32_to_bf16(hv);
+      const float r1 = hv - __uint_as_float(p0 << 16);
+      const uint32_t p1 = f32_to_bf16(r1);
+      const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
+      uint16_t *hp16 = (uint16_t *)&hpl[wave][i][0][0];
+      hp16[pos] = (uint16_t)p0;
+      hp16[64 + pos] = (uint16_t)p1;
+      hp16[128 + pos] = (uint16_t)p2;
+      const float hsum = wave_sum(hv);
+      __builtin_amdgcn_wave_barrier();
+      // the codes pass an empty asm here, or the compiler would unpack every
+      // unit's codes ahead of the polling loop and hold them all in registers
+      u32x4 q0 = R.dq0[i], q1 = R.dq1[i];
+      asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w));
+      asm volatile("" : "+v"(q1.x), "+v"(q1.y), "+v"(q1.z), "+v"(q1.w));
+      const uint32_t wd[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      u32x4 a[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
+      if (ha_lane) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&hpl[wave][i][plane][4 * w];
+      }
+      // two accumulation chains (even and odd words)
+      f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < 8; w += 2) {
+        d0 = mma16<false>(a[w], code_pairs_unit(wd[w], umagic), d0);
+        d1 = mma16<false>(a[w + 1], code_pairs_unit(wd[w + 1], umagic), d1);
+      }
+      // sum (1 + q/16) h = sum h + sum q h / 16, three planes
+      const float dsum = ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2]);
+      const float sc = f16_to_f32(R.dmw[i]), bi = f16_to_f32(R.dmw[i] >> 16);
+      vunit[i] = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+    if (use[i]) acc = fmaf(gate[i], vunit[i], acc);
+  } else {
+  // four units per wave: all hints first, then every unit (the
+  // incremental form above spills registers at this width)
   // lanes 2i, 2i + 1 poll one word of unit i's rows (the hint), then the
   // values are read (and checked).  Units a wave does not use are loaded too
   // (valid rows) and not checked.
@@ -661,7 +787,6 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
   const int plane = (lane & 15) - 4 * (lane >> 4);
   const bool ha_lane = plane >= 0 && plane < 3;
   const uint32_t umagic = opaque_vgpr(0x3F803F80u);
-  float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     if (!use[i]) continue;
@@ -686,6 +811,7 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
     const float sc = f16_to_f32(R.dmw[i]), bi = f16_to_f32(R.dmw[i] >> 16);
     const float v = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum[i]);
     acc = fmaf(gate[i], v, acc);
+  }
   }
   __syncthreads();  // red[] is reused
   red[wave][0][lane] = acc;
@@ -919,7 +1045,7 @@ __device__ __forceinline__ u32x4 finish_norm(const LayerLaunch &L, const NormIn<
 // launch): x is the residual stream, every role normalises it into the
 // layer's input, and the output rows get the post-norm and the residual.
 template <bool F16X, int M, int MAXC, bool TWO, bool NORM = false, int RT = 1>
-__global__ __launch_bounds__(kThreads, 3) void decode_layer_kernel(LayerLaunch L) {
+__global__ __launch_bounds__(kThreads, (NORM && MAXC == 8) ? 3 : 4) void decode_layer_kernel(LayerLaunch L) {
   extern __shared__ __align__(16) uint8_t dsm[];
   __shared__ float red[kNW][2][64];
   __shared__ __align__(16) uint32_t hpl[kNW][M][3][32];  // h planes as bf16 pairs
