@@ -196,8 +196,12 @@ def run_stack(cfg, a, moe, torch):
 
 
 def run_streamed(cfg, a, moe, torch):
-    """30 layers, 16 HBM slots per layer, experts streamed from pinned host memory."""
+    """30 layers, 16 HBM slots per layer, experts streamed from pinned host
+    memory.  --tokens T > 1: each call carries T tokens (a prefill chunk per
+    layer, run in slot-sized batches of its experts); --stream-tokens steps."""
     n_layers, n_tok = cfg.layers, a.stream_tokens
+    T = a.tokens if a.tokens > 0 else 1
+    n_warm = 16 if T == 1 else 2
     nb = gen.blob_bytes(cfg.D, cfg.F)
     log(f"streamed: pinning {n_layers * cfg.E * nb / 1e9:.1f} GB of host experts")
     t0 = time.perf_counter()
@@ -213,19 +217,19 @@ def run_streamed(cfg, a, moe, torch):
     slots = a.slots if a.slots > 0 else cfg.slots
     pool = moe.Pool(host, n_layers, slots, cfg.E, cfg.D, cfg.F)
     pool.set_policy(1 if a.pool_policy == "lru" else 0)
-    xb = np.stack([gen.activations(a.seed, 2000 + l, 0, n_tok + 16, cfg.D, cfg.x_dtype)
+    xb = np.stack([gen.activations(a.seed, 2000 + l, 0, (n_tok + n_warm) * T, cfg.D, cfg.x_dtype)
                    for l in range(n_layers)])
     x_all = torch.from_numpy(xb.astype(np.int16)).cuda().view(torch.bfloat16)
-    out = torch.empty(1, cfg.D, dtype=torch.float32, device="cuda")
-    ws = moe.Workspace(1, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
+    out = torch.empty(T, cfg.D, dtype=torch.float32, device="cuda")
+    ws = moe.Workspace(T, cfg.k, cfg.E, cfg.D, cfg.F, cfg.F_shared)
 
     def token(t):
         for l in range(n_layers):
             router, shared, bias = devs[l]
-            moe.moe_layer_forward(x_all[l, t:t + 1], router, cfg.k, None, shared, out, ws,
-                                  logit_bias=bias, pool=pool, layer=l)
+            moe.moe_layer_forward(x_all[l, t * T:(t + 1) * T], router, cfg.k, None, shared, out,
+                                  ws, logit_bias=bias, pool=pool, layer=l)
 
-    for t in range(16):  # warm the slots
+    for t in range(n_warm):  # warm the slots
         token(n_tok + t)
     torch.cuda.synchronize()
     pool.reset_stats()
@@ -245,9 +249,10 @@ def run_streamed(cfg, a, moe, torch):
         dst.copy_(src, non_blocking=True)
     torch.cuda.synchronize()
     peak = 4 * src.numel() / (time.perf_counter() - t1) / 1e9
-    res = {"tokens": n_tok, "layers": n_layers, "slots": slots, "policy": a.pool_policy, "s": el,
-           "tokens_per_s": n_tok / el, "hit_rate": st["hits"] / max(1, st["lookups"]),
-           "miss_MB_per_token": st["bytes_h2d"] / n_tok / 1e6,
+    res = {"tokens": n_tok * T, "tokens_per_call": T, "layers": n_layers, "slots": slots,
+           "policy": a.pool_policy, "s": el,
+           "tokens_per_s": n_tok * T / el, "hit_rate": st["hits"] / max(1, st["lookups"]),
+           "miss_MB_per_token": st["bytes_h2d"] / (n_tok * T) / 1e6,
            "h2d_GBps": st["bytes_h2d"] / el / 1e9, "pinned_copy_peak_GBps": peak, "beta": cfg.beta}
     log(f"streamed: {res}")
     pool.close()
