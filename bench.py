@@ -590,6 +590,23 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # the chip's streaming read rate, measured: a read of a 4 GiB buffer (far
+    # beyond the Infinity Cache), best of five
+    probe = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    read_gbps = 0.0
+    with torch.cuda.stream(stream):
+        for i in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            moe.moe_read_probe(probe, sink, 8192, stream)
+            e1.record(stream)
+            e1.synchronize()
+            if i:
+                read_gbps = max(read_gbps, probe.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del probe
+    log(f"streaming read of 4 GiB: {read_gbps:,.0f} GB/s")
+
     cpu = None
     if not a.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -623,6 +640,9 @@ def main():
         "hbm_GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": k_gbps / HBM_PEAK_GBPS if k_gbps else None, "traffic": traffic,
+                     "measured_read_peak": read_gbps,
+                     "frac_of_measured_read_peak": (k_gbps / read_gbps
+                                                    if k_gbps and read_gbps else None),
                      "kernel": k_name, "us_per_launch": k_us,
                      "algorithmic_bytes_per_launch": k_bytes},
         "cpu_baseline": cpu,

@@ -371,6 +371,17 @@ moe_status moe_set_profile_events(void *const *events, int32_t n_pairs);
  *   route_mfma (1)       router of 16 or more tokens on the matrix cores */
 moe_status moe_set_tuning(const char *key, int32_t value);
 
+/* Measurement helper, not a step of the method: reads `bytes` of device
+ * memory at `buf` once (16-byte aligned, a multiple of 16 bytes) with
+ * streaming 16-byte loads over `blocks` workgroups of 256 threads, and writes
+ * one uint32 per workgroup into sink (device [blocks]).  Its duration on a
+ * buffer much larger than the 256 MB Infinity Cache measures the rate at
+ * which the chip streams reads from HBM, the practical ceiling that the
+ * benchmark also reports the kernels' achieved bytes per second against.
+ * MOE_E_INVALID for a bad argument; asynchronous on `stream`. */
+moe_status moe_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,
+                          void *stream);
+
 /* Static text for a status code. */
 const char *moe_status_string(moe_status status);
 

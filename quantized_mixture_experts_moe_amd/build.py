@@ -24,7 +24,7 @@ BUILD_DIR = os.path.join(ROOT, "_build", "libmoe")
 
 SOURCES = ["moe_api.cpp", "pool.cpp", "route.hip", "expert_gemv.hip", "expert_fused.hip",
            "permute.hip", "prefill_mfma.hip", "layer_decode.hip", "block_norm.hip", "noalloc.cpp",
-           "store.cpp", "expert_mid.hip"]
+           "store.cpp", "expert_mid.hip", "probe.hip"]
 
 
 def hipcc() -> str:

@@ -39,7 +39,7 @@ EXPORTS = (
     "moe_set_profile_events", "moe_workspace_timeouts", "moe_status_string",
     "moe_layer_forward_noalloc", "moe_store_stride", "moe_store_open", "moe_store_read",
     "moe_store_get_stats", "moe_store_close", "moe_pool_create_store", "moe_block_forward",
-    "moe_block_workspace_bytes",
+    "moe_block_workspace_bytes", "moe_read_probe",
 )
 
 MOE_STORE_DIRECT = 1
@@ -114,6 +114,7 @@ def _load() -> ctypes.CDLL:
         "moe_set_profile_events": (i32, [vp, i32]),
         "moe_workspace_timeouts": (i32, [vp, sz, P(ctypes.c_uint32), vp]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_read_probe": (i32, [vp, sz, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -154,6 +155,12 @@ def moe_workspace_bytes(T: int, k: int, E: int, D: int, F: int, F_shared: int) -
 
 def moe_block_workspace_bytes(T: int, k: int, E: int, D: int, F: int, F_shared: int) -> int:
     return int(lib.moe_block_workspace_bytes(T, k, E, D, F, F_shared))
+
+
+def moe_read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks: int, stream=None) -> None:
+    """Streaming read of the whole device buffer (measurement helper)."""
+    _check(lib.moe_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), blocks,
+                              _stream(stream)), "moe_read_probe")
 
 
 def moe_set_tuning(key: str, value: int) -> None:
