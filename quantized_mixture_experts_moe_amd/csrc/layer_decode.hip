@@ -636,7 +636,6 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
                                                  float (&red)[kNW][2][64], int ot, size_t out_idx,
                                                  int wave, int lane, uint32_t tag) {
   float acc = 0.0f;
-  if constexpr (M <= 3) {
   // Each unit is taken as soon as its hidden values are published: lanes
   // 2i, 2i + 1 poll one word of unit i's rows (the hint, two polls in
   // flight); every round, the units whose hints have landed read their
@@ -758,97 +757,6 @@ __device__ __forceinline__ void down_and_combine(const LayerLaunch &L, const Dow
 #pragma unroll
   for (int i = 0; i < M; ++i)
     if (use[i]) acc = fmaf(gate[i], vunit[i], acc);
-  } else {
-  // four units per wave: all hints first, then every unit (the
-  // incremental form above spills registers at this width)
-  // lanes 2i, 2i + 1 poll one word of unit i's rows (the hint), then the
-  // values are read (and checked).  Units a wave does not use are loaded too
-  // (valid rows) and not checked.
-  const uint64_t *hint = L.hg + hp[0];
-  bool active = false;
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    if (use[i] && lane == 2 * i) hint = L.hg + hp[i], active = true;
-    if (use[i] && lane == 2 * i + 1) hint = L.hu + hp[i], active = true;
-  }
-  wait_hint(hint, active, tag, L.err);
-  uint64_t wg[M], wu[M];
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    wg[i] = ld_dev64(L.hg + hp[i] + lane);
-    wu[i] = ld_dev64(L.hu + hp[i] + lane);
-  }
-  for (long s = 0;; ++s) {
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < M; ++i) ok = ok && (!use[i] || (has_tag(wg[i], tag) && has_tag(wu[i], tag)));
-    if (__all(ok)) break;
-    if (s > kSpin) {
-      if (lane == 0) add_dev(L.err, 1u);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      wg[i] = ld_dev64(L.hg + hp[i] + lane);
-      wu[i] = ld_dev64(L.hu + hp[i] + lane);
-    }
-  }
-  float hv0[M];
-#pragma unroll
-  for (int i = 0; i < M; ++i)
-    hv0[i] = use[i] ? __uint_as_float((uint32_t)wg[i]) * __uint_as_float((uint32_t)wu[i]) : 0.0f;
-  // h as three bf16 planes (hi + mid + lo = the fp32 value) in LDS, as
-  // pairs (h[8w + m], h[8w + m + 4]) like the activations of gate/up
-  float hsum[M];
-  const int pos = 2 * (4 * (lane >> 3) + (lane & 3)) + ((lane >> 2) & 1);
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    const float hv = hv0[i];
-    const uint32_t p0 = f32_to_bf16(hv);
-    const float r1 = hv - __uint_as_float(p0 << 16);
-    const uint32_t p1 = f32_to_bf16(r1);
-    const uint32_t p2 = f32_to_bf16(r1 - __uint_as_float(p1 << 16));
-    uint16_t *hp16 = (uint16_t *)&hpl[wave][i][0][0];
-    hp16[pos] = (uint16_t)p0;
-    hp16[64 + pos] = (uint16_t)p1;
-    hp16[128 + pos] = (uint16_t)p2;
-    hsum[i] = wave_sum(hv);
-  }
-  __builtin_amdgcn_wave_barrier();
-  // matrix cores: lane l holds word w (8 hidden rows) of output row l as
-  // B (codes as 1 + q / 16); lanes with l % 16 = 4 (l / 16) + p, p < 3,
-  // hold plane p of h as A row 4 (l / 16) + p, so registers 0..2 of lane l
-  // accumulate the three planes' dot products of output row l.
-  const int plane = (lane & 15) - 4 * (lane >> 4);
-  const bool ha_lane = plane >= 0 && plane < 3;
-  const uint32_t umagic = opaque_vgpr(0x3F803F80u);
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    if (!use[i]) continue;
-    const uint32_t wd[8] = {R.dq0[i].x, R.dq0[i].y, R.dq0[i].z, R.dq0[i].w,
-                            R.dq1[i].x, R.dq1[i].y, R.dq1[i].z, R.dq1[i].w};
-    u32x4 a[8];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) a[w] = u32x4{0u, 0u, 0u, 0u};
-    if (ha_lane) {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) a[w] = *(const u32x4 *)&hpl[wave][i][plane][4 * w];
-    }
-    // two accumulation chains (even and odd words)
-    f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int w = 0; w < 8; w += 2) {
-      d0 = mma16<false>(a[w], code_pairs_unit(wd[w], umagic), d0);
-      d1 = mma16<false>(a[w + 1], code_pairs_unit(wd[w + 1], umagic), d1);
-    }
-    // sum (1 + q/16) h = sum h + sum q h / 16, three planes
-    const float dsum = ((d0[0] + d1[0]) + (d0[1] + d1[1])) + (d0[2] + d1[2]);
-    const float sc = f16_to_f32(R.dmw[i]), bi = f16_to_f32(R.dmw[i] >> 16);
-    const float v = fmaf(16.0f * sc, dsum, fmaf(-16.0f, sc, bi) * hsum[i]);
-    acc = fmaf(gate[i], v, acc);
-  }
-  }
   __syncthreads();  // red[] is reused
   red[wave][0][lane] = acc;
   __syncthreads();
