@@ -241,7 +241,7 @@ bool plan_layer(const Workspace &w, LayerLaunch *L) {
   L->sel = c.take<uint64_t>((size_t)T * L->sel_copies * L->sel_stride, 8);
   L->hg = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
   L->hu = c.take<uint64_t>((size_t)T * k * F + (size_t)T * Fs, 8);
-  if (kTaggedOff + c.off > kRouteTagOff) return false;
+  if (kTaggedOff + c.off > kRowTagOff) return false;
   L->table_off = layer_table_off(*L);
   L->err = w.err;
   return true;
@@ -432,6 +432,8 @@ moe_status moe_route(const void *x, int32_t x_dtype, int32_t T, const moe_qmat *
   a.table = nullptr; a.slot_blob = nullptr;
   a.zero = nullptr; a.zero_words = 0; a.zero2 = nullptr; a.zero2_count = 0; a.zero2_stride = 0;
   a.rtag = (uint64_t *)(w.layer + kRouteTagOff); a.rep = (uint32_t *)(w.layer + kRouteEpochOff);
+  a.rowtag = (uint64_t *)(w.layer + kRowTagOff); a.rowep = (uint32_t *)(w.layer + kRowEpochOff);
+  a.err = w.err;
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -541,6 +543,8 @@ moe_status moe_layer_forward(const void *x, int32_t x_dtype, int32_t T, const mo
   r.logits = w.logits; r.ids = ids_out ? ids_out : w.ids; r.gates = gates_out ? gates_out : w.gates;
   r.xp = w.xp; r.xs = w.xs; r.counters = w.counters;
   r.rtag = (uint64_t *)(w.layer + kRouteTagOff); r.rep = (uint32_t *)(w.layer + kRouteEpochOff);
+  r.rowtag = (uint64_t *)(w.layer + kRowTagOff); r.rowep = (uint32_t *)(w.layer + kRowEpochOff);
+  r.err = w.err;
   // resident experts: the router also resolves each selected expert's blob;
   // streamed experts: the pool writes the slot addresses after its copies
   r.table = pool ? nullptr : routed->blobs;

@@ -59,6 +59,14 @@ static_assert(kRouteEpochOff % kAlign == 0, "aligned");
 constexpr int kRouteParts = 4;
 constexpr size_t kRouteTagBytes = size_t(4) << 20;
 constexpr size_t kRouteTagOff = kRouteEpochOff - kRouteTagBytes;
+// The row router's tagged logits [T][E] (calls of at most kRowTagTokens
+// tokens) and its per-block epochs [kRowEpochs], below them; the one-launch
+// layer's tagged words end below kRowTagOff.
+constexpr int kRowTagTokens = 15;
+constexpr int kRowEpochs = 4096;
+constexpr size_t kRowEpochOff = kRouteTagOff - sizeof(uint32_t) * kRowEpochs;
+constexpr size_t kRowTagOff = kRowEpochOff - sizeof(uint64_t) * kRowTagTokens * kMaxE;
+static_assert(kRowTagOff % kAlign == 0, "aligned");
 
 __host__ __device__ inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -170,6 +178,10 @@ struct RouteLaunch {
   // [kRouteParts][T][E] and the epochs [kMaxRouteTiles], in the fixed
   // region (zero-filled once)
   uint64_t *rtag; uint32_t *rep;
+  // at most kRowTagTokens tokens (row router): tagged logits [T][E] and the
+  // per-block epochs [kRowEpochs] in the fixed region (zero-filled once);
+  // null: the last block of a token group selects (counter)
+  uint64_t *rowtag; uint32_t *rowep; uint32_t *err;
   // fewer than 16 tokens, streamed experts: the ids also go to pinned host
   // memory (device-readable addresses), then host_flag[t] = host_epoch per
   // token, so that the host reads them without a copy; null otherwise

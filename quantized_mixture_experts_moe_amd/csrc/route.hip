@@ -61,6 +61,56 @@ __device__ void topk_wave(const float *lg, int E, int k, int32_t *ids, float *ga
     topk_wave_t<16>(lg, E, k, ids, gates, table, slot_blob, xch, host_ids);
 }
 
+// Top-k of token t's logits published as tagged words (value, epoch) by the
+// token group's blocks: one wave polls the E words (NV per lane) until each
+// carries `tag` (bounded, then the error word), then selects as topk_wave;
+// the blob addresses come from the table staged in LDS.
+template <int NV>
+__device__ void topk_tagged_t(const uint64_t *lg, int E, int k, uint32_t tag, int32_t *ids,
+                              float *gates, const void *const *s_tab, const void **slot_blob,
+                              uint2 *xch, int32_t *host_ids, uint32_t *err) {
+  const int lane = threadIdx.x & 63;
+  uint64_t w[NV];
+  for (long s = 0;; ++s) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) w[j] = ld_dev(lg + min(lane + 64 * j, E - 1));
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ok = ok && (lane + 64 * j >= E || (uint32_t)(w[j] >> 32) == tag);
+    if (__all(ok)) break;
+    if (s > (1L << 20)) {
+      if (lane == 0) add_dev(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    v[j] = lane + 64 * j < E ? __uint_as_float((uint32_t)w[j]) : -INFINITY;
+  int32_t id;
+  float gate;
+  topk_regs(v, k, xch, &id, &gate);
+  if (lane < k) {
+    ids[lane] = id;
+    gates[lane] = gate;
+    if (slot_blob) slot_blob[lane] = s_tab[id];
+    if (host_ids) host_ids[lane] = id;
+  }
+}
+__device__ void topk_tagged(const uint64_t *lg, int E, int k, uint32_t tag, int32_t *ids,
+                            float *gates, const void *const *s_tab, const void **slot_blob,
+                            uint2 *xch, int32_t *host_ids, uint32_t *err) {
+  if (E <= 128)
+    topk_tagged_t<2>(lg, E, k, tag, ids, gates, s_tab, slot_blob, xch, host_ids, err);
+  else if (E <= 256)
+    topk_tagged_t<4>(lg, E, k, tag, ids, gates, s_tab, slot_blob, xch, host_ids, err);
+  else if (E <= 512)
+    topk_tagged_t<8>(lg, E, k, tag, ids, gates, s_tab, slot_blob, xch, host_ids, err);
+  else
+    topk_tagged_t<16>(lg, E, k, tag, ids, gates, s_tab, slot_blob, xch, host_ids, err);
+}
+
 // Activations [nt][D] of fp16/bf16 bits into LDS as fp32: every thread issues
 // its 16-byte loads first (clamped in range), then converts.
 template <bool F16X, int NV>
@@ -97,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
   float *red = sxs + TT * nch;       // [KL][ROWS*TT]
   __shared__ int s_last;
   __shared__ uint2 s_xch[TT][128];  // top-k exchange, one area per selecting wave
+  __shared__ const void *s_tab[kMaxE];  // the blob table (tagged selection)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,6 +177,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
   // the logit bias of the row that wave 0's lane finishes (lane % ROWS)
   const float lbias =
       a.logit_bias ? a.logit_bias[min((int)blockIdx.x * ROWS + lane % ROWS, E - 1)] : 0.0f;
+  // Calls of at most kRowTagTokens tokens publish their logits as tagged
+  // words (value, call epoch) and block 0 of each token group selects as
+  // soon as all of them carry the epoch: no wait for the stores, no counter,
+  // no reload after the last block.  Each block keeps its own copy of the
+  // epoch and every block advances the copies b, b + grid, ... so that all
+  // copies agree whatever the next call's grid.
+  const bool tagged = a.rowtag && a.T <= kRowTagTokens && TT == 1;
+  const int bid = blockIdx.y * gridDim.x + blockIdx.x, nblk = gridDim.x * gridDim.y;
+  uint32_t tag = 0;
+  const bool selector = tagged && blockIdx.x == 0;
+  if (tagged) {
+    tag = __hip_atomic_load(a.rowep + bid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // the selecting block stages the blob table while the logits are made
+    if (selector && a.slot_blob)
+      for (int i = tid; i < E; i += kThreads) s_tab[i] = a.table[i];
+  }
   stage_x<F16X, (TT * 8192 / 8 + kThreads - 1) / kThreads>(x, nt * D, sx);
   for (int i = nt * D + tid; i < TT * D; i += kThreads) sx[i] = 0.0f;
   __syncthreads();
@@ -205,8 +272,35 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteLaunch a) {
       if (ee < E && tt < nt) {
         if (a.logit_bias) s += lbias;
         st_dev(a.logits + (size_t)(t0 + tt) * E + ee, s);
+        if (tagged)
+          st_dev(a.rowtag + (size_t)(t0 + tt) * E + ee,
+                 (uint64_t)__float_as_uint(s) | ((uint64_t)tag << 32));
       }
     }
+  }
+  if (tagged) {
+    if (selector) {
+      __syncthreads();  // the staged table
+      if (wave < nt) {
+        const int t = t0 + wave;
+        topk_tagged(a.rowtag + (size_t)t * E, E, a.k, tag, a.ids + (size_t)t * a.k,
+                    a.gates + (size_t)t * a.k, s_tab,
+                    a.slot_blob ? a.slot_blob + (size_t)t * a.k : nullptr, s_xch[wave],
+                    a.host_ids ? a.host_ids + (size_t)t * a.k : nullptr, a.err);
+      }
+      if (a.host_ids) {
+        __threadfence_system();
+        __syncthreads();
+        if (tid < nt)
+          __hip_atomic_store(a.host_flag + t0 + tid, a.host_epoch, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+    if (tid == 0)
+      for (int j = bid; j < kRowEpochs; j += nblk) st_dev(a.rowep + j, tag);
+    return;
+  }
+  if (wave == 0) {
     wait_all_memory();
     uint32_t old = 0;
     if (lane == 0) old = add_dev(&a.counters[blockIdx.y], 1u);

@@ -166,6 +166,37 @@ def _route_parity(name, T, beta):
     assert np.all(np.diff(gates.cpu().numpy(), axis=1) <= 0)
 
 
+def test_route_epochs_across_calls():
+    """The row router's tagged logits on one workspace across calls of 3, 15,
+    1, 7, 2 and 40 tokens (grids of different sizes; 40 tokens take the
+    counter path with the matrix-core router off), then 5 again: every call's
+    ids, gates and logits are those of the same call on a fresh workspace,
+    and nothing timed out."""
+    _case("route: tagged logits, one workspace, varying T")
+    L = dev_layer("decode")
+    cfg = L.cfg
+    ws = moe.Workspace(40, cfg.k, cfg.E, cfg.D, 64, 0)
+    moe.moe_set_tuning("route_mfma", 0)
+    try:
+        for i, T in enumerate([3, 15, 1, 7, 2, 40, 5]):
+            xb = gen.activations(2, 0, 100 * i, T, cfg.D, cfg.x_dtype)
+            outs = []
+            for w in (ws, moe.Workspace(T, cfg.k, cfg.E, cfg.D, 64, 0)):
+                ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+                gates = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+                logits = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+                moe.moe_route(x_dev(xb, cfg.x_dtype), L.router, cfg.k, ids, gates, w, None,
+                              logits)
+                torch.cuda.synchronize()
+                assert w.timeouts() == 0
+                outs.append((ids.cpu(), gates.cpu(), logits.cpu()))
+            assert all(torch.equal(a, b) for a, b in zip(*outs)), T
+            xf = x_float(xb, cfg.x_dtype)
+            check_ids(O.router_logits(xf, L.lw.router, None), outs[0][0].numpy(), cfg.k)
+    finally:
+        moe.moe_set_tuning("route_mfma", 1)
+
+
 def test_route_x_zero_closed_form():
     _case("route x=0")
     L = dev_layer("tiny")
