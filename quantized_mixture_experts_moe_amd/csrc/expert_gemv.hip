@@ -85,9 +85,20 @@ __device__ __forceinline__ bool split_reduce(float (&v)[W], float *part, uint32_
   if (old != (uint32_t)(KS - 1)) return false;
 #pragma unroll
   for (int i = 0; i < W; ++i) v[i] = 0.0f;
-  for (int p = 0; p < KS; ++p)
+  // eight splits' partials in flight at a time, added in split order
+  for (int p0 = 0; p0 < KS; p0 += 8) {
+    float q[8][W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) v[i] += ld_dev(part + (p * W + i) * 64 + lane);
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        q[j][i] = p0 + j < KS ? ld_dev(part + ((p0 + j) * W + i) * 64 + lane) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (p0 + j < KS)
+#pragma unroll
+        for (int i = 0; i < W; ++i) v[i] += q[j][i];
+  }
   if (lane == 0) st_dev(counter, 0u);
   return true;
 }
