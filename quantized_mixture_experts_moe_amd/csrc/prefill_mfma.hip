@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256, 4) void glu_mfma_kernel(PrefillLaunch p) {
 }
 
 // ---------------------------------------------------------------- down
-constexpr int kRd = 3;    // LDS stages of the down ring (kRd - 1 groups in flight)
+constexpr int kRd = 2;    // LDS stages of the down ring (kRd - 1 groups in flight)
 constexpr int kDT = 4;    // 16-row output tiles per wave (a block covers 256 output rows)
 constexpr int kDRows = 16;  // group rows per down block (one matrix tile)
 
@@ -359,10 +359,10 @@ struct DownBuf {
 __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g, int nb, int m0,
                                           int nrow, int gbeg, int GH, float *dst, int row0,
                                           const int *s_row, const float *s_hs, DownBuf &b0,
-                                          DownBuf &b1, DownBuf &b2) {
+                                          DownBuf &b1) {
   // one LDS object per stage, so that a read of one stage does not wait for
   // the loads in flight into the others
-  auto buf = [&](int s) -> DownBuf & { return s == 0 ? b0 : s == 1 ? b1 : b2; };
+  auto buf = [&](int s) -> DownBuf & { return s == 0 ? b0 : b1; };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // hidden groups gbeg .. gbeg + GH - 1 of the expert (GHa in all)
@@ -458,11 +458,11 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   }
 }
 
-__global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
+__global__ __launch_bounds__(256, 4) void down_mfma_kernel(PrefillLaunch p) {
   __shared__ int s_row[kDRows];
   __shared__ float s_hs[kDRows * kMaxHGroups];
-  __shared__ DownBuf b0, b1, b2;
-  static_assert(kRd == 3, "one LDS object per stage");
+  __shared__ DownBuf b0, b1;
+  static_assert(kRd == 2, "one LDS object per stage");
   static_assert(kRows == 2 * kDRows, "two down row chunks per work-list item");
   // blocks: the shared expert's first, its hidden groups split sks ways (as
   // many groups per block as a routed expert has), then the work list's
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256, 3) void down_mfma_kernel(PrefillLaunch p) {
     s_hs[i] = p.hsum[hrow_off(p, s_row[m]) / 64 + gg];
   }
   __syncthreads();
-  down_body(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1, b2);
+  down_body(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1);
 }
 
 // four consecutive outputs per thread (16-byte loads of y), the k routed
