@@ -365,8 +365,9 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   auto buf = [&](int s) -> DownBuf & { return s == 0 ? b0 : b1; };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // hidden groups gbeg .. gbeg + GH - 1 of the expert (GHa in all)
-  const int D = p.D, F = g.F, GHa = F / 64;
+  // hidden groups gbeg .. gbeg + GH - 1 of the expert; s_hs holds their h
+  // sums, [row][group - gbeg]
+  const int D = p.D, F = g.F;
   const int col = lane & 15, kb = lane >> 4;
   const BlobLayout L = blob_layout(D, F);
   // this wave stages, per hidden group: plane wave % 3 of the 16 rows (two
@@ -423,7 +424,7 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
         for (int q = 0; q < 3; ++q) a_in[half][q] = B.pl[q][xslot(col, half * 4 + kb)];
       float hs[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hs[i] = s_hs[(kb * 4 + i) * GHa + gx];
+      for (int i = 0; i < 4; ++i) hs[i] = s_hs[(kb * 4 + i) * GH + (gx - gbeg)];
 #pragma unroll
       for (int j = 0; j < kDT; ++j) {
         // output tile j of this wave: rows 64 wave + 16 j + col
@@ -458,9 +459,11 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   }
 }
 
-__global__ __launch_bounds__(256, 4) void down_mfma_kernel(PrefillLaunch p) {
+__global__ __launch_bounds__(256, 5) void down_mfma_kernel(PrefillLaunch p) {
   __shared__ int s_row[kDRows];
-  __shared__ float s_hs[kDRows * kMaxHGroups];
+  // h sums of the block's own hidden groups, [row][group], sized at launch
+  // (static LDS of 30.8 KB plus these: five blocks per CU)
+  extern __shared__ float s_hs[];
   __shared__ DownBuf b0, b1;
   static_assert(kRd == 2, "one LDS object per stage");
   static_assert(kRows == 2 * kDRows, "two down row chunks per work-list item");
@@ -515,12 +518,13 @@ __global__ __launch_bounds__(256, 4) void down_mfma_kernel(PrefillLaunch p) {
   const int row0 = g.shared ? 0 : g.off;
   for (int i = threadIdx.x; i < kDRows; i += 256) s_row[i] = g.off + m0 + min(i, nrow - 1);
   __syncthreads();
-  for (int i = threadIdx.x; i < kDRows * GH; i += 256) {
-    const int m = i / GH, gg = i - m * GH;
-    s_hs[i] = p.hsum[hrow_off(p, s_row[m]) / 64 + gg];
+  const int GL = gend - gbeg;
+  for (int i = threadIdx.x; i < kDRows * GL; i += 256) {
+    const int m = i / GL, gg = i - m * GL;
+    s_hs[i] = p.hsum[hrow_off(p, s_row[m]) / 64 + gbeg + gg];
   }
   __syncthreads();
-  down_body(p, g, nb, m0, nrow, gbeg, gend - gbeg, dst, row0, s_row, s_hs, b0, b1);
+  down_body(p, g, nb, m0, nrow, gbeg, GL, dst, row0, s_row, s_hs, b0, b1);
 }
 
 // four consecutive outputs per thread (16-byte loads of y), the k routed
@@ -618,7 +622,10 @@ hipError_t launch_prefill_experts(const PrefillLaunch &p, hipStream_t s) {
   const int nb4 = (p.D + 255) / 256;  // 256 output rows per down block
   const int mch16 = (p.T + 15) / 16;  // 16-row chunks of the shared expert
   dim3 g2(grouped_blocks(max_items, 2 * nb4) + (p.sblobs ? grouped_blocks(p.sks * nb4, mch16) : 0));
-  hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), 0, s, q);
+  // h sums of a block's hidden groups: all of a routed expert's, or the
+  // largest of the shared expert's sks slices
+  const int gl = std::max(p.F / 64, p.sblobs ? (p.Fs / 64 + p.sks - 1) / p.sks : 0);
+  hipLaunchKernelGGL(down_mfma_kernel, g2, dim3(256), sizeof(float) * kDRows * gl, s, q);
   e = hipGetLastError();
   if (e != hipSuccess || p.skip_combine) return e;
   return launch_prefill_combine(p, s);
