@@ -448,12 +448,17 @@ __device__ __forceinline__ void down_body(const PrefillLaunch &p, const Group &g
   }
   // the stages past the end are still landing in LDS: let them finish
   stage_barrier<0>();
+  // the lane's column and row block, computed again rather than held
+  // through the loop (at five blocks per CU the two would be spilled)
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int col2 = ln & 15, kb2 = ln >> 4;
 #pragma unroll
   for (int j = 0; j < kDT; ++j) {
-    const int n = nb * 256 + wave * 64 + j * 16 + col;  // output row of this lane's column
+    const int n = nb * 256 + wave * 64 + j * 16 + col2;  // output row of this lane's column
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = kb * 4 + i;
+      const int m = kb2 * 4 + i;
       if (m < nrow && n < D) dst[(size_t)(row0 + m0 + m) * D + n] = (float)t[j][i];
     }
   }
